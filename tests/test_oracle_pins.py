@@ -1,0 +1,316 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+  * values derived by hand for tiny cases (the recurrence done on paper),
+  * closed forms (pure decay when beta = 0),
+  * textbook special cases written separately here (DeltaNet when every decay
+    is 1; the per-head scalar-gate recurrence  S <- a (I - b k k^T) S + b k v^T),
+  * invariants (write-then-read with unit keys, associative recall with
+    orthonormal keys, splitting a sequence and resuming from the state),
+  * two other formulations inside the oracle (chunked, brute force),
+  * the numeric claims of the pages about the 16-token exponent budget.
+
+A plausible slip in the oracle (decay applied after the write, to the columns
+instead of the rows, a dropped beta, o read from S instead of S^T, a sign) makes
+at least one of these fail.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_linear_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _np(x):
+    return x.detach().cpu().to(torch.float64).numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+
+
+def _args(x):
+    return [_np(t) for t in (x.q, x.k, x.v, x.g, x.beta)] + [x.cu_seqlens.cpu().numpy()]
+
+
+def _one(q, k, v, g, beta, S0=None):
+    """Pack a single sequence with a single head from per-token arrays."""
+    q = np.asarray(q, float)[:, None, :]
+    k = np.asarray(k, float)[:, None, :]
+    v = np.asarray(v, float)[:, None, :]
+    g = np.asarray(g, float)[:, None, :]
+    beta = np.asarray(beta, float)[:, None]
+    cu = np.array([0, q.shape[0]], np.int32)
+    S0 = None if S0 is None else np.asarray(S0, float)[None, None]
+    return oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+
+
+# ---------------------------------------------------------------- hand-derived values
+
+def test_hand_two_tokens():
+    # token 1: alpha = (1/2, 1), k = (1,0), v = (2,-1), beta = 1, q = (1,0), S0 = 0
+    #   S' = 0, r = 0, u = (2,-1), S = k u^T = [[2,-1],[0,0]], o1 = S^T q = (2,-1)
+    # token 2: alpha = (1/2, 1/4), k = (0.6,0.8), v = (1,3), beta = 1/2, q = (0,1)
+    #   S' = diag(alpha) S = [[1,-0.5],[0,0]]
+    #   r  = S'^T k = (0.6, -0.3);  u = 0.5 ((1,3) - r) = (0.2, 1.65)
+    #   S  = S' + k u^T = [[1.12, 0.49], [0.16, 1.32]];  o2 = S^T q = (0.16, 1.32)
+    o, S = _one(q=[[1, 0], [0, 1]], k=[[1, 0], [0.6, 0.8]], v=[[2, -1], [1, 3]],
+                g=[[math.log(0.5), 0.0], [math.log(0.5), math.log(0.25)]], beta=[1.0, 0.5])
+    np.testing.assert_allclose(o[:, 0], [[2, -1], [0.16, 1.32]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S[0, 0], [[1.12, 0.49], [0.16, 1.32]], rtol=0, atol=1e-14)
+
+
+def test_hand_one_token_with_initial_state():
+    # S0 = [[1,2],[3,4]], alpha = (1/2, 1), k = (0,1), v = (10,20), beta = 1/4, q = (1,1)
+    #   S' = [[0.5,1],[3,4]], r = S'^T k = (3,4), u = (1.75, 4)
+    #   S  = [[0.5,1],[4.75,8]], o = S^T q = (5.25, 9)
+    o, S = _one(q=[[1, 1]], k=[[0, 1]], v=[[10, 20]], g=[[math.log(0.5), 0.0]], beta=[0.25],
+                S0=[[1, 2], [3, 4]])
+    np.testing.assert_allclose(o[0, 0], [5.25, 9.0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S[0, 0], [[0.5, 1.0], [4.75, 8.0]], rtol=0, atol=1e-14)
+
+
+def test_hand_rectangular_state():
+    # dk = 3, dv = 1: the decay must act on the key rows of S (a column decay would
+    # not even have the right length).  S0 = (1,1,1)^T, alpha = (1, 1/2, 1/4),
+    # k = (0,0,1), v = 5, beta = 1, q = (1,1,1):
+    #   S' = (1, 0.5, 0.25), r = 0.25, u = 4.75, S = (1, 0.5, 5), o = 6.5
+    o, S = _one(q=[[1, 1, 1]], k=[[0, 0, 1]], v=[[5]], g=[[0.0, math.log(0.5), math.log(0.25)]], beta=[1.0],
+                S0=[[1], [1], [1]])
+    assert abs(o[0, 0, 0] - 6.5) < 1e-14
+    np.testing.assert_allclose(S[0, 0, :, 0], [1, 0.5, 5], rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- closed forms and special cases
+
+def test_pure_decay_closed_form():
+    # beta = 0: S_T = diag(exp(sum g)) S0 and o_t = S0^T (q_t * exp(G_t))
+    x = inputs.make_prefill_inputs([23, 0, 9], 3, 8, 5, dtype=torch.float32, gate="pages", init_state=True, seed=3)
+    q, k, v, g, _, cu = _args(x)
+    beta = np.zeros((x.T_total, 3))
+    S0 = _np(x.initial_state)
+    o, Sf = oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+    for n in range(3):
+        a, b = cu[n], cu[n + 1]
+        for h in range(3):
+            G = np.cumsum(g[a:b, h], axis=0)
+            tot = G[-1] if b > a else np.zeros(8)
+            np.testing.assert_allclose(Sf[n, h], np.exp(tot)[:, None] * S0[n, h], rtol=1e-13, atol=1e-300)
+            ref_o = (q[a:b, h] * np.exp(G)) @ S0[n, h]
+            np.testing.assert_allclose(o[a:b, h], ref_o, rtol=1e-12, atol=1e-15)
+
+
+def _deltanet(q, k, v, beta, S0):
+    """Textbook DeltaNet: S <- S + beta k (v - S^T k)^T, o = S^T q (no decay)."""
+    S = S0.copy()
+    o = np.zeros((q.shape[0], v.shape[1]))
+    for t in range(q.shape[0]):
+        S = S + beta[t] * np.outer(k[t], v[t] - S.T @ k[t])
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def test_no_decay_is_deltanet():
+    x = inputs.make_prefill_inputs([40, 17], 2, 12, 7, dtype=torch.float32, init_state=True, seed=4)
+    q, k, v, _, beta, cu = _args(x)
+    g = np.zeros_like(q)
+    S0 = _np(x.initial_state)
+    o, Sf = oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+    for n in range(2):
+        a, b = cu[n], cu[n + 1]
+        for h in range(2):
+            ro, rS = _deltanet(q[a:b, h], k[a:b, h], v[a:b, h], beta[a:b, h], S0[n, h])
+            np.testing.assert_allclose(o[a:b, h], ro, rtol=0, atol=1e-13 * np.abs(ro).max())
+            np.testing.assert_allclose(Sf[n, h], rS, rtol=0, atol=1e-13 * np.abs(rS).max())
+
+
+def _scalar_gate(q, k, v, a, beta, S0):
+    """Per-head scalar gate:  S <- a_t (I - beta_t k_t k_t^T) S + beta_t k_t v_t^T,  o = S^T q."""
+    S = S0.copy()
+    d = k.shape[1]
+    o = np.zeros((q.shape[0], v.shape[1]))
+    for t in range(q.shape[0]):
+        S = a[t] * (np.eye(d) - beta[t] * np.outer(k[t], k[t])) @ S + beta[t] * np.outer(k[t], v[t])
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def test_scalar_gate_matches_per_head_recurrence():
+    x = inputs.make_prefill_inputs([50], 3, 16, 8, dtype=torch.float32, init_state=True, seed=5)
+    q, k, v, g, beta, cu = _args(x)
+    g = np.repeat(g[:, :, :1], 16, axis=2)  # one log-decay per (token, head), on every channel
+    S0 = _np(x.initial_state)
+    o, Sf = oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+    for h in range(3):
+        ro, rS = _scalar_gate(q[:, h], k[:, h], v[:, h], np.exp(g[:, h, 0]), beta[:, h], S0[0, h])
+        np.testing.assert_allclose(o[:, h], ro, rtol=0, atol=1e-13 * np.abs(ro).max())
+        np.testing.assert_allclose(Sf[0, h], rS, rtol=0, atol=1e-13 * np.abs(rS).max())
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("gate", ["amin", "pages"])
+def test_write_then_read_returns_value(gate):
+    # unit k, beta = 1, any decay: S_t^T k_t = v_t, so querying with q_t = k_t returns v_t
+    x = inputs.make_prefill_inputs([64, 33], 2, 16, 9, dtype=torch.float32, gate=gate, init_state=True, seed=6)
+    q, k, v, g, _, cu = _args(x)
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = np.ones((x.T_total, 2))
+    o, _ = oracle.recurrent(k, k, v, g, beta, cu, initial_state=_np(x.initial_state))
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-13)
+    o32, _ = oracle.recurrent(k, k, v, g, beta, cu, initial_state=_np(x.initial_state), dtype=np.float32)
+    np.testing.assert_allclose(o32, v, rtol=0, atol=1e-5)
+
+
+def test_associative_recall_orthonormal_keys():
+    # no decay, beta = 1, keys drawn from an orthonormal basis: a query e_i returns the
+    # last value written under e_i (zero if never written)
+    d, dv, T = 8, 5, 40
+    rng = np.random.default_rng(7)
+    basis, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    idx = rng.integers(0, d, T)
+    k = basis[idx]
+    v = rng.standard_normal((T, dv))
+    qi = rng.integers(0, d, T)
+    q = basis[qi]
+    o, _ = _one(q, k, v, np.zeros((T, d)), np.ones(T))
+    for t in range(T):
+        writes = [s for s in range(t + 1) if idx[s] == qi[t]]
+        expect = v[writes[-1]] if writes else np.zeros(dv)
+        np.testing.assert_allclose(o[t, 0], expect, rtol=0, atol=1e-12)
+
+
+def test_split_and_resume_equals_whole():
+    x = inputs.make_prefill_inputs([300], 2, 16, 16, dtype=torch.float32, init_state=True, seed=8)
+    q, k, v, g, beta, cu = _args(x)
+    S0 = _np(x.initial_state)
+    o, Sf = oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+    for a in (1, 64, 77, 299):
+        c1 = np.array([0, a], np.int32)
+        c2 = np.array([0, 300 - a], np.int32)
+        o1, S1 = oracle.recurrent(q[:a], k[:a], v[:a], g[:a], beta[:a], c1, initial_state=S0)
+        o2, S2 = oracle.recurrent(q[a:], k[a:], v[a:], g[a:], beta[a:], c2, initial_state=S1)
+        np.testing.assert_allclose(np.concatenate([o1, o2]), o, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(S2, Sf, rtol=0, atol=1e-14)
+
+
+def test_empty_sequences_keep_initial_state():
+    x = inputs.make_prefill_inputs([0, 5, 0], 2, 4, 3, dtype=torch.float32, init_state=True, seed=9)
+    q, k, v, g, beta, cu = _args(x)
+    S0 = _np(x.initial_state)
+    _, Sf = oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+    np.testing.assert_array_equal(Sf[0], S0[0])
+    np.testing.assert_array_equal(Sf[2], S0[2])
+    _, Sz = oracle.recurrent(q, k, v, g, beta, cu)
+    assert not Sz[0].any() and not Sz[2].any()
+
+
+# ---------------------------------------------------------------- other formulations
+
+@pytest.mark.parametrize("gate", ["amin", "pages"])
+@pytest.mark.parametrize("chunk", [1, 16, 64, 100, 1000])
+def test_chunked_equals_recurrent(gate, chunk):
+    x = inputs.make_prefill_inputs([130, 0, 64, 1, 65], 2, 16, 8, dtype=torch.float32, gate=gate,
+                                   init_state=True, seed=10)
+    a = _args(x)
+    S0 = _np(x.initial_state)
+    o1, S1 = oracle.recurrent(*a, initial_state=S0)
+    o2, S2 = oracle.chunked(*a, initial_state=S0, chunk=chunk)
+    assert oracle.rel_err(o2, o1) < 1e-12
+    assert oracle.rel_err(S2, S1) < 1e-12
+
+
+def test_bruteforce_equals_recurrent():
+    x = inputs.make_prefill_inputs([8, 1, 0, 5], 3, 6, 4, dtype=torch.float32, gate="pages", init_state=True,
+                                   seed=11)
+    a = _args(x)
+    S0 = _np(x.initial_state)
+    o1, S1 = oracle.recurrent(*a, initial_state=S0)
+    o3, S3 = oracle.bruteforce(*a, initial_state=S0)
+    assert oracle.rel_err(o3, o1) < 1e-12
+    assert oracle.rel_err(S3, S1) < 1e-12
+    o4, S4 = oracle.bruteforce(*a)
+    o5, S5 = oracle.recurrent(*a)
+    assert oracle.rel_err(o4, o5) < 1e-12 and oracle.rel_err(S4, S5) < 1e-12
+
+
+def test_f32_instance_within_rounding_of_f64():
+    x = inputs.make_prefill_inputs([256], 2, 64, 64, dtype=torch.float32, init_state=True, seed=12)
+    a = _args(x)
+    S0 = _np(x.initial_state)
+    o64, S64 = oracle.recurrent(*a, initial_state=S0)
+    o32, S32 = oracle.recurrent(*a, initial_state=S0, dtype=np.float32)
+    assert oracle.rel_err(o32, o64) < 2e-6
+    assert oracle.rel_err(S32, S64) < 2e-6
+
+
+def test_final_state_may_alias_initial_state():
+    # the library allows final_state to alias initial_state; the oracle must too
+    x = inputs.make_prefill_inputs([20, 7], 2, 8, 8, dtype=torch.float32, init_state=True, seed=13)
+    q, k, v, g, beta, cu = [np.ascontiguousarray(t) for t in _args(x)]
+    S0 = np.ascontiguousarray(_np(x.initial_state))
+    o_ref, S_ref = oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+    lib = oracle._load()
+    S = S0.copy()
+    o = np.zeros_like(o_ref)
+    p = oracle._ptr
+    rc = lib.gdn_oracle_recurrent_f64(p(q), p(k), p(v), p(g), p(beta), p(cu), 2, 2, 8, 8, p(S), p(o), p(S), 2)
+    assert rc == 0
+    np.testing.assert_array_equal(S, S_ref)
+    np.testing.assert_array_equal(o, o_ref)
+
+
+# ---------------------------------------------------------------- the pages' exponent budget
+
+def _sig2(x):
+    return float(f"{x:.1e}")
+
+
+def test_page_constants():
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        c = json.load(f)
+    g_min, n = c["g_min"]["value"], c["tile_tokens"]["value"]
+    assert g_min * n == c["worst_tile_log_decay"]["value"]
+    assert _sig2(math.exp(-80.0)) == c["exp_minus_80"]["value"]
+    assert _sig2(math.exp(80.0)) == c["exp_plus_80"]["value"]
+    assert _sig2(float(np.finfo(np.float32).tiny)) == c["min_normal"]["value"]
+    assert _sig2(float(torch.finfo(torch.bfloat16).tiny)) == c["min_normal"]["value"]
+    assert _sig2(float(np.finfo(np.float32).max)) == c["max_finite"]["value"]
+    assert _sig2(float(torch.finfo(torch.bfloat16).max)) == c["max_finite"]["value"]
+    assert round(math.exp(g_min), 4) == c["per_step_decay_low"]["value"]
+    # the claim itself: both the tile's decay and its reciprocal are normal numbers
+    for dt in (torch.float32, torch.bfloat16):
+        lo = torch.exp(torch.tensor(-80.0)).to(dt)
+        hi = torch.exp(torch.tensor(80.0)).to(dt)
+        assert float(lo) >= torch.finfo(dt).tiny and torch.isfinite(hi)
+
+
+def test_single_reference_overflows_beyond_the_tile_budget():
+    # with g = -5 on every token, a 64-token window needs exp(320): not finite in fp32,
+    # while a 16-token window needs exp(80): finite.  This is why a chunk whose total
+    # log-decay passes -80 is split into 16-token sub-tiles.
+    with np.errstate(over="ignore"):
+        assert not np.isfinite(np.exp(np.float32(5.0 * 64)))
+    assert np.isfinite(np.exp(np.float32(5.0 * 16)))
+    assert np.exp(np.float32(-5.0 * 16)) >= np.finfo(np.float32).tiny
+
+
+def test_generator_gate_ranges():
+    x = inputs.make_prefill_inputs([4096], 2, 64, 8, dtype=torch.float32, gate="pages", seed=14)
+    assert float(x.g.min()) >= -5.0 and float(x.g.max()) <= 0.0
+    y = inputs.make_prefill_inputs([4096], 2, 64, 8, dtype=torch.float32, gate="amin", a_min=0.9, seed=14)
+    assert float(y.g.min()) >= math.log(0.9) - 1e-7 and float(y.g.max()) < 0.0
+    b = y.beta
+    assert float(b.min()) > 0.0 and float(b.max()) < 1.0
+
+
+def test_generator_is_deterministic():
+    a = inputs.make_varlen64_inputs(seed=0, H=1, dk=8, dv=8)
+    b = inputs.make_varlen64_inputs(seed=0, H=1, dk=8, dv=8)
+    assert a.lengths == b.lengths and len(a.lengths) == 64
+    assert all(512 <= n <= 16384 for n in a.lengths)
+    for t in ("q", "k", "v", "g", "beta", "initial_state"):
+        assert torch.equal(getattr(a, t), getattr(b, t))
