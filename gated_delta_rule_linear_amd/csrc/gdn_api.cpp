@@ -1,0 +1,176 @@
+// libgdn C-ABI: argument validation, status codes and dispatch to the kernels.
+// Declarations and the contract of every entry point are in include/gdn.h.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "gdn_kernels.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool supported_d(int32_t d) { return d == 64 || d == 128; }
+bool validate_mode() {
+    const char* e = std::getenv("GDN_VALIDATE");
+    return e && e[0] == '1';
+}
+
+// Host-side check of cu_seqlens and of the log-decay domain; synchronous.
+int32_t validate_inputs(const int32_t* cu_dev, int32_t num_seqs, int64_t T_total, const float* g_dev, int64_t ng,
+                        hipStream_t s) {
+    std::vector<int32_t> cu((size_t)num_seqs + 1);
+    if (hipMemcpyAsync(cu.data(), cu_dev, sizeof(int32_t) * cu.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return GDN_ERR_HIP;
+    std::vector<float> g((size_t)ng);
+    if (ng > 0 && hipMemcpyAsync(g.data(), g_dev, sizeof(float) * g.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
+    if (cu[0] != 0 || cu[(size_t)num_seqs] != T_total) return GDN_ERR_DOMAIN;
+    for (int32_t n = 0; n < num_seqs; ++n)
+        if (cu[(size_t)n + 1] < cu[(size_t)n]) return GDN_ERR_DOMAIN;
+    for (float x : g)
+        if (!(x >= -5.0f && x <= 0.0f)) return GDN_ERR_DOMAIN;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(int32_t status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, negative size, short workspace)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported configuration (d_k and d_v must be 64 or 128; dtype f32 or bf16)";
+        case GDN_ERR_DOMAIN: return "input outside the domain (g not in [-5, 0] or malformed cu_seqlens)";
+        case GDN_ERR_OOM: return "device allocation failed";
+        case GDN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t gdn_state_bytes(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v) {
+    if (num_seqs < 0 || H < 0 || d_k < 0 || d_v < 0) return 0;
+    return (size_t)num_seqs * (size_t)H * (size_t)d_k * (size_t)d_v * sizeof(float);
+}
+
+int32_t gdn_state_alloc(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, float** out, void* stream) {
+    if (!out || num_seqs < 0 || H < 1) return GDN_ERR_INVALID_ARG;
+    if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
+    *out = nullptr;
+    const size_t bytes = gdn_state_bytes(num_seqs, H, d_k, d_v);
+    if (bytes == 0) return GDN_OK;
+    if (num_seqs > (int64_t)(SIZE_MAX / 4 / (size_t)H / (size_t)d_k / (size_t)d_v)) return GDN_ERR_OOM;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* p = nullptr;
+    if (hipMallocAsync(&p, bytes, s) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return GDN_ERR_OOM;
+    }
+    if (hipMemsetAsync(p, 0, bytes, s) != hipSuccess) {
+        (void)hipFreeAsync(p, s);
+        return GDN_ERR_HIP;
+    }
+    *out = static_cast<float*>(p);
+    return GDN_OK;
+}
+
+int32_t gdn_state_free(float* state, void* stream) {
+    if (!state) return GDN_OK;
+    return hipFreeAsync(state, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v) {
+    (void)T_total;
+    (void)num_seqs;
+    (void)H;
+    (void)d_k;
+    (void)d_v;
+    return 0;
+}
+
+int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total, const float* initial_state,
+                    float* final_state, void* o, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs < 0 || T_total < 0 || H < 1) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (T_total > 0 && num_seqs == 0) return GDN_ERR_INVALID_ARG;
+    if (num_seqs == 0) return GDN_OK;
+    if (!cu_seqlens || !aligned(cu_seqlens, 4)) return GDN_ERR_INVALID_ARG;
+    if (T_total > 0) {
+        const void* ptrs16[] = {q, k, v, g, o};
+        for (const void* p : ptrs16)
+            if (!p || !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+        if (!beta || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
+    }
+    if (initial_state && !aligned(initial_state, 16)) return GDN_ERR_INVALID_ARG;
+    if (final_state && !aligned(final_state, 16)) return GDN_ERR_INVALID_ARG;
+    const size_t need = gdn_prefill_workspace_bytes(T_total, num_seqs, H, d_k, d_v);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return GDN_ERR_INVALID_ARG;
+    if ((int64_t)num_seqs * H > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validate_mode()) {
+        const int32_t st = validate_inputs(cu_seqlens, num_seqs, T_total, g, T_total * H * d_k, s);
+        if (st != GDN_OK) return st;
+    }
+    gdn::PrefillLaunch p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.cu_seqlens = cu_seqlens;
+    p.initial_state = initial_state;
+    p.final_state = final_state;
+    p.o = o;
+    p.num_seqs = num_seqs;
+    p.H = H;
+    p.dk = d_k;
+    p.dv = d_v;
+    p.bf16 = dtype == GDN_BF16;
+    return gdn::launch_prefill(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
+                   void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void* stream) {
+    if (N < 0 || H < 1) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (N == 0) return GDN_OK;
+    const void* ptrs16[] = {q, k, v, g, o, state};
+    for (const void* p : ptrs16)
+        if (!p || !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    if (!beta || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
+    if ((int64_t)N * H > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validate_mode()) {
+        std::vector<float> gh((size_t)N * H * d_k);
+        if (hipMemcpyAsync(gh.data(), g, sizeof(float) * gh.size(), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return GDN_ERR_HIP;
+        for (float x : gh)
+            if (!(x >= -5.0f && x <= 0.0f)) return GDN_ERR_DOMAIN;
+    }
+    gdn::DecodeLaunch p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.state = state;
+    p.o = o;
+    p.N = N;
+    p.H = H;
+    p.dk = d_k;
+    p.dv = d_v;
+    p.bf16 = dtype == GDN_BF16;
+    return gdn::launch_decode(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/* gdn.h — C-ABI of libgdn: the bounded-decay gated delta rule on MI355X (gfx950).
+ *
+ * The layer.  Per sequence and head, a fixed-size state S (d_k x d_v, fp32) is
+ * updated once per token, and each token reads the updated state:
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + beta_t k_t (v_t - (diag(alpha_t) S_{t-1})^T k_t)^T
+ *     o_t = S_t^T q_t,            alpha_t = exp(g_t)   (one value per key channel)
+ *
+ * i.e. the state is decayed first, then the value the decayed state returns for
+ * k_t is replaced by v_t in proportion beta_t.  This is the fixed-size state
+ * with correct-on-write updates and a position-dependent decay gate of
+ * "How to Think About Trillion-Parameter Sparse Multimodal LLMs", section 2.2;
+ * the log-decay g is the lower-bounded quantity of "Trillion-Parameter MoE
+ * Multimodal LLMs: How to Evaluate the New Generation", section 3.1, eq. 1
+ * (g = g_min * sigmoid(.), g_min = -5), so its domain is [-5, 0].  No scale is
+ * applied to q.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device pointers must address memory of the current
+ *     HIP device; pointers named as host pointers must address host memory.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it and the call returns without waiting; results are ready
+ *     when the stream reaches that point.  The library keeps no state between
+ *     calls, frees no caller memory and prints nothing.
+ *   - Every call returns a gdn_status.  Argument errors are reported before any
+ *     memory is touched or any work is enqueued.  GDN_ERR_HIP means a HIP call
+ *     (allocation aside) or a kernel launch failed; a fault inside a kernel
+ *     surfaces at the caller's next synchronisation, as for any HIP kernel.
+ *   - Inputs with NaN or Inf are not masked: they propagate into the outputs.
+ *   - Element types: q, k, v, o share one dtype (GDN_F32 or GDN_BF16); g, beta
+ *     and all states are always fp32.  With GDN_BF16 the contractions run on
+ *     bf16 matrix cores with fp32 accumulation and an fp32 state; with GDN_F32
+ *     all arithmetic is fp32.  fp32 -> bf16 conversions round to nearest even.
+ *   - Supported sizes: d_k and d_v each 64 or 128; H >= 1.
+ *   - Alignment: q, k, v, o, g, states and the workspace must be 16-byte
+ *     aligned; beta and cu_seqlens 4-byte aligned.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, short workspace */
+    GDN_ERR_UNSUPPORTED = 2, /* d_k or d_v not in {64, 128}, unknown dtype */
+    GDN_ERR_DOMAIN = 3,      /* validation mode only: g outside [-5, 0], bad cu_seqlens */
+    GDN_ERR_OOM = 4,         /* device allocation failed */
+    GDN_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Static English description of a status code (never NULL). */
+const char* gdn_status_string(int32_t status);
+
+/* Bytes of a state tensor [num_seqs, H, d_k, d_v] fp32 (d_v fastest); 0 for
+ * negative arguments. */
+size_t gdn_state_bytes(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v);
+
+/* Allocates a zero-filled state tensor [num_seqs, H, d_k, d_v] fp32 on the
+ * current device, ordered on `stream` (the zero fill is enqueued there).
+ * *out receives the device pointer; the caller releases it with
+ * gdn_state_free.  GDN_ERR_OOM when the device cannot provide the memory.
+ * The fixed-size state replaces a key-value cache: its size does not depend
+ * on the sequence length (section 5.3 of "Trillion-Parameter MoE Multimodal
+ * LLMs: How to Evaluate the New Generation"). */
+int32_t gdn_state_alloc(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, float** out, void* stream);
+
+/* Releases memory from gdn_state_alloc, ordered on `stream`.  NULL is a no-op. */
+int32_t gdn_state_free(float* state, void* stream);
+
+/* Device scratch bytes gdn_prefill needs for these sizes (may be 0).  The
+ * bound depends only on the arguments, never on the lengths inside
+ * cu_seqlens, so no device-to-host copy is needed to size it. */
+size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v);
+
+/* Chunked prefill over packed variable-length sequences.
+ *
+ *   q, k        device, [T_total, H, d_k], dtype
+ *   v           device, [T_total, H, d_v], dtype
+ *   g           device, [T_total, H, d_k] fp32, log-decay in [-5, 0]
+ *   beta        device, [T_total, H] fp32
+ *   cu_seqlens  device, int32 [num_seqs + 1]: sequence n is tokens
+ *               cu_seqlens[n] .. cu_seqlens[n+1]-1; cu_seqlens[0] = 0,
+ *               non-decreasing, cu_seqlens[num_seqs] = T_total.  Zero-length
+ *               sequences are allowed (their final state is their initial
+ *               state).  The contents are trusted unless the environment
+ *               variable GDN_VALIDATE=1 is set, which copies them to the host
+ *               (and g, to range-check it) and returns GDN_ERR_DOMAIN on a
+ *               violation.
+ *   initial_state  device, [num_seqs, H, d_k, d_v] fp32, or NULL for zeros.
+ *   final_state    device, [num_seqs, H, d_k, d_v] fp32, or NULL to skip;
+ *                  may be the same pointer as initial_state (updated in place).
+ *   o           device, [T_total, H, d_v], dtype; written for every token.
+ *   workspace   device scratch of at least
+ *               gdn_prefill_workspace_bytes(T_total, num_seqs, H, d_k, d_v)
+ *               bytes (may be NULL when that is 0).  Owned by the caller; its
+ *               contents on entry are ignored and on return are unspecified.
+ *               Two calls in flight at once need two workspaces.
+ *
+ * Method: each sequence is cut into 64-token chunks.  Inside a chunk the decay
+ * is carried as a local cumulative log-decay (the cumulative decay factor of
+ * "Architecture Evolution and Training Engineering for Trillion-Scale Sparse
+ * Multimodal Models", section 3.2), the causal intra-chunk products run as
+ * dense matrix-core tiles, and chunks are linked through the carried state.
+ * Results agree with the token-by-token recurrence up to rounding. */
+int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
+                    const float* initial_state, float* final_state, void* o,
+                    int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step: one new token for each of N sequences, state updated in
+ * place (the recurrent form of "How to Think About Trillion-Parameter Sparse
+ * Multimodal LLMs", section 2.2, whose inference cost does not grow with the
+ * context).
+ *
+ *   q, k   device, [N, H, d_k], dtype        v, o   device, [N, H, d_v], dtype
+ *   g      device, [N, H, d_k] fp32          beta   device, [N, H] fp32
+ *   state  device, [N, H, d_k, d_v] fp32, read and overwritten in place.
+ * N = 0 is a no-op.  A decode step equals a one-token gdn_prefill from the
+ * same state, up to rounding. */
+int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                   float* state, void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,86 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every entry
+point include/gdn.h declares, and rejects bad arguments with the documented
+status codes before touching any memory or the device."""
+
+import ctypes
+
+import pytest
+
+import gated_delta_rule_linear_amd as gdn
+
+OK, INVALID, UNSUPPORTED, DOMAIN, OOM, HIPERR = range(6)
+BAD = ctypes.c_void_p(0x1001)  # misaligned; never dereferenced because validation rejects it first
+NUL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdn.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = gdn.exported_symbols_in_header()
+    assert set(names) == {"gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free",
+                          "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in range(6):
+        s = gdn.gdn_status_string(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert gdn.gdn_status_string(99) == "unknown status"
+
+
+def test_state_bytes():
+    assert gdn.gdn_state_bytes(512, 32, 128, 128) == 512 * 32 * 128 * 128 * 4
+    assert gdn.gdn_state_bytes(0, 32, 128, 128) == 0
+    assert gdn.gdn_state_bytes(-1, 32, 128, 128) == 0
+
+
+def _prefill(lib, q=NUL, cu=NUL, n=1, T=10, H=4, dk=64, dv=64, dt=1, o=NUL, S0=NUL, Sf=NUL, ws=NUL, wsb=0):
+    return lib.gdn_prefill(q, q, q, q, q, cu, n, T, S0, Sf, o, H, dk, dv, dt, ws, wsb, None)
+
+
+def test_prefill_argument_errors(lib):
+    assert _prefill(lib) == INVALID                       # null pointers with T > 0
+    assert _prefill(lib, dk=96) == UNSUPPORTED
+    assert _prefill(lib, dv=32) == UNSUPPORTED
+    assert _prefill(lib, dt=7) == UNSUPPORTED
+    assert _prefill(lib, n=-1) == INVALID
+    assert _prefill(lib, T=-5) == INVALID
+    assert _prefill(lib, H=0) == INVALID
+    assert _prefill(lib, n=0, T=3) == INVALID              # tokens but no sequence
+    assert _prefill(lib, q=BAD, cu=BAD) == INVALID         # misaligned
+    assert _prefill(lib, n=0, T=0) == OK                   # nothing to do, nothing touched
+
+
+def test_decode_argument_errors(lib):
+    def dec(p=NUL, N=4, H=2, dk=128, dv=128, dt=1):
+        return lib.gdn_decode(p, p, p, p, p, p, p, N, H, dk, dv, dt, None)
+    assert dec() == INVALID
+    assert dec(dk=100) == UNSUPPORTED
+    assert dec(dt=3) == UNSUPPORTED
+    assert dec(N=-1) == INVALID
+    assert dec(H=0) == INVALID
+    assert dec(p=BAD) == INVALID
+    assert dec(N=0) == OK
+
+
+def test_state_alloc_argument_errors(lib):
+    out = ctypes.c_void_p()
+    assert lib.gdn_state_alloc(4, 2, 64, 64, None, None) == INVALID
+    assert lib.gdn_state_alloc(4, 2, 48, 64, ctypes.byref(out), None) == UNSUPPORTED
+    assert lib.gdn_state_alloc(-1, 2, 64, 64, ctypes.byref(out), None) == INVALID
+    assert lib.gdn_state_alloc(0, 2, 64, 64, ctypes.byref(out), None) == OK and not out.value
+    assert lib.gdn_state_free(None, None) == OK
+
+
+def test_workspace_bound_needs_no_lengths():
+    # the bound is a function of the arguments alone
+    a = gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128)
+    b = gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128)
+    assert a == b and a >= 0
