@@ -1,0 +1,203 @@
+"""Throughput of the gated delta rule on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one gdn_prefill call over the prefill workload: one sequence of
+65,536 tokens, 32 heads, d_k = d_v = 128, bf16 q/k/v, fp32 gates
+(alpha = 0.9 + 0.1 sigmoid(N(0,1))), zero initial state, final state written.
+W untimed steps, then exactly K steps bracketed by device synchronisation and
+timed with HIP events on the stream the kernels run on.  `value` is tokens per
+second of that workload.
+
+The decode step (512 sequences x 32 heads, one token each, fp32 state updated
+in place) is timed in the same run over K calls and reported under "decode"
+as achieved HBM bandwidth.
+
+"roofline" prices the prefill launch against MI355X's 8 TB/s HBM with the
+algorithmic bytes of the layer (q, k, v, o in bf16, g and beta in fp32, the
+final state); "cpu_baseline" is the fp32 oracle on the host cores over a
+bounded prefix of the same workload.  One JSON line is printed.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (H=32,d=128,T=64K bf16) + decode HBM GB/s; % of roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def prefill_bytes(T_tokens: int, H: int, dk: int, dv: int, n_seqs: int, elt: int = 2, init_state: bool = False):
+    """Algorithmic HBM bytes of one prefill launch: every input read once, every output written once."""
+    per_head_token = elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv
+    states = n_seqs * H * dk * dv * 4 * (2 if init_state else 1)
+    return T_tokens * H * per_head_token + states
+
+
+def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int = 2):
+    """Algorithmic HBM bytes of one decode launch: state read and written, token vectors read, o written."""
+    per = 8 * dk * dv + elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv
+    return N * H * per
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_linear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_loop(fn, steps: int, warmup: int, stream):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per call
+
+
+def cpu_baseline(x, tokens: int):
+    """fp32 oracle on the host over the first `tokens` tokens of every head."""
+    import oracle
+
+    oracle.build(force=False)
+    H = x.q.shape[1]
+    sl = lambda t: t[:tokens].to("cpu", torch.float32).numpy()
+    args = [sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), np.array([0, tokens], np.int32)]
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    threads = max(1, min(os.cpu_count() or 1, H, share))
+    t0 = time.perf_counter()
+    oracle.recurrent(*args, dtype=np.float32, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {tokens} tokens of the 65536-token sequence, all {H} heads, fp32 sequential "
+                      f"recurrence, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
+              f"(asked for --gpus {args.gpus}); sharding across GPUs is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import gated_delta_rule_linear_amd as gdn
+    from gated_delta_rule_linear_amd import inputs
+
+    gdn.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- prefill workload
+    T, H, d = 65536, 32, 128
+    x = inputs.make_workload("prefill_64k", seed=0, device=dev)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+
+    def step():
+        gdn.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, final_state=S, o=o, stream=stream)
+
+    ms = time_loop(step, args.steps, args.warmup, stream)
+    tokens_per_s = T / (ms / 1e3)
+    pbytes = prefill_bytes(T, H, d, d, 1)
+    achieved = pbytes / (ms / 1e3) / 1e9
+
+    # sampled parity on the timed inputs: head 0, first 2048 tokens
+    import oracle
+
+    tk = 2048
+    ro, _ = oracle.recurrent(*(t[:tk, :1].to("cpu", torch.float64).numpy() for t in (x.q, x.k, x.v, x.g)),
+                             x.beta[:tk, :1].to("cpu", torch.float64).numpy(), np.array([0, tk], np.int32))
+    parity = oracle.rel_err(o[:tk, :1].to("cpu", torch.float64).numpy(), ro)
+
+    # ---- decode workload
+    N, Hd = 512, 32
+    S0, draws = inputs.make_decode_steps(N, Hd, d, d, max(1, min(args.steps + args.warmup, 32)),
+                                         dtype=torch.bfloat16, seed=0, device=dev)
+    state = S0.contiguous()
+    od = torch.empty((N, Hd, d), dtype=torch.bfloat16, device=dev)
+    it = [0]
+
+    def dstep():
+        dr = draws[it[0] % len(draws)]
+        it[0] += 1
+        gdn.gdn_decode(dr.q, dr.k, dr.v, dr.g, dr.beta, state, o=od, stream=stream)
+
+    dms = time_loop(dstep, args.steps, args.warmup, stream)
+    dbytes = decode_bytes(N, Hd, d, d)
+    dgbs = dbytes / (dms / 1e3) / 1e9
+
+    traffic = measured_traffic("prefill")
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_64k", "num_seqs": 1, "T": T, "H": H, "d_k": d, "d_v": d,
+                   "gates": "alpha=0.9+0.1*sigmoid(N(0,1)) per key channel", "initial_state": "zero",
+                   "chunk": 64},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "prefill_seq_kernel<bf16,128,128>", "algorithmic_bytes_per_launch": pbytes},
+        "decode": {"workload": "decode_512x32", "N": N, "H": Hd, "d_k": d, "d_v": d, "ms_per_step": dms,
+                   "tokens_per_s": N / (dms / 1e3), "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": dgbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": dbytes,
+                   "traffic": measured_traffic("decode")},
+        "parity": {"prefill_o_rel_err_head0_first2048": parity},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(x, min(args.cpu_tokens, T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

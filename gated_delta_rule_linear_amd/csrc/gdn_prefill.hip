@@ -1,8 +1,9 @@
 // Chunked prefill of the gated delta rule on gfx950.
 //
-// One workgroup (4 waves) owns one (sequence, head) and walks its 64-token
-// chunks in order, carrying the fp32 state S (d_k x d_v) in registers: wave w
-// owns state columns [w*dv/4, (w+1)*dv/4).  Per chunk of L <= 64 tokens:
+// One workgroup owns one (sequence, head) and walks its 64-token chunks in
+// order, carrying the fp32 state S (d_k x d_v) in registers.  The workgroup has
+// d_v / 16 waves; wave w owns the 16 state columns [16w, 16w + 16).
+// Per chunk of L <= 64 tokens:
 //
 //  1. Local cumulative log-decay G_t = sum_{r<=t} g_r (per key channel),
 //     restarted at every chunk, so it never drifts towards underflow over a
@@ -15,25 +16,42 @@
 //     "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate the New
 //     Generation", section 3.1, is that with g >= -5 a 16-token window keeps
 //     both factors inside the normal fp32/bf16 range (e^-80 .. e^80).  Here:
-//       - if every G of the chunk lies in [-40, 40], one reference point (the
-//         chunk start) serves all 64 tokens: q~ = q e^G, k~ = k e^G,
-//         k^ = k e^-G, and every factor is inside e^-40 .. e^40;
+//       - if the chunk's total log-decay is >= -40 on every channel, one
+//         reference point (the chunk start) serves all 64 tokens:
+//         q~ = q e^G, k~ = k e^G, k^ = k e^-G, all factors within e^+-40;
 //       - otherwise each 16-token row block I uses its own reference m_I
-//         (G at the block's middle row): row factors e^(G_t - m_I) and
-//         column factors e^(m_I - G_s) stay inside e^-40 .. e^40 on the
-//         diagonal block and are <= 1 off it.
+//         (G at the block's middle row): row factors e^(G_t - m_I) and column
+//         factors e^(m_I - G_s) stay within e^+-40 on the diagonal block and
+//         are <= 1 off it.
 //     Either way every causal tile, the diagonal ones included, is a dense
 //     matrix-core product (section 3 of "How to Think About Trillion-Parameter
 //     Sparse Multimodal LLMs").
-//  3. Gram tiles on MFMA: A = strict_lower(diag(beta) K~ K^T), P = lower(Q~ K^T).
+//  3. Gram tiles on MFMA, computed transposed so that each result lands in
+//     the register layout of the operand that consumes it:
+//     A = strict_lower(diag(beta) K~ K^T) and P = lower(Q~ K^T).
 //  4. Unit lower-triangular solve (I + A) X = diag(beta) [K~ | V] by 16-row
-//     blocks: the four 16x16 diagonal blocks are inverted by substitution in
-//     fp32, the off-diagonal coupling runs on MFMA.  X = [W | Ut].
+//     blocks.  Every wave inverts the four 16x16 diagonal blocks in registers
+//     (forward substitution; row j is broadcast along each 16-lane row with
+//     DPP), the off-diagonal coupling runs on MFMA.  X = [W | Ut].
 //  5. State pass on MFMA:  U = Ut - W S,  O = Q~ S + P U,
 //     S <- diag(e^{G_L}) S + K_dec^T U  with K_dec = k e^{G_L - G}.
+//  With bf16 inputs the next chunk's raw inputs are copied by DMA
+//  (global_load_lds, 16 bytes per lane) into an LDS staging area while steps
+//  3-5 of the current chunk run, so the prefetch holds no registers.
+//
+// LDS holds every MFMA operand in "operand layout": for a matrix with rows in
+// 16-row blocks and a contraction index k, the fragment (block, step m) is 64
+// lanes x KW contiguous elements, lane r + 16g holding row r and the k values
+// 16*(e/4) + 4g + e%4 for e = m*KW .. m*KW + KW-1 (see gdn_mfma.h).  Reading a
+// fragment is one contiguous vector load per lane.
+//
+// Global memory is addressed from wave-uniform per-chunk bases with 32-bit
+// byte offsets, so each access costs one VGPR.
 //
 // This restates, chunk by chunk, the token recurrence
 //   S_t = diag(a_t) S_{t-1} + b_t k_t (v_t - (diag(a_t) S_{t-1})^T k_t)^T, o_t = S_t^T q_t.
+#include <type_traits>
+
 #include "gdn_kernels.h"
 #include "gdn_mfma.h"
 
@@ -49,34 +67,32 @@ struct cmax {
 
 template <typename TI, int DK, int DV>
 struct Cfg {
-    static constexpr int NT = 256, NW = 4;
+    typedef Mma<TI> M;
+    static constexpr int NW = DV / 16;        // waves; wave w owns state columns 16w .. 16w+15
+    static constexpr int NT = 64 * NW;
+    static constexpr int KW = M::KW, KSTEP = M::KSTEP;
     static constexpr int CPR = DK / 2;        // threads per token row in the load step
     static constexpr int NG = NT / CPR;       // token groups
     static constexpr int TPG = C / NG;        // tokens per group
-    static constexpr int CW = DV / NW;        // state columns per wave
-    static constexpr int NCT = CW / 16;       // 16-wide column tiles per wave
-    static constexpr int KWC = DK / NW;       // K~ columns per wave in the solve
-    static constexpr int NKT = KWC / 16;
     static constexpr int RT = DK / 16;        // 16-row tiles of the state
-    static constexpr int PAD = 16 / (int)sizeof(TI);
-    static constexpr int LDK = DK + PAD;      // Qs, Ks, Kh row stride (elements)
-    static constexpr int LDV = DV + PAD;      // Vs
-    static constexpr int LDT = C + PAD;       // KdT (d_k rows x 64 tokens)
-    static constexpr int LDP = C + PAD;       // Ps
-    static constexpr int LDA = C + 4;         // An (fp32)
-    static constexpr int LDL = 16 + PAD;      // Ls (four 16x16 inverses)
-    static constexpr int SZ_Q = C * LDK * (int)sizeof(TI);
-    static constexpr int SZ_R3 = cmax<C * LDK * (int)sizeof(TI), C * LDA * 4>::value;
-    // bf16 has LDS to spare, so K_dec^T gets its own region and is written while
-    // the chunk is loaded; the fp32 variant reuses the v region after the solve.
-    static constexpr bool KD_OWN = sizeof(TI) == 2;
-    static constexpr int SZ_KD = DK * LDT * (int)sizeof(TI);
-    static constexpr int SZ_R4 = KD_OWN ? C * LDV * (int)sizeof(TI) : cmax<C * LDV * (int)sizeof(TI), SZ_KD>::value;
-    static constexpr int SZ_P = C * LDP * (int)sizeof(TI);
-    static constexpr int SZ_L = 4 * 16 * LDL * (int)sizeof(TI);
-    static constexpr int NF = C + DK + NG * DK + 4 * DK + 8;
-    static constexpr int LDS = 2 * SZ_Q + SZ_R3 + SZ_R4 + (KD_OWN ? SZ_KD : 0) + SZ_P + SZ_L + NF * 4;
-    static_assert(NCT >= 1 && NKT >= 1 && TPG >= 1, "unsupported shape");
+    static constexpr int KM = DK / KSTEP;     // MFMA steps over d_k
+    static constexpr int TM = C / KSTEP;      // MFMA steps over the chunk's tokens
+    static constexpr int NPT = (20 + NW - 1) / NW;  // Gram tiles per wave (fast path)
+    static constexpr int NQS = (8 + NW - 1) / NW;   // Gram tiles per wave and row block (sub-tile path)
+    static constexpr bool STAGE = sizeof(TI) == 2;  // next chunk prefetched into LDS by DMA
+    static constexpr int SG_G = C * DK * 4;                // staging: g [C][DK] fp32
+    static constexpr int SG_Q = C * DK * (int)sizeof(TI);  // q, k [C][DK]
+    static constexpr int SG_V = C * DV * (int)sizeof(TI);  // v [C][DV]
+    static constexpr int SG_B = C * 4;                     // beta [C]
+    static constexpr int SZ_STG = STAGE ? SG_G + 2 * SG_Q + SG_V + SG_B : 0;
+    static constexpr int SZ_OPK = C * DK * (int)sizeof(TI);
+    static constexpr int SZ_AN = 10 * 64 * 16;  // ten 16x16 fp32 blocks of -A
+    static constexpr int SZ_R3 = cmax<SZ_OPK, SZ_AN>::value;
+    static constexpr int SZ_KD = DK * C * (int)sizeof(TI);
+    static constexpr int SZ_P = C * C * (int)sizeof(TI);
+    static constexpr int NF = C + DK + NG * DK + 4 * DK;
+    static constexpr int LDS = SZ_STG + 2 * SZ_OPK + SZ_R3 + SZ_KD + SZ_P + NF * 4;
+    static_assert(TPG >= 1 && NT <= 1024, "unsupported shape");
 };
 
 template <typename TI>
@@ -94,121 +110,257 @@ struct Args {
 };
 
 template <typename T>
-__device__ __forceinline__ floatx2 load2(const T* p);
+struct Pair;
 template <>
-__device__ __forceinline__ floatx2 load2<float>(const float* p) { return *reinterpret_cast<const floatx2*>(p); }
+struct Pair<bf16> {
+    typedef bf16x2 type;
+};
 template <>
-__device__ __forceinline__ floatx2 load2<bf16>(const bf16* p) {
-    const bf16x2 x = *reinterpret_cast<const bf16x2*>(p);
-    return floatx2{(float)x[0], (float)x[1]};
+struct Pair<float> {
+    typedef floatx2 type;
+};
+
+__device__ __forceinline__ floatx2 to_f2(bf16x2 x) { return floatx2{(float)x[0], (float)x[1]}; }
+__device__ __forceinline__ floatx2 to_f2(floatx2 x) { return x; }
+__device__ __forceinline__ floatx2 exp2v(floatx2 x) { return floatx2{fast_exp(x[0]), fast_exp(x[1])}; }
+
+// Element at a 32-bit byte offset from a wave-uniform base (one VGPR per access).
+template <typename T>
+__device__ __forceinline__ const T& at(const void* base, uint32_t byte_off) {
+    return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
 }
 template <typename T>
-__device__ __forceinline__ void store2(T* p, floatx2 x) {
-    p[0] = from_f32<T>(x[0]);
-    p[1] = from_f32<T>(x[1]);
+__device__ __forceinline__ T& at_mut(void* base, uint32_t byte_off) {
+    return *reinterpret_cast<T*>(static_cast<char*>(base) + byte_off);
 }
-
-__device__ __forceinline__ floatx2 exp2v(floatx2 x) { return floatx2{fast_exp(x[0]), fast_exp(x[1])}; }
 
 __device__ __forceinline__ float wave_min(float x) {
     for (int off = 32; off > 0; off >>= 1) x = fminf(x, __shfl_xor(x, off));
     return x;
 }
-__device__ __forceinline__ float wave_max(float x) {
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+
+// Operand layout with a bank swizzle: inside fragment (blk, m) the 16 slots of
+// lane group g are permuted by r -> r ^ ((4g + m + blk) & 15).  A fragment read
+// is still one slot per lane (a permutation), and the 16 slots that one token
+// row occupies across the fragments of its block land in 16 different bank
+// groups, so a wave storing a whole row does not conflict.
+__device__ __forceinline__ int op_slot(int blk, int m, int r, int g) { return 16 * g + ((r ^ (4 * g + m + blk)) & 15); }
+// Element offset of (row, k) in an operand-layout matrix with KM steps per 16-row block.
+template <typename TI, int KM>
+__device__ __forceinline__ int op_idx(int row, int k) {
+    constexpr int KW = Mma<TI>::KW;
+    const int ef = 4 * (k >> 4) + (k & 3);
+    const int m = ef / KW, e = ef % KW, blk = row >> 4;
+    return ((blk * KM + m) * 64 + op_slot(blk, m, row & 15, (k >> 2) & 3)) * KW + e;
+}
+// Stores columns (c, c+1) of one row (c even).
+template <typename TI, int KM>
+__device__ __forceinline__ void op_store2(TI* base, int row, int c, floatx2 x) {
+    if constexpr (sizeof(TI) == 2) {
+        *reinterpret_cast<bf16x2*>(base + op_idx<TI, KM>(row, c)) = bf16x2{(bf16)x[0], (bf16)x[1]};
+    } else {
+        base[op_idx<TI, KM>(row, c)] = x[0];
+        base[op_idx<TI, KM>(row, c + 1)] = x[1];
+    }
+}
+template <typename TI, int KM>
+__device__ __forceinline__ typename Mma<TI>::frag op_frag(const TI* base, int blk, int m, int lane) {
+    return reinterpret_cast<const typename Mma<TI>::frag*>(base)[(blk * KM + m) * 64 + op_slot(blk, m, lane & 15, lane >> 4)];
 }
 
-// Row block I and column block J of the p-th tile of the lower triangle
-// (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),(3,1),(3,2),(3,3).
+// Lane j of each 16-lane row, broadcast along the row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, false));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Index of the lower-triangle block (I, J), J <= I, in row-major order.
+__device__ __forceinline__ constexpr int tri_id(int I, int J) { return I * (I + 1) / 2 + J; }
 __device__ __forceinline__ void tri_pair(int p, int& I, int& J) {
     I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
     J = p - I * (I + 1) / 2;
 }
 
+__device__ __forceinline__ const __attribute__((address_space(1))) void* gptr(const void* p) {
+    return (const __attribute__((address_space(1))) void*)p;
+}
+__device__ __forceinline__ __attribute__((address_space(3))) void* lptr(void* p) {
+    return (__attribute__((address_space(3))) void*)p;
+}
+
+// DMA of one chunk's raw inputs into the staging area: rows of g, q, k, v land
+// row-major and beta contiguous; one wave instruction moves 1 KiB (64 lanes x
+// 16 bytes).  Rows at or past the chunk's end are not fetched.
 template <typename TI, int DK, int DV>
-__global__ __launch_bounds__(256, 1) void prefill_seq_kernel(Args<TI> a) {
+__device__ __forceinline__ void issue_stage(const Args<TI>& a, char* stg, int64_t c1, int L1, int h, int wv,
+                                            int lane) {
+    typedef Cfg<TI, DK, DV> P;
+    if (L1 <= 0) return;
+    const size_t tok0 = (size_t)c1 * a.H + h;
+    auto rows = [&](const void* src, int elems, int esize, char* dst) {
+        const int row_bytes = elems * esize, lpr = row_bytes / 16, rpi = 64 / lpr, ninst = C / rpi;
+        const char* base = static_cast<const char*>(src) + tok0 * elems * esize;
+        const uint32_t stride = (uint32_t)a.H * elems * esize;
+        for (int i = wv; i < ninst; i += P::NW) {
+            const int t = i * rpi + lane / lpr;
+            if (t < L1)
+                __builtin_amdgcn_global_load_lds(gptr(base + t * stride + (lane % lpr) * 16), lptr(dst + i * 1024), 16,
+                                                 0, 0);
+        }
+    };
+    rows(a.g, DK, 4, stg);
+    rows(a.q, DK, (int)sizeof(TI), stg + P::SG_G);
+    rows(a.k, DK, (int)sizeof(TI), stg + P::SG_G + P::SG_Q);
+    rows(a.v, DV, (int)sizeof(TI), stg + P::SG_G + 2 * P::SG_Q);
+    if (wv == 0 && lane < L1)
+        __builtin_amdgcn_global_load_lds(gptr(a.beta + tok0 + (size_t)lane * a.H),
+                                         lptr(stg + P::SG_G + 2 * P::SG_Q + P::SG_V), 4, 0, 0);
+}
+
+template <typename TI, int DK, int DV>
+__global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(Args<TI> a) {
     typedef Cfg<TI, DK, DV> P;
     typedef Mma<TI> M;
     typedef typename M::frag frag;
+    typedef typename Pair<TI>::type T2;
+    constexpr int KW = P::KW;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    TI* Qs = reinterpret_cast<TI*>(smem);
-    TI* Ks = reinterpret_cast<TI*>(smem + P::SZ_Q);
-    char* r3 = smem + 2 * P::SZ_Q;
-    char* r4 = r3 + P::SZ_R3;
-    char* r5 = r4 + P::SZ_R4;
-    TI* Ps = reinterpret_cast<TI*>(r5 + (P::KD_OWN ? P::SZ_KD : 0));
-    TI* Ls = reinterpret_cast<TI*>(reinterpret_cast<char*>(Ps) + P::SZ_P);
-    float* fs = reinterpret_cast<float*>(reinterpret_cast<char*>(Ls) + P::SZ_L);
-    TI* Kh = reinterpret_cast<TI*>(r3);      // k^ (Gram column operand) ...
-    float* An = reinterpret_cast<float*>(r3);  // ... then -A (fp32)
-    TI* Vs = reinterpret_cast<TI*>(r4);
-    TI* KdT = reinterpret_cast<TI*>(P::KD_OWN ? r5 : r4);
-    float* s_beta = fs;
+    char* stg = smem;  // next chunk's raw inputs (bf16 only)
+    const float* stg_g = reinterpret_cast<const float*>(stg);
+    const TI* stg_q = reinterpret_cast<const TI*>(stg + P::SG_G);
+    const TI* stg_k = reinterpret_cast<const TI*>(stg + P::SG_G + P::SG_Q);
+    const TI* stg_v = reinterpret_cast<const TI*>(stg + P::SG_G + 2 * P::SG_Q);
+    const float* stg_b = reinterpret_cast<const float*>(stg + P::SG_G + 2 * P::SG_Q + P::SG_V);
+    char* base = smem + P::SZ_STG;
+    TI* Qo = reinterpret_cast<TI*>(base);                      // q~ (operand layout over d_k)
+    TI* Ko = reinterpret_cast<TI*>(base + P::SZ_OPK);          // k~, then -W
+    char* r3 = base + 2 * P::SZ_OPK;
+    TI* Kh = reinterpret_cast<TI*>(r3);                        // k^ (Gram operand) ...
+    floatx4* An = reinterpret_cast<floatx4*>(r3);              // ... then the blocks of -A
+    TI* KdT = reinterpret_cast<TI*>(r3 + P::SZ_R3);            // K_dec^T (operand layout over tokens)
+    TI* Po = reinterpret_cast<TI*>(r3 + P::SZ_R3 + P::SZ_KD);  // P (operand layout over tokens)
+    float* s_beta = reinterpret_cast<float*>(reinterpret_cast<char*>(Po) + P::SZ_P);
     float* s_gam = s_beta + C;
     float* s_gtot = s_gam + DK;
     float* s_mid = s_gtot + P::NG * DK;
-    float* s_red = s_mid + 4 * DK;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+    const int tid0 = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
     const int unit = blockIdx.x;
     const int n = unit / H, h = unit - n * H;
     const int64_t tb = a.cu[n], te = a.cu[n + 1];
-    const int col0 = w * P::CW;
-    const int kcol0 = w * P::KWC;
+    const int col0 = 16 * w;  // this wave's state columns
     const size_t sbase = (size_t)unit * DK * DV;
+    const uint32_t krow = (uint32_t)H * DK;  // elements between consecutive tokens of q, k, g
+    const uint32_t vrow = (uint32_t)H * DV;  // ... of v, o
 
-    // fp32 state: S[ct][rt][i] = S[16 rt + 4g + i][col0 + 16 ct + r]
-    floatx4 S[P::NCT][P::RT];
+    // fp32 state: S[rt][i] = S[16 rt + 4g + i][col0 + r]
+    const int r0 = tid0 & 15, g0 = (tid0 & 63) >> 4;
+    floatx4 S[P::RT];
 #pragma unroll
-    for (int ct = 0; ct < P::NCT; ++ct)
+    for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[ct][rt][i] = a.S0 ? a.S0[sbase + (size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * ct + r] : 0.f;
+        for (int i = 0; i < 4; ++i)
+            S[rt][i] = a.S0 ? at<float>(a.S0 + sbase, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) : 0.f;
 
-    const int cp = tid % P::CPR, grp = tid / P::CPR, ch = 2 * cp;
+    if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, tb, (int)(te - tb < C ? te - tb : C), h, w, tid0 & 63);
+
+    // A chunk's outputs are stored at the start of the next chunk, after its
+    // wait for the prefetch: vmcnt also counts stores, so storing them at the
+    // end of the chunk would make that wait a full store round trip.
+    typedef typename std::conditional<sizeof(TI) == 2, bf16x4, floatx4>::type OV;
+    OV opend[4];
+    TI* opend_base = nullptr;
+    int opend_L = 0;
+    auto flush_o = [&](int gl, int rl) {
+        if (opend_base) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * rb + 4 * gl + i;
+                    if (t < opend_L) at_mut<TI>(opend_base, (t * vrow + col0 + rl) * (uint32_t)sizeof(TI)) = opend[rb][i];
+                }
+        }
+    };
 
     for (int64_t c0 = tb; c0 < te; c0 += C) {
+        // Lane-derived values are recomputed every chunk: kept opaque to the
+        // compiler, so that addresses built from them are not hoisted out of
+        // the loop and held in registers for its whole length.
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+        const int cp = tid % P::CPR, grp = tid / P::CPR, ch = 2 * cp;
         const int L = (int)(te - c0 < C ? te - c0 : C);
+        const int64_t c1 = c0 + C;
+        const int L1 = (int)(te - c1 < C ? te - c1 : C);  // valid tokens of the next chunk (<= 0: none)
+        const size_t tok0 = (size_t)c0 * H + h;            // (token, head) row of the chunk's first token
+        const float* gbase = a.g + tok0 * DK;
+        const TI* qbase = a.q + tok0 * DK;
+        const TI* kbase = a.k + tok0 * DK;
+        const TI* vbase = a.v + tok0 * DV;
+        TI* obase = a.o + tok0 * DV;
 
-        // ---- 1. raw loads and the local cumulative log-decay ------------------
-        floatx2 G[P::TPG], qv[P::TPG], kv[P::TPG];
+        // ---- 1. local cumulative log-decay ------------------------------------
+        // Thread (cp, grp) owns key channels (ch, ch+1) of the tokens
+        // grp*TPG .. grp*TPG+TPG-1.  Its inputs are read twice (from the
+        // staging area, or from global memory where the second read hits the
+        // cache): once to sum the group's log-decays, once to build the
+        // operands, so few registers stay live.
+        auto rd_g = [&](int t) -> floatx2 {
+            if (t >= L) return floatx2{0.f, 0.f};
+            if constexpr (P::STAGE) return *reinterpret_cast<const floatx2*>(stg_g + t * DK + ch);
+            else return at<floatx2>(gbase, (t * krow + ch) * 4);
+        };
+        auto rd_qk = [&](const TI* sp, const TI* gp, int t) -> floatx2 {
+            if (t >= L) return floatx2{0.f, 0.f};
+            if constexpr (P::STAGE) return to_f2(*reinterpret_cast<const T2*>(sp + t * DK + ch));
+            else return to_f2(at<T2>(gp, (t * krow + ch) * (uint32_t)sizeof(TI)));
+        };
+        if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
+        __syncthreads();  // ... and every other wave's; the previous chunk is done with LDS
+        flush_o(g, r);    // the previous chunk's outputs
+        // the solve's v right-hand side in accumulator layout: vr[I][i] = v[16I + 4g + i][col0 + r]
+        typedef typename std::conditional<sizeof(TI) == 2, bf16x4, floatx4>::type VR;
+        VR vr[4];
 #pragma unroll
-        for (int tt = 0; tt < P::TPG; ++tt) {
-            const int t = grp * P::TPG + tt;
-            if (t < L) {
-                const size_t off = ((size_t)(c0 + t) * H + h) * DK + ch;
-                G[tt] = *reinterpret_cast<const floatx2*>(a.g + off);
-                qv[tt] = load2(a.q + off);
-                kv[tt] = load2(a.k + off);
-            } else {
-                G[tt] = floatx2{0.f, 0.f};
-                qv[tt] = floatx2{0.f, 0.f};
-                kv[tt] = floatx2{0.f, 0.f};
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * I + 4 * g + i;
+                TI x = TI(0.f);
+                if (t < L) {
+                    if constexpr (P::STAGE) x = stg_v[t * DV + col0 + r];
+                    else x = at<TI>(vbase, (t * vrow + col0 + r) * (uint32_t)sizeof(TI));
+                }
+                vr[I][i] = x;
             }
+        if (tid < C) {
+            float b = 0.f;
+            if (tid < L) {
+                if constexpr (P::STAGE) b = stg_b[tid];
+                else b = at<float>(a.beta + tok0, tid * H * 4);
+            }
+            s_beta[tid] = b;
         }
+        const int t0 = grp * P::TPG;
         {
-            constexpr int per_row = DV * (int)sizeof(TI) / 16;
-            for (int e = tid; e < C * per_row; e += P::NT) {
-                const int t = e / per_row, part = e - t * per_row;
-                floatx4 x = floatx4{0.f, 0.f, 0.f, 0.f};
-                if (t < L)
-                    x = *reinterpret_cast<const floatx4*>(a.v + ((size_t)(c0 + t) * H + h) * DV + part * (16 / sizeof(TI)));
-                *reinterpret_cast<floatx4*>(Vs + t * P::LDV + part * (16 / sizeof(TI))) = x;
-            }
+            floatx2 sum = floatx2{0.f, 0.f};
+#pragma unroll 4
+            for (int tt = 0; tt < P::TPG; ++tt) sum += rd_g(t0 + tt);
+            s_gtot[grp * DK + ch] = sum[0];
+            s_gtot[grp * DK + ch + 1] = sum[1];
         }
-        if (tid < C) s_beta[tid] = tid < L ? a.beta[(size_t)(c0 + tid) * H + h] : 0.f;
-        floatx2 run = floatx2{0.f, 0.f};
-#pragma unroll
-        for (int tt = 0; tt < P::TPG; ++tt) {
-            run += G[tt];
-            G[tt] = run;
-        }
-        s_gtot[grp * DK + ch] = run[0];
-        s_gtot[grp * DK + ch + 1] = run[1];
         __syncthreads();
         floatx2 off = floatx2{0.f, 0.f}, tot = floatx2{0.f, 0.f};
 #pragma unroll
@@ -217,295 +369,319 @@ __global__ __launch_bounds__(256, 1) void prefill_seq_kernel(Args<TI> a) {
             tot += x;
             if (gg < grp) off += x;
         }
-        float gmin = 0.f, gmax = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < P::TPG; ++tt) {
-            G[tt] += off;
-            gmin = fminf(gmin, fminf(G[tt][0], G[tt][1]));
-            gmax = fmaxf(gmax, fmaxf(G[tt][0], G[tt][1]));
-        }
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            if ((16 * I + 7) / P::TPG == grp) {
-                s_mid[I * DK + ch] = G[(16 * I + 7) % P::TPG][0];
-                s_mid[I * DK + ch + 1] = G[(16 * I + 7) % P::TPG][1];
-            }
-        }
-        gmin = wave_min(gmin);
-        gmax = wave_max(gmax);
-        if (lane == 0) {
-            s_red[w] = gmin;
-            s_red[4 + w] = gmax;
-        }
+        // With g <= 0 the cumulative log-decay is non-increasing, so its most
+        // negative value on a channel is the chunk total; every wave sees all
+        // channels, so the decision is uniform over the workgroup.
+        const bool fast = wave_min(fminf(tot[0], tot[1])) >= -40.f;
         const floatx2 gam = exp2v(tot);
         if (grp == 0) {
             s_gam[ch] = gam[0];
             s_gam[ch + 1] = gam[1];
         }
-        __syncthreads();  // s_red, s_mid visible
-        const bool fast = fminf(fminf(s_red[0], s_red[1]), fminf(s_red[2], s_red[3])) >= -40.f &&
-                          fmaxf(fmaxf(s_red[4], s_red[5]), fmaxf(s_red[6], s_red[7])) <= 40.f;
 
         // ---- 2. decay-scaled operands --------------------------------------
-        floatx2 kd[P::TPG];  // K_dec = k e^{G_L - G}, stored transposed
-        if (fast) {
+        // K_dec^T is stored four tokens at a time (one 8-byte store per channel).
+        auto store_kd4 = [&](int t, const floatx2* kd) {
+            if constexpr (sizeof(TI) == 2) {
+                *reinterpret_cast<bf16x4*>(KdT + op_idx<TI, P::TM>(ch, t)) =
+                    bf16x4{(bf16)kd[0][0], (bf16)kd[1][0], (bf16)kd[2][0], (bf16)kd[3][0]};
+                *reinterpret_cast<bf16x4*>(KdT + op_idx<TI, P::TM>(ch + 1, t)) =
+                    bf16x4{(bf16)kd[0][1], (bf16)kd[1][1], (bf16)kd[2][1], (bf16)kd[3][1]};
+            } else {
 #pragma unroll
-            for (int tt = 0; tt < P::TPG; ++tt) {
-                const int t = grp * P::TPG + tt;
-                const floatx2 e = exp2v(G[tt]), ei = exp2v(-G[tt]);
-                store2(Qs + t * P::LDK + ch, qv[tt] * e);
-                store2(Ks + t * P::LDK + ch, kv[tt] * e);
-                store2(Kh + t * P::LDK + ch, kv[tt] * ei);
-                kd[tt] = kv[tt] * ei * gam;
-            }
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < P::TPG; ++tt) {
-                const int t = grp * P::TPG + tt;
-                const floatx2 m = floatx2{s_mid[(t >> 4) * DK + ch], s_mid[(t >> 4) * DK + ch + 1]};
-                const floatx2 e = exp2v(G[tt] - m);
-                store2(Qs + t * P::LDK + ch, qv[tt] * e);
-                store2(Ks + t * P::LDK + ch, kv[tt] * e);
-                kd[tt] = kv[tt] * exp2v(tot - G[tt]);
-            }
-        }
-        auto store_kd = [&]() {
-#pragma unroll
-            for (int tt = 0; tt < P::TPG; ++tt) {
-                const int t = grp * P::TPG + tt;
-                KdT[ch * P::LDT + t] = from_f32<TI>(kd[tt][0]);
-                KdT[(ch + 1) * P::LDT + t] = from_f32<TI>(kd[tt][1]);
-            }
-        };
-        if (P::KD_OWN) store_kd();
-
-        // ---- 3. Gram tiles ---------------------------------------------------
-        floatx4 accA[5];
-        int aI[5], aJ[5];
-#pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            accA[j] = zero4();
-            aI[j] = -1;
-            aJ[j] = 0;
-        }
-        auto gram = [&](const TI* rows, int I, int J) {
-            floatx4 acc = zero4();
-            const TI* ra = rows + (16 * I + r) * P::LDK;
-            const TI* rb = Kh + (16 * J + r) * P::LDK;
-#pragma unroll
-            for (int m = 0; m < DK / M::KSTEP; ++m) acc = M::mma(lds_nat(ra, m, g), lds_nat(rb, m, g), acc);
-            return acc;
-        };
-        auto store_p = [&](const floatx4& acc, int I, int J) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * I + 4 * g + i, s = 16 * J + r;
-                Ps[t * P::LDP + s] = from_f32<TI>(s <= t ? acc[i] : 0.f);
-            }
-        };
-        if (fast) {
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < 5; ++j) {
-                const int p = w + 4 * j;
-                int I, J;
-                tri_pair(p % 10, I, J);
-                if (p < 10) {
-                    accA[j] = gram(Ks, I, J);
-                    aI[j] = I;
-                    aJ[j] = J;
-                } else {
-                    store_p(gram(Qs, I, J), I, J);
+                for (int j = 0; j < 4; ++j) {
+                    KdT[op_idx<TI, P::TM>(ch, t + j)] = kd[j][0];
+                    KdT[op_idx<TI, P::TM>(ch + 1, t + j)] = kd[j][1];
                 }
             }
-            __syncthreads();  // all Gram reads of Kh done
-        } else {
+        };
+        if (fast) {
+            floatx2 G = off;
+#pragma unroll 1
+            for (int tq = 0; tq < P::TPG; tq += 4) {
+                floatx2 kd[4];
 #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = t0 + tq + j;
+                    G += rd_g(t);
+                    const floatx2 e = exp2v(G), ei = exp2v(-G);
+                    const floatx2 kk = rd_qk(stg_k, kbase, t);
+                    const floatx2 kh = kk * ei;
+                    op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
+                    op_store2<TI, P::KM>(Ko, t, ch, kk * e);
+                    op_store2<TI, P::KM>(Kh, t, ch, kh);
+                    kd[j] = kh * gam;  // K_dec = k e^{G_L - G}
+                }
+                store_kd4(t0 + tq, kd);
+            }
+        } else {
+            // reference of row block I: G at its middle row 16I + 7
+            {
+                floatx2 G = off;
+                for (int tt = 0; tt < P::TPG; ++tt) {
+                    const int t = t0 + tt;
+                    G += rd_g(t);
+                    if ((t & 15) == 7) {
+                        s_mid[(t >> 4) * DK + ch] = G[0];
+                        s_mid[(t >> 4) * DK + ch + 1] = G[1];
+                    }
+                }
+            }
+            __syncthreads();  // s_mid visible
+            floatx2 G = off;
+#pragma unroll 1
+            for (int tq = 0; tq < P::TPG; tq += 4) {
+                floatx2 kd[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = t0 + tq + j;
+                    G += rd_g(t);
+                    const floatx2 m = floatx2{s_mid[(t >> 4) * DK + ch], s_mid[(t >> 4) * DK + ch + 1]};
+                    const floatx2 e = exp2v(G - m);
+                    const floatx2 kk = rd_qk(stg_k, kbase, t);
+                    op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
+                    op_store2<TI, P::KM>(Ko, t, ch, kk * e);
+                    kd[j] = kk * exp2v(tot - G);
+                }
+                store_kd4(t0 + tq, kd);
+            }
+        }
+
+        // ---- 3. Gram tiles (transposed) -------------------------------------
+        // tile (I, J): C[s][t] = sum_c k^[s][c] x[t][c], s in block J, t in block I;
+        // lane r + 16g ends with x-row t = 16I + r against columns s = 16J + 4g + i.
+        auto gram = [&](const TI* rows, int I, int J) {
+            frag fa[P::KM], fb[P::KM];
+#pragma unroll
+            for (int m = 0; m < P::KM; ++m) {
+                fa[m] = op_frag<TI, P::KM>(Kh, J, m, lane);
+                fb[m] = op_frag<TI, P::KM>(rows, I, m, lane);
+            }
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < P::KM; ++m) acc = M::mma(fa[m], fb[m], acc);
+            return acc;
+        };
+        // P tile (I, J) into the operand layout of P over tokens (rows t, k = s).
+        auto store_p = [&](const floatx4& acc, int I, int J) {
+            const int t = 16 * I + r;
+            floatx4 p;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = (16 * J + 4 * g + i <= t) ? acc[i] : 0.f;
+            if constexpr (KW == 8) {
+                const bf16x4 pb = bf16x4{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3]};
+                bf16* dst = reinterpret_cast<bf16*>(Po) + ((I * P::TM + J / 2) * 64 + op_slot(I, J / 2, r, g)) * 8 + 4 * (J & 1);
+                *reinterpret_cast<bf16x4*>(dst) = pb;
+                if (J == I && (I & 1) == 0) *reinterpret_cast<bf16x4*>(dst + 4) = bf16x4{};  // block above the diagonal
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    reinterpret_cast<float*>(Po)[(I * P::TM + 4 * J + i) * 64 + op_slot(I, 4 * J + i, r, g)] = p[i];
+            }
+        };
+        constexpr int NACC = P::NPT > 4 ? P::NPT : 4;
+        floatx4 accA[NACC];
+        int aP[NACC];
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+            accA[j] = zero4();
+            aP[j] = -1;
+        }
+        if (fast) {
+            __syncthreads();
+            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane);
+            // 20 tiles (10 of A, 10 of P); wave w takes tiles w, w+NW, ...
+#pragma unroll
+            for (int j = 0; j < P::NPT; ++j) {
+                const int q = w + P::NW * j;
+                if (q < 20) {
+                    int I, J;
+                    tri_pair(q % 10, I, J);
+                    const floatx4 acc = gram(q < 10 ? Ko : Qo, I, J);
+                    if (q < 10) {
+                        accA[j] = acc;
+                        aP[j] = q;
+                    } else {
+                        store_p(acc, I, J);
+                    }
+                }
+            }
+            __syncthreads();  // every read of Kh is done
+        } else {
             for (int I = 0; I < 4; ++I) {
                 __syncthreads();  // readers of the previous Kh are done
-#pragma unroll
-                for (int tt = 0; tt < P::TPG; ++tt) {
-                    const int t = grp * P::TPG + tt;
-                    if (t < 16 * (I + 1)) {
-                        const floatx2 m = floatx2{s_mid[I * DK + ch], s_mid[I * DK + ch + 1]};
-                        store2(Kh + t * P::LDK + ch, kv[tt] * exp2v(m - G[tt]));
+                {
+                    const floatx2 m = floatx2{s_mid[I * DK + ch], s_mid[I * DK + ch + 1]};
+                    floatx2 G = off;
+                    for (int tt = 0; tt < P::TPG; ++tt) {
+                        const int t = t0 + tt;
+                        G += rd_g(t);
+                        if (t < 16 * (I + 1))
+                            op_store2<TI, P::KM>(Kh, t, ch, rd_qk(stg_k, kbase, t) * exp2v(m - G));
                     }
                 }
                 __syncthreads();
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int qq = w + 4 * jj;
+                for (int jj = 0; jj < P::NQS; ++jj) {
+                    const int qq = w + P::NW * jj;
                     if (qq < 2 * (I + 1)) {
                         if (qq < I + 1) {
-                            accA[I] = gram(Ks, I, qq);
-                            aI[I] = I;
-                            aJ[I] = qq;
+                            // at most one A tile per wave and row block: slot I
+#pragma unroll
+                            for (int sI = 0; sI < 4; ++sI)
+                                if (sI == I) {
+                                    accA[sI] = gram(Ko, I, qq);
+                                    aP[sI] = tri_id(I, qq);
+                                }
                         } else {
-                            store_p(gram(Qs, I, qq - I - 1), I, qq - I - 1);
+                            store_p(gram(Qo, I, qq - I - 1), I, qq - I - 1);
                         }
                     }
                 }
             }
-            __syncthreads();  // all Gram reads of Qs/Ks/Kh done
+            __syncthreads();  // every read of Qo/Ko/Kh is done
             // the inter-chunk products use the chunk start as reference
-#pragma unroll
-            for (int tt = 0; tt < P::TPG; ++tt) {
-                const int t = grp * P::TPG + tt;
-                const floatx2 e = exp2v(G[tt]);
-                store2(Qs + t * P::LDK + ch, qv[tt] * e);
-                store2(Ks + t * P::LDK + ch, kv[tt] * e);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            if (aI[j] >= 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * aI[j] + 4 * g + i, s = 16 * aJ[j] + r;
-                    An[t * P::LDA + s] = s < t ? -s_beta[t] * accA[j][i] : 0.f;
+            {
+                floatx2 G = off;
+                for (int tt = 0; tt < P::TPG; ++tt) {
+                    const int t = t0 + tt;
+                    G += rd_g(t);
+                    const floatx2 e = exp2v(G);
+                    op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
+                    op_store2<TI, P::KM>(Ko, t, ch, rd_qk(stg_k, kbase, t) * e);
                 }
             }
+            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane);
+        }
+        // -A tiles: lane r + 16g holds -beta_t A[t][s], t = 16I + r, s = 16J + 4g + i
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+            if (aP[j] >= 0) {
+                int I, J;
+                tri_pair(aP[j], I, J);
+                const int t = 16 * I + r;
+                const float bt = s_beta[t];
+                floatx4 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = (16 * J + 4 * g + i < t) ? -bt * accA[j][i] : 0.f;
+                An[aP[j] * 64 + lane] = x;
+            }
         }
         __syncthreads();
 
-        // ---- 4a. inverses of the four 16x16 diagonal blocks of (I + A) --------
-        if (lane < 16) {
-            const int c = lane;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = i == c ? 1.f : 0.f;
-            const float* blk = An + (16 * w) * P::LDA + 16 * w;
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-#pragma unroll
-                for (int i = j + 1; i < 16; ++i) x[i] += blk[i * P::LDA + j] * x[j];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) Ls[(16 * w + i) * P::LDL + c] = from_f32<TI>(x[i]);
-        }
-        __syncthreads();
-
-        // ---- 4b. block forward substitution for X = [W | Ut] (own columns) ----
-        constexpr int NX = P::NKT + P::NCT;
-        floatx4 X[NX][4];
+        // ---- 4a. inverses of the diagonal blocks of (I + A), every wave -------
+        // lane r + 16g ends with Linv_I[r][4g .. 4g+3]
+        floatx4 Linv[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
+            float arow[16];
 #pragma unroll
-            for (int tile = 0; tile < NX; ++tile) {
-                const bool isK = tile < P::NKT;
-                const int cc = isK ? kcol0 + 16 * tile : col0 + 16 * (tile - P::NKT);
-                floatx4 acc;
+            for (int gg = 0; gg < 4; ++gg) {
+                const floatx4 x = An[tri_id(I, I) * 64 + r + 16 * gg];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * I + 4 * g + i;
-                    const TI x = isK ? Ks[t * P::LDK + cc + r] : Vs[t * P::LDV + cc + r];
-                    acc[i] = s_beta[t] * to_f32(x);
-                }
-                if (I > 0) {
-                    const float* arow = An + (16 * I + r) * P::LDA;
-#pragma unroll
-                    for (int m = 0; m < (16 * I + M::KSTEP - 1) / M::KSTEP; ++m)
-                        acc = M::mma(lds_perm_f32<TI>(arow, m, g, 16 * I), acc_perm<TI>(X[tile], m, I), acc);
-                }
-                floatx4 xi = zero4();
-                const TI* lrow = Ls + (16 * I + r) * P::LDL;
-#pragma unroll
-                for (int m = 0; m < (16 + M::KSTEP - 1) / M::KSTEP; ++m)
-                    xi = M::mma(lds_perm(lrow, m, g, 16), acc_perm<TI>(&acc, m, 1), xi);
-                X[tile][I] = xi;
+                for (int i = 0; i < 4; ++i) arow[4 * gg + i] = x[i];
             }
-        }
-        // -W into the own K~ columns of Ks (each wave only ever read its own)
+            floatx4 x;
 #pragma unroll
-        for (int tile = 0; tile < P::NKT; ++tile)
+            for (int i = 0; i < 4; ++i) x[i] = (r == 4 * g + i) ? 1.f : 0.f;
+            static_for<0, 15>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Ks[(16 * I + 4 * g + i) * P::LDK + kcol0 + 16 * tile + r] = from_f32<TI>(-X[tile][I][i]);
-        __syncthreads();  // Vs is free, -W complete
-        if (!P::KD_OWN) {
-            store_kd();
-            __syncthreads();
+                for (int i = 0; i < 4; ++i) x[i] += arow[j] * row_bcast<j>(x[i]);
+            });
+            Linv[I] = x;
         }
 
-        // ---- 5. state pass (own columns) --------------------------------------
-        floatx4 U[P::NCT][4], O[P::NCT][4];
+        // ---- 4b. U = (I + A)^-1 diag(beta) (V - K~ S), own columns -----------
+        // This is U = Ut - W S with W = (I + A)^-1 diag(beta) K~ never formed:
+        // the right-hand side takes K~ S first, then the block forward
+        // substitution runs on the wave's 16 columns only.
+        frag bS[P::KM];
 #pragma unroll
-        for (int ct = 0; ct < P::NCT; ++ct)
+        for (int m = 0; m < P::KM; ++m) bS[m] = acc_perm<TI>(S, m, P::RT);
+        floatx4 U[4];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                U[ct][rb] = X[P::NKT + ct][rb];
-                O[ct][rb] = zero4();
-            }
-        // U += (-W) S ; O += Q~ S
+        for (int I = 0; I < 4; ++I) {
+            frag ak[P::KM];
 #pragma unroll
-        for (int m = 0; m < DK / M::KSTEP; ++m) {
-            frag bS[P::NCT];
+            for (int m = 0; m < P::KM; ++m) ak[m] = op_frag<TI, P::KM>(Ko, I, m, lane);
+            floatx4 ks = zero4();
 #pragma unroll
-            for (int ct = 0; ct < P::NCT; ++ct) bS[ct] = acc_perm<TI>(S[ct], m, P::RT);
+            for (int m = 0; m < P::KM; ++m) ks = M::mma(ak[m], bS[m], ks);
+            floatx4 acc;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const frag aw = lds_perm(Ks + (16 * rb + r) * P::LDK, m, g);
-                const frag aq = lds_perm(Qs + (16 * rb + r) * P::LDK, m, g);
+            for (int i = 0; i < 4; ++i) acc[i] = s_beta[16 * I + 4 * g + i] * ((float)vr[I][i] - ks[i]);
+            if constexpr (KW == 8) {
 #pragma unroll
-                for (int ct = 0; ct < P::NCT; ++ct) {
-                    U[ct][rb] = M::mma(aw, bS[ct], U[ct][rb]);
-                    O[ct][rb] = M::mma(aq, bS[ct], O[ct][rb]);
+                for (int m = 0; 2 * m < I; ++m) {
+                    const floatx4 lo = An[tri_id(I, 2 * m) * 64 + lane];
+                    const floatx4 hi = (2 * m + 1 < I) ? An[tri_id(I, 2 * m + 1) * 64 + lane] : zero4();
+                    const bf16x8 af = bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                                             (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+                    acc = M::mma(af, acc_perm<TI>(U, m, I), acc);
                 }
+                const bf16x8 lf = bf16x8{(bf16)Linv[I][0], (bf16)Linv[I][1], (bf16)Linv[I][2], (bf16)Linv[I][3],
+                                         (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+                U[I] = M::mma(lf, acc_perm<TI>(&acc, 0, 1), zero4());
+            } else {
+#pragma unroll
+                for (int J = 0; J < I; ++J) {
+                    const floatx4 an = An[tri_id(I, J) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc = M::mma(an[e], U[J][e], acc);
+                }
+                floatx4 ui = zero4();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ui = M::mma(Linv[I][e], acc[e], ui);
+                U[I] = ui;
             }
         }
-        // S <- diag(e^{G_L}) S before the chunk's writes are added
+
+        // ---- 5. outputs and state (own columns) -------------------------------
+        // O = Q~ S + P U one row block at a time, then S <- diag(e^{G_L}) S + K_dec^T U.
+        frag bU[P::TM];
 #pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt)
+        for (int m = 0; m < P::TM; ++m) bU[m] = acc_perm<TI>(U, m, 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float d = s_gam[16 * rt + 4 * g + i];
+        for (int rb = 0; rb < 4; ++rb) {
+            frag aq[P::KM];
 #pragma unroll
-                for (int ct = 0; ct < P::NCT; ++ct) S[ct][rt][i] *= d;
-            }
-        // O += P U ; S += K_dec^T U
+            for (int m = 0; m < P::KM; ++m) aq[m] = op_frag<TI, P::KM>(Qo, rb, m, lane);
+            floatx4 O = zero4();
 #pragma unroll
-        for (int m = 0; m < C / M::KSTEP; ++m) {
-            frag bU[P::NCT];
+            for (int m = 0; m < P::KM; ++m) O = M::mma(aq[m], bS[m], O);
 #pragma unroll
-            for (int ct = 0; ct < P::NCT; ++ct) bU[ct] = acc_perm<TI>(U[ct], m, 4);
-            const int first_tile = (m * M::KW) / 4;
+            for (int m = 0; m < P::TM; ++m)
+                if ((m * KW) / 4 <= rb) O = M::mma(op_frag<TI, P::TM>(Po, rb, m, lane), bU[m], O);
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                if (first_tile <= rb) {
-                    // blocks above the diagonal of P are never written: mask them
-                    const frag ap = lds_perm(Ps + (16 * rb + r) * P::LDP, m, g, 16 * (rb + 1));
-#pragma unroll
-                    for (int ct = 0; ct < P::NCT; ++ct) O[ct][rb] = M::mma(ap, bU[ct], O[ct][rb]);
-                }
-            }
-#pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt) {
-                const frag ak = lds_perm(KdT + (16 * rt + r) * P::LDT, m, g);
-#pragma unroll
-                for (int ct = 0; ct < P::NCT; ++ct) S[ct][rt] = M::mma(ak, bU[ct], S[ct][rt]);
-            }
+            for (int i = 0; i < 4; ++i) opend[rb][i] = from_f32<TI>(O[i]);
         }
 #pragma unroll
-        for (int ct = 0; ct < P::NCT; ++ct)
+        for (int rt = 0; rt < P::RT; ++rt) {
+            const floatx4 d = *reinterpret_cast<const floatx4*>(s_gam + 16 * rt + 4 * g);
+            S[rt] *= d;
+        }
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+        for (int rt = 0; rt < P::RT; ++rt) {
+            frag ak[P::TM];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * rb + 4 * g + i;
-                    if (t < L) a.o[((size_t)(c0 + t) * H + h) * DV + col0 + 16 * ct + r] = from_f32<TI>(O[ct][rb][i]);
-                }
-        __syncthreads();  // LDS is rewritten by the next chunk
+            for (int m = 0; m < P::TM; ++m) ak[m] = op_frag<TI, P::TM>(KdT, rt, m, lane);
+#pragma unroll
+            for (int m = 0; m < P::TM; ++m) S[rt] = M::mma(ak[m], bU[m], S[rt]);
+        }
+        opend_base = obase;
+        opend_L = L;
+        // The next chunk writes LDS only after its first barrier, which every
+        // wave reaches after finishing this state pass.
     }
+    flush_o(g0, r0);
 
     if (a.Sf) {
 #pragma unroll
-        for (int ct = 0; ct < P::NCT; ++ct)
+        for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.Sf[sbase + (size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * ct + r] = S[ct][rt][i];
+            for (int i = 0; i < 4; ++i)
+                at_mut<float>(a.Sf + sbase, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) = S[rt][i];
     }
 }
 
