@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -38,6 +39,46 @@ int32_t validate_inputs(const int32_t* cu_dev, int32_t num_seqs, int64_t T_total
 }
 
 }  // namespace
+
+namespace gdn {
+
+// Time split of long sequences.  One workgroup carries one (sequence, head)
+// through its chunks in order, so a batch of few long sequences leaves most of
+// the 256 compute units idle.  Cutting sequences into segments of Ls tokens
+// costs a second pass over the non-last segments (their transitions M and N,
+// about MAP_COST of a full pass, for both M and N) and buys parallelism.  The
+// plan compares, in units of one chunk of the full pass, the critical path
+//   whole sequences:  ceil(units / CUs) * chunks
+//   split:            ceil(2 units (P-1) / CUs) * Ls/64 * MAP_COST + ceil(units P / CUs) * Ls/64
+// for sequences of the mean length (the lengths themselves are on the device),
+// and splits only when that saves at least 15%.
+int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H) {
+    if (const char* e = std::getenv("GDN_PREFILL_SEGMENT")) {
+        if (*e) {
+            const long long v = std::strtoll(e, nullptr, 10);
+            return v <= 0 ? 0 : (int64_t)((v + 63) / 64 * 64);
+        }
+    }
+    if (num_seqs <= 0 || T_total <= 0 || H <= 0) return 0;
+    constexpr double CUS = 256.0, MAP_COST = 0.6;
+    const double units = (double)num_seqs * H;
+    const int64_t len = (T_total + num_seqs - 1) / num_seqs;
+    auto rounds = [&](double wgs) { return std::ceil(wgs / CUS); };
+    const double whole = rounds(units) * std::ceil(len / 64.0);
+    double best = whole;
+    int64_t best_seg = 0;
+    for (int64_t ls = 1024; ls < len; ls += 512) {
+        const double P = std::ceil((double)len / ls), ch = ls / 64.0;
+        const double t = rounds(2 * units * (P - 1)) * ch * MAP_COST + rounds(units * P) * ch;
+        if (t < best) {
+            best = t;
+            best_seg = ls;
+        }
+    }
+    return best < 0.85 * whole ? best_seg : 0;
+}
+
+}  // namespace gdn
 
 extern "C" {
 
@@ -85,12 +126,9 @@ int32_t gdn_state_free(float* state, void* stream) {
 }
 
 size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v) {
-    (void)T_total;
-    (void)num_seqs;
-    (void)H;
-    (void)d_k;
-    (void)d_v;
-    return 0;
+    if (T_total < 0 || num_seqs < 0 || H < 1 || d_k < 0 || d_v < 0) return 0;
+    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H);
+    return gdn::prefill_workspace_layout(T_total, num_seqs, H, d_k, d_v, seg).bytes;
 }
 
 int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -111,9 +149,10 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     }
     if (initial_state && !aligned(initial_state, 16)) return GDN_ERR_INVALID_ARG;
     if (final_state && !aligned(final_state, 16)) return GDN_ERR_INVALID_ARG;
-    const size_t need = gdn_prefill_workspace_bytes(T_total, num_seqs, H, d_k, d_v);
+    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H);
+    const size_t need = gdn::prefill_workspace_layout(T_total, num_seqs, H, d_k, d_v, seg).bytes;
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return GDN_ERR_INVALID_ARG;
-    if ((int64_t)num_seqs * H > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+    if (((int64_t)num_seqs + (seg > 0 ? T_total / seg : 0)) * H * (d_v / 16) > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (validate_mode()) {
         const int32_t st = validate_inputs(cu_seqlens, num_seqs, T_total, g, T_total * H * d_k, s);
@@ -134,6 +173,9 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     p.dk = d_k;
     p.dv = d_v;
     p.bf16 = dtype == GDN_BF16;
+    p.T_total = T_total;
+    p.seg = seg;
+    p.workspace = workspace;
     return gdn::launch_prefill(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -21,7 +21,37 @@ struct PrefillLaunch {
     int32_t dk;
     int32_t dv;
     bool bf16;
+    int64_t T_total;
+    int64_t seg;      // segment length of the time split (tokens, multiple of 64); 0: none
+    void* workspace;  // prefill_workspace_layout(...).bytes bytes when seg > 0
 };
+
+// Workspace of the time-split prefill, for segments of `seg` tokens.  A
+// sequence's non-last segments hold exactly seg tokens, so there are at most
+// T_total / seg of them over the batch; each (non-last segment, head) owns an
+// M slot (d_k x d_k fp32) and an N slot (d_k x d_v fp32).  nl is the int32
+// table of non-last segment counts [num_seqs + 1].
+struct PrefillWorkspace {
+    int64_t slots = 0;
+    size_t m_off = 0, n_off = 0, nl_off = 0, bytes = 0;
+};
+inline PrefillWorkspace prefill_workspace_layout(int64_t T_total, int32_t num_seqs, int32_t H, int32_t dk,
+                                                 int32_t dv, int64_t seg) {
+    PrefillWorkspace w;
+    if (seg <= 0) return w;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    w.slots = T_total / seg;
+    w.m_off = 0;
+    w.n_off = al((size_t)w.slots * H * dk * dk * sizeof(float));
+    w.nl_off = w.n_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
+    w.bytes = w.nl_off + al(((size_t)num_seqs + 1) * sizeof(int32_t));
+    return w;
+}
+
+// Segment length chosen for a batch of these sizes (0: one workgroup per whole
+// sequence and head).  Depends on the arguments only, and on the environment
+// variable GDN_PREFILL_SEGMENT, which forces a length (0 = never split).
+int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H);
 
 struct DecodeLaunch {
     const void* q;

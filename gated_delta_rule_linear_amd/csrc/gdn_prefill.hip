@@ -107,6 +107,18 @@ struct Args {
     float* Sf;
     TI* o;
     int H;
+    // Time split of long sequences (seg > 0): sequence n is cut into segments of
+    // `seg` tokens (the last one shorter); nl[n] counts the non-last segments of
+    // sequences 0 .. n-1.  Non-last segment k (head h) owns slot k*H + h of the
+    // map areas: wsM holds its d_k x d_k transition M, wsN its offset N, which
+    // the fold step then replaces by the state at the start of segment k+1.
+    int num_seqs;
+    int seg;
+    const int32_t* nl;
+    float* wsM;
+    float* wsN;
+    int m_blocks;       // map launches: blocks [0, m_blocks) compute M, the rest N
+    int final_to_slot;  // final state of a split sequence goes to its last slot (final_state aliases S0)
 };
 
 template <typename T>
@@ -201,7 +213,7 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lptr(void* p)
 // 16 bytes).  Rows at or past the chunk's end are not fetched.
 template <typename TI, int DK, int DV>
 __device__ __forceinline__ void issue_stage(const Args<TI>& a, char* stg, int64_t c1, int L1, int h, int wv,
-                                            int lane) {
+                                            int lane, bool withq, bool withv) {
     typedef Cfg<TI, DK, DV> P;
     if (L1 <= 0) return;
     const size_t tok0 = (size_t)c1 * a.H + h;
@@ -217,17 +229,35 @@ __device__ __forceinline__ void issue_stage(const Args<TI>& a, char* stg, int64_
         }
     };
     rows(a.g, DK, 4, stg);
-    rows(a.q, DK, (int)sizeof(TI), stg + P::SG_G);
+    if (withq) rows(a.q, DK, (int)sizeof(TI), stg + P::SG_G);
     rows(a.k, DK, (int)sizeof(TI), stg + P::SG_G + P::SG_Q);
-    rows(a.v, DV, (int)sizeof(TI), stg + P::SG_G + 2 * P::SG_Q);
+    if (withv) rows(a.v, DV, (int)sizeof(TI), stg + P::SG_G + 2 * P::SG_Q);
     if (wv == 0 && lane < L1)
         __builtin_amdgcn_global_load_lds(gptr(a.beta + tok0 + (size_t)lane * a.H),
                                          lptr(stg + P::SG_G + 2 * P::SG_Q + P::SG_V), 4, 0, 0);
 }
 
-template <typename TI, int DK, int DV>
+// First sequence n in [0, num_seqs) with nl[n + 1] + bias * (n + 1) > key.
+__device__ __forceinline__ int seq_of(const int32_t* nl, int num_seqs, int key, int bias) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (nl[mid + 1] + bias * (mid + 1) > key) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+
+// MAP = false: outputs o for a token range and carries the state from S0 to Sf
+// (a whole sequence, or one segment of a split one).
+// MAP = true: the transition of one full non-last segment.  The recurrence is
+// affine in the state, S_end = M S_start + N, so M is the end state reached from
+// S_start = I with v = 0 (a d_k-column state) and N the one reached from
+// S_start = 0 with the real v; no q, P or o is formed.
+template <typename TI, int DK, int DV, bool MAP>
 __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(Args<TI> a) {
     typedef Cfg<TI, DK, DV> P;
+    constexpr bool OUT = !MAP;
     typedef Mma<TI> M;
     typedef typename M::frag frag;
     typedef typename Pair<TI>::type T2;
@@ -255,11 +285,46 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
     const int tid0 = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
-    const int unit = blockIdx.x;
-    const int n = unit / H, h = unit - n * H;
-    const int64_t tb = a.cu[n], te = a.cu[n + 1];
+    const int b = blockIdx.x;
+    // the workgroup's token range [tb, te) of head h, its start state (s0, or
+    // the identity, or zero) and where its end state goes (sf, or nowhere)
+    int h;
+    int64_t tb, te;
+    const float* s0 = nullptr;
+    float* sf = nullptr;
+    bool eye = false, vzero = false;
+    if constexpr (MAP) {
+        const bool kindM = b < a.m_blocks;
+        const int idx = kindM ? b : b - a.m_blocks;
+        const int k = idx / H;
+        h = idx - k * H;
+        if (k >= a.nl[a.num_seqs]) return;  // fewer non-last segments than the bound the grid was sized for
+        const int n = seq_of(a.nl, a.num_seqs, k, 0);
+        tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
+        te = tb + a.seg;
+        eye = vzero = kindM;
+        sf = kindM ? a.wsM + ((size_t)k * H + h) * DK * DK : a.wsN + ((size_t)k * H + h) * DK * DV;
+    } else if (a.seg > 0) {
+        const int u = b / H;
+        h = b - u * H;
+        if (u >= a.nl[a.num_seqs] + a.num_seqs) return;
+        const int n = seq_of(a.nl, a.num_seqs, u, 1);
+        const int j = u - (a.nl[n] + n), last = a.nl[n + 1] - a.nl[n];
+        const size_t unit = (size_t)n * H + h;
+        tb = a.cu[n] + (int64_t)j * a.seg;
+        te = tb + a.seg < a.cu[n + 1] ? tb + a.seg : a.cu[n + 1];
+        if (j == 0) s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
+        else s0 = a.wsN + ((size_t)(a.nl[n] + j - 1) * H + h) * DK * DV;
+        if (j == last && a.Sf) sf = (j > 0 && a.final_to_slot) ? const_cast<float*>(s0) : a.Sf + unit * DK * DV;
+    } else {
+        const int n = b / H;
+        h = b - n * H;
+        tb = a.cu[n];
+        te = a.cu[n + 1];
+        s0 = a.S0 ? a.S0 + (size_t)b * DK * DV : nullptr;
+        sf = a.Sf ? a.Sf + (size_t)b * DK * DV : nullptr;
+    }
     const int col0 = 16 * w;  // this wave's state columns
-    const size_t sbase = (size_t)unit * DK * DV;
     const uint32_t krow = (uint32_t)H * DK;  // elements between consecutive tokens of q, k, g
     const uint32_t vrow = (uint32_t)H * DV;  // ... of v, o
 
@@ -269,14 +334,17 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[rt][i] = a.S0 ? at<float>(a.S0 + sbase, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g0 + i;
+            S[rt][i] = s0 ? at<float>(s0, (row * DV + col0 + r0) * 4) : (eye && row == col0 + r0) ? 1.f : 0.f;
+        }
 
-    if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, tb, (int)(te - tb < C ? te - tb : C), h, w, tid0 & 63);
+    if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, tb, (int)(te - tb < C ? te - tb : C), h, w, tid0 & 63, OUT, !vzero);
 
     // A chunk's outputs are stored at the start of the next chunk, after its
     // wait for the prefetch: vmcnt also counts stores, so storing them at the
     // end of the chunk would make that wait a full store round trip.
+    // opend[rb] holds o[16 rb + r][col0 + 4g .. col0 + 4g + 3] (lane r + 16g).
     typedef typename std::conditional<sizeof(TI) == 2, bf16x4, floatx4>::type OV;
     OV opend[4];
     TI* opend_base = nullptr;
@@ -284,12 +352,10 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
     auto flush_o = [&](int gl, int rl) {
         if (opend_base) {
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * rb + 4 * gl + i;
-                    if (t < opend_L) at_mut<TI>(opend_base, (t * vrow + col0 + rl) * (uint32_t)sizeof(TI)) = opend[rb][i];
-                }
+            for (int rb = 0; rb < 4; ++rb) {
+                const int t = 16 * rb + rl;
+                if (t < opend_L) at_mut<OV>(opend_base, (t * vrow + col0 + 4 * gl) * (uint32_t)sizeof(TI)) = opend[rb];
+            }
         }
     };
 
@@ -317,19 +383,24 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
         // staging area, or from global memory where the second read hits the
         // cache): once to sum the group's log-decays, once to build the
         // operands, so few registers stay live.
+        // Rows at or past L read in-bounds memory (a stale staging row, or the
+        // chunk's last token) and are replaced by zeros with a select, so the
+        // loads carry no branches and can be issued together.
         auto rd_g = [&](int t) -> floatx2 {
-            if (t >= L) return floatx2{0.f, 0.f};
-            if constexpr (P::STAGE) return *reinterpret_cast<const floatx2*>(stg_g + t * DK + ch);
-            else return at<floatx2>(gbase, (t * krow + ch) * 4);
+            floatx2 x;
+            if constexpr (P::STAGE) x = *reinterpret_cast<const floatx2*>(stg_g + t * DK + ch);
+            else x = at<floatx2>(gbase, ((t < L ? t : L - 1) * krow + ch) * 4);
+            return t < L ? x : floatx2{0.f, 0.f};
         };
         auto rd_qk = [&](const TI* sp, const TI* gp, int t) -> floatx2 {
-            if (t >= L) return floatx2{0.f, 0.f};
-            if constexpr (P::STAGE) return to_f2(*reinterpret_cast<const T2*>(sp + t * DK + ch));
-            else return to_f2(at<T2>(gp, (t * krow + ch) * (uint32_t)sizeof(TI)));
+            floatx2 x;
+            if constexpr (P::STAGE) x = to_f2(*reinterpret_cast<const T2*>(sp + t * DK + ch));
+            else x = to_f2(at<T2>(gp, ((t < L ? t : L - 1) * krow + ch) * (uint32_t)sizeof(TI)));
+            return t < L ? x : floatx2{0.f, 0.f};
         };
         if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
         __syncthreads();  // ... and every other wave's; the previous chunk is done with LDS
-        flush_o(g, r);    // the previous chunk's outputs
+        if constexpr (OUT) flush_o(g, r);  // the previous chunk's outputs
         // the solve's v right-hand side in accumulator layout: vr[I][i] = v[16I + 4g + i][col0 + r]
         typedef typename std::conditional<sizeof(TI) == 2, bf16x4, floatx4>::type VR;
         VR vr[4];
@@ -338,20 +409,16 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * I + 4 * g + i;
-                TI x = TI(0.f);
-                if (t < L) {
-                    if constexpr (P::STAGE) x = stg_v[t * DV + col0 + r];
-                    else x = at<TI>(vbase, (t * vrow + col0 + r) * (uint32_t)sizeof(TI));
-                }
-                vr[I][i] = x;
+                TI x;
+                if constexpr (P::STAGE) x = stg_v[t * DV + col0 + r];
+                else x = at<TI>(vbase, ((t < L ? t : L - 1) * vrow + col0 + r) * (uint32_t)sizeof(TI));
+                vr[I][i] = (t < L && !vzero) ? x : TI(0.f);
             }
         if (tid < C) {
-            float b = 0.f;
-            if (tid < L) {
-                if constexpr (P::STAGE) b = stg_b[tid];
-                else b = at<float>(a.beta + tok0, tid * H * 4);
-            }
-            s_beta[tid] = b;
+            float b;
+            if constexpr (P::STAGE) b = stg_b[tid];
+            else b = at<float>(a.beta + tok0, (tid < L ? tid : L - 1) * H * 4);
+            s_beta[tid] = tid < L ? b : 0.f;
         }
         const int t0 = grp * P::TPG;
         {
@@ -407,7 +474,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                     const floatx2 e = exp2v(G), ei = exp2v(-G);
                     const floatx2 kk = rd_qk(stg_k, kbase, t);
                     const floatx2 kh = kk * ei;
-                    op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
+                    if constexpr (OUT) op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
                     op_store2<TI, P::KM>(Ko, t, ch, kk * e);
                     op_store2<TI, P::KM>(Kh, t, ch, kh);
                     kd[j] = kh * gam;  // K_dec = k e^{G_L - G}
@@ -439,7 +506,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                     const floatx2 m = floatx2{s_mid[(t >> 4) * DK + ch], s_mid[(t >> 4) * DK + ch + 1]};
                     const floatx2 e = exp2v(G - m);
                     const floatx2 kk = rd_qk(stg_k, kbase, t);
-                    op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
+                    if constexpr (OUT) op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
                     op_store2<TI, P::KM>(Ko, t, ch, kk * e);
                     kd[j] = kk * exp2v(tot - G);
                 }
@@ -489,19 +556,19 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
         }
         if (fast) {
             __syncthreads();
-            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane);
+            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
             // 20 tiles (10 of A, 10 of P); wave w takes tiles w, w+NW, ...
 #pragma unroll
             for (int j = 0; j < P::NPT; ++j) {
                 const int q = w + P::NW * j;
-                if (q < 20) {
+                if (q < (OUT ? 20 : 10)) {
                     int I, J;
                     tri_pair(q % 10, I, J);
                     const floatx4 acc = gram(q < 10 ? Ko : Qo, I, J);
                     if (q < 10) {
                         accA[j] = acc;
                         aP[j] = q;
-                    } else {
+                    } else if constexpr (OUT) {
                         store_p(acc, I, J);
                     }
                 }
@@ -524,7 +591,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
                 for (int jj = 0; jj < P::NQS; ++jj) {
                     const int qq = w + P::NW * jj;
-                    if (qq < 2 * (I + 1)) {
+                    if (qq < (OUT ? 2 : 1) * (I + 1)) {
                         if (qq < I + 1) {
                             // at most one A tile per wave and row block: slot I
 #pragma unroll
@@ -533,7 +600,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                                     accA[sI] = gram(Ko, I, qq);
                                     aP[sI] = tri_id(I, qq);
                                 }
-                        } else {
+                        } else if constexpr (OUT) {
                             store_p(gram(Qo, I, qq - I - 1), I, qq - I - 1);
                         }
                     }
@@ -547,11 +614,11 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                     const int t = t0 + tt;
                     G += rd_g(t);
                     const floatx2 e = exp2v(G);
-                    op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
+                    if constexpr (OUT) op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
                     op_store2<TI, P::KM>(Ko, t, ch, rd_qk(stg_k, kbase, t) * e);
                 }
             }
-            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane);
+            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
         }
         // -A tiles: lane r + 16g holds -beta_t A[t][s], t = 16I + r, s = 16J + 4g + i
 #pragma unroll
@@ -639,20 +706,24 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 
         // ---- 5. outputs and state (own columns) -------------------------------
         // O = Q~ S + P U one row block at a time, then S <- diag(e^{G_L}) S + K_dec^T U.
+        // O is formed transposed, O^T = S^T Q~^T + U^T P^T: the operand layouts
+        // of MFMA's two inputs coincide, so the same fragments serve with their
+        // roles swapped, and each lane ends with four adjacent columns of one
+        // token row (one 8- or 16-byte store).
         frag bU[P::TM];
 #pragma unroll
         for (int m = 0; m < P::TM; ++m) bU[m] = acc_perm<TI>(U, m, 4);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < (OUT ? 4 : 0); ++rb) {
             frag aq[P::KM];
 #pragma unroll
             for (int m = 0; m < P::KM; ++m) aq[m] = op_frag<TI, P::KM>(Qo, rb, m, lane);
             floatx4 O = zero4();
 #pragma unroll
-            for (int m = 0; m < P::KM; ++m) O = M::mma(aq[m], bS[m], O);
+            for (int m = 0; m < P::KM; ++m) O = M::mma(bS[m], aq[m], O);
 #pragma unroll
             for (int m = 0; m < P::TM; ++m)
-                if ((m * KW) / 4 <= rb) O = M::mma(op_frag<TI, P::TM>(Po, rb, m, lane), bU[m], O);
+                if ((m * KW) / 4 <= rb) O = M::mma(bU[m], op_frag<TI, P::TM>(Po, rb, m, lane), O);
 #pragma unroll
             for (int i = 0; i < 4; ++i) opend[rb][i] = from_f32<TI>(O[i]);
         }
@@ -669,30 +740,129 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
             for (int m = 0; m < P::TM; ++m) S[rt] = M::mma(ak[m], bU[m], S[rt]);
         }
-        opend_base = obase;
-        opend_L = L;
+        if constexpr (OUT) {
+            opend_base = obase;
+            opend_L = L;
+        }
         // The next chunk writes LDS only after its first barrier, which every
         // wave reaches after finishing this state pass.
     }
-    flush_o(g0, r0);
+    if constexpr (OUT) flush_o(g0, r0);
 
-    if (a.Sf) {
+    if (sf) {
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                at_mut<float>(a.Sf + sbase, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) = S[rt][i];
+            for (int i = 0; i < 4; ++i) at_mut<float>(sf, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) = S[rt][i];
     }
+}
+
+// nl[0] = 0, nl[n + 1] = nl[n] + (number of non-last segments of sequence n):
+// a sequence of len > 0 tokens has ceil(len / seg) segments, an empty one has
+// one (of zero tokens).  One workgroup, a block-wide scan per 256 sequences.
+__global__ __launch_bounds__(256) void seg_table_kernel(const int32_t* __restrict__ cu, int num_seqs, int seg,
+                                                        int32_t* __restrict__ nl) {
+    __shared__ int part[256];
+    const int t = threadIdx.x;
+    int carry = 0;
+    if (t == 0) nl[0] = 0;
+    for (int base = 0; base < num_seqs; base += 256) {
+        const int n = base + t;
+        int c = 0;
+        if (n < num_seqs) {
+            const int len = cu[n + 1] - cu[n];
+            c = len > 0 ? (len - 1) / seg : 0;
+        }
+        part[t] = c;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int x = t >= off ? part[t - off] : 0;
+            __syncthreads();
+            part[t] += x;
+            __syncthreads();
+        }
+        if (n < num_seqs) nl[n + 1] = carry + part[t];
+        carry += part[255];
+        __syncthreads();
+    }
+}
+
+// Serial fold over the segments of one (sequence, head), 16 state columns per
+// workgroup (columns of the state evolve independently):
+//   S_start(j + 1) = M_j S_start(j) + N_j,  S_start(0) = S0 (or zero),
+// written over N_j.  fp32 FMA; M_j is staged in LDS, S in LDS.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void seg_fold_kernel(const int32_t* __restrict__ nl, int H,
+                                                       const float* __restrict__ S0, const float* __restrict__ wsM,
+                                                       float* __restrict__ wsN) {
+    constexpr int NCB = DV / 16, RPT = DK / 16, LDM = DK + 4;
+    extern __shared__ __attribute__((aligned(16))) float fsm[];
+    float* Ms = fsm;              // [DK][LDM]
+    float* Ss = fsm + DK * LDM;  // [DK][16]
+    const int bid = blockIdx.x, cb = bid % NCB, unit = bid / NCB, n = unit / H, h = unit - n * H;
+    const int k0 = nl[n], cnt = nl[n + 1] - k0;
+    if (cnt == 0) return;
+    const int t = threadIdx.x, c = t & 15, rg = t >> 4;  // column c, rows rg + 16 r
+    const int col = 16 * cb + c;
+    for (int i = rg; i < DK; i += 16) Ss[i * 16 + c] = S0 ? S0[((size_t)unit * DK + i) * DV + col] : 0.f;
+    for (int j = 0; j < cnt; ++j) {
+        const size_t slot = (size_t)(k0 + j) * H + h;
+        const floatx4* M = reinterpret_cast<const floatx4*>(wsM + slot * DK * DK);
+        float* N = wsN + slot * DK * DV;
+        __syncthreads();  // S written, previous readers of Ms done
+        for (int e = t; e < DK * DK / 4; e += 256) {
+            const int row = e / (DK / 4), c4 = e - row * (DK / 4);
+            *reinterpret_cast<floatx4*>(Ms + row * LDM + 4 * c4) = M[e];
+        }
+        __syncthreads();
+        float acc[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) acc[r] = N[(rg + 16 * r) * DV + col];
+        for (int kk = 0; kk < DK; kk += 4) {
+            const float s0v = Ss[kk * 16 + c], s1v = Ss[(kk + 1) * 16 + c], s2v = Ss[(kk + 2) * 16 + c],
+                        s3v = Ss[(kk + 3) * 16 + c];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const floatx4 m = *reinterpret_cast<const floatx4*>(Ms + (rg + 16 * r) * LDM + kk);
+                acc[r] += m[0] * s0v + m[1] * s1v + m[2] * s2v + m[3] * s3v;
+            }
+        }
+        __syncthreads();  // every read of S is done
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            Ss[(rg + 16 * r) * 16 + c] = acc[r];
+            N[(rg + 16 * r) * DV + col] = acc[r];
+        }
+    }
+}
+
+// final_state of every split sequence, from its last slot (used when
+// final_state aliases the initial state, which segment 0 still reads).
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void seg_final_kernel(const int32_t* __restrict__ nl, int H,
+                                                        const float* __restrict__ wsN, float* __restrict__ Sf) {
+    const int unit = blockIdx.x, n = unit / H, h = unit - n * H;
+    if (nl[n + 1] == nl[n]) return;  // one segment: written by its own workgroup
+    const floatx4* src = reinterpret_cast<const floatx4*>(wsN + ((size_t)(nl[n + 1] - 1) * H + h) * DK * DV);
+    floatx4* dst = reinterpret_cast<floatx4*>(Sf + (size_t)unit * DK * DV);
+    for (int e = threadIdx.x; e < DK * DV / 4; e += 256) dst[e] = src[e];
+}
+
+template <typename TI, int DK, int DV, bool MAP>
+hipError_t launch_seq(const Args<TI>& a, int64_t blocks, hipStream_t s) {
+    typedef Cfg<TI, DK, DV> P;
+    static_assert(P::LDS <= 160 * 1024, "LDS budget");
+    if (blocks <= 0) return hipSuccess;
+    auto kern = prefill_seq_kernel<TI, DK, DV, MAP>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(P::NT), P::LDS, s, a);
+    return hipGetLastError();
 }
 
 template <typename TI, int DK, int DV>
 hipError_t run(const PrefillLaunch& p, hipStream_t s) {
-    typedef Cfg<TI, DK, DV> P;
-    static_assert(P::LDS <= 160 * 1024, "LDS budget");
-    auto kern = prefill_seq_kernel<TI, DK, DV>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS);
-    if (e != hipSuccess) return e;
     Args<TI> a;
     a.q = static_cast<const TI*>(p.q);
     a.k = static_cast<const TI*>(p.k);
@@ -704,8 +874,51 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     a.Sf = p.final_state;
     a.o = static_cast<TI*>(p.o);
     a.H = p.H;
+    a.num_seqs = p.num_seqs;
+    a.seg = 0;
+    a.nl = nullptr;
+    a.wsM = a.wsN = nullptr;
+    a.m_blocks = 0;
+    a.final_to_slot = 0;
     const int64_t units = (int64_t)p.num_seqs * p.H;
-    hipLaunchKernelGGL(kern, dim3((unsigned)units), dim3(P::NT), P::LDS, s, a);
+    if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
+
+    // Time split: maps of the non-last segments, fold, then every segment.
+    const PrefillWorkspace ws = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
+    char* w = static_cast<char*>(p.workspace);
+    a.seg = p.seg;
+    a.nl = reinterpret_cast<int32_t*>(w + ws.nl_off);
+    a.wsM = reinterpret_cast<float*>(w + ws.m_off);
+    a.wsN = reinterpret_cast<float*>(w + ws.n_off);
+    a.final_to_slot = p.final_state && p.final_state == p.initial_state;
+    hipLaunchKernelGGL(seg_table_kernel, dim3(1), dim3(256), 0, s, p.cu_seqlens, p.num_seqs, p.seg,
+                       const_cast<int32_t*>(a.nl));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t map_blocks = ws.slots * p.H;
+    if (map_blocks > 0) {
+        if (DK == DV) {
+            a.m_blocks = (int)map_blocks;
+            e = launch_seq<TI, DK, DV, true>(a, 2 * map_blocks, s);
+        } else {
+            a.m_blocks = (int)map_blocks;
+            e = launch_seq<TI, DK, DK, true>(a, map_blocks, s);
+            a.m_blocks = 0;
+            if (e == hipSuccess) e = launch_seq<TI, DK, DV, true>(a, map_blocks, s);
+        }
+        if (e != hipSuccess) return e;
+        constexpr int FOLD_LDS = (DK * (DK + 4) + DK * 16) * 4;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(seg_fold_kernel<DK, DV>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, FOLD_LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((seg_fold_kernel<DK, DV>), dim3((unsigned)(units * (DV / 16))), dim3(256), FOLD_LDS, s,
+                           a.nl, p.H, p.initial_state, a.wsM, a.wsN);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    e = launch_seq<TI, DK, DV, false>(a, ((int64_t)p.num_seqs + ws.slots) * p.H, s);
+    if (e != hipSuccess || !a.final_to_slot || map_blocks == 0) return e;
+    hipLaunchKernelGGL((seg_final_kernel<DK, DV>), dim3((unsigned)units), dim3(256), 0, s, a.nl, p.H, a.wsN,
+                       p.final_state);
     return hipGetLastError();
 }
 

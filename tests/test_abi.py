@@ -84,3 +84,36 @@ def test_workspace_bound_needs_no_lengths():
     a = gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128)
     b = gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128)
     assert a == b and a >= 0
+
+
+def test_time_split_plan(monkeypatch):
+    monkeypatch.delenv("GDN_PREFILL_SEGMENT", raising=False)
+    # one 65,536-token sequence x 32 heads: 32 workgroups would leave most CUs idle -> split
+    assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128) > 0
+    # 64 sequences of ~8K tokens x 32 heads: 2048 workgroups already -> no split
+    assert gdn.gdn_prefill_workspace_bytes(540000, 64, 32, 128, 128) == 0
+    # short sequences are never split
+    assert gdn.gdn_prefill_workspace_bytes(256, 1, 2, 64, 64) == 0
+    assert gdn.gdn_prefill_workspace_bytes(0, 3, 2, 64, 64) == 0
+
+
+def test_time_split_workspace_layout(monkeypatch):
+    # forced 8192-token segments: 8 full segments -> at most 8 non-last ones per
+    # 65,536 tokens; each (slot, head) holds M (d_k x d_k) and N (d_k x d_v) in
+    # fp32, each area rounded up to 256 bytes, then the int32 table [n + 1]
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "8192")
+    assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 64) == 8 * 32 * 128 * 128 * 4 + 8 * 32 * 128 * 64 * 4 + 256
+    assert gdn.gdn_prefill_workspace_bytes(65535, 3, 2, 64, 64) == 7 * 2 * 64 * 64 * 4 * 2 + 256
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "100")  # rounded up to 128
+    assert gdn.gdn_prefill_workspace_bytes(1000, 1, 1, 64, 64) == 7 * 64 * 64 * 4 * 2 + 256
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "0")
+    assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128) == 0
+
+
+def test_short_workspace_rejected(lib, monkeypatch):
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "64")
+    p = ctypes.c_void_p(0x10000)  # aligned; never dereferenced because validation rejects the call first
+    need = gdn.gdn_prefill_workspace_bytes(1000, 1, 2, 64, 64)
+    assert need > 0
+    assert _prefill(lib, q=p, cu=p, o=p, T=1000, H=2, ws=NUL, wsb=0) == INVALID
+    assert _prefill(lib, q=p, cu=p, o=p, T=1000, H=2, ws=p, wsb=need - 1) == INVALID
