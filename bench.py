@@ -13,10 +13,21 @@ The decode step (512 sequences x 32 heads, one token each, fp32 state updated
 in place) is timed in the same run over K calls and reported under "decode"
 as achieved HBM bandwidth.
 
-"roofline" prices the prefill launch against MI355X's 8 TB/s HBM with the
+"roofline" prices one gdn_prefill call against MI355X's 8 TB/s HBM with the
 algorithmic bytes of the layer (q, k, v, o in bf16, g and beta in fp32, the
-final state); "cpu_baseline" is the fp32 oracle on the host cores over a
-bounded prefix of the same workload.  One JSON line is printed.
+final state).  The call is a short sequence of kernels on one stream (for this
+workload: segment table, segment transitions, fold, replay of every segment);
+its duration is measured with HIP events around the calls on that stream.
+"traffic" is the HBM bytes the rocprofv3 counters FETCH_SIZE and WRITE_SIZE
+read for those kernels, scaled by what the same counters read for a plain
+copy of known size (profiles/traffic.json; null when the kernel sources have
+changed since).  "cpu_baseline" is the fp32 oracle on the host cores over the
+same workload.  One JSON line is printed.
+
+    python bench.py --copy-calibration 1073741824
+
+runs only a device-to-device copy of that many bytes (three times), the
+reference for scaling the counters.
 """
 
 from __future__ import annotations
@@ -37,7 +48,8 @@ if ROOT not in sys.path:
 
 METRIC = "prefill tokens/s (H=32,d=128,T=64K bf16) + decode HBM GB/s; % of roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp"]
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published (no sparsity)
+KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp", "gdn_kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -46,6 +58,14 @@ def prefill_bytes(T_tokens: int, H: int, dk: int, dv: int, n_seqs: int, elt: int
     per_head_token = elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv
     states = n_seqs * H * dk * dv * 4 * (2 if init_state else 1)
     return T_tokens * H * per_head_token + states
+
+
+def prefill_flops(T_tokens: int, H: int, dk: int, dv: int, C: int = 64):
+    """Algorithmic flops of one prefill launch with the causal intra-chunk tiles counted dense:
+    three d_k x d_v state contractions per token (Q~S, W S, K_dec^T U), the two Gram products and
+    the P U and W, U~ products inside the chunk, and the C^3/3 triangular solve spread over C tokens."""
+    per = 6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3
+    return T_tokens * H * per
 
 
 def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int = 2):
@@ -90,6 +110,15 @@ def time_loop(fn, steps: int, warmup: int, stream):
     return start.elapsed_time(stop) / steps  # ms per call
 
 
+def copy_calibration(nbytes: int):
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "calls": 3}), flush=True)
+
+
 def cpu_baseline(x, tokens: int):
     """fp32 oracle on the host over the first `tokens` tokens of every head."""
     import oracle
@@ -103,9 +132,16 @@ def cpu_baseline(x, tokens: int):
     t0 = time.perf_counter()
     oracle.recurrent(*args, dtype=np.float32, threads=threads)
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    whole = "the whole 65536-token sequence" if tokens >= x.q.shape[0] else f"the first {tokens} tokens"
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {tokens} tokens of the 65536-token sequence, all {H} heads, fp32 sequential "
-                      f"recurrence, {dt:.1f} s wall"}
+            "sample": f"{whole}, all {H} heads, fp32 sequential recurrence (OpenMP over heads), {dt:.2f} s wall; "
+                      f"host {model or 'unknown CPU'}, {os.cpu_count()} logical CPUs visible"}
 
 
 def main():
@@ -115,11 +151,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
               f"(asked for --gpus {args.gpus}); sharding across GPUs is described in DESIGN.md.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import gated_delta_rule_linear_amd as gdn
     from gated_delta_rule_linear_amd import inputs
@@ -134,14 +175,18 @@ def main():
     x = inputs.make_workload("prefill_64k", seed=0, device=dev)
     o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
     S = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+    ws_bytes = gdn.gdn_prefill_workspace_bytes(T, 1, H, d, d)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step():
-        gdn.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, final_state=S, o=o, stream=stream)
+        gdn.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, final_state=S, o=o, workspace=ws, stream=stream)
 
     ms = time_loop(step, args.steps, args.warmup, stream)
     tokens_per_s = T / (ms / 1e3)
     pbytes = prefill_bytes(T, H, d, d, 1)
     achieved = pbytes / (ms / 1e3) / 1e9
+    pflops = prefill_flops(T, H, d, d)
+    tflops = pflops / (ms / 1e3) / 1e12
 
     # sampled parity on the timed inputs: head 0, first 2048 tokens
     import oracle
@@ -184,14 +229,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill_64k", "num_seqs": 1, "T": T, "H": H, "d_k": d, "d_v": d,
                    "gates": "alpha=0.9+0.1*sigmoid(N(0,1)) per key channel", "initial_state": "zero",
-                   "chunk": 64},
+                   "chunk": 64, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "prefill_seq_kernel<bf16,128,128>", "algorithmic_bytes_per_launch": pbytes},
+                     "kernel": "gdn_prefill call (seg_table, prefill_seq_kernel<bf16,128,128,map>, seg_fold, "
+                               "prefill_seq_kernel<bf16,128,128,out>)",
+                     "algorithmic_bytes_per_launch": pbytes},
         "decode": {"workload": "decode_512x32", "N": N, "H": Hd, "d_k": d, "d_v": d, "ms_per_step": dms,
                    "tokens_per_s": N / (dms / 1e3), "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": dgbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": dbytes,
                    "traffic": measured_traffic("decode")},
+        "mfma": {"algorithmic_flops_per_launch": pflops, "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS},
+        "attainable_roofline_frac": max(pflops / (MFMA_BF16_PEAK_TFLOPS * 1e12), pbytes / (HBM_PEAK_GBS * 1e9))
+                                    / (ms / 1e3),
         "parity": {"prefill_o_rel_err_head0_first2048": parity},
     }
     if not args.no_cpu:

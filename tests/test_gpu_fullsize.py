@@ -1,0 +1,131 @@
+"""GPU parity at full workload sizes, in the launch configuration bench.py
+times (the split plan the library picks by itself).  The fp64 oracle computes
+sampled (sequence, head) units in full — every output token and the final
+state of each sampled unit — and the library's result for those units is
+compared element by element.  The 2^20-token case is checked on one head in
+full with the fp32 oracle, and on every head against the unsplit kernel."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_linear_amd as gdn
+import oracle
+from gated_delta_rule_linear_amd import inputs
+from helpers import assert_close, log, np64
+
+pytestmark = pytest.mark.gpu
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+    os.environ.pop("GDN_PREFILL_SEGMENT", None)
+
+
+def _oracle_units(x, units, dtype=np.float64):
+    """{(n, h): (o, S)} from the oracle, one call per sequence over its sampled heads."""
+    cu = x.cu_seqlens.cpu().numpy()
+    by_seq = {}
+    for n, h in units:
+        by_seq.setdefault(n, []).append(h)
+    res = {}
+    for n, hs in by_seq.items():
+        a, b = int(cu[n]), int(cu[n + 1])
+        idx = torch.tensor(hs, device=x.q.device)
+        sl = lambda t: t[a:b].index_select(1, idx).to("cpu", torch.float64).numpy()
+        S0 = None
+        if x.initial_state is not None:
+            S0 = x.initial_state[n:n + 1].index_select(1, idx).to("cpu", torch.float64).numpy()
+        o, S = oracle.recurrent(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), np.array([0, b - a], np.int32),
+                                initial_state=S0, dtype=dtype, threads=min(len(hs), 16))
+        for j, h in enumerate(hs):
+            res[(n, h)] = (o[:, j], S[0, j])
+    return res
+
+
+def _check_units(x, o, S, units, tol=TOL_BF16):
+    cu = x.cu_seqlens.cpu().numpy()
+    ref = _oracle_units(x, units)
+    for (n, h), (ro, rS) in ref.items():
+        a, b = int(cu[n]), int(cu[n + 1])
+        assert_close(f"seq {n} head {h}: o", np64(o[a:b, h]), ro, tol)
+        assert_close(f"seq {n} head {h}: final state", np64(S[n, h]), rS, tol)
+
+
+def _run(x):
+    T, H, dk = x.q.shape
+    dv = x.v.shape[-1]
+    n = len(x.lengths)
+    ws = gdn.gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+    log(f"  T={T} H={H} seqs={n}: workspace {ws} bytes ({'split' if ws else 'whole sequences'})")
+    o, S = gdn.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def test_prefill_64k_as_benchmarked():
+    log("prefill_64k: one 65536-token sequence, 32 heads, d 128, bf16")
+    x = inputs.make_workload("prefill_64k", seed=0, device="cuda")
+    o, S = _run(x)
+    _check_units(x, o, S, [(0, 0), (0, 13), (0, 31)])
+
+
+def test_batch4_t8k():
+    log("batch4_t8k: four 8192-token sequences, 32 heads")
+    x = inputs.make_workload("batch4_t8k", seed=1, device="cuda")
+    o, S = _run(x)
+    _check_units(x, o, S, [(0, 0), (1, 7), (2, 20), (3, 31)])
+
+
+def test_varlen64():
+    log("varlen64: 64 sequences of 512..16384 tokens, 32 heads, random initial states")
+    x = inputs.make_workload("varlen64", seed=2, device="cuda")
+    o, S = _run(x)
+    L = x.lengths
+    longest, shortest = int(np.argmax(L)), int(np.argmin(L))
+    _check_units(x, o, S, [(longest, 3), (shortest, 30), (17, 16), (63, 0)])
+
+
+@pytest.mark.timeout(600)
+def test_long_1m():
+    log("long_1m: one 2^20-token sequence, 16 heads, a_min 0.99")
+    x = inputs.make_workload("long_1m", seed=3, device="cuda")
+    o, S = _run(x)
+    # every head against the unsplit kernel (one workgroup per head, no time split)
+    os.environ["GDN_PREFILL_SEGMENT"] = "0"
+    try:
+        o1, S1 = gdn.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("GDN_PREFILL_SEGMENT", None)
+    for h in range(16):
+        assert_close(f"head {h}: o split vs unsplit", np64(o[:, h]), np64(o1[:, h]), TOL_BF16)
+        assert_close(f"head {h}: state split vs unsplit", np64(S[0, h]), np64(S1[0, h]), TOL_BF16)
+    del o1, S1
+    # head 5 in full with the fp32 oracle
+    ref = _oracle_units(x, [(0, 5)], dtype=np.float32)
+    ro, rS = ref[(0, 5)]
+    assert_close("head 5: o (fp32 oracle)", np64(o[:, 5]), ro, TOL_BF16)
+    assert_close("head 5: final state (fp32 oracle)", np64(S[0, 5]), rS, TOL_BF16)
+
+
+def test_decode_512x32_steps():
+    log("decode: 512 sequences x 32 heads, d 128, bf16, 4 steps")
+    N, H, d = 512, 32, 128
+    S0, draws = inputs.make_decode_steps(N, H, d, d, 4, dtype=torch.bfloat16, seed=4, device="cuda")
+    state = S0.clone()
+    sample = [0, 131, 511]
+    ref_S = np64(S0[sample])
+    for st, dr in enumerate(draws):
+        o = gdn.gdn_decode(dr.q, dr.k, dr.v, dr.g, dr.beta, state)
+        torch.cuda.synchronize()
+        pick = lambda t: np64(t[sample])
+        ref_o, ref_S = oracle.decode_step(pick(dr.q), pick(dr.k), pick(dr.v), pick(dr.g), pick(dr.beta), ref_S)
+        assert_close(f"step {st}: o", np64(o[sample]), ref_o, 1e-2)
+    assert_close("state", np64(state[sample]), ref_S, 1e-5)

@@ -197,6 +197,38 @@ def test_split_and_resume_equals_whole():
         np.testing.assert_allclose(S2, Sf, rtol=0, atol=1e-14)
 
 
+def test_affine_compose_identity():
+    # The token update is affine in the state: S_t = (I - b k k^T) diag(a) S_{t-1} + b k v^T.
+    # So over any token range S_end = M S_start + N, with M the end state reached
+    # from S_start = I and v = 0 (a d_k-column state), N the one reached from 0.
+    # Composing two ranges: S_end = M2 (M1 S0 + N1) + N2.  The time split of the
+    # prefill rests on exactly this.
+    x = inputs.make_prefill_inputs([260], 1, 16, 12, dtype=torch.float32, init_state=True, seed=31)
+    q, k, v, g, beta, cu = _args(x)
+    S0 = _np(x.initial_state)
+    _, Sf = oracle.recurrent(q, k, v, g, beta, cu, initial_state=S0)
+
+    def maps(lo, hi):
+        c = np.array([0, hi - lo], np.int32)
+        eye = np.eye(16)[None, None]
+        zv = np.zeros((hi - lo, 1, 16))
+        _, M = oracle.recurrent(q[lo:hi], k[lo:hi], zv, g[lo:hi], beta[lo:hi], c, initial_state=eye)
+        _, N = oracle.recurrent(q[lo:hi], k[lo:hi], v[lo:hi], g[lo:hi], beta[lo:hi], c)
+        return M[0, 0], N[0, 0]
+
+    M, N = maps(0, 260)
+    np.testing.assert_allclose(M @ S0[0, 0] + N, Sf[0, 0], rtol=0, atol=1e-13)
+    M1, N1 = maps(0, 100)
+    M2, N2 = maps(100, 260)
+    np.testing.assert_allclose(M2 @ (M1 @ S0[0, 0] + N1) + N2, Sf[0, 0], rtol=0, atol=1e-13)
+    # M is the product of the per-token transitions, built here directly
+    P = np.eye(16)
+    for t in range(100):
+        kt = k[t, 0]
+        P = (np.eye(16) - beta[t, 0] * np.outer(kt, kt)) @ np.diag(np.exp(g[t, 0])) @ P
+    np.testing.assert_allclose(M1, P, rtol=0, atol=1e-13)
+
+
 def test_empty_sequences_keep_initial_state():
     x = inputs.make_prefill_inputs([0, 5, 0], 2, 4, 3, dtype=torch.float32, init_state=True, seed=9)
     q, k, v, g, beta, cu = _args(x)
