@@ -46,12 +46,15 @@ namespace gdn {
 // through its chunks in order, so a batch of few long sequences leaves most of
 // the 256 compute units idle.  Cutting sequences into segments of Ls tokens
 // costs a second pass over the non-last segments (their transitions M and N,
-// about MAP_COST of a full pass, for both M and N) and buys parallelism.  The
-// plan compares, in units of one chunk of the full pass, the critical path
-//   whole sequences:  ceil(units / CUs) * chunks
-//   split:            ceil(2 units (P-1) / CUs) * Ls/64 * MAP_COST + ceil(units P / CUs) * Ls/64
+// each about MAP_COST of a full pass) and a serial fold, and buys parallelism.
+// The plan compares critical paths in units of one chunk of the full pass,
+// with START chunks of fixed cost per workgroup and FOLD per fold step:
+//   whole sequences:  ceil(units / CUs) * (chunks + START)
+//   split into P:     ceil(2 units (P-1) / CUs) * (Ls/64 * MAP_COST + START)
+//                     + (P-1) * FOLD + ceil(units P / CUs) * (Ls/64 + START)
 // for sequences of the mean length (the lengths themselves are on the device),
-// and splits only when that saves at least 15%.
+// and splits when that saves at least 5%.  The constants are fitted to
+// measured times of the two passes on MI355X.
 int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H) {
     if (const char* e = std::getenv("GDN_PREFILL_SEGMENT")) {
         if (*e) {
@@ -60,22 +63,23 @@ int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H) {
         }
     }
     if (num_seqs <= 0 || T_total <= 0 || H <= 0) return 0;
-    constexpr double CUS = 256.0, MAP_COST = 0.6;
+    constexpr double CUS = 256.0, MAP_COST = 0.76, START = 2.0, FOLD = 1.0;
     const double units = (double)num_seqs * H;
     const int64_t len = (T_total + num_seqs - 1) / num_seqs;
     auto rounds = [&](double wgs) { return std::ceil(wgs / CUS); };
-    const double whole = rounds(units) * std::ceil(len / 64.0);
+    const double whole = rounds(units) * (std::ceil(len / 64.0) + START);
     double best = whole;
     int64_t best_seg = 0;
     for (int64_t ls = 1024; ls < len; ls += 512) {
         const double P = std::ceil((double)len / ls), ch = ls / 64.0;
-        const double t = rounds(2 * units * (P - 1)) * ch * MAP_COST + rounds(units * P) * ch;
+        const double t = rounds(2 * units * (P - 1)) * (ch * MAP_COST + START) + (P - 1) * FOLD +
+                         rounds(units * P) * (ch + START);
         if (t < best) {
             best = t;
             best_seg = ls;
         }
     }
-    return best < 0.85 * whole ? best_seg : 0;
+    return best < 0.95 * whole ? best_seg : 0;
 }
 
 }  // namespace gdn
