@@ -74,6 +74,7 @@ struct Cfg {
     static constexpr int CPR = DK / 2;        // threads per token row in the load step
     static constexpr int NG = NT / CPR;       // token groups
     static constexpr int TPG = C / NG;        // tokens per group
+    static constexpr bool UG = CPR == 64;     // one token group per wave: token indices are wave-uniform
     static constexpr int RT = DK / 16;        // 16-row tiles of the state
     static constexpr int KM = DK / KSTEP;     // MFMA steps over d_k
     static constexpr int TM = C / KSTEP;      // MFMA steps over the chunk's tokens
@@ -86,7 +87,7 @@ struct Cfg {
     static constexpr int SG_B = C * 4;                     // beta [C]
     static constexpr int SZ_STG = STAGE ? SG_G + 2 * SG_Q + SG_V + SG_B : 0;
     static constexpr int SZ_OPK = C * DK * (int)sizeof(TI);
-    static constexpr int SZ_AN = 10 * 64 * 16;  // ten 16x16 fp32 blocks of -A
+    static constexpr int SZ_AN = 14 * 64 * 16;  // ten 16x16 fp32 blocks of -A, then the four diagonal inverses
     static constexpr int SZ_R3 = cmax<SZ_OPK, SZ_AN>::value;
     static constexpr int SZ_KD = DK * C * (int)sizeof(TI);
     static constexpr int SZ_P = C * C * (int)sizeof(TI);
@@ -134,7 +135,15 @@ struct Pair<float> {
 
 __device__ __forceinline__ floatx2 to_f2(bf16x2 x) { return floatx2{(float)x[0], (float)x[1]}; }
 __device__ __forceinline__ floatx2 to_f2(floatx2 x) { return x; }
-__device__ __forceinline__ floatx2 exp2v(floatx2 x) { return floatx2{fast_exp(x[0]), fast_exp(x[1])}; }
+// Cumulative log-decays are carried in log2 units (g * log2(e)), so every
+// decay factor is one v_exp_f32 (2^x), negated arguments included.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ floatx2 pow2v(floatx2 x) {
+    return floatx2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])};
+}
+__device__ __forceinline__ floatx2 fma2(floatx2 a, float b, floatx2 c) {
+    return floatx2{__builtin_fmaf(a[0], b, c[0]), __builtin_fmaf(a[1], b, c[1])};
+}
 
 // Element at a 32-bit byte offset from a wave-uniform base (one VGPR per access).
 template <typename T>
@@ -144,11 +153,6 @@ __device__ __forceinline__ const T& at(const void* base, uint32_t byte_off) {
 template <typename T>
 __device__ __forceinline__ T& at_mut(void* base, uint32_t byte_off) {
     return *reinterpret_cast<T*>(static_cast<char*>(base) + byte_off);
-}
-
-__device__ __forceinline__ float wave_min(float x) {
-    for (int off = 32; off > 0; off >>= 1) x = fminf(x, __shfl_xor(x, off));
-    return x;
 }
 
 // Operand layout with a bank swizzle: inside fragment (blk, m) the 16 slots of
@@ -180,10 +184,12 @@ __device__ __forceinline__ typename Mma<TI>::frag op_frag(const TI* base, int bl
     return reinterpret_cast<const typename Mma<TI>::frag*>(base)[(blk * KM + m) * 64 + op_slot(blk, m, lane & 15, lane >> 4)];
 }
 
-// Lane j of each 16-lane row, broadcast along the row (DPP row_newbcast).
+// acc + a * x[lane J of this lane's 16-lane row]: the row broadcast is a DPP
+// row_newbcast source modifier, which folds into v_fmac_f32.
 template <int J>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, false));
+__device__ __forceinline__ float fma_row_bcast(float a, float x, float acc) {
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, false));
+    return __builtin_fmaf(b, a, acc);
 }
 
 template <int I, int N, typename F>
@@ -210,32 +216,81 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lptr(void* p)
 
 // DMA of one chunk's raw inputs into the staging area: rows of g, q, k, v land
 // row-major and beta contiguous; one wave instruction moves 1 KiB (64 lanes x
-// 16 bytes).  Rows at or past the chunk's end are not fetched.
+// 16 bytes).  Rows at or past the chunk's end fetch a copy of its last row
+// (no branches); the chunk zeroes them after the wait.
+// The copy is a list of 1-KiB wave instructions, NI_* per input; wave w takes
+// instructions w, w + NW, ... of each, so its own list has N entries (g, q, k,
+// v in that order; beta goes with the last).  A wave that issues many of them
+// at once stalls until the memory pipeline has accepted them, so the list is
+// cut into NS slots placed between the chunk's compute steps.
 template <typename TI, int DK, int DV>
-__device__ __forceinline__ void issue_stage(const Args<TI>& a, char* stg, int64_t c1, int L1, int h, int wv,
-                                            int lane, bool withq, bool withv) {
+struct Dma {
+    typedef Cfg<TI, DK, DV> P;
+    static constexpr int RB_G = DK * 4, RB_Q = DK * (int)sizeof(TI), RB_V = DV * (int)sizeof(TI);
+    static constexpr int NI_G = C * RB_G / 1024, NI_Q = C * RB_Q / 1024, NI_V = C * RB_V / 1024;
+    static_assert(NI_G % P::NW == 0 && NI_Q % P::NW == 0 && NI_V % P::NW == 0, "copy list does not split");
+    static constexpr int PG = NI_G / P::NW, PQ = NI_Q / P::NW, PV = NI_V / P::NW;
+    static constexpr int N = PG + 2 * PQ + PV;
+    static constexpr int NS = 6;
+};
+
+// Entry J of wave wv's copy list for the chunk whose first (token, head) row is
+// tok0 and which holds L1 > 0 tokens.
+template <int J, typename TI, int DK, int DV>
+__device__ __forceinline__ void dma_one(const Args<TI>& a, char* stg, size_t tok0, int L1, int wv, int lane, bool withq,
+                                        bool withv) {
+    typedef Dma<TI, DK, DV> D;
+    typedef Cfg<TI, DK, DV> P;
+    auto row = [&](const void* src, int RB, char* dst, int i) {
+        const int lpr = RB / 16, rpi = 64 / lpr;
+        const int t = min(i * rpi + lane / lpr, L1 - 1);
+        const char* base = static_cast<const char*>(src) + tok0 * RB;
+        __builtin_amdgcn_global_load_lds(gptr(base + (uint32_t)(t * a.H * RB + (lane % lpr) * 16)), lptr(dst + i * 1024),
+                                         16, 0, 0);
+    };
+    if constexpr (J < D::PG) {
+        row(a.g, D::RB_G, stg, wv + P::NW * J);
+    } else if constexpr (J < D::PG + D::PQ) {
+        if (withq) row(a.q, D::RB_Q, stg + P::SG_G, wv + P::NW * (J - D::PG));
+    } else if constexpr (J < D::PG + 2 * D::PQ) {
+        row(a.k, D::RB_Q, stg + P::SG_G + P::SG_Q, wv + P::NW * (J - D::PG - D::PQ));
+    } else {
+        if (withv) row(a.v, D::RB_V, stg + P::SG_G + 2 * P::SG_Q, wv + P::NW * (J - D::PG - 2 * D::PQ));
+    }
+}
+
+// Slot S of the copy of the chunk starting at token c1 (L1 tokens; none if <= 0).
+template <int S, typename TI, int DK, int DV>
+__device__ __forceinline__ void dma_slot(const Args<TI>& a, char* stg, int64_t c1, int L1, int h, int wv, int lane,
+                                         bool withq, bool withv) {
+    typedef Dma<TI, DK, DV> D;
     typedef Cfg<TI, DK, DV> P;
     if (L1 <= 0) return;
     const size_t tok0 = (size_t)c1 * a.H + h;
-    auto rows = [&](const void* src, int elems, int esize, char* dst) {
-        const int row_bytes = elems * esize, lpr = row_bytes / 16, rpi = 64 / lpr, ninst = C / rpi;
-        const char* base = static_cast<const char*>(src) + tok0 * elems * esize;
-        const uint32_t stride = (uint32_t)a.H * elems * esize;
-        for (int i = wv; i < ninst; i += P::NW) {
-            const int t = i * rpi + lane / lpr;
-            if (t < L1)
-                __builtin_amdgcn_global_load_lds(gptr(base + t * stride + (lane % lpr) * 16), lptr(dst + i * 1024), 16,
-                                                 0, 0);
-        }
-    };
-    rows(a.g, DK, 4, stg);
-    if (withq) rows(a.q, DK, (int)sizeof(TI), stg + P::SG_G);
-    rows(a.k, DK, (int)sizeof(TI), stg + P::SG_G + P::SG_Q);
-    if (withv) rows(a.v, DV, (int)sizeof(TI), stg + P::SG_G + 2 * P::SG_Q);
-    if (wv == 0 && lane < L1)
-        __builtin_amdgcn_global_load_lds(gptr(a.beta + tok0 + (size_t)lane * a.H),
-                                         lptr(stg + P::SG_G + 2 * P::SG_Q + P::SG_V), 4, 0, 0);
+    static_for<S * D::N / D::NS, (S + 1) * D::N / D::NS>(
+        [&](auto jc) { dma_one<decltype(jc)::value, TI, DK, DV>(a, stg, tok0, L1, wv, lane, withq, withv); });
+    if constexpr (S == D::NS - 1) {
+        if (wv == 0)
+            __builtin_amdgcn_global_load_lds(gptr(a.beta + tok0 + (size_t)min(lane, L1 - 1) * a.H),
+                                             lptr(stg + P::SG_G + 2 * P::SG_Q + P::SG_V), 4, 0, 0);
+    }
 }
+
+template <typename TI, int DK, int DV>
+__device__ __forceinline__ void dma_all(const Args<TI>& a, char* stg, int64_t c1, int L1, int h, int wv, int lane,
+                                        bool withq, bool withv) {
+    static_for<0, Dma<TI, DK, DV>::NS>(
+        [&](auto sc) { dma_slot<decltype(sc)::value, TI, DK, DV>(a, stg, c1, L1, h, wv, lane, withq, withv); });
+}
+
+// Workgroup barrier for LDS traffic only: each wave waits for its own LDS
+// operations (lgkmcnt), not for its outstanding global loads and stores.  The
+// prefetch copy writes LDS through the vector-memory path, so a memory-model
+// fence on LDS (as in __syncthreads) would wait for it to land at every
+// barrier; the copy's destination is only read after the explicit wait at the
+// next chunk's start.  The "memory" clobber keeps the compiler from moving
+// memory operations across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // First sequence n in [0, num_seqs) with nl[n + 1] + bias * (n + 1) > key.
 __device__ __forceinline__ int seq_of(const int32_t* nl, int num_seqs, int key, int bias) {
@@ -339,7 +394,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
             S[rt][i] = s0 ? at<float>(s0, (row * DV + col0 + r0) * 4) : (eye && row == col0 + r0) ? 1.f : 0.f;
         }
 
-    if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, tb, (int)(te - tb < C ? te - tb : C), h, w, tid0 & 63, OUT, !vzero);
+    if constexpr (P::STAGE) dma_all<TI, DK, DV>(a, stg, tb, (int)(te - tb < C ? te - tb : C), h, w, tid0 & 63, OUT, !vzero);
 
     // A chunk's outputs are stored at the start of the next chunk, after its
     // wait for the prefetch: vmcnt also counts stores, so storing them at the
@@ -366,7 +421,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
-        const int cp = tid % P::CPR, grp = tid / P::CPR, ch = 2 * cp;
+        const int cp = tid % P::CPR, grp = P::UG ? w : tid / P::CPR, ch = 2 * cp;
         const int L = (int)(te - c0 < C ? te - c0 : C);
         const int64_t c1 = c0 + C;
         const int L1 = (int)(te - c1 < C ? te - c1 : C);  // valid tokens of the next chunk (<= 0: none)
@@ -379,27 +434,43 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 
         // ---- 1. local cumulative log-decay ------------------------------------
         // Thread (cp, grp) owns key channels (ch, ch+1) of the tokens
-        // grp*TPG .. grp*TPG+TPG-1.  Its inputs are read twice (from the
+        // grp*TPG .. grp*TPG+TPG-1 (at d_k = 128 a wave is one token group, so
+        // token indices are wave-uniform).  Its inputs are read twice (from the
         // staging area, or from global memory where the second read hits the
         // cache): once to sum the group's log-decays, once to build the
-        // operands, so few registers stay live.
-        // Rows at or past L read in-bounds memory (a stale staging row, or the
-        // chunk's last token) and are replaced by zeros with a select, so the
-        // loads carry no branches and can be issued together.
+        // operands, so few registers stay live.  G is kept in log2 units.
+        // Staged rows at or past L are zero; global reads clamp the row and
+        // select zero, so the loads carry no branches.
         auto rd_g = [&](int t) -> floatx2 {
-            floatx2 x;
-            if constexpr (P::STAGE) x = *reinterpret_cast<const floatx2*>(stg_g + t * DK + ch);
-            else x = at<floatx2>(gbase, ((t < L ? t : L - 1) * krow + ch) * 4);
+            if constexpr (P::STAGE) return *reinterpret_cast<const floatx2*>(stg_g + t * DK + ch);
+            const floatx2 x = at<floatx2>(gbase, ((t < L ? t : L - 1) * krow + ch) * 4);
             return t < L ? x : floatx2{0.f, 0.f};
         };
         auto rd_qk = [&](const TI* sp, const TI* gp, int t) -> floatx2 {
-            floatx2 x;
-            if constexpr (P::STAGE) x = to_f2(*reinterpret_cast<const T2*>(sp + t * DK + ch));
-            else x = to_f2(at<T2>(gp, ((t < L ? t : L - 1) * krow + ch) * (uint32_t)sizeof(TI)));
+            if constexpr (P::STAGE) return to_f2(*reinterpret_cast<const T2*>(sp + t * DK + ch));
+            const floatx2 x = to_f2(at<T2>(gp, ((t < L ? t : L - 1) * krow + ch) * (uint32_t)sizeof(TI)));
             return t < L ? x : floatx2{0.f, 0.f};
         };
-        if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
-        __syncthreads();  // ... and every other wave's; the previous chunk is done with LDS
+        if constexpr (P::STAGE) {
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
+            lds_barrier();                // ... and every other wave's; the previous chunk is done with LDS
+            if (L < C) {
+                // a partial chunk: zero the staging rows L .. C-1
+                auto zero = [&](char* base, int row_bytes) {
+                    floatx4* p = reinterpret_cast<floatx4*>(base + L * row_bytes);
+                    const int n = (C - L) * row_bytes / 16;
+                    for (int i = tid; i < n; i += P::NT) p[i] = zero4();
+                };
+                zero(stg, DK * 4);
+                zero(stg + P::SG_G, DK * (int)sizeof(TI));
+                zero(stg + P::SG_G + P::SG_Q, DK * (int)sizeof(TI));
+                zero(stg + P::SG_G + 2 * P::SG_Q, DV * (int)sizeof(TI));
+                if (tid >= L && tid < C) const_cast<float*>(stg_b)[tid] = 0.f;
+                lds_barrier();
+            }
+        } else {
+            lds_barrier();  // the previous chunk is done with LDS
+        }
         if constexpr (OUT) flush_o(g, r);  // the previous chunk's outputs
         // the solve's v right-hand side in accumulator layout: vr[I][i] = v[16I + 4g + i][col0 + r]
         typedef typename std::conditional<sizeof(TI) == 2, bf16x4, floatx4>::type VR;
@@ -409,42 +480,44 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * I + 4 * g + i;
-                TI x;
-                if constexpr (P::STAGE) x = stg_v[t * DV + col0 + r];
-                else x = at<TI>(vbase, ((t < L ? t : L - 1) * vrow + col0 + r) * (uint32_t)sizeof(TI));
-                vr[I][i] = (t < L && !vzero) ? x : TI(0.f);
+                if constexpr (P::STAGE) {
+                    vr[I][i] = vzero ? TI(0.f) : stg_v[t * DV + col0 + r];
+                } else {
+                    const TI x = at<TI>(vbase, ((t < L ? t : L - 1) * vrow + col0 + r) * (uint32_t)sizeof(TI));
+                    vr[I][i] = (t < L && !vzero) ? x : TI(0.f);
+                }
             }
         if (tid < C) {
             float b;
-            if constexpr (P::STAGE) b = stg_b[tid];
-            else b = at<float>(a.beta + tok0, (tid < L ? tid : L - 1) * H * 4);
-            s_beta[tid] = tid < L ? b : 0.f;
+            if constexpr (P::STAGE) {
+                b = stg_b[tid];
+            } else {
+                b = at<float>(a.beta + tok0, (tid < L ? tid : L - 1) * H * 4);
+                b = tid < L ? b : 0.f;
+            }
+            s_beta[tid] = b;
         }
         const int t0 = grp * P::TPG;
         {
             floatx2 sum = floatx2{0.f, 0.f};
 #pragma unroll 4
-            for (int tt = 0; tt < P::TPG; ++tt) sum += rd_g(t0 + tt);
-            s_gtot[grp * DK + ch] = sum[0];
-            s_gtot[grp * DK + ch + 1] = sum[1];
+            for (int tt = 0; tt < P::TPG; ++tt) sum = fma2(rd_g(t0 + tt), LOG2E, sum);
+            *reinterpret_cast<floatx2*>(s_gtot + grp * DK + ch) = sum;
         }
-        __syncthreads();
+        lds_barrier();
         floatx2 off = floatx2{0.f, 0.f}, tot = floatx2{0.f, 0.f};
 #pragma unroll
         for (int gg = 0; gg < P::NG; ++gg) {
-            const floatx2 x = floatx2{s_gtot[gg * DK + ch], s_gtot[gg * DK + ch + 1]};
-            tot += x;
-            if (gg < grp) off += x;
+            if (gg == grp) off = tot;
+            tot += *reinterpret_cast<const floatx2*>(s_gtot + gg * DK + ch);
         }
         // With g <= 0 the cumulative log-decay is non-increasing, so its most
         // negative value on a channel is the chunk total; every wave sees all
         // channels, so the decision is uniform over the workgroup.
-        const bool fast = wave_min(fminf(tot[0], tot[1])) >= -40.f;
-        const floatx2 gam = exp2v(tot);
-        if (grp == 0) {
-            s_gam[ch] = gam[0];
-            s_gam[ch + 1] = gam[1];
-        }
+        constexpr float BUDGET = -40.f * LOG2E;  // e^-40, in log2 units
+        const bool fast = __all(tot[0] >= BUDGET && tot[1] >= BUDGET);
+        const floatx2 gam = pow2v(tot);
+        if (grp == 0) *reinterpret_cast<floatx2*>(s_gam + ch) = gam;
 
         // ---- 2. decay-scaled operands --------------------------------------
         // K_dec^T is stored four tokens at a time (one 8-byte store per channel).
@@ -470,8 +543,8 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int t = t0 + tq + j;
-                    G += rd_g(t);
-                    const floatx2 e = exp2v(G), ei = exp2v(-G);
+                    G = fma2(rd_g(t), LOG2E, G);
+                    const floatx2 e = pow2v(G), ei = pow2v(-G);
                     const floatx2 kk = rd_qk(stg_k, kbase, t);
                     const floatx2 kh = kk * ei;
                     if constexpr (OUT) op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
@@ -487,14 +560,11 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                 floatx2 G = off;
                 for (int tt = 0; tt < P::TPG; ++tt) {
                     const int t = t0 + tt;
-                    G += rd_g(t);
-                    if ((t & 15) == 7) {
-                        s_mid[(t >> 4) * DK + ch] = G[0];
-                        s_mid[(t >> 4) * DK + ch + 1] = G[1];
-                    }
+                    G = fma2(rd_g(t), LOG2E, G);
+                    if ((t & 15) == 7) *reinterpret_cast<floatx2*>(s_mid + (t >> 4) * DK + ch) = G;
                 }
             }
-            __syncthreads();  // s_mid visible
+            lds_barrier();  // s_mid visible
             floatx2 G = off;
 #pragma unroll 1
             for (int tq = 0; tq < P::TPG; tq += 4) {
@@ -502,13 +572,13 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int t = t0 + tq + j;
-                    G += rd_g(t);
-                    const floatx2 m = floatx2{s_mid[(t >> 4) * DK + ch], s_mid[(t >> 4) * DK + ch + 1]};
-                    const floatx2 e = exp2v(G - m);
+                    G = fma2(rd_g(t), LOG2E, G);
+                    const floatx2 m = *reinterpret_cast<const floatx2*>(s_mid + (t >> 4) * DK + ch);
+                    const floatx2 e = pow2v(G - m);
                     const floatx2 kk = rd_qk(stg_k, kbase, t);
                     if constexpr (OUT) op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
                     op_store2<TI, P::KM>(Ko, t, ch, kk * e);
-                    kd[j] = kk * exp2v(tot - G);
+                    kd[j] = kk * pow2v(tot - G);
                 }
                 store_kd4(t0 + tq, kd);
             }
@@ -555,8 +625,10 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
             aP[j] = -1;
         }
         if (fast) {
-            __syncthreads();
-            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
+            lds_barrier();
+            // the staging area is free from here on: the next chunk's copy is
+            // issued in slots over steps 3-4b
+            if constexpr (P::STAGE) dma_slot<0, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
             // 20 tiles (10 of A, 10 of P); wave w takes tiles w, w+NW, ...
 #pragma unroll
             for (int j = 0; j < P::NPT; ++j) {
@@ -573,21 +645,22 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                     }
                 }
             }
-            __syncthreads();  // every read of Kh is done
+            if constexpr (P::STAGE) dma_slot<1, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
+            lds_barrier();  // every read of Kh is done
         } else {
             for (int I = 0; I < 4; ++I) {
-                __syncthreads();  // readers of the previous Kh are done
+                lds_barrier();  // readers of the previous Kh are done
                 {
-                    const floatx2 m = floatx2{s_mid[I * DK + ch], s_mid[I * DK + ch + 1]};
+                    const floatx2 m = *reinterpret_cast<const floatx2*>(s_mid + I * DK + ch);
                     floatx2 G = off;
                     for (int tt = 0; tt < P::TPG; ++tt) {
                         const int t = t0 + tt;
-                        G += rd_g(t);
+                        G = fma2(rd_g(t), LOG2E, G);
                         if (t < 16 * (I + 1))
-                            op_store2<TI, P::KM>(Kh, t, ch, rd_qk(stg_k, kbase, t) * exp2v(m - G));
+                            op_store2<TI, P::KM>(Kh, t, ch, rd_qk(stg_k, kbase, t) * pow2v(m - G));
                     }
                 }
-                __syncthreads();
+                lds_barrier();
 #pragma unroll
                 for (int jj = 0; jj < P::NQS; ++jj) {
                     const int qq = w + P::NW * jj;
@@ -606,19 +679,19 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                     }
                 }
             }
-            __syncthreads();  // every read of Qo/Ko/Kh is done
+            lds_barrier();  // every read of Qo/Ko/Kh is done
             // the inter-chunk products use the chunk start as reference
             {
                 floatx2 G = off;
                 for (int tt = 0; tt < P::TPG; ++tt) {
                     const int t = t0 + tt;
-                    G += rd_g(t);
-                    const floatx2 e = exp2v(G);
+                    G = fma2(rd_g(t), LOG2E, G);
+                    const floatx2 e = pow2v(G);
                     if constexpr (OUT) op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
                     op_store2<TI, P::KM>(Ko, t, ch, rd_qk(stg_k, kbase, t) * e);
                 }
             }
-            if constexpr (P::STAGE) issue_stage<TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
+            if constexpr (P::STAGE) dma_all<TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
         }
         // -A tiles: lane r + 16g holds -beta_t A[t][s], t = 16I + r, s = 16J + 4g + i
 #pragma unroll
@@ -634,13 +707,17 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                 An[aP[j] * 64 + lane] = x;
             }
         }
-        __syncthreads();
+        if constexpr (P::STAGE)
+            if (fast) dma_slot<2, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
+        lds_barrier();
 
-        // ---- 4a. inverses of the diagonal blocks of (I + A), every wave -------
-        // lane r + 16g ends with Linv_I[r][4g .. 4g+3]
-        floatx4 Linv[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        // ---- 4a. inverses of the diagonal blocks of (I + A) -------------------
+        // Wave I < 4 inverts block I by forward substitution (row j of the
+        // inverse is final once rows < j have been applied, and is broadcast
+        // along each 16-lane row) and publishes it after the blocks of -A;
+        // lane r + 16g holds Linv_I[r][4g .. 4g+3].
+        if (w < 4) {
+            const int I = w;
             float arow[16];
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
@@ -654,10 +731,16 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
             static_for<0, 15>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] += arow[j] * row_bcast<j>(x[i]);
+                for (int i = 0; i < 4; ++i) x[i] = fma_row_bcast<j>(arow[j], x[i], x[i]);
             });
-            Linv[I] = x;
+            An[(10 + I) * 64 + lane] = x;
         }
+        lds_barrier();
+        floatx4 Linv[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) Linv[I] = An[(10 + I) * 64 + lane];
+        if constexpr (P::STAGE)
+            if (fast) dma_slot<3, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
 
         // ---- 4b. U = (I + A)^-1 diag(beta) (V - K~ S), own columns -----------
         // This is U = Ut - W S with W = (I + A)^-1 diag(beta) K~ never formed:
@@ -702,7 +785,11 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                 for (int e = 0; e < 4; ++e) ui = M::mma(Linv[I][e], acc[e], ui);
                 U[I] = ui;
             }
+            if constexpr (P::STAGE)
+                if (I == 1 && fast) dma_slot<4, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
         }
+        if constexpr (P::STAGE)
+            if (fast) dma_slot<5, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
 
         // ---- 5. outputs and state (own columns) -------------------------------
         // O = Q~ S + P U one row block at a time, then S <- diag(e^{G_L}) S + K_dec^T U.
