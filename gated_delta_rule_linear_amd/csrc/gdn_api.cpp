@@ -45,17 +45,16 @@ namespace gdn {
 // Time split of long sequences.  One workgroup carries one (sequence, head)
 // through its chunks in order, so a batch of few long sequences leaves most of
 // the 256 compute units idle.  Cutting sequences into segments of Ls tokens
-// costs a second pass over the non-last segments (their transitions M and N,
-// each about MAP_COST of a full pass) and a serial fold, and buys parallelism.
-// The plan compares critical paths in units of one chunk of the full pass,
-// with START chunks of fixed cost per workgroup and FOLD per fold step:
+// costs a second pass over the non-last segments (their transitions M and N)
+// and a serial fold, and buys parallelism.  The plan compares critical paths
+// (SplitCost, in chunk-times of the output pass) for sequences of the mean
+// length (the lengths themselves are on the device):
 //   whole sequences:  ceil(units / CUs) * (chunks + START)
-//   split into P:     ceil(2 units (P-1) / CUs) * (Ls/64 * MAP_COST + START)
-//                     + (P-1) * FOLD + ceil(units P / CUs) * (Ls/64 + START)
-// for sequences of the mean length (the lengths themselves are on the device),
-// and splits when that saves at least 5%.  The constants are fitted to
-// measured times of the two passes on MI355X.
-int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H) {
+//   split into P:     maps_pass(units (P-1), Ls/64) + (P-1) * FOLD
+//                     + ceil(units P / CUs) * (Ls/64 + START)
+// and splits when that saves at least 5%.  The workspace bound, and so the
+// plan, depends on the arguments only.
+int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
     if (const char* e = std::getenv("GDN_PREFILL_SEGMENT")) {
         if (*e) {
             const long long v = std::strtoll(e, nullptr, 10);
@@ -63,17 +62,17 @@ int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H) {
         }
     }
     if (num_seqs <= 0 || T_total <= 0 || H <= 0) return 0;
-    constexpr double CUS = 256.0, MAP_COST = 0.76, START = 2.0, FOLD = 1.0;
+    typedef SplitCost K;
+    const bool share = bf16 && d_k == d_v;
     const double units = (double)num_seqs * H;
     const int64_t len = (T_total + num_seqs - 1) / num_seqs;
-    auto rounds = [&](double wgs) { return std::ceil(wgs / CUS); };
-    const double whole = rounds(units) * (std::ceil(len / 64.0) + START);
+    const double whole = K::rounds(units) * (std::ceil(len / 64.0) + K::START);
     double best = whole;
     int64_t best_seg = 0;
     for (int64_t ls = 1024; ls < len; ls += 512) {
         const double P = std::ceil((double)len / ls), ch = ls / 64.0;
-        const double t = rounds(2 * units * (P - 1)) * (ch * MAP_COST + START) + (P - 1) * FOLD +
-                         rounds(units * P) * (ch + START);
+        const double t = K::maps_pass(units * (P - 1), ch, share, nullptr) + (P - 1) * K::FOLD +
+                         K::rounds(units * P) * (ch + K::START);
         if (t < best) {
             best = t;
             best_seg = ls;
@@ -131,7 +130,7 @@ int32_t gdn_state_free(float* state, void* stream) {
 
 size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v) {
     if (T_total < 0 || num_seqs < 0 || H < 1 || d_k < 0 || d_v < 0) return 0;
-    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H);
+    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H, d_k, d_v, true);
     return gdn::prefill_workspace_layout(T_total, num_seqs, H, d_k, d_v, seg).bytes;
 }
 
@@ -153,7 +152,7 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     }
     if (initial_state && !aligned(initial_state, 16)) return GDN_ERR_INVALID_ARG;
     if (final_state && !aligned(final_state, 16)) return GDN_ERR_INVALID_ARG;
-    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H);
+    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H, d_k, d_v, true);
     const size_t need = gdn::prefill_workspace_layout(T_total, num_seqs, H, d_k, d_v, seg).bytes;
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return GDN_ERR_INVALID_ARG;
     if (((int64_t)num_seqs + (seg > 0 ? T_total / seg : 0)) * H * (d_v / 16) > 0x7fffffff) return GDN_ERR_UNSUPPORTED;

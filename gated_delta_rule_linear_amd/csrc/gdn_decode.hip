@@ -11,11 +11,14 @@
 // Multimodal LLMs", section 2.2: a fixed-size state updated token by token).
 //
 // The step reads and writes the 64 KiB state once and does ~7 d_k d_v flops, so
-// it is bound by HBM.  One workgroup of 256 threads owns one (sequence, head):
+// it is bound by HBM.  One workgroup of NTHR threads owns one (sequence, head):
 // a thread holds 4 adjacent columns (one 16-byte vector per row) of a band of
 // rows, so every row of S is read and written as whole 512-byte segments.  The
 // two reductions over d_k (S'^T k and S'^T q) are summed in registers over the
-// thread's rows and then across row bands through LDS.
+// thread's rows and then across row bands through LDS.  The state is touched
+// once per step, so it is read and written with non-temporal hints (it does not
+// displace the small per-token vectors from the caches); few rows per thread
+// and many threads keep more requests in flight per CU.
 #include "gdn_device.h"
 #include "gdn_kernels.h"
 
@@ -40,15 +43,17 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, floatx4 x) {
     *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
 }
 
+constexpr int NTHR = 256;
+
 template <typename TI, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
+__global__ __launch_bounds__(NTHR) void decode_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                                                     const TI* __restrict__ v, const float* __restrict__ g,
                                                     const float* __restrict__ beta, float* __restrict__ state,
                                                     TI* __restrict__ o) {
     constexpr int CG = DV / 4;     // 4-column groups per row
-    constexpr int RG = 256 / CG;   // row bands
+    constexpr int RG = NTHR / CG;  // row bands
     constexpr int RPB = DK / RG;   // rows per band
-    static_assert(RPB >= 1 && RG * CG == 256, "unsupported shape");
+    static_assert(RPB >= 1 && RG * CG == NTHR, "unsupported shape");
 
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
     __shared__ floatx4 s_r[RG][CG], s_p[RG][CG];
@@ -73,7 +78,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const TI* __restrict__ q, c
     float* S = state + unit * (int64_t)DK * DV + 4 * cg;
     floatx4 Sv[RPB];
 #pragma unroll
-    for (int j = 0; j < RPB; ++j) Sv[j] = *reinterpret_cast<const floatx4*>(S + (int64_t)(rb * RPB + j) * DV);
+    for (int j = 0; j < RPB; ++j)
+        Sv[j] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (int64_t)(rb * RPB + j) * DV));
     floatx4 r = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < RPB; ++j) {
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const TI* __restrict__ q, c
 #pragma unroll
     for (int j = 0; j < RPB; ++j) {
         const int i = rb * RPB + j;
-        *reinterpret_cast<floatx4*>(S + (int64_t)i * DV) = Sv[j] + s_k[i] * u;
+        __builtin_nontemporal_store(Sv[j] + s_k[i] * u, reinterpret_cast<floatx4*>(S + (int64_t)i * DV));
     }
     if (rb == 0) store4(o + unit * DV + 4 * cg, pt + s_kq * u);
 }
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const TI* __restrict__ q, c
 template <typename TI, int DK, int DV>
 hipError_t run(const DecodeLaunch& p, hipStream_t s) {
     const int64_t units = (int64_t)p.N * p.H;
-    hipLaunchKernelGGL((decode_kernel<TI, DK, DV>), dim3((unsigned)units), dim3(256), 0, s,
+    hipLaunchKernelGGL((decode_kernel<TI, DK, DV>), dim3((unsigned)units), dim3(NTHR), 0, s,
                        static_cast<const TI*>(p.q), static_cast<const TI*>(p.k), static_cast<const TI*>(p.v), p.g,
                        p.beta, p.state, static_cast<TI*>(p.o));
     return hipGetLastError();

@@ -48,10 +48,29 @@ inline PrefillWorkspace prefill_workspace_layout(int64_t T_total, int32_t num_se
     return w;
 }
 
+// Cost model of the time split, in chunk-times of the output pass, fitted to
+// measured kernel times on MI355X (one workgroup per CU at a time).
+struct SplitCost {
+    static constexpr double CUS = 256.0;     // compute units
+    static constexpr double MAP_ONE = 0.68;   // a transition workgroup computing M or N
+    static constexpr double MAP_BOTH = 0.93;  // one computing M and N together (bf16, d_k = d_v)
+    static constexpr double START = 2.0;     // fixed cost per workgroup
+    static constexpr double FOLD = 1.0;      // per fold step
+    static double rounds(double wgs) { return wgs <= 0 ? 0 : (double)(int64_t)((wgs + CUS - 1) / CUS); }
+    // Critical path of the transition pass over `maps` (segment, head) pairs of
+    // `chunks` chunks; *both says whether M and N share a workgroup.
+    static double maps_pass(double maps, double chunks, bool can_share, bool* both) {
+        const double one = rounds(2 * maps) * (chunks * MAP_ONE + START);
+        const double two = can_share ? rounds(maps) * (chunks * MAP_BOTH + START) : one + 1;
+        if (both) *both = two < one;
+        return two < one ? two : one;
+    }
+};
+
 // Segment length chosen for a batch of these sizes (0: one workgroup per whole
 // sequence and head).  Depends on the arguments only, and on the environment
 // variable GDN_PREFILL_SEGMENT, which forces a length (0 = never split).
-int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H);
+int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
 
 struct DecodeLaunch {
     const void* q;

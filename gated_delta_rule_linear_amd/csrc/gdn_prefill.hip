@@ -92,7 +92,13 @@ struct Cfg {
     static constexpr int SZ_KD = DK * C * (int)sizeof(TI);
     static constexpr int SZ_P = C * C * (int)sizeof(TI);
     static constexpr int NF = C + DK + NG * DK + 4 * DK;
-    static constexpr int LDS = SZ_STG + 2 * SZ_OPK + SZ_R3 + SZ_KD + SZ_P + NF * 4;
+    // LDS layout: the MFMA operands first (inside the 64 KiB reach of a
+    // ds_read/ds_write immediate offset from one base), then the small
+    // per-chunk vectors, then the staging area.
+    static constexpr int OFF_QO = 0, OFF_KO = SZ_OPK, OFF_R3 = 2 * SZ_OPK, OFF_KD = OFF_R3 + SZ_R3;
+    static constexpr int OFF_P = OFF_KD + SZ_KD, OFF_F = OFF_P + SZ_P;
+    static constexpr int OFF_STG = (OFF_F + NF * 4 + 1023) / 1024 * 1024;
+    static constexpr int LDS = OFF_STG + SZ_STG;
     static_assert(TPG >= 1 && NT <= 1024, "unsupported shape");
 };
 
@@ -308,31 +314,36 @@ __device__ __forceinline__ int seq_of(const int32_t* nl, int num_seqs, int key, 
 // MAP = true: the transition of one full non-last segment.  The recurrence is
 // affine in the state, S_end = M S_start + N, so M is the end state reached from
 // S_start = I with v = 0 (a d_k-column state) and N the one reached from
-// S_start = 0 with the real v; no q, P or o is formed.
-template <typename TI, int DK, int DV, bool MAP>
+// S_start = 0 with the real v; no q, P or o is formed.  With NCB = 1 a
+// workgroup computes one of them (blocks below m_blocks: M); with NCB = 2
+// (d_k = d_v) it computes both, wave w carrying columns 16w .. 16w+15 of each,
+// so the key-side work of the chunk is done once for the two.
+template <typename TI, int DK, int DV, bool MAP, int NCB = 1>
 __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(Args<TI> a) {
     typedef Cfg<TI, DK, DV> P;
     constexpr bool OUT = !MAP;
+    static_assert(NCB == 1 || (MAP && DK == DV), "two column blocks only for transitions with d_k = d_v");
     typedef Mma<TI> M;
     typedef typename M::frag frag;
     typedef typename Pair<TI>::type T2;
     constexpr int KW = P::KW;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* stg = smem;  // next chunk's raw inputs (bf16 only)
+    // static, so that every LDS address is a compile-time offset that folds
+    // into the instruction's immediate
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
+    char* stg = smem + P::OFF_STG;  // next chunk's raw inputs (bf16 only)
     const float* stg_g = reinterpret_cast<const float*>(stg);
     const TI* stg_q = reinterpret_cast<const TI*>(stg + P::SG_G);
     const TI* stg_k = reinterpret_cast<const TI*>(stg + P::SG_G + P::SG_Q);
     const TI* stg_v = reinterpret_cast<const TI*>(stg + P::SG_G + 2 * P::SG_Q);
     const float* stg_b = reinterpret_cast<const float*>(stg + P::SG_G + 2 * P::SG_Q + P::SG_V);
-    char* base = smem + P::SZ_STG;
-    TI* Qo = reinterpret_cast<TI*>(base);                      // q~ (operand layout over d_k)
-    TI* Ko = reinterpret_cast<TI*>(base + P::SZ_OPK);          // k~, then -W
-    char* r3 = base + 2 * P::SZ_OPK;
+    TI* Qo = reinterpret_cast<TI*>(smem + P::OFF_QO);          // q~ (operand layout over d_k)
+    TI* Ko = reinterpret_cast<TI*>(smem + P::OFF_KO);          // k~
+    char* r3 = smem + P::OFF_R3;
     TI* Kh = reinterpret_cast<TI*>(r3);                        // k^ (Gram operand) ...
     floatx4* An = reinterpret_cast<floatx4*>(r3);              // ... then the blocks of -A
-    TI* KdT = reinterpret_cast<TI*>(r3 + P::SZ_R3);            // K_dec^T (operand layout over tokens)
-    TI* Po = reinterpret_cast<TI*>(r3 + P::SZ_R3 + P::SZ_KD);  // P (operand layout over tokens)
-    float* s_beta = reinterpret_cast<float*>(reinterpret_cast<char*>(Po) + P::SZ_P);
+    TI* KdT = reinterpret_cast<TI*>(smem + P::OFF_KD);         // K_dec^T (operand layout over tokens)
+    TI* Po = reinterpret_cast<TI*>(smem + P::OFF_P);           // P (operand layout over tokens)
+    float* s_beta = reinterpret_cast<float*>(smem + P::OFF_F);
     float* s_gam = s_beta + C;
     float* s_gtot = s_gam + DK;
     float* s_mid = s_gtot + P::NG * DK;
@@ -347,8 +358,19 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
     int64_t tb, te;
     const float* s0 = nullptr;
     float* sf = nullptr;
+    float* sf2 = nullptr;  // NCB = 2: where N goes (M goes to sf)
     bool eye = false, vzero = false;
-    if constexpr (MAP) {
+    if constexpr (MAP && NCB == 2) {
+        const int k = b / H;
+        h = b - k * H;
+        if (k >= a.nl[a.num_seqs]) return;
+        const int n = seq_of(a.nl, a.num_seqs, k, 0);
+        tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
+        te = tb + a.seg;
+        eye = true;
+        sf = a.wsM + ((size_t)k * H + h) * DK * DK;
+        sf2 = a.wsN + ((size_t)k * H + h) * DK * DV;
+    } else if constexpr (MAP) {
         const bool kindM = b < a.m_blocks;
         const int idx = kindM ? b : b - a.m_blocks;
         const int k = idx / H;
@@ -385,13 +407,15 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 
     // fp32 state: S[rt][i] = S[16 rt + 4g + i][col0 + r]
     const int r0 = tid0 & 15, g0 = (tid0 & 63) >> 4;
-    floatx4 S[P::RT];
+    // (NCB = 2: S[0] is the M part, started at the identity, S[1] the N part)
+    floatx4 S[NCB][P::RT];
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rt + 4 * g0 + i;
-            S[rt][i] = s0 ? at<float>(s0, (row * DV + col0 + r0) * 4) : (eye && row == col0 + r0) ? 1.f : 0.f;
+            S[0][rt][i] = s0 ? at<float>(s0, (row * DV + col0 + r0) * 4) : (eye && row == col0 + r0) ? 1.f : 0.f;
+            if constexpr (NCB == 2) S[1][rt][i] = 0.f;
         }
 
     if constexpr (P::STAGE) dma_all<TI, DK, DV>(a, stg, tb, (int)(te - tb < C ? te - tb : C), h, w, tid0 & 63, OUT, !vzero);
@@ -404,14 +428,13 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
     OV opend[4];
     TI* opend_base = nullptr;
     int opend_L = 0;
-    auto flush_o = [&](int gl, int rl) {
-        if (opend_base) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int t = 16 * rb + rl;
-                if (t < opend_L) at_mut<OV>(opend_base, (t * vrow + col0 + 4 * gl) * (uint32_t)sizeof(TI)) = opend[rb];
-            }
-        }
+    // Row block rb of the pending outputs; the four stores are spread over the
+    // next chunk's first steps (a wave that issues several vector-memory
+    // instructions at once waits for the pipeline to take them).
+    auto flush_o = [&](int rb, int gl, int rl) {
+        const int t = 16 * rb + rl;
+        if (opend_base && t < opend_L)
+            at_mut<OV>(opend_base, (t * vrow + col0 + 4 * gl) * (uint32_t)sizeof(TI)) = opend[rb];
     };
 
     for (int64_t c0 = tb; c0 < te; c0 += C) {
@@ -471,7 +494,8 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
         } else {
             lds_barrier();  // the previous chunk is done with LDS
         }
-        if constexpr (OUT) flush_o(g, r);  // the previous chunk's outputs
+        if constexpr (OUT)
+            for (int rb = 0; rb < 4; ++rb) flush_o(rb, g, r);  // the previous chunk's outputs
         // the solve's v right-hand side in accumulator layout: vr[I][i] = v[16I + 4g + i][col0 + r]
         typedef typename std::conditional<sizeof(TI) == 2, bf16x4, floatx4>::type VR;
         VR vr[4];
@@ -537,19 +561,32 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
         };
         if (fast) {
             floatx2 G = off;
+            // In the bf16 operand layout the byte offset of (t0 + tt, ch) is
+            // that of (t0, ch) with tt XORed into bits 4.. (t0 is a multiple of
+            // TPG, a power of two, and a token group stays in one 16-row block),
+            // and Qo, Ko, Kh share it.
+            const uint32_t a0 = op_idx<TI, P::KM>(t0, ch) * (uint32_t)sizeof(TI);
+            auto put = [&](TI* mat, int tt, int t, floatx2 x) {
+                if constexpr (KW == 8) {
+                    *reinterpret_cast<bf16x2*>(reinterpret_cast<char*>(mat) + (a0 ^ (uint32_t)(tt << 4))) =
+                        bf16x2{(bf16)x[0], (bf16)x[1]};
+                } else {
+                    op_store2<TI, P::KM>(mat, t, ch, x);
+                }
+            };
 #pragma unroll 1
             for (int tq = 0; tq < P::TPG; tq += 4) {
                 floatx2 kd[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int t = t0 + tq + j;
+                    const int tt = tq + j, t = t0 + tt;
                     G = fma2(rd_g(t), LOG2E, G);
                     const floatx2 e = pow2v(G), ei = pow2v(-G);
                     const floatx2 kk = rd_qk(stg_k, kbase, t);
                     const floatx2 kh = kk * ei;
-                    if constexpr (OUT) op_store2<TI, P::KM>(Qo, t, ch, rd_qk(stg_q, qbase, t) * e);
-                    op_store2<TI, P::KM>(Ko, t, ch, kk * e);
-                    op_store2<TI, P::KM>(Kh, t, ch, kh);
+                    if constexpr (OUT) put(Qo, tt, t, rd_qk(stg_q, qbase, t) * e);
+                    put(Ko, tt, t, kk * e);
+                    put(Kh, tt, t, kh);
                     kd[j] = kh * gam;  // K_dec = k e^{G_L - G}
                 }
                 store_kd4(t0 + tq, kd);
@@ -736,9 +773,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
             An[(10 + I) * 64 + lane] = x;
         }
         lds_barrier();
-        floatx4 Linv[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) Linv[I] = An[(10 + I) * 64 + lane];
+        // (each consumer reads Linv_I from LDS where it needs it)
         if constexpr (P::STAGE)
             if (fast) dma_slot<3, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
 
@@ -746,9 +781,13 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
         // This is U = Ut - W S with W = (I + A)^-1 diag(beta) K~ never formed:
         // the right-hand side takes K~ S first, then the block forward
         // substitution runs on the wave's 16 columns only.
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+        // column block cb of the wave (NCB = 2: the M part has v = 0)
+        const bool vblock = NCB == 1 || cb == 1;
         frag bS[P::KM];
 #pragma unroll
-        for (int m = 0; m < P::KM; ++m) bS[m] = acc_perm<TI>(S, m, P::RT);
+        for (int m = 0; m < P::KM; ++m) bS[m] = acc_perm<TI>(S[cb], m, P::RT);
         floatx4 U[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -760,7 +799,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
             for (int m = 0; m < P::KM; ++m) ks = M::mma(ak[m], bS[m], ks);
             floatx4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = s_beta[16 * I + 4 * g + i] * ((float)vr[I][i] - ks[i]);
+            for (int i = 0; i < 4; ++i) acc[i] = s_beta[16 * I + 4 * g + i] * ((vblock ? (float)vr[I][i] : 0.f) - ks[i]);
             if constexpr (KW == 8) {
 #pragma unroll
                 for (int m = 0; 2 * m < I; ++m) {
@@ -770,7 +809,8 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                                              (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
                     acc = M::mma(af, acc_perm<TI>(U, m, I), acc);
                 }
-                const bf16x8 lf = bf16x8{(bf16)Linv[I][0], (bf16)Linv[I][1], (bf16)Linv[I][2], (bf16)Linv[I][3],
+                const floatx4 li = An[(10 + I) * 64 + lane];
+                const bf16x8 lf = bf16x8{(bf16)li[0], (bf16)li[1], (bf16)li[2], (bf16)li[3],
                                          (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
                 U[I] = M::mma(lf, acc_perm<TI>(&acc, 0, 1), zero4());
             } else {
@@ -781,15 +821,16 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
                     for (int e = 0; e < 4; ++e) acc = M::mma(an[e], U[J][e], acc);
                 }
                 floatx4 ui = zero4();
+                const floatx4 li = An[(10 + I) * 64 + lane];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ui = M::mma(Linv[I][e], acc[e], ui);
+                for (int e = 0; e < 4; ++e) ui = M::mma(li[e], acc[e], ui);
                 U[I] = ui;
             }
             if constexpr (P::STAGE)
-                if (I == 1 && fast) dma_slot<4, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
+                if (I == 1 && cb == 0 && fast) dma_slot<4, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
         }
         if constexpr (P::STAGE)
-            if (fast) dma_slot<5, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
+            if (cb == 0 && fast) dma_slot<5, TI, DK, DV>(a, stg, c1, L1, h, w, lane, OUT, !vzero);
 
         // ---- 5. outputs and state (own columns) -------------------------------
         // O = Q~ S + P U one row block at a time, then S <- diag(e^{G_L}) S + K_dec^T U.
@@ -817,7 +858,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt) {
             const floatx4 d = *reinterpret_cast<const floatx4*>(s_gam + 16 * rt + 4 * g);
-            S[rt] *= d;
+            S[cb][rt] *= d;
         }
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt) {
@@ -825,8 +866,10 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
             for (int m = 0; m < P::TM; ++m) ak[m] = op_frag<TI, P::TM>(KdT, rt, m, lane);
 #pragma unroll
-            for (int m = 0; m < P::TM; ++m) S[rt] = M::mma(ak[m], bU[m], S[rt]);
+            for (int m = 0; m < P::TM; ++m) S[cb][rt] = M::mma(ak[m], bU[m], S[cb][rt]);
         }
+        if constexpr (NCB > 1) __builtin_amdgcn_sched_barrier(0);  // keep the blocks' live ranges apart
+        }  // column blocks
         if constexpr (OUT) {
             opend_base = obase;
             opend_L = L;
@@ -834,13 +877,19 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
         // The next chunk writes LDS only after its first barrier, which every
         // wave reaches after finishing this state pass.
     }
-    if constexpr (OUT) flush_o(g0, r0);
+    if constexpr (OUT)
+        for (int rb = 0; rb < 4; ++rb) flush_o(rb, g0, r0);
 
-    if (sf) {
 #pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt)
+    for (int cb = 0; cb < NCB; ++cb) {
+        float* dst = cb == 0 ? sf : sf2;
+        if (dst) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) at_mut<float>(sf, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) = S[rt][i];
+            for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    at_mut<float>(dst, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) = S[cb][rt][i];
+        }
     }
 }
 
@@ -935,16 +984,13 @@ __global__ __launch_bounds__(256) void seg_final_kernel(const int32_t* __restric
     for (int e = threadIdx.x; e < DK * DV / 4; e += 256) dst[e] = src[e];
 }
 
-template <typename TI, int DK, int DV, bool MAP>
+template <typename TI, int DK, int DV, bool MAP, int NCB = 1>
 hipError_t launch_seq(const Args<TI>& a, int64_t blocks, hipStream_t s) {
     typedef Cfg<TI, DK, DV> P;
     static_assert(P::LDS <= 160 * 1024, "LDS budget");
     if (blocks <= 0) return hipSuccess;
-    auto kern = prefill_seq_kernel<TI, DK, DV, MAP>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(P::NT), P::LDS, s, a);
+    auto kern = prefill_seq_kernel<TI, DK, DV, MAP, NCB>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -984,9 +1030,20 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int64_t map_blocks = ws.slots * p.H;
     if (map_blocks > 0) {
-        if (DK == DV) {
-            a.m_blocks = (int)map_blocks;
-            e = launch_seq<TI, DK, DV, true>(a, 2 * map_blocks, s);
+        // M and N in one workgroup or in two: decided for the number of
+        // transitions that sequences of the mean length would have (the grid
+        // is sized for the bound; surplus workgroups exit at once)
+        const int64_t len = (p.T_total + p.num_seqs - 1) / p.num_seqs;
+        const double maps = (double)p.num_seqs * p.H * (len > 0 ? (len - 1) / p.seg : 0);
+        bool both = false;
+        SplitCost::maps_pass(maps, p.seg / 64.0, DK == DV && sizeof(TI) == 2, &both);
+        if constexpr (DK == DV && sizeof(TI) == 2) {
+            if (both) {
+                e = launch_seq<TI, DK, DV, true, 2>(a, map_blocks, s);
+            } else {
+                a.m_blocks = (int)map_blocks;
+                e = launch_seq<TI, DK, DV, true>(a, 2 * map_blocks, s);
+            }
         } else {
             a.m_blocks = (int)map_blocks;
             e = launch_seq<TI, DK, DK, true>(a, map_blocks, s);
