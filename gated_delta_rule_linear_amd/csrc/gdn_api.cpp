@@ -179,6 +179,10 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     p.T_total = T_total;
     p.seg = seg;
     p.workspace = workspace;
+    {
+        const char* e = std::getenv("GDN_PREFILL_KERNEL");
+        p.legacy = e && std::strcmp(e, "seq") == 0;
+    }
     return gdn::launch_prefill(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -24,6 +24,7 @@ struct PrefillLaunch {
     int64_t T_total;
     int64_t seg;      // segment length of the time split (tokens, multiple of 64); 0: none
     void* workspace;  // prefill_workspace_layout(...).bytes bytes when seg > 0
+    bool legacy;      // bf16: single-role kernel (GDN_PREFILL_KERNEL=seq) instead of the warp-specialised one
 };
 
 // Workspace of the time-split prefill, for segments of `seg` tokens.  A

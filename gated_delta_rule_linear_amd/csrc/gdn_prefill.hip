@@ -126,6 +126,7 @@ struct Args {
     float* wsN;
     int m_blocks;       // map launches: blocks [0, m_blocks) compute M, the rest N
     int final_to_slot;  // final state of a split sequence goes to its last slot (final_state aliases S0)
+    int legacy;         // bf16: use the single-role kernel instead of the warp-specialised one
 };
 
 template <typename T>
@@ -309,6 +310,80 @@ __device__ __forceinline__ int seq_of(const int32_t* nl, int num_seqs, int key, 
     return lo;
 }
 
+// What one workgroup works on: the token range [tb, te) of head h, its start
+// state (s0, or the identity (eye), or zero) and where its end state goes
+// (sf; with NCB = 2 the N part goes to sf2).  See the kernels below for the
+// three modes; `valid` is false for the surplus workgroups of a grid sized for
+// a bound.
+struct Unit {
+    int h;
+    int64_t tb, te;
+    const float* s0;
+    float* sf;
+    float* sf2;
+    bool eye, vzero, valid;
+};
+template <typename TI, int DK, int DV, bool MAP, int NCB>
+__device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
+    const int H = a.H;
+    Unit u;
+    u.s0 = nullptr;
+    u.sf = u.sf2 = nullptr;
+    u.eye = u.vzero = false;
+    u.valid = true;
+    if constexpr (MAP && NCB == 2) {
+        const int k = b / H;
+        u.h = b - k * H;
+        if (k >= a.nl[a.num_seqs]) {
+            u.valid = false;
+            return u;
+        }
+        const int n = seq_of(a.nl, a.num_seqs, k, 0);
+        u.tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
+        u.te = u.tb + a.seg;
+        u.eye = true;
+        u.sf = a.wsM + ((size_t)k * H + u.h) * DK * DK;
+        u.sf2 = a.wsN + ((size_t)k * H + u.h) * DK * DV;
+    } else if constexpr (MAP) {
+        const bool kindM = b < a.m_blocks;
+        const int idx = kindM ? b : b - a.m_blocks;
+        const int k = idx / H;
+        u.h = idx - k * H;
+        if (k >= a.nl[a.num_seqs]) {  // fewer non-last segments than the bound the grid was sized for
+            u.valid = false;
+            return u;
+        }
+        const int n = seq_of(a.nl, a.num_seqs, k, 0);
+        u.tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
+        u.te = u.tb + a.seg;
+        u.eye = u.vzero = kindM;
+        u.sf = kindM ? a.wsM + ((size_t)k * H + u.h) * DK * DK : a.wsN + ((size_t)k * H + u.h) * DK * DV;
+    } else if (a.seg > 0) {
+        const int q = b / H;
+        u.h = b - q * H;
+        if (q >= a.nl[a.num_seqs] + a.num_seqs) {
+            u.valid = false;
+            return u;
+        }
+        const int n = seq_of(a.nl, a.num_seqs, q, 1);
+        const int j = q - (a.nl[n] + n), last = a.nl[n + 1] - a.nl[n];
+        const size_t unit = (size_t)n * H + u.h;
+        u.tb = a.cu[n] + (int64_t)j * a.seg;
+        u.te = u.tb + a.seg < a.cu[n + 1] ? u.tb + a.seg : a.cu[n + 1];
+        if (j == 0) u.s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
+        else u.s0 = a.wsN + ((size_t)(a.nl[n] + j - 1) * H + u.h) * DK * DV;
+        if (j == last && a.Sf) u.sf = (j > 0 && a.final_to_slot) ? const_cast<float*>(u.s0) : a.Sf + unit * DK * DV;
+    } else {
+        const int n = b / H;
+        u.h = b - n * H;
+        u.tb = a.cu[n];
+        u.te = a.cu[n + 1];
+        u.s0 = a.S0 ? a.S0 + (size_t)b * DK * DV : nullptr;
+        u.sf = a.Sf ? a.Sf + (size_t)b * DK * DV : nullptr;
+    }
+    return u;
+}
+
 // MAP = false: outputs o for a token range and carries the state from S0 to Sf
 // (a whole sequence, or one segment of a split one).
 // MAP = true: the transition of one full non-last segment.  The recurrence is
@@ -351,56 +426,14 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
     const int tid0 = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
-    const int b = blockIdx.x;
-    // the workgroup's token range [tb, te) of head h, its start state (s0, or
-    // the identity, or zero) and where its end state goes (sf, or nowhere)
-    int h;
-    int64_t tb, te;
-    const float* s0 = nullptr;
-    float* sf = nullptr;
-    float* sf2 = nullptr;  // NCB = 2: where N goes (M goes to sf)
-    bool eye = false, vzero = false;
-    if constexpr (MAP && NCB == 2) {
-        const int k = b / H;
-        h = b - k * H;
-        if (k >= a.nl[a.num_seqs]) return;
-        const int n = seq_of(a.nl, a.num_seqs, k, 0);
-        tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
-        te = tb + a.seg;
-        eye = true;
-        sf = a.wsM + ((size_t)k * H + h) * DK * DK;
-        sf2 = a.wsN + ((size_t)k * H + h) * DK * DV;
-    } else if constexpr (MAP) {
-        const bool kindM = b < a.m_blocks;
-        const int idx = kindM ? b : b - a.m_blocks;
-        const int k = idx / H;
-        h = idx - k * H;
-        if (k >= a.nl[a.num_seqs]) return;  // fewer non-last segments than the bound the grid was sized for
-        const int n = seq_of(a.nl, a.num_seqs, k, 0);
-        tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
-        te = tb + a.seg;
-        eye = vzero = kindM;
-        sf = kindM ? a.wsM + ((size_t)k * H + h) * DK * DK : a.wsN + ((size_t)k * H + h) * DK * DV;
-    } else if (a.seg > 0) {
-        const int u = b / H;
-        h = b - u * H;
-        if (u >= a.nl[a.num_seqs] + a.num_seqs) return;
-        const int n = seq_of(a.nl, a.num_seqs, u, 1);
-        const int j = u - (a.nl[n] + n), last = a.nl[n + 1] - a.nl[n];
-        const size_t unit = (size_t)n * H + h;
-        tb = a.cu[n] + (int64_t)j * a.seg;
-        te = tb + a.seg < a.cu[n + 1] ? tb + a.seg : a.cu[n + 1];
-        if (j == 0) s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
-        else s0 = a.wsN + ((size_t)(a.nl[n] + j - 1) * H + h) * DK * DV;
-        if (j == last && a.Sf) sf = (j > 0 && a.final_to_slot) ? const_cast<float*>(s0) : a.Sf + unit * DK * DV;
-    } else {
-        const int n = b / H;
-        h = b - n * H;
-        tb = a.cu[n];
-        te = a.cu[n + 1];
-        s0 = a.S0 ? a.S0 + (size_t)b * DK * DV : nullptr;
-        sf = a.Sf ? a.Sf + (size_t)b * DK * DV : nullptr;
-    }
+    const Unit u = resolve_unit<TI, DK, DV, MAP, NCB>(a, blockIdx.x);
+    if (!u.valid) return;
+    const int h = u.h;
+    const int64_t tb = u.tb, te = u.te;
+    const float* s0 = u.s0;
+    float* sf = u.sf;
+    float* sf2 = u.sf2;
+    const bool eye = u.eye, vzero = u.vzero;
     const int col0 = 16 * w;  // this wave's state columns
     const uint32_t krow = (uint32_t)H * DK;  // elements between consecutive tokens of q, k, g
     const uint32_t vrow = (uint32_t)H * DV;  // ... of v, o
@@ -893,6 +926,475 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
     }
 }
 
+// ============================================================================
+// Warp-specialised prefill (bf16 inputs).
+//
+// The per-chunk work splits into a key side that does not touch the state
+// (local decay, decay-scaled operands, Gram tiles, inverses of the diagonal
+// blocks) and a state side (K~S, the solve for U, outputs, state update).  A
+// workgroup has NK = 4 key waves and d_v/16 state waves: while the state waves
+// run chunk j, the key waves prepare chunk j+1 into the other half of a
+// double-buffered LDS area, so the two instruction mixes (exponentials and
+// vector ALU on one side, matrix cores on the other) overlap on every SIMD,
+// and a chunk costs three workgroup barriers.
+//
+// Chunks are 32 tokens.  With g >= -5 a 32-token chunk spans at most -160,
+// so a reference at its 16th token keeps every factor inside e^+-80 (the
+// 16-token window of "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate
+// the New Generation", section 3.1, taken on both sides of the reference):
+//   - if the chunk total is >= -64 on every channel, the chunk start is the
+//     reference for everything (q~ = q e^G, k~ = k e^G, k^ = k e^-G);
+//   - otherwise the Gram operands use the middle reference m (q e^(G-m),
+//     k e^(G-m), k e^(m-G)) while the inter-chunk operands keep the chunk
+//     start (q e^G, k e^G <= 1, which may underflow harmlessly).
+// No sub-tile path is needed.
+//
+// Per chunk (2 row blocks of 16 tokens):
+//   key:   G (log2 units) -> group sums | operands QO, KO, KH, KD, gamma, beta
+//          | Gram A, P tiles; -beta A masked; Linv_0, Linv_1 by forward
+//          substitution; An_10
+//   state: KS = K~ S; R = beta (V - KS) | U_0 = Linv_0 R_0,
+//          U_1 = Linv_1 (R_1 + An_10 U_0); O = Q~ S + P U (stored) |
+//          S <- diag(gamma) S + K_dec^T U
+// ============================================================================
+
+template <int DK, int DV, int NCB = 1>
+struct CfgW {
+    static constexpr int CW = 32;             // chunk length (tokens)
+    static constexpr int NK = 4;              // key waves
+    static constexpr int NS = DV / 16;        // state waves; state wave s owns columns 16s .. 16s+15
+    static constexpr int NT = 64 * (NK + NS);
+    static constexpr int KM = DK / 32;        // MFMA k-steps over d_k
+    static constexpr int RT = DK / 16;        // 16-row tiles of the state
+    static constexpr int CPR = DK / 2;        // key lanes per token row (two channels per lane)
+    static constexpr int NG = NK * 64 / CPR;  // token groups of the key side
+    static constexpr int TPL = CW / NG;       // tokens per group (8 at d_k = 128, 4 at 64)
+    static constexpr int TPW = CW / NK;       // tokens whose inputs one key wave copies (8)
+    static constexpr int SZ_OP = CW * DK * 2;
+    static constexpr int SZ_PO = CW * CW * 2;
+    // one half of the double buffer: written by the key side for chunk j,
+    // read by the state side one chunk later
+    static constexpr int B_QO = 0, B_KO = SZ_OP, B_KD = 2 * SZ_OP, B_PO = 3 * SZ_OP;
+    static constexpr int B_TB = B_PO + SZ_PO;  // Linv_0, Linv_1, An_10 as A-operand fragments, 1 KiB each
+    static constexpr int B_BETA = B_TB + 3 * 1024, B_GM = B_BETA + CW * 4;
+    static constexpr int SZ_BUF = (B_GM + DK * 4 + 255) / 256 * 256;
+    // key-side scratch
+    static constexpr int OFF_KH = 2 * SZ_BUF, OFF_QM = OFF_KH + SZ_OP, OFF_KM = OFF_QM + SZ_OP;
+    static constexpr int OFF_AN = OFF_KM + SZ_OP, OFF_GT = OFF_AN + 2 * 1024;
+    static constexpr int OFF_STG = (OFF_GT + NG * DK * 4 + 1023) / 1024 * 1024;
+    static constexpr int SG_G = CW * DK * 4, SG_Q = CW * DK * 2;
+    static constexpr int LDS = OFF_STG + SG_G + 2 * SG_Q + 64 * 4;
+    static_assert(TPL >= 4 && (TPL & (TPL - 1)) == 0, "token groups");
+};
+
+// Key side: waves 0 .. NK-1.  Prepares chunk i in iteration i.
+template <int DK, int DV, bool MAP, int NCB>
+__device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, int h, int64_t tb, int64_t te,
+                                       int nch) {
+    typedef CfgW<DK, DV, NCB> P;
+    typedef bf16 TI;
+    typedef Mma<bf16> M;
+    typedef bf16x8 frag;
+    constexpr bool OUT = !MAP;
+    constexpr int CW = P::CW, KM = P::KM;
+    const int H = a.H;
+    char* stg = smem + P::OFF_STG;
+    const float* stg_g = reinterpret_cast<const float*>(stg);
+    const TI* stg_q = reinterpret_cast<const TI*>(stg + P::SG_G);
+    const TI* stg_k = reinterpret_cast<const TI*>(stg + P::SG_G + P::SG_Q);
+    float* stg_b = reinterpret_cast<float*>(stg + P::SG_G + 2 * P::SG_Q);
+    TI* KH = reinterpret_cast<TI*>(smem + P::OFF_KH);
+    TI* QM = reinterpret_cast<TI*>(smem + P::OFF_QM);
+    TI* KMm = reinterpret_cast<TI*>(smem + P::OFF_KM);
+    floatx4* AN = reinterpret_cast<floatx4*>(smem + P::OFF_AN);
+    float* s_gt = reinterpret_cast<float*>(smem + P::OFF_GT);
+
+    // copy of chunk j's g, q, k rows TPW*kw .. TPW*kw+TPW-1 (and, wave 0, beta)
+    auto dma = [&](int j, int lane) {
+        const int64_t c0 = tb + (int64_t)j * CW;
+        const int L = (int)(te - c0 < CW ? te - c0 : CW);
+        const size_t tok0 = (size_t)c0 * H + h;
+        auto rows = [&](const void* src, int RB, char* dst) {
+            const int lpr = RB / 16, rpi = 64 / lpr;
+            const char* base = static_cast<const char*>(src) + tok0 * RB;
+#pragma unroll
+            for (int i = 0; i < P::TPW / rpi; ++i) {
+                const int r0 = P::TPW * kw + rpi * i;
+                const int t = min(r0 + lane / lpr, L - 1);
+                __builtin_amdgcn_global_load_lds(gptr(base + (uint32_t)(t * H * RB + (lane % lpr) * 16)),
+                                                 lptr(dst + r0 * RB), 16, 0, 0);
+            }
+        };
+        rows(a.g, DK * 4, stg);
+        if (OUT) rows(a.q, DK * 2, stg + P::SG_G);
+        rows(a.k, DK * 2, stg + P::SG_G + P::SG_Q);
+        if (kw == 0)
+            __builtin_amdgcn_global_load_lds(gptr(a.beta + tok0 + (size_t)min(lane, L - 1) * H), lptr(stg_b), 4, 0, 0);
+    };
+    if (nch > 0) dma(0, threadIdx.x & 63);
+
+    for (int i = 0; i <= nch; ++i) {
+        int tid = kw * 64 + (threadIdx.x & 63);
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+        const int cp = tid % P::CPR, grp = tid / P::CPR, ch = 2 * cp, t0 = grp * P::TPL;
+        const bool act = i < nch;
+        char* buf = smem + (i & 1) * P::SZ_BUF;
+        TI* QO = reinterpret_cast<TI*>(buf + P::B_QO);
+        TI* KO = reinterpret_cast<TI*>(buf + P::B_KO);
+        TI* KD = reinterpret_cast<TI*>(buf + P::B_KD);
+        TI* PO = reinterpret_cast<TI*>(buf + P::B_PO);
+        frag* TB = reinterpret_cast<frag*>(buf + P::B_TB);
+        float* BETA = reinterpret_cast<float*>(buf + P::B_BETA);
+        float* GM = reinterpret_cast<float*>(buf + P::B_GM);
+        const int64_t c0 = tb + (int64_t)i * CW;
+        const int L = (int)(te - c0 < CW ? te - c0 : CW);
+
+        // ---- K1: this wave's copy has landed; its rows go to registers (their
+        // latency hides behind the barrier) and the group sums of g (log2 units)
+        // to LDS
+        floatx2 gv[P::TPL];
+        bf16x2 kv[P::TPL], qv[P::TPL];
+        if (act) {
+            __builtin_amdgcn_s_waitcnt(0);
+            if (L < CW) {
+                // rows L .. CW-1 of this wave's part hold copies of row L-1: zero them
+                for (int t = P::TPW * kw; t < P::TPW * (kw + 1); ++t)
+                    if (t >= L) {
+                        if (lane < DK / 4) reinterpret_cast<floatx4*>(const_cast<float*>(stg_g) + t * DK)[lane] = zero4();
+                        if (lane < DK / 8) {
+                            reinterpret_cast<floatx4*>(const_cast<TI*>(stg_q) + t * DK)[lane] = zero4();
+                            reinterpret_cast<floatx4*>(const_cast<TI*>(stg_k) + t * DK)[lane] = zero4();
+                        }
+                    }
+                if (kw == 0 && lane >= L && lane < CW) stg_b[lane] = 0.f;
+            }
+#pragma unroll
+            for (int tt = 0; tt < P::TPL; ++tt) {
+                gv[tt] = *reinterpret_cast<const floatx2*>(stg_g + (t0 + tt) * DK + ch);
+                kv[tt] = *reinterpret_cast<const bf16x2*>(stg_k + (t0 + tt) * DK + ch);
+                if constexpr (OUT) qv[tt] = *reinterpret_cast<const bf16x2*>(stg_q + (t0 + tt) * DK + ch);
+            }
+        }
+        // inverses of the previous chunk's diagonal blocks (waves 0, 1): forward
+        // substitution; row j of the inverse is final once rows < j have been
+        // applied, and is broadcast along the 16-lane row
+        if (i >= 1 && kw < 2) {
+            float arow[16];
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const floatx4 y = AN[kw * 64 + r + 16 * gg];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * gg + e] = y[e];
+            }
+            floatx4 li;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) li[e] = (r == 4 * g + e) ? 1.f : 0.f;
+            static_for<0, 15>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) li[e] = fma_row_bcast<j>(arow[j], li[e], li[e]);
+            });
+            frag* TBp = reinterpret_cast<frag*>(smem + ((i - 1) & 1) * P::SZ_BUF + P::B_TB);
+            TBp[kw * 64 + lane] =
+                frag{(bf16)li[0], (bf16)li[1], (bf16)li[2], (bf16)li[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+        }
+        if (act) {
+            floatx2 sum = floatx2{0.f, 0.f};
+#pragma unroll
+            for (int tt = 0; tt < P::TPL; ++tt) sum = fma2(gv[tt], LOG2E, sum);
+            *reinterpret_cast<floatx2*>(s_gt + grp * DK + ch) = sum;
+            if (kw == 0 && lane < CW) BETA[lane] = stg_b[lane];
+            // this wave's staging rows are in registers: copy the next chunk
+            // (it lands during the rest of this iteration and is waited for
+            // at the start of the next)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (i + 1 < nch) dma(i + 1, lane);
+        }
+        lds_barrier();  // B1
+
+        // ---- K2: decay-scaled operands
+        bool fast = true;
+        if (act) {
+            floatx2 off = floatx2{0.f, 0.f}, tot = floatx2{0.f, 0.f}, mid = floatx2{0.f, 0.f};
+#pragma unroll
+            for (int gg = 0; gg < P::NG; ++gg) {
+                if (gg == grp) off = tot;
+                if (gg == 16 / P::TPL) mid = tot;  // G after token 15
+                tot += *reinterpret_cast<const floatx2*>(s_gt + gg * DK + ch);
+            }
+            constexpr float BUDGET = -64.f * LOG2E;  // e^-64, in log2 units
+            fast = __all(tot[0] >= BUDGET && tot[1] >= BUDGET);
+            const floatx2 gam = pow2v(tot);
+            if (grp == 0) *reinterpret_cast<floatx2*>(GM + ch) = gam;
+            // byte offset of (t0 + tt, ch) in the bf16 operand layout: that of
+            // (t0, ch) with tt XORed into bits 4.. (t0 is a multiple of TPL, a
+            // power of two, and a group stays in one 16-row block)
+            const uint32_t a0 = op_idx<TI, KM>(t0, ch) * 2u;
+            auto put = [&](TI* mat, int tt, floatx2 x) {
+                *reinterpret_cast<bf16x2*>(reinterpret_cast<char*>(mat) + (a0 ^ (uint32_t)(tt << 4))) =
+                    bf16x2{(bf16)x[0], (bf16)x[1]};
+            };
+            auto store_kd4 = [&](int t, const floatx2* kd) {
+                *reinterpret_cast<bf16x4*>(KD + op_idx<TI, 1>(ch, t)) =
+                    bf16x4{(bf16)kd[0][0], (bf16)kd[1][0], (bf16)kd[2][0], (bf16)kd[3][0]};
+                *reinterpret_cast<bf16x4*>(KD + op_idx<TI, 1>(ch + 1, t)) =
+                    bf16x4{(bf16)kd[0][1], (bf16)kd[1][1], (bf16)kd[2][1], (bf16)kd[3][1]};
+            };
+            // one loop per case (the choice is uniform), so that the loads of
+            // all TPL tokens can be issued together
+            auto ld_g = [&](int t) { return gv[t - t0]; };
+            auto ld_k = [&](int t) { return to_f2(kv[t - t0]); };
+            auto ld_q = [&](int t) {
+                if constexpr (OUT) return to_f2(qv[t - t0]);
+                return floatx2{0.f, 0.f};
+            };
+            floatx2 G = off;
+            if (fast) {
+#pragma unroll
+                for (int tq = 0; tq < P::TPL; tq += 4) {
+                    floatx2 kd[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int tt = tq + j, t = t0 + tt;
+                        G = fma2(ld_g(t), LOG2E, G);
+                        const floatx2 kk = ld_k(t), e = pow2v(G), ei = pow2v(-G);
+                        const floatx2 kh = kk * ei;
+                        if constexpr (OUT) put(QO, tt, ld_q(t) * e);
+                        put(KO, tt, kk * e);
+                        put(KH, tt, kh);
+                        kd[j] = kh * gam;  // K_dec = k e^(G_L - G)
+                    }
+                    store_kd4(t0 + tq, kd);
+                }
+            } else {
+#pragma unroll
+                for (int tq = 0; tq < P::TPL; tq += 4) {
+                    floatx2 kd[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int tt = tq + j, t = t0 + tt;
+                        G = fma2(ld_g(t), LOG2E, G);
+                        const floatx2 kk = ld_k(t);
+                        const floatx2 e0 = pow2v(G), em = pow2v(G - mid), eim = pow2v(mid - G);
+                        if constexpr (OUT) {
+                            const floatx2 qq = ld_q(t);
+                            put(QO, tt, qq * e0);
+                            put(QM, tt, qq * em);
+                        }
+                        put(KO, tt, kk * e0);
+                        put(KMm, tt, kk * em);
+                        put(KH, tt, kk * eim);
+                        kd[j] = kk * pow2v(tot - G);
+                    }
+                    store_kd4(t0 + tq, kd);
+                }
+            }
+        }
+        lds_barrier();  // B2
+
+        // ---- K3: Gram tiles (0,0), (1,1), (1,0) on waves 0, 1, 2
+        if (act && kw < 3) {
+            const int I = kw == 0 ? 0 : 1, J = kw == 1 ? 1 : 0;
+            const TI* rk = fast ? KO : KMm;
+            const TI* rq = fast ? QO : QM;
+            frag fa[KM], fk[KM];
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+                fa[m] = op_frag<TI, KM>(KH, J, m, lane);
+                fk[m] = op_frag<TI, KM>(rk, I, m, lane);
+            }
+            floatx4 accA = zero4();
+#pragma unroll
+            for (int m = 0; m < KM; ++m) accA = M::mma(fa[m], fk[m], accA);
+            const int t = 16 * I + r;
+            if constexpr (OUT) {
+                frag fq[KM];
+#pragma unroll
+                for (int m = 0; m < KM; ++m) fq[m] = op_frag<TI, KM>(rq, I, m, lane);
+                floatx4 accP = zero4();
+#pragma unroll
+                for (int m = 0; m < KM; ++m) accP = M::mma(fa[m], fq[m], accP);
+                floatx4 p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[e] = (16 * J + 4 * g + e <= t) ? accP[e] : 0.f;
+                bf16* dst = reinterpret_cast<bf16*>(PO) + (I * 64 + op_slot(I, 0, r, g)) * 8 + 4 * J;
+                *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3]};
+                if (I == 0) *reinterpret_cast<bf16x4*>(dst + 4) = bf16x4{};  // block above the diagonal
+            }
+            // -beta_t A[t][s], s < t; lane r + 16g: row t, columns 16J + 4g + e
+            const float bt = BETA[t];
+            floatx4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (16 * J + 4 * g + e < t) ? -bt * accA[e] : 0.f;
+            if (I == J) {
+                AN[kw * 64 + lane] = x;  // inverted at the start of the next iteration
+            } else {
+                TB[2 * 64 + lane] = frag{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3], (bf16)0.f, (bf16)0.f,
+                                         (bf16)0.f, (bf16)0.f};
+            }
+        }
+        lds_barrier();  // B3
+    }
+}
+
+// State side: waves NK .. NK+NS-1.  Runs chunk i-1 in iteration i.
+template <int DK, int DV, bool MAP, int NCB>
+__device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw, const Unit& u, int nch) {
+    typedef CfgW<DK, DV, NCB> P;
+    typedef bf16 TI;
+    typedef Mma<bf16> M;
+    typedef bf16x8 frag;
+    constexpr bool OUT = !MAP;
+    constexpr int CW = P::CW, KM = P::KM, RT = P::RT;
+    const int H = a.H, h = u.h;
+    const int64_t tb = u.tb, te = u.te;
+    const int col0 = 16 * sw;
+    const uint32_t vrow = (uint32_t)H * DV;
+    const int r0 = threadIdx.x & 15, g0 = (threadIdx.x & 63) >> 4;
+
+    // fp32 state: S[cb][rt][i] = S[16 rt + 4g + i][col0 + r] (NCB = 2: [0] the M part from I, [1] the N part)
+    floatx4 S[NCB][RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g0 + i;
+            S[0][rt][i] = u.s0 ? at<float>(u.s0, (row * DV + col0 + r0) * 4) : (u.eye && row == col0 + r0) ? 1.f : 0.f;
+            if constexpr (NCB == 2) S[1][rt][i] = 0.f;
+        }
+    const bool vuse = !u.vzero;
+    // v of chunk j in accumulator layout: vr[I][i] = v[16I + 4g + i][col0 + r] (rows clamped to the chunk)
+    TI vnext[2][4];
+    auto load_v = [&](int j, int g, int r) {
+        const int64_t c0 = tb + (int64_t)j * CW;
+        const int L = (int)(te - c0 < CW ? te - c0 : CW);
+        const TI* vb = a.v + ((size_t)c0 * H + h) * DV;
+#pragma unroll
+        for (int I = 0; I < 2; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = min(16 * I + 4 * g + i, L - 1);
+                vnext[I][i] = vuse ? at<TI>(vb, (t * vrow + col0 + r) * 2u) : TI(0.f);
+            }
+    };
+    if (nch > 0) load_v(0, g0, r0);
+
+    for (int i = 0; i <= nch; ++i) {
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+        const bool act = i >= 1;
+        const int j = i - 1;
+        const char* buf = smem + (j & 1) * P::SZ_BUF;
+        const TI* QO = reinterpret_cast<const TI*>(buf + P::B_QO);
+        const TI* KO = reinterpret_cast<const TI*>(buf + P::B_KO);
+        const TI* KD = reinterpret_cast<const TI*>(buf + P::B_KD);
+        const TI* PO = reinterpret_cast<const TI*>(buf + P::B_PO);
+        const frag* TB = reinterpret_cast<const frag*>(buf + P::B_TB);
+        const float* BETA = reinterpret_cast<const float*>(buf + P::B_BETA);
+        const float* GM = reinterpret_cast<const float*>(buf + P::B_GM);
+        const int64_t c0 = tb + (int64_t)j * CW;
+        const int L = (int)(te - c0 < CW ? te - c0 : CW);
+
+        TI vr[2][4];
+#pragma unroll
+        for (int I = 0; I < 2; ++I)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[I][e] = vnext[I][e];
+        if (i < nch) load_v(i, g, r);
+
+        // ---- S1: K~ S and the right-hand side beta (V - K~ S)
+        frag bS[NCB][KM];
+        floatx4 R[NCB][2];
+        if (act) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const bool vblock = NCB == 1 || cb == 1;
+#pragma unroll
+                for (int m = 0; m < KM; ++m) bS[cb][m] = acc_perm<TI>(S[cb], m, RT);
+#pragma unroll
+                for (int I = 0; I < 2; ++I) {
+                    floatx4 ks = zero4();
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) ks = M::mma(op_frag<TI, KM>(KO, I, m, lane), bS[cb][m], ks);
+                    const floatx4 bt = *reinterpret_cast<const floatx4*>(BETA + 16 * I + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) R[cb][I][e] = bt[e] * ((vblock ? (float)vr[I][e] : 0.f) - ks[e]);
+                }
+            }
+        }
+        lds_barrier();  // B1
+
+        // ---- S2: U by block forward substitution; outputs
+        frag bU[NCB];
+        if (act) {
+            const frag l0 = TB[lane], l1 = TB[64 + lane], an = TB[128 + lane];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                floatx4 U[2];
+                U[0] = M::mma(l0, acc_perm<TI>(&R[cb][0], 0, 1), zero4());
+                const floatx4 r1 = M::mma(an, acc_perm<TI>(U, 0, 1), R[cb][1]);
+                U[1] = M::mma(l1, acc_perm<TI>(&r1, 0, 1), zero4());
+                bU[cb] = acc_perm<TI>(U, 0, 2);
+            }
+            if constexpr (OUT) {
+                TI* ob = a.o + ((size_t)c0 * H + h) * DV;
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    floatx4 O = zero4();
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) O = M::mma(bS[0][m], op_frag<TI, KM>(QO, rb, m, lane), O);
+                    O = M::mma(bU[0], op_frag<TI, 1>(PO, rb, 0, lane), O);
+                    const int t = 16 * rb + r;
+                    if (t < L)
+                        at_mut<bf16x4>(ob, (t * vrow + col0 + 4 * g) * 2u) =
+                            bf16x4{(bf16)O[0], (bf16)O[1], (bf16)O[2], (bf16)O[3]};
+                }
+            }
+        }
+        lds_barrier();  // B2
+
+        // ---- S3: S <- diag(gamma) S + K_dec^T U
+        if (act) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const floatx4 d = *reinterpret_cast<const floatx4*>(GM + 16 * rt + 4 * g);
+                    S[cb][rt] *= d;
+                    S[cb][rt] = M::mma(op_frag<TI, 1>(KD, rt, 0, lane), bU[cb], S[cb][rt]);
+                }
+            }
+        }
+        lds_barrier();  // B3
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        float* dst = cb == 0 ? u.sf : u.sf2;
+        if (dst) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    at_mut<float>(dst, ((16 * rt + 4 * g0 + i) * DV + col0 + r0) * 4) = S[cb][rt][i];
+        }
+    }
+}
+
+template <int DK, int DV, bool MAP, int NCB = 1>
+__global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(Args<bf16> a) {
+    typedef CfgW<DK, DV, NCB> P;
+    static_assert(NCB == 1 || (MAP && DK == DV), "two column blocks only for transitions with d_k = d_v");
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
+    const Unit u = resolve_unit<bf16, DK, DV, MAP, NCB>(a, blockIdx.x);
+    if (!u.valid) return;
+    const int nch = (int)((u.te - u.tb + P::CW - 1) / P::CW);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w < P::NK) ws_key<DK, DV, MAP, NCB>(a, smem, w, u.h, u.tb, u.te, nch);
+    else ws_state<DK, DV, MAP, NCB>(a, smem, w - P::NK, u, nch);
+}
+
 // nl[0] = 0, nl[n + 1] = nl[n] + (number of non-last segments of sequence n):
 // a sequence of len > 0 tokens has ceil(len / seg) segments, an empty one has
 // one (of zero tokens).  One workgroup, a block-wide scan per 256 sequences.
@@ -984,11 +1486,23 @@ __global__ __launch_bounds__(256) void seg_final_kernel(const int32_t* __restric
     for (int e = threadIdx.x; e < DK * DV / 4; e += 256) dst[e] = src[e];
 }
 
+template <int DK, int DV, bool MAP, int NCB = 1>
+hipError_t launch_ws(const Args<bf16>& a, int64_t blocks, hipStream_t s) {
+    typedef CfgW<DK, DV, NCB> P;
+    static_assert(P::LDS <= 160 * 1024, "LDS budget");
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
+    return hipGetLastError();
+}
+
 template <typename TI, int DK, int DV, bool MAP, int NCB = 1>
 hipError_t launch_seq(const Args<TI>& a, int64_t blocks, hipStream_t s) {
     typedef Cfg<TI, DK, DV> P;
     static_assert(P::LDS <= 160 * 1024, "LDS budget");
     if (blocks <= 0) return hipSuccess;
+    if constexpr (sizeof(TI) == 2) {
+        if (!a.legacy) return launch_ws<DK, DV, MAP, NCB>(a, blocks, s);
+    }
     auto kern = prefill_seq_kernel<TI, DK, DV, MAP, NCB>;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
     return hipGetLastError();
@@ -1013,6 +1527,7 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     a.wsM = a.wsN = nullptr;
     a.m_blocks = 0;
     a.final_to_slot = 0;
+    a.legacy = p.legacy;
     const int64_t units = (int64_t)p.num_seqs * p.H;
     if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
 
