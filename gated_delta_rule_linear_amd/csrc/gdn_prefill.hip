@@ -191,20 +191,50 @@ __device__ __forceinline__ typename Mma<TI>::frag op_frag(const TI* base, int bl
     return reinterpret_cast<const typename Mma<TI>::frag*>(base)[(blk * KM + m) * 64 + op_slot(blk, m, lane & 15, lane >> 4)];
 }
 
-// acc + a * x[lane J of this lane's 16-lane row]: the row broadcast is a DPP
-// row_newbcast source modifier, which folds into v_fmac_f32.
-template <int J>
-__device__ __forceinline__ float fma_row_bcast(float a, float x, float acc) {
-    const float b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, false));
-    return __builtin_fmaf(b, a, acc);
-}
-
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (I < N) {
         f(std::integral_constant<int, I>{});
         static_for<I + 1, N>(f);
     }
+}
+
+// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle); with stride 0, accesses at or past num_records bytes
+// are dropped (stores) or return 0 (loads).
+constexpr uint32_t BUFFER_RSRC_WORD3 = 0x00020000u;
+typedef unsigned int u32x2 __attribute__((__vector_size__(8)));
+
+// x[e] += a * x[e][lane J of this lane's 16-lane row], e = 0..3: four
+// v_fmac_f32 whose first source is read through the DPP row_newbcast
+// modifier.  A broadcast read needs two wait states after the VALU write of
+// its register: consecutive calls leave three instructions between them, and
+// row_inverse puts them before the first call.
+template <int J>
+__device__ __forceinline__ void fma4_row_bcast(float a, float& x0, float& x1, float& x2, float& x3) {
+    asm volatile(
+        "v_fmac_f32_dpp %0, %0, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+        : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+        : "v"(a), "n"(J));
+}
+
+// Inverse of the unit lower-triangular 16 x 16 matrix I - N, N strictly lower,
+// by forward substitution.  Lane r + 16g holds row r of N in arow[0..15] and
+// returns entries (r, 4g + e) of the inverse.  Row j of the inverse is final
+// once rows < j have been applied, so step j broadcasts row j along the
+// 16-lane row.
+__device__ __forceinline__ floatx4 row_inverse(const float (&arow)[16], int r, int g) {
+    float x0 = r == 4 * g ? 1.f : 0.f, x1 = r == 4 * g + 1 ? 1.f : 0.f;
+    float x2 = r == 4 * g + 2 ? 1.f : 0.f, x3 = r == 4 * g + 3 ? 1.f : 0.f;
+    asm volatile("s_nop 4" ::: "memory");  // wait states before the first broadcast read (and an EXEC write)
+    static_for<0, 15>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        fma4_row_bcast<j>(arow[j], x0, x1, x2, x3);
+    });
+    return floatx4{x0, x1, x2, x3};
 }
 
 // Index of the lower-triangle block (I, J), J <= I, in row-major order.
@@ -795,14 +825,7 @@ __global__ __launch_bounds__((Cfg<TI, DK, DV>::NT), 1) void prefill_seq_kernel(A
 #pragma unroll
                 for (int i = 0; i < 4; ++i) arow[4 * gg + i] = x[i];
             }
-            floatx4 x;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (r == 4 * g + i) ? 1.f : 0.f;
-            static_for<0, 15>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = fma_row_bcast<j>(arow[j], x[i], x[i]);
-            });
+            const floatx4 x = row_inverse(arow, r, g);
             An[(10 + I) * 64 + lane] = x;
         }
         lds_barrier();
@@ -1009,6 +1032,23 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
     floatx4* AN = reinterpret_cast<floatx4*>(smem + P::OFF_AN);
     float* s_gt = reinterpret_cast<float*>(smem + P::OFF_GT);
 
+    // waves 0, 1: inverse of the diagonal block kw of (I + beta A), whose
+    // strictly lower part -beta A is in this wave's AN area, as an A-operand
+    // fragment (each lane gathers its row of the block from LDS)
+    auto inverse_to = [&](frag* tb) {
+        const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+        float arow[16];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            const floatx4 y = AN[kw * 64 + r + 16 * gg];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) arow[4 * gg + e] = y[e];
+        }
+        const floatx4 li = row_inverse(arow, r, g);
+        tb[kw * 64 + lane] =
+            frag{(bf16)li[0], (bf16)li[1], (bf16)li[2], (bf16)li[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    };
+
     // copy of chunk j's g, q, k rows TPW*kw .. TPW*kw+TPW-1 (and, wave 0, beta)
     auto dma = [&](int j, int lane) {
         const int64_t c0 = tb + (int64_t)j * CW;
@@ -1076,29 +1116,8 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                 if constexpr (OUT) qv[tt] = *reinterpret_cast<const bf16x2*>(stg_q + (t0 + tt) * DK + ch);
             }
         }
-        // inverses of the previous chunk's diagonal blocks (waves 0, 1): forward
-        // substitution; row j of the inverse is final once rows < j have been
-        // applied, and is broadcast along the 16-lane row
-        if (i >= 1 && kw < 2) {
-            float arow[16];
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const floatx4 y = AN[kw * 64 + r + 16 * gg];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) arow[4 * gg + e] = y[e];
-            }
-            floatx4 li;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) li[e] = (r == 4 * g + e) ? 1.f : 0.f;
-            static_for<0, 15>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) li[e] = fma_row_bcast<j>(arow[j], li[e], li[e]);
-            });
-            frag* TBp = reinterpret_cast<frag*>(smem + ((i - 1) & 1) * P::SZ_BUF + P::B_TB);
-            TBp[kw * 64 + lane] =
-                frag{(bf16)li[0], (bf16)li[1], (bf16)li[2], (bf16)li[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-        }
+        if constexpr (MAP)
+            if (i >= 1 && kw < 2) inverse_to(reinterpret_cast<frag*>(smem + ((i - 1) & 1) * P::SZ_BUF + P::B_TB));
         if (act) {
             floatx2 sum = floatx2{0.f, 0.f};
 #pragma unroll
@@ -1193,45 +1212,68 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
         }
         lds_barrier();  // B2
 
-        // ---- K3: Gram tiles (0,0), (1,1), (1,0) on waves 0, 1, 2
-        if (act && kw < 3) {
-            const int I = kw == 0 ? 0 : 1, J = kw == 1 ? 1 : 0;
+        // ---- K3: Gram tiles.  Waves 0, 1: block (I, I) of -beta A and its
+        // inverse; wave 2: block (1, 0) of -beta A and of P; wave 3: the
+        // diagonal blocks of P
+        if (act) {
             const TI* rk = fast ? KO : KMm;
             const TI* rq = fast ? QO : QM;
-            frag fa[KM], fk[KM];
-#pragma unroll
-            for (int m = 0; m < KM; ++m) {
-                fa[m] = op_frag<TI, KM>(KH, J, m, lane);
-                fk[m] = op_frag<TI, KM>(rk, I, m, lane);
-            }
-            floatx4 accA = zero4();
-#pragma unroll
-            for (int m = 0; m < KM; ++m) accA = M::mma(fa[m], fk[m], accA);
-            const int t = 16 * I + r;
-            if constexpr (OUT) {
+            // block (I, J) of Q~ K^^T, masked to s <= t, to PO
+            auto p_tile = [&](int I, int J, const frag (&fa)[KM]) {
                 frag fq[KM];
 #pragma unroll
                 for (int m = 0; m < KM; ++m) fq[m] = op_frag<TI, KM>(rq, I, m, lane);
                 floatx4 accP = zero4();
 #pragma unroll
                 for (int m = 0; m < KM; ++m) accP = M::mma(fa[m], fq[m], accP);
+                const int t = 16 * I + r;
                 floatx4 p;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) p[e] = (16 * J + 4 * g + e <= t) ? accP[e] : 0.f;
                 bf16* dst = reinterpret_cast<bf16*>(PO) + (I * 64 + op_slot(I, 0, r, g)) * 8 + 4 * J;
                 *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3]};
                 if (I == 0) *reinterpret_cast<bf16x4*>(dst + 4) = bf16x4{};  // block above the diagonal
-            }
-            // -beta_t A[t][s], s < t; lane r + 16g: row t, columns 16J + 4g + e
-            const float bt = BETA[t];
-            floatx4 x;
+            };
+            // block (I, J) of -beta_t A[t][s], s < t; lane r + 16g: row t, columns 16J + 4g + e
+            auto a_tile = [&](int I, int J, const frag (&fa)[KM]) {
+                frag fk[KM];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (16 * J + 4 * g + e < t) ? -bt * accA[e] : 0.f;
-            if (I == J) {
-                AN[kw * 64 + lane] = x;  // inverted at the start of the next iteration
-            } else {
+                for (int m = 0; m < KM; ++m) fk[m] = op_frag<TI, KM>(rk, I, m, lane);
+                floatx4 accA = zero4();
+#pragma unroll
+                for (int m = 0; m < KM; ++m) accA = M::mma(fa[m], fk[m], accA);
+                const int t = 16 * I + r;
+                const float bt = BETA[t];
+                floatx4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (16 * J + 4 * g + e < t) ? -bt * accA[e] : 0.f;
+                return x;
+            };
+            auto kh = [&](int J, frag (&fa)[KM]) {
+#pragma unroll
+                for (int m = 0; m < KM; ++m) fa[m] = op_frag<TI, KM>(KH, J, m, lane);
+            };
+            frag fa[KM];
+            if (kw < 2) {
+                kh(kw, fa);
+                AN[kw * 64 + lane] = a_tile(kw, kw, fa);
+                // (transition maps: inverted at the start of the next iteration,
+                // where the key side has more slack)
+                if constexpr (OUT) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS operations of a wave complete in order
+                    inverse_to(TB);
+                }
+            } else if (kw == 2) {
+                kh(0, fa);
+                const floatx4 x = a_tile(1, 0, fa);
                 TB[2 * 64 + lane] = frag{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3], (bf16)0.f, (bf16)0.f,
                                          (bf16)0.f, (bf16)0.f};
+                if constexpr (OUT) p_tile(1, 0, fa);
+            } else if constexpr (OUT) {
+                kh(0, fa);
+                p_tile(0, 0, fa);
+                kh(1, fa);
+                p_tile(1, 1, fa);
             }
         }
         lds_barrier();  // B3
@@ -1339,7 +1381,11 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                 bU[cb] = acc_perm<TI>(U, 0, 2);
             }
             if constexpr (OUT) {
-                TI* ob = a.o + ((size_t)c0 * H + h) * DV;
+                // buffer stores: rows t >= L lie past the extent of the
+                // resource and the hardware drops them, so every lane stores
+                // (no branch, and the count of stores in flight is fixed)
+                const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
+                    a.o + ((size_t)c0 * H + h) * DV, 0, L * vrow * 2, BUFFER_RSRC_WORD3);
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     floatx4 O = zero4();
@@ -1347,9 +1393,9 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                     for (int m = 0; m < KM; ++m) O = M::mma(bS[0][m], op_frag<TI, KM>(QO, rb, m, lane), O);
                     O = M::mma(bU[0], op_frag<TI, 1>(PO, rb, 0, lane), O);
                     const int t = 16 * rb + r;
-                    if (t < L)
-                        at_mut<bf16x4>(ob, (t * vrow + col0 + 4 * g) * 2u) =
-                            bf16x4{(bf16)O[0], (bf16)O[1], (bf16)O[2], (bf16)O[3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(u32x2, bf16x4{(bf16)O[0], (bf16)O[1], (bf16)O[2], (bf16)O[3]}), ob,
+                        (t * vrow + col0 + 4 * g) * 2u, 0, 0);
                 }
             }
         }
