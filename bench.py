@@ -147,8 +147,8 @@ def cpu_baseline(x, tokens: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -229,11 +229,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill_64k", "num_seqs": 1, "T": T, "H": H, "d_k": d, "d_v": d,
                    "gates": "alpha=0.9+0.1*sigmoid(N(0,1)) per key channel", "initial_state": "zero",
-                   "chunk": 64, "workspace_bytes": ws_bytes},
+                   "chunk": 32, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn_prefill call (seg_table, prefill_seq_kernel<bf16,128,128,map>, seg_fold, "
-                               "prefill_seq_kernel<bf16,128,128,out>)",
+                     "kernel": "gdn_prefill call (seg_table, prefill_ws_kernel<128,128,map>, seg_fold, "
+                               "prefill_ws_kernel<128,128,out>)",
                      "algorithmic_bytes_per_launch": pbytes},
         "decode": {"workload": "decode_512x32", "N": N, "H": Hd, "d_k": d, "d_v": d, "ms_per_step": dms,
                    "tokens_per_s": N / (dms / 1e3), "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

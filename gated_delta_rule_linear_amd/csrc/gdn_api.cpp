@@ -49,10 +49,11 @@ namespace gdn {
 // and a serial fold, and buys parallelism.  The plan compares critical paths
 // (SplitCost, in chunk-times of the output pass) for sequences of the mean
 // length (the lengths themselves are on the device):
-//   whole sequences:  ceil(units / CUs) * (chunks + START)
-//   split into P:     maps_pass(units (P-1), Ls/64) + (P-1) * FOLD
-//                     + ceil(units P / CUs) * (Ls/64 + START)
-// and splits when that saves at least 5%.  The workspace bound, and so the
+//   whole sequences:  rounds(units) * (chunks + START)
+//   split into P:     maps_pass(units (P-1), Ls/64) + fold_pass(P-1, units d_v/16)
+//                     + rounds(units P) * (Ls/64 + START)
+// where rounds() weights a partly filled round by its occupancy, and splits
+// when that saves at least 5%.  The workspace bound, and so the
 // plan, depends on the arguments only.
 int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
     if (const char* e = std::getenv("GDN_PREFILL_SEGMENT")) {
@@ -71,8 +72,8 @@ int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32
     int64_t best_seg = 0;
     for (int64_t ls = 1024; ls < len; ls += 512) {
         const double P = std::ceil((double)len / ls), ch = ls / 64.0;
-        const double t = K::maps_pass(units * (P - 1), ch, share, nullptr) + (P - 1) * K::FOLD +
-                         K::rounds(units * P) * (ch + K::START);
+        const double t = K::maps_pass(units * (P - 1), ch, share, nullptr) +
+                         K::fold_pass(P - 1, units * (d_v / 16)) + K::rounds(units * P) * (ch + K::START);
         if (t < best) {
             best = t;
             best_seg = ls;

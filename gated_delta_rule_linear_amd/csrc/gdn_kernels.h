@@ -52,12 +52,29 @@ inline PrefillWorkspace prefill_workspace_layout(int64_t T_total, int32_t num_se
 // Cost model of the time split, in chunk-times of the output pass, fitted to
 // measured kernel times on MI355X (one workgroup per CU at a time).
 struct SplitCost {
+    // Costs in units of one 64-token chunk of the output pass with every CU busy
+    // (fitted to kernel traces of the bf16 kernels at d = 128 on MI355X).
     static constexpr double CUS = 256.0;     // compute units
-    static constexpr double MAP_ONE = 0.68;   // a transition workgroup computing M or N
-    static constexpr double MAP_BOTH = 0.93;  // one computing M and N together (bf16, d_k = d_v)
-    static constexpr double START = 2.0;     // fixed cost per workgroup
-    static constexpr double FOLD = 1.0;      // per fold step
-    static double rounds(double wgs) { return wgs <= 0 ? 0 : (double)(int64_t)((wgs + CUS - 1) / CUS); }
+    static constexpr double MAP_ONE = 0.76;  // a transition workgroup computing M or N
+    static constexpr double MAP_BOTH = 0.87; // one computing M and N together (bf16, d_k = d_v)
+    static constexpr double START = 0.7;     // fixed cost per workgroup
+    static constexpr double FOLD = 1.8;      // per fold step and round of 256 fold workgroups
+    // Relative time of a round in which a fraction `occ` of the CUs is busy: a
+    // chunk runs faster when fewer workgroups share HBM and the power budget
+    // (measured 0.79 with 1/8 of the CUs busy, 0.80 at 1/4, 0.85 at 1/2).
+    static double occ_factor(double occ) {
+        static const double X[5] = {0.0, 0.125, 0.25, 0.5, 1.0}, Y[5] = {0.79, 0.791, 0.801, 0.845, 1.0};
+        if (occ >= 1.0) return 1.0;
+        int i = 0;
+        while (occ > X[i + 1]) ++i;
+        return Y[i] + (Y[i + 1] - Y[i]) * (occ - X[i]) / (X[i + 1] - X[i]);
+    }
+    // Critical path of `wgs` workgroups in rounds of CUS, the last round weighted by its occupancy.
+    static double rounds(double wgs) {
+        if (wgs <= 0) return 0;
+        const double full = (double)(int64_t)(wgs / CUS), rem = wgs - full * CUS;
+        return full + (rem > 0 ? occ_factor(rem / CUS) : 0.0);
+    }
     // Critical path of the transition pass over `maps` (segment, head) pairs of
     // `chunks` chunks; *both says whether M and N share a workgroup.
     static double maps_pass(double maps, double chunks, bool can_share, bool* both) {
@@ -65,6 +82,10 @@ struct SplitCost {
         const double two = can_share ? rounds(maps) * (chunks * MAP_BOTH + START) : one + 1;
         if (both) *both = two < one;
         return two < one ? two : one;
+    }
+    // The fold: `steps` sequential steps, each over (sequence, head, 16 columns) workgroups.
+    static double fold_pass(double steps, double fold_wgs) {
+        return steps * FOLD * (double)(int64_t)((fold_wgs + CUS - 1) / CUS);
     }
 };
 
