@@ -55,9 +55,18 @@ def test_fp32_ragged(dk, dv):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_pages_gate_forces_subtiles(dtype):
-    # g = -5 sigmoid(z): a chunk's total log-decay reaches about -160, beyond the
-    # single-reference budget, so every chunk takes the 16-token sub-tile path
+    # g = -5 sigmoid(z): a chunk's total log-decay reaches about -80 (32 tokens)
+    # or -160 (64 tokens), beyond the single-reference budget, so every chunk
+    # takes the per-16-token-block middle reference
     _prefill_case([320, 320], 4, 128, 128, dtype, gate="pages", seed=3)
+
+
+@pytest.mark.parametrize("gate", ["amin", "pages"])
+def test_bf16_single_role_kernel(monkeypatch, gate):
+    # the single-role bf16 kernel (64-token chunks), selected by GDN_PREFILL_KERNEL=seq
+    monkeypatch.setenv("GDN_PREFILL_KERNEL", "seq")
+    lengths = [1, 63, 64, 65, 130, 0, 200] if gate == "amin" else [320, 320]
+    _prefill_case(lengths, 3, 128, 128, torch.bfloat16, gate=gate, seed=5)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
