@@ -20,14 +20,15 @@ bool validate_mode() {
     return e && e[0] == '1';
 }
 
-// Host-side check of cu_seqlens and of the log-decay domain; synchronous.
+// Host-side check of cu_seqlens and of the log-decay domain (g_dev may be
+// null); synchronous.
 int32_t validate_inputs(const int32_t* cu_dev, int32_t num_seqs, int64_t T_total, const float* g_dev, int64_t ng,
                         hipStream_t s) {
     std::vector<int32_t> cu((size_t)num_seqs + 1);
     if (hipMemcpyAsync(cu.data(), cu_dev, sizeof(int32_t) * cu.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
         return GDN_ERR_HIP;
-    std::vector<float> g((size_t)ng);
-    if (ng > 0 && hipMemcpyAsync(g.data(), g_dev, sizeof(float) * g.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
+    std::vector<float> g(g_dev ? (size_t)ng : 0);  // no g (logit gates): cu_seqlens only
+    if (g_dev && ng > 0 && hipMemcpyAsync(g.data(), g_dev, sizeof(float) * g.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
         return GDN_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
     if (cu[0] != 0 || cu[(size_t)num_seqs] != T_total) return GDN_ERR_DOMAIN;
@@ -84,6 +85,14 @@ int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32
 
 }  // namespace gdn
 
+// The logit entry points' gate and parameter; the parameter keeps every
+// log-decay in [-5, 0].
+static int32_t check_gate(int32_t gate, float p) {
+    if (gate == GDN_GATE_SCALED_SIGMOID) return p >= -5.0f && p <= 0.0f ? GDN_OK : GDN_ERR_DOMAIN;
+    if (gate == GDN_GATE_ALPHA_MIN) return p >= 0.006737947f && p <= 1.0f ? GDN_OK : GDN_ERR_DOMAIN;  // e^-5 rounded up
+    return GDN_ERR_INVALID_ARG;
+}
+
 extern "C" {
 
 const char* gdn_status_string(int32_t status) {
@@ -135,10 +144,11 @@ size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H,
     return gdn::prefill_workspace_layout(T_total, num_seqs, H, d_k, d_v, seg).bytes;
 }
 
-int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                    const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total, const float* initial_state,
-                    float* final_state, void* o, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+static int32_t prefill_impl(const void* q, const void* k, const void* v, const float* g, const void* z,
+                            int32_t gate, float gate_param, const float* beta, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int64_t T_total, const float* initial_state, float* final_state,
+                            void* o, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     if (num_seqs < 0 || T_total < 0 || H < 1) return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
@@ -146,7 +156,7 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     if (num_seqs == 0) return GDN_OK;
     if (!cu_seqlens || !aligned(cu_seqlens, 4)) return GDN_ERR_INVALID_ARG;
     if (T_total > 0) {
-        const void* ptrs16[] = {q, k, v, g, o};
+        const void* ptrs16[] = {q, k, v, gate == GDN_GATE_LOG ? static_cast<const void*>(g) : z, o};
         for (const void* p : ptrs16)
             if (!p || !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
         if (!beta || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
@@ -159,7 +169,9 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     if (((int64_t)num_seqs + (seg > 0 ? T_total / seg : 0)) * H * (d_v / 16) > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (validate_mode()) {
-        const int32_t st = validate_inputs(cu_seqlens, num_seqs, T_total, g, T_total * H * d_k, s);
+        // (logits: every finite or infinite z maps into the domain, so only cu_seqlens is checked)
+        const int32_t st = validate_inputs(cu_seqlens, num_seqs, T_total, gate == GDN_GATE_LOG ? g : nullptr,
+                                           T_total * H * d_k, s);
         if (st != GDN_OK) return st;
     }
     gdn::PrefillLaunch p;
@@ -180,6 +192,9 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     p.T_total = T_total;
     p.seg = seg;
     p.workspace = workspace;
+    p.z = z;
+    p.gate = gate;
+    p.gate_param = gate_param;
     {
         const char* e = std::getenv("GDN_PREFILL_KERNEL");
         p.legacy = e && std::strcmp(e, "seq") == 0;
@@ -187,19 +202,40 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
     return gdn::launch_prefill(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
-                   void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void* stream) {
+int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total, const float* initial_state,
+                    float* final_state, void* o, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, g, nullptr, GDN_GATE_LOG, 0.f, beta, cu_seqlens, num_seqs, T_total, initial_state,
+                        final_state, o, H, d_k, d_v, dtype, workspace, workspace_bytes, stream);
+}
+
+int32_t gdn_prefill_logits(const void* q, const void* k, const void* v, const void* z, int32_t gate,
+                           float gate_param, const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int64_t T_total, const float* initial_state, float* final_state, void* o, int32_t H,
+                           int32_t d_k, int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    const int32_t st = check_gate(gate, gate_param);
+    if (st != GDN_OK) return st;
+    if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    return prefill_impl(q, k, v, nullptr, z, gate, gate_param, beta, cu_seqlens, num_seqs, T_total, initial_state,
+                        final_state, o, H, d_k, d_v, dtype, workspace, workspace_bytes, stream);
+}
+
+static int32_t decode_impl(const void* q, const void* k, const void* v, const float* g, const void* z, int32_t gate,
+                           float gate_param, const float* beta, float* state, void* o, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, int32_t dtype, void* stream) {
     if (N < 0 || H < 1) return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
     if (N == 0) return GDN_OK;
-    const void* ptrs16[] = {q, k, v, g, o, state};
+    const void* ptrs16[] = {q, k, v, gate == GDN_GATE_LOG ? static_cast<const void*>(g) : z, o, state};
     for (const void* p : ptrs16)
         if (!p || !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
     if (!beta || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
     if ((int64_t)N * H > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (validate_mode()) {
+    if (validate_mode() && gate == GDN_GATE_LOG) {
         std::vector<float> gh((size_t)N * H * d_k);
         if (hipMemcpyAsync(gh.data(), g, sizeof(float) * gh.size(), hipMemcpyDeviceToHost, s) != hipSuccess ||
             hipStreamSynchronize(s) != hipSuccess)
@@ -220,7 +256,25 @@ int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, 
     p.dk = d_k;
     p.dv = d_v;
     p.bf16 = dtype == GDN_BF16;
+    p.z = z;
+    p.gate = gate;
+    p.gate_param = gate_param;
     return gdn::launch_decode(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
+
+int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
+                   void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void* stream) {
+    return decode_impl(q, k, v, g, nullptr, GDN_GATE_LOG, 0.f, beta, state, o, N, H, d_k, d_v, dtype, stream);
+}
+
+int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const void* z, int32_t gate, float gate_param,
+                          const float* beta, float* state, void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                          int32_t dtype, void* stream) {
+    const int32_t st = check_gate(gate, gate_param);
+    if (st != GDN_OK) return st;
+    if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    return decode_impl(q, k, v, nullptr, z, gate, gate_param, beta, state, o, N, H, d_k, d_v, dtype, stream);
+}
+
 
 }  // extern "C"

@@ -49,7 +49,8 @@ template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(NTHR) void decode_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                                                     const TI* __restrict__ v, const float* __restrict__ g,
                                                     const float* __restrict__ beta, float* __restrict__ state,
-                                                    TI* __restrict__ o) {
+                                                    TI* __restrict__ o, const bf16* __restrict__ z, int gate,
+                                                    float gate_param) {
     constexpr int CG = DV / 4;     // 4-column groups per row
     constexpr int RG = NTHR / CG;  // row bands
     constexpr int RPB = DK / RG;   // rows per band
@@ -62,7 +63,9 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(const TI* __restrict__ q, 
     const int tid = threadIdx.x;
     const int64_t unit = blockIdx.x;  // sequence * H + head
     if (tid < DK) {
-        s_a[tid] = __expf(g[unit * DK + tid]);
+        // decay factor: e^g, or from the gate logit (gate != GATE_LOG)
+        s_a[tid] = gate == GATE_LOG ? __expf(g[unit * DK + tid])
+                                    : gate_alpha((float)z[unit * DK + tid], gate, gate_param);
         s_k[tid] = to_f32(k[unit * DK + tid]);
         s_q[tid] = to_f32(q[unit * DK + tid]);
     }
@@ -112,7 +115,8 @@ hipError_t run(const DecodeLaunch& p, hipStream_t s) {
     const int64_t units = (int64_t)p.N * p.H;
     hipLaunchKernelGGL((decode_kernel<TI, DK, DV>), dim3((unsigned)units), dim3(NTHR), 0, s,
                        static_cast<const TI*>(p.q), static_cast<const TI*>(p.k), static_cast<const TI*>(p.v), p.g,
-                       p.beta, p.state, static_cast<TI*>(p.o));
+                       p.beta, p.state, static_cast<TI*>(p.o), static_cast<const bf16*>(p.z), p.gate,
+                       p.gate_param);
     return hipGetLastError();
 }
 

@@ -28,4 +28,27 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // 
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// Gate parameterisations of the logit entry points (values of gdn_gate).
+constexpr int GATE_LOG = 0;             // g given directly
+constexpr int GATE_SCALED_SIGMOID = 1;  // g = p sigmoid(z), p = g_min
+constexpr int GATE_ALPHA_MIN = 2;       // g = log(p + (1 - p) sigmoid(z)), p = a_min
+
+// sigmoid(z) = 1 / (1 + e^-z) with the hardware base-2 exponential and
+// reciprocal; z -> -inf gives 0 (1/inf), z -> +inf gives 1.
+__device__ __forceinline__ float sigmoid_hw(float z) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+// Log-decay g of one key channel from its logit z.
+__device__ __forceinline__ float gate_log_decay(float z, int gate, float p) {
+    const float s = sigmoid_hw(z);
+    if (gate == GATE_SCALED_SIGMOID) return p * s;
+    return __builtin_amdgcn_logf(p + (1.f - p) * s) * 0.6931471805599453f;  // log2 -> natural log
+}
+// Decay factor alpha = e^g of one key channel from its logit z.
+__device__ __forceinline__ float gate_alpha(float z, int gate, float p) {
+    const float s = sigmoid_hw(z);
+    if (gate == GATE_SCALED_SIGMOID) return __builtin_amdgcn_exp2f(1.4426950408889634f * p * s);
+    return p + (1.f - p) * s;
+}
+
 }  // namespace gdn

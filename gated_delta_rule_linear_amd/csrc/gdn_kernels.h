@@ -25,6 +25,9 @@ struct PrefillLaunch {
     int64_t seg;      // segment length of the time split (tokens, multiple of 64); 0: none
     void* workspace;  // prefill_workspace_layout(...).bytes bytes when seg > 0
     bool legacy;      // bf16: single-role kernel (GDN_PREFILL_KERNEL=seq) instead of the warp-specialised one
+    const void* z = nullptr;  // bf16 gate logits [T_total, H, d_k] (gate != 0; g unused)
+    int32_t gate = 0;         // 0: g given; 1, 2: gdn_gate parameterisation of z
+    float gate_param = 0.f;
 };
 
 // Workspace of the time-split prefill, for segments of `seg` tokens.  A
@@ -107,6 +110,9 @@ struct DecodeLaunch {
     int32_t dk;
     int32_t dv;
     bool bf16;
+    const void* z = nullptr;  // bf16 gate logits [N, H, d_k] (gate != 0; g unused)
+    int32_t gate = 0;
+    float gate_param = 0.f;
 };
 
 // Each returns hipSuccess or the launch error.  Sizes are validated by the caller.

@@ -127,6 +127,11 @@ struct Args {
     int m_blocks;       // map launches: blocks [0, m_blocks) compute M, the rest N
     int final_to_slot;  // final state of a split sequence goes to its last slot (final_state aliases S0)
     int legacy;         // bf16: use the single-role kernel instead of the warp-specialised one
+    // gate != GATE_LOG: g is not read; the log-decay comes from the bf16 logits
+    // z in the same layout (warp-specialised kernel only)
+    const bf16* z;
+    int gate;
+    float gate_param;
 };
 
 template <typename T>
@@ -1011,7 +1016,7 @@ struct CfgW {
 };
 
 // Key side: waves 0 .. NK-1.  Prepares chunk i in iteration i.
-template <int DK, int DV, bool MAP, int NCB>
+template <int DK, int DV, bool MAP, int NCB, bool ZG>
 __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, int h, int64_t tb, int64_t te,
                                        int nch) {
     typedef CfgW<DK, DV, NCB> P;
@@ -1065,7 +1070,8 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                                                  lptr(dst + r0 * RB), 16, 0, 0);
             }
         };
-        rows(a.g, DK * 4, stg);
+        if constexpr (ZG) rows(a.z, DK * 2, stg);  // logits: bf16 rows
+        else rows(a.g, DK * 4, stg);
         if (OUT) rows(a.q, DK * 2, stg + P::SG_G);
         rows(a.k, DK * 2, stg + P::SG_G + P::SG_Q);
         if (kw == 0)
@@ -1101,7 +1107,8 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                 // rows L .. CW-1 of this wave's part hold copies of row L-1: zero them
                 for (int t = P::TPW * kw; t < P::TPW * (kw + 1); ++t)
                     if (t >= L) {
-                        if (lane < DK / 4) reinterpret_cast<floatx4*>(const_cast<float*>(stg_g) + t * DK)[lane] = zero4();
+                        if (!ZG && lane < DK / 4)
+                            reinterpret_cast<floatx4*>(const_cast<float*>(stg_g) + t * DK)[lane] = zero4();
                         if (lane < DK / 8) {
                             reinterpret_cast<floatx4*>(const_cast<TI*>(stg_q) + t * DK)[lane] = zero4();
                             reinterpret_cast<floatx4*>(const_cast<TI*>(stg_k) + t * DK)[lane] = zero4();
@@ -1109,9 +1116,24 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                     }
                 if (kw == 0 && lane >= L && lane < CW) stg_b[lane] = 0.f;
             }
+            if constexpr (!ZG) {
+#pragma unroll
+                for (int tt = 0; tt < P::TPL; ++tt)
+                    gv[tt] = *reinterpret_cast<const floatx2*>(stg_g + (t0 + tt) * DK + ch);
+            } else {
+                // the gate parameterisation, in registers; rows past the end
+                // get g = 0 (their logits are copies of the last row's)
+                const TI* stg_z = reinterpret_cast<const TI*>(stg);
+#pragma unroll
+                for (int tt = 0; tt < P::TPL; ++tt) {
+                    const bf16x2 zz = *reinterpret_cast<const bf16x2*>(stg_z + (t0 + tt) * DK + ch);
+                    const bool in = t0 + tt < L;
+                    gv[tt] = floatx2{in ? gate_log_decay((float)zz[0], a.gate, a.gate_param) : 0.f,
+                                     in ? gate_log_decay((float)zz[1], a.gate, a.gate_param) : 0.f};
+                }
+            }
 #pragma unroll
             for (int tt = 0; tt < P::TPL; ++tt) {
-                gv[tt] = *reinterpret_cast<const floatx2*>(stg_g + (t0 + tt) * DK + ch);
                 kv[tt] = *reinterpret_cast<const bf16x2*>(stg_k + (t0 + tt) * DK + ch);
                 if constexpr (OUT) qv[tt] = *reinterpret_cast<const bf16x2*>(stg_q + (t0 + tt) * DK + ch);
             }
@@ -1428,7 +1450,8 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
     }
 }
 
-template <int DK, int DV, bool MAP, int NCB = 1>
+// ZG: the log-decay comes from bf16 logits (Args::z, gate, gate_param)
+template <int DK, int DV, bool MAP, int NCB, bool ZG>
 __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(Args<bf16> a) {
     typedef CfgW<DK, DV, NCB> P;
     static_assert(NCB == 1 || (MAP && DK == DV), "two column blocks only for transitions with d_k = d_v");
@@ -1437,7 +1460,7 @@ __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(
     if (!u.valid) return;
     const int nch = (int)((u.te - u.tb + P::CW - 1) / P::CW);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w < P::NK) ws_key<DK, DV, MAP, NCB>(a, smem, w, u.h, u.tb, u.te, nch);
+    if (w < P::NK) ws_key<DK, DV, MAP, NCB, ZG>(a, smem, w, u.h, u.tb, u.te, nch);
     else ws_state<DK, DV, MAP, NCB>(a, smem, w - P::NK, u, nch);
 }
 
@@ -1537,7 +1560,10 @@ hipError_t launch_ws(const Args<bf16>& a, int64_t blocks, hipStream_t s) {
     typedef CfgW<DK, DV, NCB> P;
     static_assert(P::LDS <= 160 * 1024, "LDS budget");
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
+    if (a.gate != GATE_LOG)
+        hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB, true>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB, false>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1547,7 +1573,7 @@ hipError_t launch_seq(const Args<TI>& a, int64_t blocks, hipStream_t s) {
     static_assert(P::LDS <= 160 * 1024, "LDS budget");
     if (blocks <= 0) return hipSuccess;
     if constexpr (sizeof(TI) == 2) {
-        if (!a.legacy) return launch_ws<DK, DV, MAP, NCB>(a, blocks, s);
+        if (!a.legacy || a.gate != GATE_LOG) return launch_ws<DK, DV, MAP, NCB>(a, blocks, s);
     }
     auto kern = prefill_seq_kernel<TI, DK, DV, MAP, NCB>;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
@@ -1574,6 +1600,9 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     a.m_blocks = 0;
     a.final_to_slot = 0;
     a.legacy = p.legacy;
+    a.z = static_cast<const bf16*>(p.z);
+    a.gate = p.gate;
+    a.gate_param = p.gate_param;
     const int64_t units = (int64_t)p.num_seqs * p.H;
     if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
 

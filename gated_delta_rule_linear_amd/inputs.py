@@ -22,6 +22,9 @@ Distributions
                     "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate the
                     New Generation", section 3.1).
   S0     0.02 * N(0, 1), fp32, layout [num_seqs, H, d_k, d_v].
+  z      (logits=True) the decay logits N(0,1) themselves, cast to bf16 (RNE),
+         for the entry points that compute the gate in the kernel; g is still
+         the recipe applied to the fp32 logits.
 
 Layouts: q, k, g are [T_total, H, d_k]; v is [T_total, H, d_v]; beta is
 [T_total, H]; sequences are packed back to back and described by int32
@@ -48,6 +51,7 @@ class PrefillInputs:
     cu_seqlens: torch.Tensor  # int32, on the same device as the tensors
     lengths: list
     initial_state: Optional[torch.Tensor]
+    z: Optional[torch.Tensor] = None  # bf16 decay logits [T, H, dk] (logits=True)
 
     @property
     def T_total(self) -> int:
@@ -65,6 +69,7 @@ class DecodeStep:
     v: torch.Tensor  # [N, H, dv]
     g: torch.Tensor  # [N, H, dk] fp32
     beta: torch.Tensor  # [N, H] fp32
+    z: Optional[torch.Tensor] = None  # bf16 decay logits [N, H, dk] (logits=True)
 
 
 def make_generator(seed: int, device) -> torch.Generator:
@@ -100,31 +105,34 @@ def _draw_gates(gen, shape_beta, shape_g, gate: str, a_min: float, device):
         g = G_MIN * torch.sigmoid(z)
     else:
         raise ValueError(f"unknown gate recipe {gate!r}")
-    return beta, g.contiguous()
+    return beta, g.contiguous(), z
 
 
 def make_prefill_inputs(lengths: Sequence[int], H: int, dk: int, dv: int, dtype=torch.bfloat16,
                         gate: str = "amin", a_min: float = 0.9, init_state: bool = False,
-                        seed: int = 0, device="cpu", gen: Optional[torch.Generator] = None) -> PrefillInputs:
+                        seed: int = 0, device="cpu", gen: Optional[torch.Generator] = None,
+                        logits: bool = False) -> PrefillInputs:
     """Packed prefill inputs for the given sequence lengths (draw order above)."""
     if gen is None:
         gen = make_generator(seed, device)
     lengths = [int(x) for x in lengths]
     T = sum(lengths)
     q, k, v = _draw_qkv(gen, (T, H, dk), (T, H, dv), dtype, device)
-    beta, g = _draw_gates(gen, (T, H), (T, H, dk), gate, a_min, device)
+    beta, g, z = _draw_gates(gen, (T, H), (T, H, dk), gate, a_min, device)
+    zb = z.to(torch.bfloat16) if logits else None
+    del z
     S0 = None
     if init_state:
         S0 = 0.02 * torch.randn((len(lengths), H, dk, dv), generator=gen, device=device, dtype=torch.float32)
     cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
     if lengths:
         cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
-    return PrefillInputs(q, k, v, g, beta, cu.to(device), lengths, S0)
+    return PrefillInputs(q, k, v, g, beta, cu.to(device), lengths, S0, zb)
 
 
 def make_decode_steps(N: int, H: int, dk: int, dv: int, steps: int, dtype=torch.bfloat16,
                       gate: str = "amin", a_min: float = 0.9, seed: int = 0, device="cpu",
-                      gen: Optional[torch.Generator] = None):
+                      gen: Optional[torch.Generator] = None, logits: bool = False):
     """Initial states (0.02*N(0,1)) followed by `steps` one-token draws for N sequences."""
     if gen is None:
         gen = make_generator(seed, device)
@@ -132,8 +140,8 @@ def make_decode_steps(N: int, H: int, dk: int, dv: int, steps: int, dtype=torch.
     out = []
     for _ in range(steps):
         q, k, v = _draw_qkv(gen, (N, H, dk), (N, H, dv), dtype, device)
-        beta, g = _draw_gates(gen, (N, H), (N, H, dk), gate, a_min, device)
-        out.append(DecodeStep(q, k, v, g, beta))
+        beta, g, z = _draw_gates(gen, (N, H), (N, H, dk), gate, a_min, device)
+        out.append(DecodeStep(q, k, v, g, beta, z.to(torch.bfloat16) if logits else None))
     return S0, out
 
 
@@ -155,16 +163,17 @@ WORKLOADS = {
 
 
 def make_varlen64_inputs(seed: int = 0, device="cpu", n_seqs: int = 64, lo: int = 512, hi: int = 16384,
-                         H: int = 32, dk: int = 128, dv: int = 128, dtype=torch.bfloat16) -> PrefillInputs:
+                         H: int = 32, dk: int = 128, dv: int = 128, dtype=torch.bfloat16,
+                         logits: bool = False) -> PrefillInputs:
     """64 packed sequences with lengths uniform on [512, 16384], random initial states."""
     gen = make_generator(seed, device)
     lengths = draw_lengths(gen, n_seqs, lo, hi)
     return make_prefill_inputs(lengths, H, dk, dv, dtype=dtype, gate="amin", a_min=0.9, init_state=True,
-                               device=device, gen=gen)
+                               device=device, gen=gen, logits=logits)
 
 
-def make_workload(name: str, seed: int = 0, device="cpu") -> PrefillInputs:
+def make_workload(name: str, seed: int = 0, device="cpu", logits: bool = False) -> PrefillInputs:
     if name == "varlen64":
-        return make_varlen64_inputs(seed=seed, device=device)
+        return make_varlen64_inputs(seed=seed, device=device, logits=logits)
     spec = dict(WORKLOADS[name])
-    return make_prefill_inputs(seed=seed, device=device, **spec)
+    return make_prefill_inputs(seed=seed, device=device, logits=logits, **spec)

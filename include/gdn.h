@@ -56,6 +56,22 @@ typedef enum gdn_status {
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
+/* Gate of the logit entry points (gdn_prefill_logits, gdn_decode_logits): the
+ * log-decay of each (token, head, key channel) is computed inside the kernels
+ * from a bf16 logit z and a scalar parameter p, so the gate costs 2 bytes per
+ * channel instead of 4.
+ *   GDN_GATE_SCALED_SIGMOID  g = p * sigmoid(z), p = g_min in [-5, 0]: the
+ *       lower-bounded scaled-sigmoid decay of "Trillion-Parameter MoE
+ *       Multimodal LLMs: How to Evaluate the New Generation", section 3.1,
+ *       eq. 1 (there g_min = -5); g lies in [g_min, 0].
+ *   GDN_GATE_ALPHA_MIN       g = log(p + (1 - p) * sigmoid(z)), p = a_min in
+ *       [e^-5, 1]: the decay factor alpha = e^g bounded below by a_min
+ *       instead; g lies in [log a_min, 0].
+ * Either way g stays inside [-5, 0] for every z (z = -inf and +inf give the
+ * endpoints).  GDN_GATE_LOG (g given in fp32) is what gdn_prefill and
+ * gdn_decode take. */
+typedef enum gdn_gate { GDN_GATE_LOG = 0, GDN_GATE_SCALED_SIGMOID = 1, GDN_GATE_ALPHA_MIN = 2 } gdn_gate;
+
 /* Static English description of a status code (never NULL). */
 const char* gdn_status_string(int32_t status);
 
@@ -104,7 +120,9 @@ size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H,
  *               contents on entry are ignored and on return are unspecified.
  *               Two calls in flight at once need two workspaces.
  *
- * Method: each sequence is cut into 64-token chunks.  Inside a chunk the decay
+ * Method: each sequence is cut into chunks (32 tokens with GDN_BF16, 64 with
+ * GDN_F32), long sequences also into segments run in parallel and joined
+ * through the affine map of the state.  Inside a chunk the decay
  * is carried as a local cumulative log-decay (the cumulative decay factor of
  * "Architecture Evolution and Training Engineering for Trillion-Scale Sparse
  * Multimodal Models", section 3.2), the causal intra-chunk products run as
@@ -115,6 +133,22 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
                     const float* initial_state, float* final_state, void* o,
                     int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* gdn_prefill with the gate given as bf16 logits (see gdn_gate):
+ *   z           device, [T_total, H, d_k] bf16, 16-byte aligned (replaces g)
+ *   gate        GDN_GATE_SCALED_SIGMOID or GDN_GATE_ALPHA_MIN, else
+ *               GDN_ERR_INVALID_ARG
+ *   gate_param  g_min in [-5, 0], or a_min in [e^-5, 1]; outside the range
+ *               GDN_ERR_DOMAIN
+ *   dtype       GDN_BF16 only (GDN_F32: GDN_ERR_UNSUPPORTED)
+ * Every other argument, the workspace size and the result are as for
+ * gdn_prefill with g = the parameterisation of z (computed in fp32 from the
+ * bf16 logits). */
+int32_t gdn_prefill_logits(const void* q, const void* k, const void* v, const void* z, int32_t gate,
+                           float gate_param, const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int64_t T_total, const float* initial_state, float* final_state, void* o, int32_t H,
+                           int32_t d_k, int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* One decode step: one new token for each of N sequences, state updated in
  * place (the recurrent form of "How to Think About Trillion-Parameter Sparse
@@ -129,6 +163,13 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
 int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    float* state, void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
                    void* stream);
+
+/* gdn_decode with the gate given as bf16 logits z [N, H, d_k] (16-byte
+ * aligned), gate and gate_param as for gdn_prefill_logits; dtype GDN_BF16
+ * only. */
+int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const void* z, int32_t gate,
+                          float gate_param, const float* beta, float* state, void* o, int32_t N, int32_t H,
+                          int32_t d_k, int32_t d_v, int32_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

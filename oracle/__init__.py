@@ -130,6 +130,35 @@ def decode_step(q, k, v, g, beta, state, dtype=np.float64):
     return recurrent(q, k, v, g, beta, cu, initial_state=state, dtype=dtype)
 
 
+# Gate parameterisations computed from logits (the values of gdn_gate).
+GATE_SCALED_SIGMOID = 1
+GATE_ALPHA_MIN = 2
+
+
+def sigmoid(z):
+    """1 / (1 + e^-z) in fp64, without overflow for large |z|."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gates_from_logits(z, gate, p):
+    """The log-decay g from logits z, in fp64.
+
+    GATE_SCALED_SIGMOID: g = p * sigmoid(z) with p = g_min -- the lower-bounded
+    scaled-sigmoid decay of "Trillion-Parameter MoE Multimodal LLMs: How to
+    Evaluate the New Generation", section 3.1, eq. 1 (g_min = -5 there).
+    GATE_ALPHA_MIN: g = log(p + (1 - p) * sigmoid(z)) with p = a_min, the
+    decay factor alpha = e^g bounded below by a_min.
+    """
+    s = sigmoid(z)
+    if gate == GATE_SCALED_SIGMOID:
+        return float(p) * s
+    if gate == GATE_ALPHA_MIN:
+        return np.log(float(p) + (1.0 - float(p)) * s)
+    raise ValueError(f"unknown gate {gate!r}")
+
+
 def rel_err(x, ref) -> float:
     """max|x - ref| / max|ref| over the whole tensor, in fp64."""
     x = np.asarray(x, dtype=np.float64)

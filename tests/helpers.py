@@ -26,19 +26,22 @@ def np64(t):
 
 def to_device(x, device="cuda"):
     """Copy a PrefillInputs to the device (in place of the CPU tensors)."""
-    for name in ("q", "k", "v", "g", "beta", "cu_seqlens", "initial_state"):
+    for name in ("q", "k", "v", "g", "beta", "cu_seqlens", "initial_state", "z"):
         t = getattr(x, name)
         if t is not None:
             setattr(x, name, t.to(device).contiguous())
     return x
 
 
-def oracle_prefill(x, units=None):
+def oracle_prefill(x, units=None, gate=None):
     """fp64 oracle for the inputs in x (tensors anywhere).  With `units` a list of
-    (sequence, head) pairs, only those are computed: returns dict {(n, h): (o, S)}."""
+    (sequence, head) pairs, only those are computed: returns dict {(n, h): (o, S)}.
+    With gate = (kind, p) the log-decay is the oracle's parameterisation of the
+    bf16 logits x.z instead of x.g."""
     cu = x.cu_seqlens.cpu().numpy().astype(np.int32)
+    gof = (lambda a: oracle.gates_from_logits(a(x.z), *gate)) if gate else (lambda a: a(x.g))
     if units is None:
-        o, S = oracle.recurrent(np64(x.q), np64(x.k), np64(x.v), np64(x.g), np64(x.beta), cu,
+        o, S = oracle.recurrent(np64(x.q), np64(x.k), np64(x.v), gof(np64), np64(x.beta), cu,
                                 initial_state=None if x.initial_state is None else np64(x.initial_state))
         return o, S
     res = {}
@@ -46,7 +49,7 @@ def oracle_prefill(x, units=None):
         a, b = int(cu[n]), int(cu[n + 1])
         sl = lambda t: np64(t[a:b, h:h + 1])
         S0 = None if x.initial_state is None else np64(x.initial_state[n:n + 1, h:h + 1])
-        o, S = oracle.recurrent(sl(x.q), sl(x.k), sl(x.v), sl(x.g), np64(x.beta[a:b, h:h + 1]),
+        o, S = oracle.recurrent(sl(x.q), sl(x.k), sl(x.v), gof(sl), np64(x.beta[a:b, h:h + 1]),
                                 np.array([0, b - a], np.int32), initial_state=S0)
         res[(n, h)] = (o[:, 0], S[0, 0])
     return res

@@ -21,7 +21,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = gdn.exported_symbols_in_header()
     assert set(names) == {"gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free",
-                          "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode"}
+                          "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_prefill_logits",
+                          "gdn_decode_logits"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -117,3 +118,29 @@ def test_short_workspace_rejected(lib, monkeypatch):
     assert need > 0
     assert _prefill(lib, q=p, cu=p, o=p, T=1000, H=2, ws=NUL, wsb=0) == INVALID
     assert _prefill(lib, q=p, cu=p, o=p, T=1000, H=2, ws=p, wsb=need - 1) == INVALID
+
+
+def _prefill_logits(lib, gate=1, p=-5.0, q=NUL, cu=NUL, n=1, T=10, H=4, dk=64, dv=64, dt=1):
+    return lib.gdn_prefill_logits(q, q, q, q, gate, p, q, cu, n, T, NUL, NUL, q, H, dk, dv, dt, NUL, 0, None)
+
+
+def _decode_logits(lib, gate=1, p=-5.0, q=NUL, cu=NUL, N=2, H=4, dk=64, dv=64, dt=1):
+    return lib.gdn_decode_logits(q, q, q, q, gate, p, q, q, q, N, H, dk, dv, dt, None)
+
+
+def test_logit_gate_argument_errors(lib):
+    # gate kind, then its parameter's range (g must stay in [-5, 0]), then the
+    # dtype (bf16 only), all before any pointer is looked at
+    for f in (_prefill_logits, _decode_logits):
+        assert f(lib, gate=0) == INVALID                    # GDN_GATE_LOG is not a logit gate
+        assert f(lib, gate=3) == INVALID
+        assert f(lib, gate=1, p=-5.5) == DOMAIN             # g_min below -5
+        assert f(lib, gate=1, p=0.5) == DOMAIN              # g_min above 0
+        assert f(lib, gate=2, p=0.005) == DOMAIN            # a_min below e^-5
+        assert f(lib, gate=2, p=1.5) == DOMAIN
+        assert f(lib, gate=1, p=float("nan")) == DOMAIN
+        assert f(lib, gate=1, p=-5.0, dt=0) == UNSUPPORTED  # fp32 inputs
+        assert f(lib, gate=2, p=0.9) == INVALID             # valid gate, then null pointers
+        assert f(lib, gate=1, p=-5.0, q=BAD, cu=BAD) == INVALID
+    assert _prefill_logits(lib, n=0, T=0) == OK
+    assert _decode_logits(lib, N=0) == OK

@@ -218,3 +218,42 @@ def test_state_alloc_is_zeroed():
     finally:
         gdn.gdn_state_free(p)
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- gates from bf16 logits
+
+LOGIT_GATES = [("pages", gdn.GDN_GATE_SCALED_SIGMOID, -5.0), ("amin", gdn.GDN_GATE_ALPHA_MIN, 0.9)]
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+@pytest.mark.parametrize("gate,kind,p", LOGIT_GATES)
+def test_prefill_logits(gate, kind, p, dk, dv):
+    # the log-decay computed in the kernel from bf16 logits; the oracle applies
+    # its own fp64 parameterisation to the same logits
+    lengths = [1, 63, 64, 65, 130, 0, 200]
+    log(f"logits case lengths={lengths} H=3 dk={dk} dv={dv} gate={gate} p={p}")
+    x = inputs.make_prefill_inputs(lengths, 3, dk, dv, dtype=torch.bfloat16, gate=gate, a_min=0.9, init_state=True,
+                                   seed=6, logits=True)
+    ref_o, ref_S = oracle_prefill(x, gate=(kind, p))
+    to_device(x)
+    o, S = gdn.gdn_prefill_logits(x.q, x.k, x.v, x.z, kind, p, x.beta, x.cu_seqlens, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    assert_close("o", np64(o), ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", np64(S), ref_S, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("gate,kind,p", LOGIT_GATES)
+def test_decode_logits(gate, kind, p):
+    N, H, d, steps = 5, 3, 128, 4
+    log(f"decode logits N={N} H={H} d={d} gate={gate}")
+    S0, draws = inputs.make_decode_steps(N, H, d, d, steps, dtype=torch.bfloat16, gate=gate, a_min=0.9, seed=12,
+                                         logits=True)
+    ref_S = np64(S0)
+    state = S0.cuda()
+    for st, dr in enumerate(draws):
+        g = oracle.gates_from_logits(np64(dr.z), kind, p)
+        ref_o, ref_S = oracle.decode_step(np64(dr.q), np64(dr.k), np64(dr.v), g, np64(dr.beta), ref_S)
+        o = gdn.gdn_decode_logits(dr.q.cuda(), dr.k.cuda(), dr.v.cuda(), dr.z.cuda(), kind, p, dr.beta.cuda(), state)
+        torch.cuda.synchronize()
+        assert_close(f"step {st} o", np64(o), ref_o, 1e-2)
+    assert_close("state", np64(state), ref_S, 1e-5)

@@ -108,3 +108,20 @@ def test_split_caller_workspace(monkeypatch):
         torch.cuda.synchronize()
         assert_close("o", np64(o), ref_o, 2e-2)
         assert_close("final_state", np64(S), ref_S, 2e-2)
+
+
+@pytest.mark.parametrize("kind,p,gate", [(gdn.GDN_GATE_SCALED_SIGMOID, -5.0, "pages"),
+                                         (gdn.GDN_GATE_ALPHA_MIN, 0.9, "amin")])
+def test_split_logits(monkeypatch, kind, p, gate):
+    # the logit gate through the transition, fold and replay kernels
+    lengths = [1, 255, 256, 257, 0, 700]
+    log(f"split logits lengths={lengths} gate={gate}")
+    x = inputs.make_prefill_inputs(lengths, 3, 128, 128, dtype=torch.bfloat16, gate=gate, a_min=0.9, init_state=True,
+                                   seed=23, logits=True)
+    ref_o, ref_S = oracle_prefill(x, gate=(kind, p))
+    to_device(x)
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "256")
+    o, S = gdn.gdn_prefill_logits(x.q, x.k, x.v, x.z, kind, p, x.beta, x.cu_seqlens, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    assert_close("o", np64(o), ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", np64(S), ref_S, TOL[torch.bfloat16])

@@ -346,3 +346,54 @@ def test_generator_is_deterministic():
     assert all(512 <= n <= 16384 for n in a.lengths)
     for t in ("q", "k", "v", "g", "beta", "initial_state"):
         assert torch.equal(getattr(a, t), getattr(b, t))
+
+
+# ---------------------------------------------------------------- gates from logits
+
+def test_logit_gates_closed_forms():
+    # sigmoid(0) = 1/2 and sigmoid(log 3) = 3/4 exactly.  Scaled sigmoid of the
+    # pages' eq. 1 with g_min = -5: g = -5/2 and -15/4.  alpha bounded below by
+    # a_min = 0.9: alpha = 0.95 and 0.975.
+    S, A = oracle.GATE_SCALED_SIGMOID, oracle.GATE_ALPHA_MIN
+    z = np.array([0.0, math.log(3.0)])
+    assert np.max(np.abs(oracle.gates_from_logits(z, S, -5.0) - [-2.5, -3.75])) < 1e-15
+    assert np.max(np.abs(oracle.gates_from_logits(z, A, 0.9) - np.log([0.95, 0.975]))) < 1e-15
+    # sigmoid(-z) = 1 - sigmoid(z), on both branches of the overflow-free formula
+    zz = np.linspace(-60.0, 60.0, 241)
+    s = oracle.sigmoid(zz)
+    assert np.max(np.abs(s + s[::-1] - 1.0)) < 1e-15
+    assert np.all(np.diff(s) >= 0) and np.all(np.diff(s[:180]) > 0)  # (rounds to 1.0 in fp64 beyond z ~ 35)
+    # the endpoints.  Scaled sigmoid: z -> -inf keeps the state (g = 0), z -> +inf
+    # decays the most (g = g_min).  alpha bounded below: z -> -inf gives alpha =
+    # a_min, z -> +inf gives alpha = 1.
+    big = np.array([-1.0e4, 1.0e4])
+    assert np.array_equal(oracle.gates_from_logits(big, S, -5.0), [0.0, -5.0])
+    assert np.max(np.abs(oracle.gates_from_logits(big, A, 0.9) - [math.log(0.9), 0.0])) < 1e-15
+    with pytest.raises(ValueError):
+        oracle.gates_from_logits(z, 0, -5.0)
+
+
+def test_logit_gates_stay_in_the_pages_domain():
+    # whatever the logit, g_min = -5 keeps g in [-5, 0]: the per-step retention
+    # never drops below the pages' e^-5 (tests/golden/page_constants.json)
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        c = json.load(f)
+    g_min = c["g_min"]["value"]
+    z = np.concatenate([np.linspace(-100.0, 100.0, 2001), [-3.0e38, 3.0e38]])
+    g = oracle.gates_from_logits(z, oracle.GATE_SCALED_SIGMOID, g_min)
+    assert g.min() >= g_min and g.max() <= 0.0
+    assert round(math.exp(g.min()), 4) == c["per_step_decay_low"]["value"]
+    ga = oracle.gates_from_logits(z, oracle.GATE_ALPHA_MIN, math.exp(g_min))
+    assert ga.min() >= g_min - 1e-12 and ga.max() <= 0.0
+
+
+def test_generator_logits_match_its_gates():
+    # the bf16 logits the generator stores are the logits it drew (rounded):
+    # the oracle's parameterisation of them reproduces the generator's g to
+    # bf16 precision, for both recipes
+    for gate, kind, p in (("pages", oracle.GATE_SCALED_SIGMOID, -5.0), ("amin", oracle.GATE_ALPHA_MIN, 0.9)):
+        x = inputs.make_prefill_inputs([300], 2, 64, 8, dtype=torch.bfloat16, gate=gate, a_min=0.9, seed=15,
+                                       logits=True)
+        assert x.z.dtype == torch.bfloat16 and x.z.shape == x.g.shape
+        g = oracle.gates_from_logits(_np(x.z), kind, p)
+        assert np.max(np.abs(g - _np(x.g))) < 0.02 * abs(p if kind == oracle.GATE_SCALED_SIGMOID else math.log(p))
