@@ -1100,7 +1100,7 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
         // latency hides behind the barrier) and the group sums of g (log2 units)
         // to LDS
         floatx2 gv[P::TPL];
-        bf16x2 kv[P::TPL], qv[P::TPL];
+        bf16x2 kv[P::TPL], qv[P::TPL], zv[P::TPL];
         if (act) {
             __builtin_amdgcn_s_waitcnt(0);
             if (L < CW) {
@@ -1121,16 +1121,9 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                 for (int tt = 0; tt < P::TPL; ++tt)
                     gv[tt] = *reinterpret_cast<const floatx2*>(stg_g + (t0 + tt) * DK + ch);
             } else {
-                // the gate parameterisation, in registers; rows past the end
-                // get g = 0 (their logits are copies of the last row's)
                 const TI* stg_z = reinterpret_cast<const TI*>(stg);
 #pragma unroll
-                for (int tt = 0; tt < P::TPL; ++tt) {
-                    const bf16x2 zz = *reinterpret_cast<const bf16x2*>(stg_z + (t0 + tt) * DK + ch);
-                    const bool in = t0 + tt < L;
-                    gv[tt] = floatx2{in ? gate_log_decay((float)zz[0], a.gate, a.gate_param) : 0.f,
-                                     in ? gate_log_decay((float)zz[1], a.gate, a.gate_param) : 0.f};
-                }
+                for (int tt = 0; tt < P::TPL; ++tt) zv[tt] = *reinterpret_cast<const bf16x2*>(stg_z + (t0 + tt) * DK + ch);
             }
 #pragma unroll
             for (int tt = 0; tt < P::TPL; ++tt) {
@@ -1141,16 +1134,39 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
         if constexpr (MAP)
             if (i >= 1 && kw < 2) inverse_to(reinterpret_cast<frag*>(smem + ((i - 1) & 1) * P::SZ_BUF + P::B_TB));
         if (act) {
-            floatx2 sum = floatx2{0.f, 0.f};
+            auto group_sum = [&]() {
+                floatx2 sum = floatx2{0.f, 0.f};
 #pragma unroll
-            for (int tt = 0; tt < P::TPL; ++tt) sum = fma2(gv[tt], LOG2E, sum);
-            *reinterpret_cast<floatx2*>(s_gt + grp * DK + ch) = sum;
+                for (int tt = 0; tt < P::TPL; ++tt) sum = fma2(gv[tt], LOG2E, sum);
+                *reinterpret_cast<floatx2*>(s_gt + grp * DK + ch) = sum;
+            };
+            if constexpr (!ZG) group_sum();
             if (kw == 0 && lane < CW) BETA[lane] = stg_b[lane];
             // this wave's staging rows are in registers: copy the next chunk
             // (it lands during the rest of this iteration and is waited for
             // at the start of the next)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (i + 1 < nch) dma(i + 1, lane);
+            if constexpr (ZG) {
+                // the gate parameterisation, after the copy is under way; rows
+                // past the end then get g = 0 (their logits are copies of the
+                // last row's).  One branch-free loop per parameterisation, so
+                // that the 2 TPL independent exp -> rcp (-> log) chains
+                // interleave.
+                const float p = a.gate_param;
+                auto from_logits = [&](auto fn) {
+#pragma unroll
+                    for (int tt = 0; tt < P::TPL; ++tt) gv[tt] = floatx2{fn((float)zv[tt][0]), fn((float)zv[tt][1])};
+                };
+                if (a.gate == GATE_SCALED_SIGMOID) from_logits([&](float x) { return p * sigmoid_hw(x); });
+                else from_logits([&](float x) { return gate_log_decay(x, GATE_ALPHA_MIN, p); });
+                if (L < CW) {
+#pragma unroll
+                    for (int tt = 0; tt < P::TPL; ++tt)
+                        if (t0 + tt >= L) gv[tt] = floatx2{0.f, 0.f};
+                }
+                group_sum();
+            }
         }
         lds_barrier();  // B1
 
