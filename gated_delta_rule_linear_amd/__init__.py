@@ -62,6 +62,10 @@ def _load():
     lib.gdn_prefill_logits.restype = i32
     lib.gdn_decode_logits.argtypes = [P, P, P, P, i32, f32, P, P, P, i32, i32, i32, i32, i32, P]
     lib.gdn_decode_logits.restype = i32
+    lib.gdn_prefill_head_gate.argtypes = [P, P, P, P, P, P, i32, i64, P, P, P, i32, i32, i32, i32, P, sz, P]
+    lib.gdn_prefill_head_gate.restype = i32
+    lib.gdn_decode_head_gate.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.gdn_decode_head_gate.restype = i32
     _LIB = lib
     return lib
 
@@ -176,6 +180,65 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=No
     return o, final_state
 
 
+def gdn_prefill_head_gate(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=None, o=None, workspace=None,
+                          output_final_state: bool = True, stream=None):
+    """gdn_prefill with one fp32 log-decay per (token, head): g [T, H]."""
+    _need(q, "q", dims=3)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(k, "k", dt, 3)
+    _need(v, "v", dt, 3)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if k.shape != (T, H, dk) or g.shape != (T, H) or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes")
+    n = cu_seqlens.shape[0] - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, 4)
+        if initial_state.shape != (n, H, dk, dv):
+            raise ValueError("initial_state must be [num_seqs, H, dk, dv]")
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=dt, device=q.device)
+    _need(o, "o", dt, 3)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, 4)
+    need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().gdn_prefill_head_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                       _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
+                                       _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "gdn_prefill_head_gate")
+    return o, final_state
+
+
+def gdn_decode_head_gate(q, k, v, g, beta, state, o=None, stream=None):
+    """gdn_decode with one fp32 log-decay per (sequence, head): g [N, H]."""
+    _need(q, "q", dims=3)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(k, "k", dt, 3)
+    _need(v, "v", dt, 3)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(state, "state", torch.float32, 4)
+    if state.shape != (N, H, dk, dv) or k.shape != (N, H, dk) or g.shape != (N, H) or beta.shape != (N, H):
+        raise ValueError("inconsistent shapes")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    _need(o, "o", dt, 3)
+    st = _load().gdn_decode_head_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H,
+                                      dk, dv, _dtype_code(q), _stream(stream))
+    _check(st, "gdn_decode_head_gate")
+    return o
+
+
 def gdn_prefill_logits(q, k, v, z, gate, gate_param, beta, cu_seqlens, initial_state=None, final_state=None, o=None,
                        workspace=None, output_final_state: bool = True, stream=None):
     """gdn_prefill with bf16 gate logits z [T, H, dk] and a gdn_gate parameterisation
@@ -260,6 +323,7 @@ def gdn_decode(q, k, v, g, beta, state, o=None, stream=None):
 
 __all__ = [
     "gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free", "gdn_prefill_workspace_bytes",
-    "gdn_prefill", "gdn_decode", "gdn_prefill_logits", "gdn_decode_logits", "GdnError", "load_library", "LIB_PATH",
+    "gdn_prefill", "gdn_decode", "gdn_prefill_logits", "gdn_decode_logits", "gdn_prefill_head_gate",
+    "gdn_decode_head_gate", "GdnError", "load_library", "LIB_PATH",
     "GDN_GATE_LOG", "GDN_GATE_SCALED_SIGMOID", "GDN_GATE_ALPHA_MIN",
 ]

@@ -156,10 +156,12 @@ static int32_t prefill_impl(const void* q, const void* k, const void* v, const f
     if (num_seqs == 0) return GDN_OK;
     if (!cu_seqlens || !aligned(cu_seqlens, 4)) return GDN_ERR_INVALID_ARG;
     if (T_total > 0) {
-        const void* ptrs16[] = {q, k, v, gate == GDN_GATE_LOG ? static_cast<const void*>(g) : z, o};
+        const bool head = gate == gdn::GATE_HEAD;
+        const void* ptrs16[] = {q, k, v, gate == GDN_GATE_LOG ? static_cast<const void*>(g) : head ? q : z, o};
         for (const void* p : ptrs16)
             if (!p || !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
         if (!beta || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
+        if (head && (!g || !aligned(g, 4))) return GDN_ERR_INVALID_ARG;
     }
     if (initial_state && !aligned(initial_state, 16)) return GDN_ERR_INVALID_ARG;
     if (final_state && !aligned(final_state, 16)) return GDN_ERR_INVALID_ARG;
@@ -170,8 +172,9 @@ static int32_t prefill_impl(const void* q, const void* k, const void* v, const f
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (validate_mode()) {
         // (logits: every finite or infinite z maps into the domain, so only cu_seqlens is checked)
-        const int32_t st = validate_inputs(cu_seqlens, num_seqs, T_total, gate == GDN_GATE_LOG ? g : nullptr,
-                                           T_total * H * d_k, s);
+        const bool has_g = gate == GDN_GATE_LOG || gate == gdn::GATE_HEAD;
+        const int32_t st = validate_inputs(cu_seqlens, num_seqs, T_total, has_g ? g : nullptr,
+                                           T_total * H * (gate == gdn::GATE_HEAD ? 1 : d_k), s);
         if (st != GDN_OK) return st;
     }
     gdn::PrefillLaunch p;
@@ -210,6 +213,15 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
                         final_state, o, H, d_k, d_v, dtype, workspace, workspace_bytes, stream);
 }
 
+int32_t gdn_prefill_head_gate(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
+                              const float* initial_state, float* final_state, void* o, int32_t H, int32_t d_k,
+                              int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    return prefill_impl(q, k, v, g, nullptr, gdn::GATE_HEAD, 0.f, beta, cu_seqlens, num_seqs, T_total,
+                        initial_state, final_state, o, H, d_k, d_v, dtype, workspace, workspace_bytes, stream);
+}
+
 int32_t gdn_prefill_logits(const void* q, const void* k, const void* v, const void* z, int32_t gate,
                            float gate_param, const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
                            int64_t T_total, const float* initial_state, float* final_state, void* o, int32_t H,
@@ -229,14 +241,16 @@ static int32_t decode_impl(const void* q, const void* k, const void* v, const fl
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
     if (N == 0) return GDN_OK;
-    const void* ptrs16[] = {q, k, v, gate == GDN_GATE_LOG ? static_cast<const void*>(g) : z, o, state};
+    const bool head = gate == gdn::GATE_HEAD;
+    const void* ptrs16[] = {q, k, v, gate == GDN_GATE_LOG ? static_cast<const void*>(g) : head ? q : z, o, state};
     for (const void* p : ptrs16)
         if (!p || !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
     if (!beta || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
+    if (head && (!g || !aligned(g, 4))) return GDN_ERR_INVALID_ARG;
     if ((int64_t)N * H > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (validate_mode() && gate == GDN_GATE_LOG) {
-        std::vector<float> gh((size_t)N * H * d_k);
+    if (validate_mode() && (gate == GDN_GATE_LOG || head)) {
+        std::vector<float> gh((size_t)N * H * (head ? 1 : d_k));
         if (hipMemcpyAsync(gh.data(), g, sizeof(float) * gh.size(), hipMemcpyDeviceToHost, s) != hipSuccess ||
             hipStreamSynchronize(s) != hipSuccess)
             return GDN_ERR_HIP;
@@ -265,6 +279,12 @@ static int32_t decode_impl(const void* q, const void* k, const void* v, const fl
 int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
                    void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void* stream) {
     return decode_impl(q, k, v, g, nullptr, GDN_GATE_LOG, 0.f, beta, state, o, N, H, d_k, d_v, dtype, stream);
+}
+
+int32_t gdn_decode_head_gate(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             float* state, void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                             void* stream) {
+    return decode_impl(q, k, v, g, nullptr, gdn::GATE_HEAD, 0.f, beta, state, o, N, H, d_k, d_v, dtype, stream);
 }
 
 int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const void* z, int32_t gate, float gate_param,

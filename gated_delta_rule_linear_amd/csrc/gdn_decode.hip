@@ -63,9 +63,10 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(const TI* __restrict__ q, 
     const int tid = threadIdx.x;
     const int64_t unit = blockIdx.x;  // sequence * H + head
     if (tid < DK) {
-        // decay factor: e^g, or from the gate logit (gate != GATE_LOG)
-        s_a[tid] = gate == GATE_LOG ? __expf(g[unit * DK + tid])
-                                    : gate_alpha((float)z[unit * DK + tid], gate, gate_param);
+        // decay factor: e^g (per channel or per head), or from the gate logit
+        s_a[tid] = gate == GATE_LOG    ? __expf(g[unit * DK + tid])
+                   : gate == GATE_HEAD ? __expf(g[unit])  // one gate per (sequence, head)
+                                       : gate_alpha((float)z[unit * DK + tid], gate, gate_param);
         s_k[tid] = to_f32(k[unit * DK + tid]);
         s_q[tid] = to_f32(q[unit * DK + tid]);
     }

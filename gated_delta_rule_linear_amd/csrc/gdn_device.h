@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn_kernels.h"  // GATE_* values
+
 namespace gdn {
 
 typedef __bf16 bf16;
@@ -28,10 +30,6 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // 
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
-// Gate parameterisations of the logit entry points (values of gdn_gate).
-constexpr int GATE_LOG = 0;             // g given directly
-constexpr int GATE_SCALED_SIGMOID = 1;  // g = p sigmoid(z), p = g_min
-constexpr int GATE_ALPHA_MIN = 2;       // g = log(p + (1 - p) sigmoid(z)), p = a_min
 
 // sigmoid(z) = 1 / (1 + e^-z) with the hardware base-2 exponential and
 // reciprocal; z -> -inf gives 0 (1/inf), z -> +inf gives 1.

@@ -6,6 +6,13 @@
 
 namespace gdn {
 
+// Gate of a call: GATE_LOG, GATE_SCALED_SIGMOID and GATE_ALPHA_MIN are the
+// values of gdn_gate; GATE_HEAD is the one-gate-per-(token, head) entry points.
+constexpr int GATE_LOG = 0;             // g given per key channel
+constexpr int GATE_SCALED_SIGMOID = 1;  // g = p sigmoid(z), p = g_min
+constexpr int GATE_ALPHA_MIN = 2;       // g = log(p + (1 - p) sigmoid(z)), p = a_min
+constexpr int GATE_HEAD = 3;            // one g per (token, head), shared by the key channels
+
 struct PrefillLaunch {
     const void* q;
     const void* k;

@@ -1005,7 +1005,11 @@ struct CfgW {
     static constexpr int B_QO = 0, B_KO = SZ_OP, B_KD = 2 * SZ_OP, B_PO = 3 * SZ_OP;
     static constexpr int B_TB = B_PO + SZ_PO;  // Linv_0, Linv_1, An_10 as A-operand fragments, 1 KiB each
     static constexpr int B_BETA = B_TB + 3 * 1024, B_GM = B_BETA + CW * 4;
-    static constexpr int SZ_BUF = (B_GM + DK * 4 + 255) / 256 * 256;
+    // per-head gates: e^{G_t} [CW], e^{G_L - G_t} [CW], e^{G_L} in place of
+    // the per-channel gamma (a kernel uses one or the other)
+    static constexpr int B_EG = B_GM;
+    static constexpr int SZ_GM = DK * 4 > (2 * CW + 1) * 4 ? DK * 4 : (2 * CW + 1) * 4;
+    static constexpr int SZ_BUF = (B_GM + SZ_GM + 255) / 256 * 256;
     // key-side scratch
     static constexpr int OFF_KH = 2 * SZ_BUF, OFF_QM = OFF_KH + SZ_OP, OFF_KM = OFF_QM + SZ_OP;
     static constexpr int OFF_AN = OFF_KM + SZ_OP, OFF_GT = OFF_AN + 2 * 1024;
@@ -1318,8 +1322,224 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
     }
 }
 
-// State side: waves NK .. NK+NS-1.  Runs chunk i-1 in iteration i.
+// Key side with one gate per (token, head): the decay of a pair (t, s) is the
+// scalar e^{G_t - G_s}, so it multiplies the products instead of the operands.
+// The chunk's q and k go to the operand layouts unscaled (no exponential per
+// element); the Gram blocks are scaled by the 32 x 32 decay matrix; the state
+// side scales rows by e^{G_t} and e^{G_L - G_t} (exponentials of non-positive
+// numbers only, so there is no exponent budget to keep).
 template <int DK, int DV, bool MAP, int NCB>
+__device__ __forceinline__ void ws_key_head(const Args<bf16>& a, char* smem, int kw, int h, int64_t tb, int64_t te,
+                                            int nch) {
+    typedef CfgW<DK, DV, NCB> P;
+    typedef bf16 TI;
+    typedef Mma<bf16> M;
+    typedef bf16x8 frag;
+    constexpr bool OUT = !MAP;
+    constexpr int CW = P::CW, KM = P::KM;
+    const int H = a.H;
+    char* stg = smem + P::OFF_STG;
+    float* stg_gs = reinterpret_cast<float*>(stg);  // the chunk's gates (the per-channel g area is not used)
+    const TI* stg_q = reinterpret_cast<const TI*>(stg + P::SG_G);
+    const TI* stg_k = reinterpret_cast<const TI*>(stg + P::SG_G + P::SG_Q);
+    float* stg_b = reinterpret_cast<float*>(stg + P::SG_G + 2 * P::SG_Q);
+    floatx4* AN = reinterpret_cast<floatx4*>(smem + P::OFF_AN);
+    float* s_gs = reinterpret_cast<float*>(smem + P::OFF_GT);  // gates of chunk i [CW]
+    float* s_G = s_gs + CW;                                     // G_t of chunk i [CW]
+
+    auto inverse_to = [&](frag* tb) {
+        const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+        float arow[16];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            const floatx4 y = AN[kw * 64 + r + 16 * gg];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) arow[4 * gg + e] = y[e];
+        }
+        const floatx4 li = row_inverse(arow, r, g);
+        tb[kw * 64 + lane] =
+            frag{(bf16)li[0], (bf16)li[1], (bf16)li[2], (bf16)li[3], (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    };
+
+    // copy of chunk j's q, k rows TPW*kw .. TPW*kw+TPW-1; wave 0 beta, wave 1 the gates
+    auto dma = [&](int j, int lane) {
+        const int64_t c0 = tb + (int64_t)j * CW;
+        const int L = (int)(te - c0 < CW ? te - c0 : CW);
+        const size_t tok0 = (size_t)c0 * H + h;
+        auto rows = [&](const void* src, int RB, char* dst) {
+            const int lpr = RB / 16, rpi = 64 / lpr;
+            const char* base = static_cast<const char*>(src) + tok0 * RB;
+#pragma unroll
+            for (int i = 0; i < P::TPW / rpi; ++i) {
+                const int r0 = P::TPW * kw + rpi * i;
+                const int t = min(r0 + lane / lpr, L - 1);
+                __builtin_amdgcn_global_load_lds(gptr(base + (uint32_t)(t * H * RB + (lane % lpr) * 16)),
+                                                 lptr(dst + r0 * RB), 16, 0, 0);
+            }
+        };
+        if (OUT) rows(a.q, DK * 2, stg + P::SG_G);
+        rows(a.k, DK * 2, stg + P::SG_G + P::SG_Q);
+        if (kw < 2)
+            __builtin_amdgcn_global_load_lds(gptr((kw == 0 ? a.beta : a.g) + tok0 + (size_t)min(lane, L - 1) * H),
+                                             lptr(kw == 0 ? stg_b : stg_gs), 4, 0, 0);
+    };
+    if (nch > 0) dma(0, threadIdx.x & 63);
+
+    for (int i = 0; i <= nch; ++i) {
+        int tid = kw * 64 + (threadIdx.x & 63);
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+        const int cp = tid % P::CPR, grp = tid / P::CPR, ch = 2 * cp, t0 = grp * P::TPL;
+        const bool act = i < nch;
+        char* buf = smem + (i & 1) * P::SZ_BUF;
+        TI* QO = reinterpret_cast<TI*>(buf + P::B_QO);
+        TI* KO = reinterpret_cast<TI*>(buf + P::B_KO);
+        TI* KD = reinterpret_cast<TI*>(buf + P::B_KD);
+        TI* PO = reinterpret_cast<TI*>(buf + P::B_PO);
+        frag* TB = reinterpret_cast<frag*>(buf + P::B_TB);
+        float* BETA = reinterpret_cast<float*>(buf + P::B_BETA);
+        float* EG = reinterpret_cast<float*>(buf + P::B_EG);
+        const int64_t c0 = tb + (int64_t)i * CW;
+        const int L = (int)(te - c0 < CW ? te - c0 : CW);
+
+        // ---- K1: this wave's rows to registers; beta and the gates (zero past
+        // the end) out of the staging area; the next chunk's copy
+        bf16x2 kv[P::TPL], qv[P::TPL];
+        if (act) {
+            __builtin_amdgcn_s_waitcnt(0);
+            if (L < CW) {
+                for (int t = P::TPW * kw; t < P::TPW * (kw + 1); ++t)
+                    if (t >= L && lane < DK / 8) {
+                        reinterpret_cast<floatx4*>(const_cast<TI*>(stg_q) + t * DK)[lane] = zero4();
+                        reinterpret_cast<floatx4*>(const_cast<TI*>(stg_k) + t * DK)[lane] = zero4();
+                    }
+            }
+#pragma unroll
+            for (int tt = 0; tt < P::TPL; ++tt) {
+                kv[tt] = *reinterpret_cast<const bf16x2*>(stg_k + (t0 + tt) * DK + ch);
+                if constexpr (OUT) qv[tt] = *reinterpret_cast<const bf16x2*>(stg_q + (t0 + tt) * DK + ch);
+            }
+            if (kw == 0 && lane < CW) BETA[lane] = lane < L ? stg_b[lane] : 0.f;
+            if (kw == 1 && lane < CW) s_gs[lane] = lane < L ? stg_gs[lane] : 0.f;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (i + 1 < nch) dma(i + 1, lane);
+        }
+        if constexpr (MAP)
+            if (i >= 1 && kw < 2) inverse_to(reinterpret_cast<frag*>(smem + ((i - 1) & 1) * P::SZ_BUF + P::B_TB));
+        lds_barrier();  // B1
+
+        // ---- K2: q, k unscaled into the operand layouts; wave 3: G_t and the
+        // decay vectors of the state side
+        if (act) {
+            const uint32_t a0 = op_idx<TI, KM>(t0, ch) * 2u;
+            auto put = [&](TI* mat, int tt, bf16x2 x) {
+                *reinterpret_cast<bf16x2*>(reinterpret_cast<char*>(mat) + (a0 ^ (uint32_t)(tt << 4))) = x;
+            };
+#pragma unroll
+            for (int tt = 0; tt < P::TPL; ++tt) {
+                if constexpr (OUT) put(QO, tt, qv[tt]);
+                put(KO, tt, kv[tt]);
+            }
+#pragma unroll
+            for (int tq = 0; tq < P::TPL; tq += 4) {
+                *reinterpret_cast<bf16x4*>(KD + op_idx<TI, 1>(ch, t0 + tq)) =
+                    bf16x4{kv[tq][0], kv[tq + 1][0], kv[tq + 2][0], kv[tq + 3][0]};
+                *reinterpret_cast<bf16x4*>(KD + op_idx<TI, 1>(ch + 1, t0 + tq)) =
+                    bf16x4{kv[tq][1], kv[tq + 1][1], kv[tq + 2][1], kv[tq + 3][1]};
+            }
+            if (kw == 3) {
+                // inclusive prefix of the gates over lanes 0 .. CW-1 (rows past
+                // the end hold 0): log-step scan through lane shuffles
+                float G = lane < CW ? s_gs[lane] : 0.f;
+#pragma unroll
+                for (int off = 1; off < CW; off <<= 1) {
+                    const float y = __shfl_up(G, off, 64);
+                    if (lane >= off) G += y;
+                }
+                const float GL = __shfl(G, CW - 1, 64);
+                if (lane < CW) {
+                    s_G[lane] = G;
+                    EG[lane] = __expf(G);
+                    EG[CW + lane] = __expf(GL - G);
+                }
+                if (lane == 0) EG[2 * CW] = __expf(GL);
+            }
+        }
+        lds_barrier();  // B2
+
+        // ---- K3: Gram blocks of the unscaled q, k, times the decay e^{G_t - G_s}
+        if (act) {
+            // lane r + 16g of block (I, J): row t = 16I + r, columns s = 16J + 4g + e
+            auto decay = [&](int I, int J) {
+                const float Gt = s_G[16 * I + r];
+                const floatx4 Gs = *reinterpret_cast<const floatx4*>(s_G + 16 * J + 4 * g);
+                floatx4 d;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[e] = __expf(Gt - Gs[e]);
+                return d;
+            };
+            auto p_tile = [&](int I, int J, const frag (&fa)[KM]) {
+                frag fq[KM];
+#pragma unroll
+                for (int m = 0; m < KM; ++m) fq[m] = op_frag<TI, KM>(QO, I, m, lane);
+                floatx4 accP = zero4();
+#pragma unroll
+                for (int m = 0; m < KM; ++m) accP = M::mma(fa[m], fq[m], accP);
+                const int t = 16 * I + r;
+                const floatx4 d = decay(I, J);
+                floatx4 p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[e] = (16 * J + 4 * g + e <= t) ? d[e] * accP[e] : 0.f;
+                bf16* dst = reinterpret_cast<bf16*>(PO) + (I * 64 + op_slot(I, 0, r, g)) * 8 + 4 * J;
+                *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3]};
+                if (I == 0) *reinterpret_cast<bf16x4*>(dst + 4) = bf16x4{};  // block above the diagonal
+            };
+            auto a_tile = [&](int I, int J, const frag (&fa)[KM]) {
+                frag fk[KM];
+#pragma unroll
+                for (int m = 0; m < KM; ++m) fk[m] = op_frag<TI, KM>(KO, I, m, lane);
+                floatx4 accA = zero4();
+#pragma unroll
+                for (int m = 0; m < KM; ++m) accA = M::mma(fa[m], fk[m], accA);
+                const int t = 16 * I + r;
+                const float bt = BETA[t];
+                const floatx4 d = decay(I, J);
+                floatx4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (16 * J + 4 * g + e < t) ? -bt * d[e] * accA[e] : 0.f;
+                return x;
+            };
+            auto kf = [&](int J, frag (&fa)[KM]) {
+#pragma unroll
+                for (int m = 0; m < KM; ++m) fa[m] = op_frag<TI, KM>(KO, J, m, lane);
+            };
+            frag fa[KM];
+            if (kw < 2) {
+                kf(kw, fa);
+                AN[kw * 64 + lane] = a_tile(kw, kw, fa);
+                if constexpr (OUT) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS operations of a wave complete in order
+                    inverse_to(TB);
+                }
+            } else if (kw == 2) {
+                kf(0, fa);
+                const floatx4 x = a_tile(1, 0, fa);
+                TB[2 * 64 + lane] = frag{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3], (bf16)0.f, (bf16)0.f,
+                                         (bf16)0.f, (bf16)0.f};
+                if constexpr (OUT) p_tile(1, 0, fa);
+            } else if constexpr (OUT) {
+                kf(0, fa);
+                p_tile(0, 0, fa);
+                kf(1, fa);
+                p_tile(1, 1, fa);
+            }
+        }
+        lds_barrier();  // B3
+    }
+}
+
+// State side: waves NK .. NK+NS-1.  Runs chunk i-1 in iteration i.
+template <int DK, int DV, bool MAP, int NCB, bool HG>
 __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw, const Unit& u, int nch) {
     typedef CfgW<DK, DV, NCB> P;
     typedef bf16 TI;
@@ -1374,6 +1594,7 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
         const frag* TB = reinterpret_cast<const frag*>(buf + P::B_TB);
         const float* BETA = reinterpret_cast<const float*>(buf + P::B_BETA);
         const float* GM = reinterpret_cast<const float*>(buf + P::B_GM);
+        const float* EG = reinterpret_cast<const float*>(buf + P::B_EG);  // per-head gates
         const int64_t c0 = tb + (int64_t)j * CW;
         const int L = (int)(te - c0 < CW ? te - c0 : CW);
 
@@ -1398,6 +1619,7 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                     floatx4 ks = zero4();
 #pragma unroll
                     for (int m = 0; m < KM; ++m) ks = M::mma(op_frag<TI, KM>(KO, I, m, lane), bS[cb][m], ks);
+                    if constexpr (HG) ks *= *reinterpret_cast<const floatx4*>(EG + 16 * I + 4 * g);  // rows t: e^{G_t}
                     const floatx4 bt = *reinterpret_cast<const floatx4*>(BETA + 16 * I + 4 * g);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) R[cb][I][e] = bt[e] * ((vblock ? (float)vr[I][e] : 0.f) - ks[e]);
@@ -1407,7 +1629,7 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
         lds_barrier();  // B1
 
         // ---- S2: U by block forward substitution; outputs
-        frag bU[NCB];
+        frag bU[NCB], bUs[NCB];  // bUs: rows t scaled by e^{G_L - G_t} (per-head gates)
         if (act) {
             const frag l0 = TB[lane], l1 = TB[64 + lane], an = TB[128 + lane];
 #pragma unroll
@@ -1417,9 +1639,15 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                 const floatx4 r1 = M::mma(an, acc_perm<TI>(U, 0, 1), R[cb][1]);
                 U[1] = M::mma(l1, acc_perm<TI>(&r1, 0, 1), zero4());
                 bU[cb] = acc_perm<TI>(U, 0, 2);
+                if constexpr (HG) {
+#pragma unroll
+                    for (int I = 0; I < 2; ++I) U[I] *= *reinterpret_cast<const floatx4*>(EG + CW + 16 * I + 4 * g);
+                    bUs[cb] = acc_perm<TI>(U, 0, 2);
+                }
             }
             if constexpr (OUT) {
-                // buffer stores: rows t >= L lie past the extent of the
+                // O = Q~ S + P U from the state at the chunk start (bS) and U,
+                // with buffer stores: rows t >= L lie past the extent of the
                 // resource and the hardware drops them, so every lane stores
                 // (no branch, and the count of stores in flight is fixed)
                 const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
@@ -1429,6 +1657,7 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                     floatx4 O = zero4();
 #pragma unroll
                     for (int m = 0; m < KM; ++m) O = M::mma(bS[0][m], op_frag<TI, KM>(QO, rb, m, lane), O);
+                    if constexpr (HG) O *= EG[16 * rb + r];  // this lane's token: e^{G_t}
                     O = M::mma(bU[0], op_frag<TI, 1>(PO, rb, 0, lane), O);
                     const int t = 16 * rb + r;
                     __builtin_amdgcn_raw_buffer_store_b64(
@@ -1445,9 +1674,14 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
             for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    const floatx4 d = *reinterpret_cast<const floatx4*>(GM + 16 * rt + 4 * g);
-                    S[cb][rt] *= d;
-                    S[cb][rt] = M::mma(op_frag<TI, 1>(KD, rt, 0, lane), bU[cb], S[cb][rt]);
+                    if constexpr (HG) {
+                        S[cb][rt] *= EG[2 * CW];  // e^{G_L}
+                        S[cb][rt] = M::mma(op_frag<TI, 1>(KD, rt, 0, lane), bUs[cb], S[cb][rt]);
+                    } else {
+                        const floatx4 d = *reinterpret_cast<const floatx4*>(GM + 16 * rt + 4 * g);
+                        S[cb][rt] *= d;
+                        S[cb][rt] = M::mma(op_frag<TI, 1>(KD, rt, 0, lane), bU[cb], S[cb][rt]);
+                    }
                 }
             }
         }
@@ -1466,8 +1700,9 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
     }
 }
 
-// ZG: the log-decay comes from bf16 logits (Args::z, gate, gate_param)
-template <int DK, int DV, bool MAP, int NCB, bool ZG>
+// GMODE 0: per-channel g; 1: per-channel g from bf16 logits (Args::z, gate,
+// gate_param); 2: one g per (token, head) (Args::g is [T, H])
+template <int DK, int DV, bool MAP, int NCB, int GMODE>
 __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(Args<bf16> a) {
     typedef CfgW<DK, DV, NCB> P;
     static_assert(NCB == 1 || (MAP && DK == DV), "two column blocks only for transitions with d_k = d_v");
@@ -1476,8 +1711,12 @@ __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(
     if (!u.valid) return;
     const int nch = (int)((u.te - u.tb + P::CW - 1) / P::CW);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w < P::NK) ws_key<DK, DV, MAP, NCB, ZG>(a, smem, w, u.h, u.tb, u.te, nch);
-    else ws_state<DK, DV, MAP, NCB>(a, smem, w - P::NK, u, nch);
+    if (w < P::NK) {
+        if constexpr (GMODE == 2) ws_key_head<DK, DV, MAP, NCB>(a, smem, w, u.h, u.tb, u.te, nch);
+        else ws_key<DK, DV, MAP, NCB, GMODE == 1>(a, smem, w, u.h, u.tb, u.te, nch);
+    } else {
+        ws_state<DK, DV, MAP, NCB, GMODE == 2>(a, smem, w - P::NK, u, nch);
+    }
 }
 
 // nl[0] = 0, nl[n + 1] = nl[n] + (number of non-last segments of sequence n):
@@ -1576,10 +1815,12 @@ hipError_t launch_ws(const Args<bf16>& a, int64_t blocks, hipStream_t s) {
     typedef CfgW<DK, DV, NCB> P;
     static_assert(P::LDS <= 160 * 1024, "LDS budget");
     if (blocks <= 0) return hipSuccess;
-    if (a.gate != GATE_LOG)
-        hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB, true>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
+    if (a.gate == GATE_HEAD)
+        hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB, 2>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
+    else if (a.gate != GATE_LOG)
+        hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB, 1>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB, false>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
+        hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, MAP, NCB, 0>), dim3((unsigned)blocks), dim3(P::NT), 0, s, a);
     return hipGetLastError();
 }
 

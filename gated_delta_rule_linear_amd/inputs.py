@@ -22,6 +22,7 @@ Distributions
                     "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate the
                     New Generation", section 3.1).
   S0     0.02 * N(0, 1), fp32, layout [num_seqs, H, d_k, d_v].
+  g      (head_gate=True) one log-decay per (token, head), [T_total, H], same recipes.
   z      (logits=True) the decay logits N(0,1) themselves, cast to bf16 (RNE),
          for the entry points that compute the gate in the kernel; g is still
          the recipe applied to the fp32 logits.
@@ -111,14 +112,14 @@ def _draw_gates(gen, shape_beta, shape_g, gate: str, a_min: float, device):
 def make_prefill_inputs(lengths: Sequence[int], H: int, dk: int, dv: int, dtype=torch.bfloat16,
                         gate: str = "amin", a_min: float = 0.9, init_state: bool = False,
                         seed: int = 0, device="cpu", gen: Optional[torch.Generator] = None,
-                        logits: bool = False) -> PrefillInputs:
+                        logits: bool = False, head_gate: bool = False) -> PrefillInputs:
     """Packed prefill inputs for the given sequence lengths (draw order above)."""
     if gen is None:
         gen = make_generator(seed, device)
     lengths = [int(x) for x in lengths]
     T = sum(lengths)
     q, k, v = _draw_qkv(gen, (T, H, dk), (T, H, dv), dtype, device)
-    beta, g, z = _draw_gates(gen, (T, H), (T, H, dk), gate, a_min, device)
+    beta, g, z = _draw_gates(gen, (T, H), (T, H) if head_gate else (T, H, dk), gate, a_min, device)
     zb = z.to(torch.bfloat16) if logits else None
     del z
     S0 = None
@@ -132,7 +133,7 @@ def make_prefill_inputs(lengths: Sequence[int], H: int, dk: int, dv: int, dtype=
 
 def make_decode_steps(N: int, H: int, dk: int, dv: int, steps: int, dtype=torch.bfloat16,
                       gate: str = "amin", a_min: float = 0.9, seed: int = 0, device="cpu",
-                      gen: Optional[torch.Generator] = None, logits: bool = False):
+                      gen: Optional[torch.Generator] = None, logits: bool = False, head_gate: bool = False):
     """Initial states (0.02*N(0,1)) followed by `steps` one-token draws for N sequences."""
     if gen is None:
         gen = make_generator(seed, device)
@@ -140,7 +141,7 @@ def make_decode_steps(N: int, H: int, dk: int, dv: int, steps: int, dtype=torch.
     out = []
     for _ in range(steps):
         q, k, v = _draw_qkv(gen, (N, H, dk), (N, H, dv), dtype, device)
-        beta, g, z = _draw_gates(gen, (N, H), (N, H, dk), gate, a_min, device)
+        beta, g, z = _draw_gates(gen, (N, H), (N, H) if head_gate else (N, H, dk), gate, a_min, device)
         out.append(DecodeStep(q, k, v, g, beta, z.to(torch.bfloat16) if logits else None))
     return S0, out
 
@@ -164,16 +165,17 @@ WORKLOADS = {
 
 def make_varlen64_inputs(seed: int = 0, device="cpu", n_seqs: int = 64, lo: int = 512, hi: int = 16384,
                          H: int = 32, dk: int = 128, dv: int = 128, dtype=torch.bfloat16,
-                         logits: bool = False) -> PrefillInputs:
+                         logits: bool = False, head_gate: bool = False) -> PrefillInputs:
     """64 packed sequences with lengths uniform on [512, 16384], random initial states."""
     gen = make_generator(seed, device)
     lengths = draw_lengths(gen, n_seqs, lo, hi)
     return make_prefill_inputs(lengths, H, dk, dv, dtype=dtype, gate="amin", a_min=0.9, init_state=True,
-                               device=device, gen=gen, logits=logits)
+                               device=device, gen=gen, logits=logits, head_gate=head_gate)
 
 
-def make_workload(name: str, seed: int = 0, device="cpu", logits: bool = False) -> PrefillInputs:
+def make_workload(name: str, seed: int = 0, device="cpu", logits: bool = False,
+                  head_gate: bool = False) -> PrefillInputs:
     if name == "varlen64":
-        return make_varlen64_inputs(seed=seed, device=device, logits=logits)
+        return make_varlen64_inputs(seed=seed, device=device, logits=logits, head_gate=head_gate)
     spec = dict(WORKLOADS[name])
-    return make_prefill_inputs(seed=seed, device=device, logits=logits, **spec)
+    return make_prefill_inputs(seed=seed, device=device, logits=logits, head_gate=head_gate, **spec)

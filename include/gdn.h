@@ -134,6 +134,21 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
                     int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* gdn_prefill with one log-decay per (token, head), shared by the key
+ * channels: the gate g_th of "How to Think About Trillion-Parameter Sparse
+ * Multimodal LLMs", section 3 item 3, written per token t and head h.
+ *   g   device, [T_total, H] fp32, log-decay in [-5, 0], 4-byte aligned
+ *   dtype GDN_BF16 only (GDN_F32: GDN_ERR_UNSUPPORTED)
+ * Everything else, the workspace size included, is as for gdn_prefill, and
+ * the result equals gdn_prefill with g broadcast over the d_k channels, up to
+ * rounding.  With one gate per head the decay of a token pair is a scalar, so
+ * the kernels scale the products instead of the operands (no exponential per
+ * element and no exponent budget). */
+int32_t gdn_prefill_head_gate(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
+                              const float* initial_state, float* final_state, void* o, int32_t H, int32_t d_k,
+                              int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* gdn_prefill with the gate given as bf16 logits (see gdn_gate):
  *   z           device, [T_total, H, d_k] bf16, 16-byte aligned (replaces g)
  *   gate        GDN_GATE_SCALED_SIGMOID or GDN_GATE_ALPHA_MIN, else
@@ -163,6 +178,12 @@ int32_t gdn_prefill_logits(const void* q, const void* k, const void* v, const vo
 int32_t gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    float* state, void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
                    void* stream);
+
+/* gdn_decode with one log-decay per (sequence, head): g [N, H] fp32 in
+ * [-5, 0], 4-byte aligned; dtype GDN_F32 or GDN_BF16. */
+int32_t gdn_decode_head_gate(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             float* state, void* o, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                             void* stream);
 
 /* gdn_decode with the gate given as bf16 logits z [N, H, d_k] (16-byte
  * aligned), gate and gate_param as for gdn_prefill_logits; dtype GDN_BF16

@@ -37,9 +37,15 @@ def oracle_prefill(x, units=None, gate=None):
     """fp64 oracle for the inputs in x (tensors anywhere).  With `units` a list of
     (sequence, head) pairs, only those are computed: returns dict {(n, h): (o, S)}.
     With gate = (kind, p) the log-decay is the oracle's parameterisation of the
-    bf16 logits x.z instead of x.g."""
+    bf16 logits x.z instead of x.g; a 2-D x.g is one gate per (token, head)."""
     cu = x.cu_seqlens.cpu().numpy().astype(np.int32)
-    gof = (lambda a: oracle.gates_from_logits(a(x.z), *gate)) if gate else (lambda a: a(x.g))
+    dk = x.q.shape[2]
+    if gate:
+        gof = lambda a: oracle.gates_from_logits(a(x.z), *gate)
+    elif x.g.dim() == 2:  # one gate per (token, head): the same decay on every key channel
+        gof = lambda a: np.repeat(a(x.g)[:, :, None], dk, axis=2)
+    else:
+        gof = lambda a: a(x.g)
     if units is None:
         o, S = oracle.recurrent(np64(x.q), np64(x.k), np64(x.v), gof(np64), np64(x.beta), cu,
                                 initial_state=None if x.initial_state is None else np64(x.initial_state))

@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(lib):
     names = gdn.exported_symbols_in_header()
     assert set(names) == {"gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free",
                           "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_prefill_logits",
-                          "gdn_decode_logits"}
+                          "gdn_decode_logits", "gdn_prefill_head_gate", "gdn_decode_head_gate"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -144,3 +144,18 @@ def test_logit_gate_argument_errors(lib):
         assert f(lib, gate=1, p=-5.0, q=BAD, cu=BAD) == INVALID
     assert _prefill_logits(lib, n=0, T=0) == OK
     assert _decode_logits(lib, N=0) == OK
+
+
+def test_head_gate_argument_errors(lib):
+    P = ctypes.c_void_p(0x10000)  # aligned; never dereferenced because validation rejects the call first
+    pre = lambda q=NUL, g=NUL, dt=1, n=1, T=10: lib.gdn_prefill_head_gate(q, q, q, g, q, q, n, T, NUL, NUL, q, 4, 64,
+                                                                         64, dt, NUL, 0, None)
+    dec = lambda q=NUL, g=NUL, dt=1, N=2: lib.gdn_decode_head_gate(q, q, q, g, q, q, q, N, 4, 64, 64, dt, None)
+    assert pre(dt=0) == UNSUPPORTED            # prefill: bf16 only
+    assert pre() == INVALID                    # null pointers
+    assert pre(q=P, g=NUL) == INVALID          # null gates
+    assert pre(q=P, g=ctypes.c_void_p(0x10002)) == INVALID  # gates misaligned
+    assert pre(n=0, T=0) == OK
+    assert dec() == INVALID
+    assert dec(q=P, g=NUL) == INVALID
+    assert dec(N=0) == OK

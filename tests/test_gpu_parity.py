@@ -257,3 +257,61 @@ def test_decode_logits(gate, kind, p):
         torch.cuda.synchronize()
         assert_close(f"step {st} o", np64(o), ref_o, 1e-2)
     assert_close("state", np64(state), ref_S, 1e-5)
+
+
+# ---------------------------------------------------------------- one gate per (token, head)
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("gate", ["amin", "pages"])
+def test_prefill_head_gate(gate, dk, dv):
+    # the oracle runs the per-channel recurrence with the gate repeated over
+    # the key channels (pinned against the scalar-gate recurrence on the CPU)
+    lengths = [1, 63, 64, 65, 130, 0, 200]
+    log(f"head-gate case lengths={lengths} H=3 dk={dk} dv={dv} gate={gate}")
+    x = inputs.make_prefill_inputs(lengths, 3, dk, dv, dtype=torch.bfloat16, gate=gate, a_min=0.9, init_state=True,
+                                   seed=7, head_gate=True)
+    assert x.g.shape == (sum(lengths), 3)
+    ref_o, ref_S = oracle_prefill(x)
+    to_device(x)
+    o, S = gdn.gdn_prefill_head_gate(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    assert_close("o", np64(o), ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", np64(S), ref_S, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_head_gate(dtype):
+    N, H, d, steps = 5, 3, 128, 4
+    log(f"decode head gate N={N} H={H} d={d} {dtype}")
+    S0, draws = inputs.make_decode_steps(N, H, d, d, steps, dtype=dtype, seed=13, head_gate=True)
+    ref_S = np64(S0)
+    state = S0.cuda()
+    for st, dr in enumerate(draws):
+        g = np.repeat(np64(dr.g)[:, :, None], d, axis=2)
+        ref_o, ref_S = oracle.decode_step(np64(dr.q), np64(dr.k), np64(dr.v), g, np64(dr.beta), ref_S)
+        o = gdn.gdn_decode_head_gate(dr.q.cuda(), dr.k.cuda(), dr.v.cuda(), dr.g.cuda(), dr.beta.cuda(), state)
+        torch.cuda.synchronize()
+        assert_close(f"step {st} o", np64(o), ref_o, 1e-5 if dtype == torch.float32 else 1e-2)
+    assert_close("state", np64(state), ref_S, 1e-5)
+
+
+def test_head_gate_endpoints_and_beta_extremes():
+    # one gate per (token, head): exactly -5 on even 64-token blocks and 0 on
+    # odd ones (a 32-token chunk at -5 spans e^-160, which underflows fp32 in
+    # e^{G_t}: the true contribution lies far below bf16 resolution), beta in
+    # {0, 1}, lengths {0, 1, 63, 64, 65, 300}
+    lengths = [0, 1, 63, 64, 65, 300]
+    H, d = 2, 128
+    x = inputs.make_prefill_inputs(lengths, H, d, d, dtype=torch.bfloat16, init_state=True, seed=4, head_gate=True)
+    cu = x.cu_seqlens.tolist()
+    for n in range(len(lengths)):
+        for t in range(cu[n], cu[n + 1]):
+            x.g[t] = -5.0 if ((t - cu[n]) // 64) % 2 == 0 else 0.0
+    x.beta.copy_((torch.arange(x.T_total)[:, None] + torch.arange(H)[None, :]) % 2 == 0)
+    log(f"head-gate endpoints lengths={lengths}")
+    ref_o, ref_S = oracle_prefill(x)
+    to_device(x)
+    o, S = gdn.gdn_prefill_head_gate(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    assert_close("o", np64(o), ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", np64(S), ref_S, TOL[torch.bfloat16])

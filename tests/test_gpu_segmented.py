@@ -125,3 +125,23 @@ def test_split_logits(monkeypatch, kind, p, gate):
     torch.cuda.synchronize()
     assert_close("o", np64(o), ref_o, TOL[torch.bfloat16])
     assert_close("final_state", np64(S), ref_S, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("gate", ["amin", "pages"])
+def test_split_head_gate(monkeypatch, gate):
+    # one gate per (token, head) through the transition, fold and replay kernels
+    lengths = [1, 255, 256, 257, 0, 700]
+    log(f"split head gate lengths={lengths} gate={gate}")
+    x = inputs.make_prefill_inputs(lengths, 3, 128, 128, dtype=torch.bfloat16, gate=gate, a_min=0.9, init_state=True,
+                                   seed=24, head_gate=True)
+    ref_o, ref_S = oracle_prefill(x)
+    to_device(x)
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "256")
+    o, S = gdn.gdn_prefill_head_gate(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    assert_close("o", np64(o), ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", np64(S), ref_S, TOL[torch.bfloat16])
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "0")
+    o1, S1 = gdn.gdn_prefill_head_gate(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    assert_close("o vs unsplit", np64(o), np64(o1), TOL[torch.bfloat16])
