@@ -22,16 +22,17 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "gdn_oracle_backward.c")
 _LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile gdn_oracle.c with gcc into oracle/libgdn_oracle.so."""
+    """Compile gdn_oracle.c and gdn_oracle_backward.c with gcc into oracle/libgdn_oracle.so."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
         cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
         subprocess.run(cmd, check=True, cwd=_HERE)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -50,8 +51,10 @@ def _load():
     lib.gdn_oracle_recurrent_f32.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, i32]
     lib.gdn_oracle_chunked_f64.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, i32]
     lib.gdn_oracle_bruteforce_f64.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, P]
+    lib.gdn_oracle_backward_f64.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, i32, P, P, P, P, P, P,
+                                            i32]
     for f in (lib.gdn_oracle_recurrent_f64, lib.gdn_oracle_recurrent_f32, lib.gdn_oracle_chunked_f64,
-              lib.gdn_oracle_bruteforce_f64):
+              lib.gdn_oracle_bruteforce_f64, lib.gdn_oracle_backward_f64):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -121,6 +124,31 @@ def bruteforce(q, k, v, g, beta, cu_seqlens, initial_state=None):
     if rc != 0:
         raise RuntimeError(f"oracle brute force failed ({rc})")
     return o, Sf
+
+
+def backward(q, k, v, g, beta, cu_seqlens, d_o, initial_state=None, d_final_state=None, interval=64,
+             threads=None):
+    """Gradients of a loss with the given dL/do [T,H,dv] and dL/d(final state)
+    [N,H,dk,dv] (None: zero), in fp64, by the reverse-mode recurrence of
+    gdn_oracle_backward.c.  Returns a dict with dq, dk, dg [T,H,dk], dv
+    [T,H,dv], dbeta [T,H] and d_initial_state [N,H,dk,dv]."""
+    q, k, v, g, beta, cu, S0, T, H, dk, dv, n = _prep(q, k, v, g, beta, cu_seqlens, initial_state, np.float64)
+    dO = _as(d_o, np.float64)
+    assert dO.shape == (T, H, dv)
+    dSf = None if d_final_state is None else _as(d_final_state, np.float64)
+    if dSf is not None:
+        assert dSf.shape == (n, H, dk, dv)
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)), dg=np.zeros((T, H, dk)),
+               dbeta=np.zeros((T, H)), d_initial_state=np.zeros((n, H, dk, dv)))
+    if threads is None:
+        threads = min(os.cpu_count() or 1, max(1, n * H))
+    rc = _load().gdn_oracle_backward_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), n, H, dk, dv,
+                                         _ptr(S0), _ptr(dO), _ptr(dSf), int(interval), _ptr(out["dq"]),
+                                         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                                         _ptr(out["d_initial_state"]), int(threads))
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return out
 
 
 def decode_step(q, k, v, g, beta, state, dtype=np.float64):
