@@ -66,6 +66,11 @@ def _load():
     lib.gdn_prefill_head_gate.restype = i32
     lib.gdn_decode_head_gate.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
     lib.gdn_decode_head_gate.restype = i32
+    lib.gdn_prefill_backward_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.gdn_prefill_backward_workspace_bytes.restype = sz
+    lib.gdn_prefill_backward.argtypes = [P, P, P, P, P, P, i32, i64, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
+                                         P, sz, P]
+    lib.gdn_prefill_backward.restype = i32
     _LIB = lib
     return lib
 
@@ -321,9 +326,58 @@ def gdn_decode(q, k, v, g, beta, state, o=None, stream=None):
     return o
 
 
+def gdn_prefill_backward_workspace_bytes(T_total: int, num_seqs: int, H: int, dk: int, dv: int, dtype) -> int:
+    """Scratch bytes of gdn_prefill_backward (dtype: torch.bfloat16 or torch.float32)."""
+    code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(_load().gdn_prefill_backward_workspace_bytes(int(T_total), int(num_seqs), int(H), int(dk), int(dv),
+                                                            code))
+
+
+def gdn_prefill_backward(q, k, v, g, beta, cu_seqlens, d_o, initial_state=None, d_final_state=None,
+                         want_d_initial_state: bool = True, workspace=None, stream=None):
+    """Gradients of gdn_prefill: given dL/do [T, H, dv] (and dL/d final state [N, H, dk, dv] fp32, or None
+    for zero) returns (dq, dk, dv, dg, dbeta, d_initial_state); dq, dk, dv have the dtype of q, dg and dbeta
+    are fp32, d_initial_state is fp32 [N, H, dk, dv] (None when not wanted)."""
+    _need(q, "q", dims=3)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(k, "k", dt, 3)
+    _need(v, "v", dt, 3)
+    _need(d_o, "d_o", dt, 3)
+    _need(g, "g", torch.float32, 3)
+    _need(beta, "beta", torch.float32, 2)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if k.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) or d_o.shape != (T, H, dv) \
+            or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes")
+    n = cu_seqlens.shape[0] - 1
+    for name, s in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if s is not None:
+            _need(s, name, torch.float32, 4)
+            if s.shape != (n, H, dk, dv):
+                raise ValueError(f"{name} must be [num_seqs, H, dk, dv]")
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    db = torch.empty_like(beta)
+    dS0 = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device) if want_d_initial_state else None
+    need = gdn_prefill_backward_workspace_bytes(T, n, H, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _load().gdn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                      _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dkk),
+                                      _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dS0), H, dk, dv, _dtype_code(q),
+                                      _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "gdn_prefill_backward")
+    return dq, dkk, dvv, dg, db, dS0
+
+
 __all__ = [
     "gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free", "gdn_prefill_workspace_bytes",
     "gdn_prefill", "gdn_decode", "gdn_prefill_logits", "gdn_decode_logits", "gdn_prefill_head_gate",
-    "gdn_decode_head_gate", "GdnError", "load_library", "LIB_PATH",
+    "gdn_decode_head_gate", "gdn_prefill_backward", "gdn_prefill_backward_workspace_bytes", "GdnError", "load_library", "LIB_PATH",
     "GDN_GATE_LOG", "GDN_GATE_SCALED_SIGMOID", "GDN_GATE_ALPHA_MIN",
 ]

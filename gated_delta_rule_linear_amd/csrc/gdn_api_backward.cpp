@@ -1,0 +1,100 @@
+// libgdn C-ABI, backward pass: argument validation and dispatch.  The
+// contract of each entry point is in include/gdn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_backward.h"
+
+namespace {
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+// GDN_VALIDATE=1: synchronous host check of cu_seqlens and of g's domain.
+int32_t validate_backward_inputs(const int32_t* cu_dev, int32_t num_seqs, int64_t T_total, const float* g_dev,
+                                 int64_t ng, hipStream_t s) {
+    std::vector<int32_t> cu((size_t)num_seqs + 1);
+    std::vector<float> g((size_t)ng);
+    if (hipMemcpyAsync(cu.data(), cu_dev, sizeof(int32_t) * cu.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (ng > 0 && hipMemcpyAsync(g.data(), g_dev, sizeof(float) * g.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
+    if (cu[0] != 0 || cu[(size_t)num_seqs] != T_total) return GDN_ERR_DOMAIN;
+    for (int32_t n = 0; n < num_seqs; ++n)
+        if (cu[(size_t)n + 1] < cu[(size_t)n]) return GDN_ERR_DOMAIN;
+    for (float x : g)
+        if (!(x >= -5.0f && x <= 0.0f)) return GDN_ERR_DOMAIN;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v,
+                                            int32_t dtype) {
+    if (T_total < 0 || num_seqs < 0 || H < 1 || d_k < 0 || d_v < 0) return 0;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
+    return gdn::backward_workspace_bytes(T_total, num_seqs, H, d_k, d_v, dtype == GDN_BF16);
+}
+
+int32_t gdn_prefill_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
+                             const float* initial_state, const void* d_o, const float* d_final_state, void* dq,
+                             void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state, int32_t H,
+                             int32_t d_k, int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (num_seqs < 0 || T_total < 0 || H < 1) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (T_total > 0 && num_seqs == 0) return GDN_ERR_INVALID_ARG;
+    if (num_seqs == 0) return GDN_OK;
+    if (!cu_seqlens || !aligned_to(cu_seqlens, 4)) return GDN_ERR_INVALID_ARG;
+    if (T_total > 0) {
+        const void* p16[] = {q, k, v, g, d_o, dq, dk, dv, dg};
+        for (const void* p : p16)
+            if (!p || !aligned_to(p, 16)) return GDN_ERR_INVALID_ARG;
+        if (!beta || !aligned_to(beta, 4) || !dbeta || !aligned_to(dbeta, 4)) return GDN_ERR_INVALID_ARG;
+    }
+    const void* st16[] = {initial_state, d_final_state, d_initial_state};
+    for (const void* p : st16)
+        if (p && !aligned_to(p, 16)) return GDN_ERR_INVALID_ARG;
+    const size_t need = gdn::backward_workspace_bytes(T_total, num_seqs, H, d_k, d_v, dtype == GDN_BF16);
+    if (!workspace || workspace_bytes < need || !aligned_to(workspace, 16)) return GDN_ERR_INVALID_ARG;
+    if ((int64_t)num_seqs * H > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (const char* e = std::getenv("GDN_VALIDATE"); e && e[0] == '1') {
+        const int32_t st = validate_backward_inputs(cu_seqlens, num_seqs, T_total, g, T_total * H * d_k, s);
+        if (st != GDN_OK) return st;
+    }
+    gdn::BackwardLaunch p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.cu_seqlens = cu_seqlens;
+    p.initial_state = initial_state;
+    p.d_o = d_o;
+    p.d_final_state = d_final_state;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dg = dg;
+    p.dbeta = dbeta;
+    p.d_initial_state = d_initial_state;
+    p.num_seqs = num_seqs;
+    p.H = H;
+    p.dk_dim = d_k;
+    p.dv_dim = d_v;
+    p.bf16 = dtype == GDN_BF16;
+    p.T_total = T_total;
+    p.workspace = workspace;
+    return gdn::launch_backward(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

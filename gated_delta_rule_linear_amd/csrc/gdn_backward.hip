@@ -1,0 +1,690 @@
+// Gradients of the chunked gated delta rule on gfx950 (reverse mode).
+//
+// The forward map per (sequence, head), token by token, is
+//   X_t = diag(a_t) S_{t-1},  a_t = e^{g_t},  u_t = b_t (v_t - X_t^T k_t),
+//   S_t = X_t + k_t u_t^T,    o_t = S_t^T q_t,
+// the fixed-size state with correct-on-write updates and a position-dependent
+// decay of "How to Think About Trillion-Parameter Sparse Multimodal LLMs",
+// section 2.2, with the lower-bounded log-decay g in [-5, 0] of
+// "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate the New
+// Generation", section 3.1.  The method is trained by back-propagation
+// ("Architecture Evolution and Training Engineering for Trillion-Scale Sparse
+// Multimodal Models", section 3.3); the pages do not write the backward pass
+// out, so this file computes the plain adjoint of the forward map, organised
+// in chunks of 16 tokens:
+//
+// Inside a 16-token sub-chunk with start state S0 and local cumulative
+// log-decay G_t = sum_{r<=t} g_r (per key channel), and with m = G_7 the
+// reference point of the window (the 16-token tile of the pages' bound keeps
+// every factor e^{+-(G_t - m)} inside e^{+-40}):
+//   q~ = q e^{G-m},  k~ = k e^{G-m},  k^ = k e^{m-G},  E = diag(e^m),
+//   F = diag(e^{G_15 - m}),  gamma = e^{G_15}
+//   P  = lower(q~ k^T)             KK = strict_lower(k~ k^T)
+//   M  = (I + diag(b) KK)^-1
+//   R  = V - k~ (E S0),  U = M diag(b) R
+//   O  = q~ (E S0) + P U,  S_end = gamma S0 + F k^T U
+// Given dO and dS = dL/dS_end, the adjoint of the sub-chunk is
+//   dU  = P^T dO + k^ (F dS)           dRm = M^T dU,  dR = diag(b) dRm,  dv = dR
+//   dA  = -strict_lower(dRm U^T)      dKK = diag(b) dA     dP = lower(dO U^T)
+//   db_t = R_t . dRm_t + sum_s dA_ts KK_ts
+//   dS0 = gamma dS + E (q~^T dO - k~^T dR)
+//   Z = dO (E S0)^T + dP k^,  X = -dR (E S0)^T + dKK k^,
+//   Y = dKK^T k~ + dP^T q~ + U (F dS)^T
+//   dq = e^{G-m} Z,  dk = e^{G-m} X + e^{m-G} Y
+//   dG = q~ Z + k~ X - k^ Y  (elementwise), plus on the last row
+//   dG_15 += rowsum(dS * S_end) = rowsum((F dS) * (E S0)) + colsum(k^ * U (F dS)^T)
+//   dg_t = sum_{t' >= t} dG_t'
+// Every product is a 16 x 16 matrix-core tile (bf16 operands and fp32
+// accumulation for bf16 inputs, fp32 throughout for fp32 inputs).
+//
+// Two kernels per call, one workgroup per (sequence, head) each:
+//  1. bwd_states_kernel walks the sub-chunks forward and stores every
+//     sub-chunk's start state (a checkpoint, in the input dtype) in the
+//     caller's workspace;
+//  2. bwd_grad_kernel walks them backward, carrying dS in registers, and
+//     writes dq, dk, dv, dg, dbeta and the initial state's gradient.
+// The workgroup has d_v / 16 waves; for state-shaped quantities wave w owns
+// the 16 value columns [16w, 16w + 16), for the key-channel outputs the
+// 16-channel tiles w, w + d_v/16, ...
+#include <type_traits>
+
+#include "gdn_backward.h"
+#include "gdn_mfma.h"
+
+namespace gdn {
+namespace {
+
+constexpr int CB = 16;                           // tokens per sub-chunk
+constexpr float LOG2E_B = 1.4426950408889634f;   // G is carried in log2 units
+
+// Contractions over the 16 tokens of a sub-chunk.  Lane r + 16g supplies
+// A[r][4g .. 4g+3] and B[4g .. 4g+3][r]: the register layout of a 16 x 16
+// accumulator (lane r + 16g holds C[4g + i][r]) is such a B operand as it is,
+// and the A operand of the transposed matrix.
+template <typename TI>
+struct K16;
+template <>
+struct K16<bf16> {
+    typedef bf16x4 frag;
+    __device__ __forceinline__ static frag cvt(floatx4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+    __device__ __forceinline__ static frag load(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+    __device__ __forceinline__ static floatx4 mma(frag a, frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct K16<float> {
+    typedef floatx4 frag;
+    __device__ __forceinline__ static frag cvt(floatx4 x) { return x; }
+    __device__ __forceinline__ static frag load(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+    // four 16x16x4 steps; step e pairs lane group g's element e, i.e. k = 4g + e
+    __device__ __forceinline__ static floatx4 mma(frag a, frag b, floatx4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+        return c;
+    }
+};
+
+template <typename T>
+struct Two;
+template <>
+struct Two<bf16> {
+    typedef bf16x2 type;
+    __device__ __forceinline__ static floatx2 f(bf16x2 x) { return floatx2{(float)x[0], (float)x[1]}; }
+    __device__ __forceinline__ static bf16x2 t(floatx2 x) { return bf16x2{(bf16)x[0], (bf16)x[1]}; }
+};
+template <>
+struct Two<float> {
+    typedef floatx2 type;
+    __device__ __forceinline__ static floatx2 f(floatx2 x) { return x; }
+    __device__ __forceinline__ static floatx2 t(floatx2 x) { return x; }
+};
+template <typename T>
+struct Four;
+template <>
+struct Four<bf16> {
+    typedef bf16x4 type;
+    __device__ __forceinline__ static floatx4 f(bf16x4 x) { return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+    __device__ __forceinline__ static bf16x4 t(floatx4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+};
+template <>
+struct Four<float> {
+    typedef floatx4 type;
+    __device__ __forceinline__ static floatx4 f(floatx4 x) { return x; }
+    __device__ __forceinline__ static floatx4 t(floatx4 x) { return x; }
+};
+
+__device__ __forceinline__ floatx4 exp2v(floatx4 x) {
+    return floatx4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]), __builtin_amdgcn_exp2f(x[2]),
+                   __builtin_amdgcn_exp2f(x[3])};
+}
+__device__ __forceinline__ floatx2 exp2v(floatx2 x) {
+    return floatx2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])};
+}
+// Sum over the 16 lanes of a lane group (lanes 16g .. 16g+15); every lane gets it.
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1, 16);
+    x += __shfl_xor(x, 2, 16);
+    x += __shfl_xor(x, 4, 16);
+    x += __shfl_xor(x, 8, 16);
+    return x;
+}
+// Suffix sum inside a lane group: lane r gets the sum over lanes r .. 15.
+__device__ __forceinline__ float suffix16(float x, int r) {
+#pragma unroll
+    for (int d = 1; d < 16; d *= 2) {
+        const float y = __shfl_down(x, d, 16);
+        if (r + d < 16) x += y;
+    }
+    return x;
+}
+
+template <typename TI>
+struct BArgs {
+    const TI* q;
+    const TI* k;
+    const TI* v;
+    const float* g;
+    const float* beta;
+    const int32_t* cu;
+    const float* S0;   // [num_seqs, H, DK, DV] or null (zero)
+    const TI* dO;      // [T, H, DV]
+    const float* dSf;  // [num_seqs, H, DK, DV] or null (zero)
+    TI* dq;
+    TI* dk;
+    TI* dv;
+    float* dg;
+    float* dbeta;
+    float* dS0;        // [num_seqs, H, DK, DV] or null (not wanted)
+    TI* ck;            // checkpoints: slot (cu[n] / 16 + n + c, h) is the start state of sub-chunk c of sequence n
+    int H;
+};
+
+// LDS layout.  "Natural" matrices are row-major over the contraction index
+// with one 16-byte pad per row; "transposed" ones hold 16 tokens per key
+// channel.  FULL: the gradient kernel's buffers; otherwise the forward one's.
+template <typename TI, int DK, int DV, bool FULL>
+struct BCfg {
+    typedef Mma<TI> M;
+    static constexpr int NW = DV / 16, NT = 64 * NW;
+    static constexpr int ES = (int)sizeof(TI);
+    static constexpr int KSTEP = M::KSTEP, KW = M::KW;
+    static constexpr int KM = DK / KSTEP, KV = DV / KSTEP;  // MFMA steps over d_k, d_v
+    static constexpr int RT = DK / 16;                      // 16-row tiles of d_k
+    static constexpr int SK = DK + 16 / ES, SV = DV + 16 / ES;
+    static constexpr int B_NK = CB * SK * ES, B_TK = DK * CB * ES, B_NV = CB * SV * ES, B_FS = DK * SV * ES;
+    static constexpr int OFF_KN = 0;                                   // k~ natural [16][SK]
+    static constexpr int OFF_HN = OFF_KN + B_NK;                       // k^ natural
+    static constexpr int OFF_HT = OFF_HN + B_NK;                       // k^ transposed [DK][16]
+    static constexpr int OFF_QN = OFF_HT + B_TK;                       // q~ natural      (FULL)
+    static constexpr int OFF_KT = OFF_QN + (FULL ? B_NK : 0);          // k~ transposed   (FULL)
+    static constexpr int OFF_QT = OFF_KT + (FULL ? B_TK : 0);          // q~ transposed   (FULL)
+    static constexpr int OFF_DO = OFF_QT + (FULL ? B_TK : 0);          // dO natural [16][SV]   (FULL)
+    static constexpr int OFF_U = OFF_DO + (FULL ? B_NV : 0);           // U natural       (FULL)
+    static constexpr int OFF_DR = OFF_U + (FULL ? B_NV : 0);           // dRm natural     (FULL)
+    static constexpr int OFF_FS = OFF_DR + (FULL ? B_NV : 0);          // F dS [DK][SV]   (FULL)
+    static constexpr int OFF_G = OFF_FS + (FULL ? B_FS : 0);           // G (log2) [16][DK] fp32
+    static constexpr int OFF_ML = OFF_G + CB * DK * 4;                 // m (log2) [DK]
+    static constexpr int OFF_EM = OFF_ML + DK * 4;                     // e^m [DK]
+    static constexpr int OFF_FF = OFF_EM + DK * 4;                     // e^{G_15 - m} [DK]
+    static constexpr int OFF_GAM = OFF_FF + DK * 4;                    // e^{G_15} [DK]
+    static constexpr int OFF_DG15 = OFF_GAM + DK * 4;                  // dG_15 part [DK]  (FULL)
+    static constexpr int OFF_BETA = OFF_DG15 + DK * 4;                 // beta [16]
+    static constexpr int OFF_DB = OFF_BETA + CB * 4;                   // R . dRm per wave [NW][16]  (FULL)
+    static constexpr int OFF_N = OFF_DB + NW * CB * 4;                 // -diag(b) KK [16][16]
+    static constexpr int OFF_MI = OFF_N + 256 * 4;                     // M [16][16]
+    static constexpr int OFF_MT = OFF_MI + 256 * 4;                    // M^T [16][16]
+    static constexpr int LDS = OFF_MT + 256 * 4;
+    static_assert(B_NK % 16 == 0 && B_TK % 16 == 0 && B_NV % 16 == 0 && B_FS % 16 == 0, "alignment");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Per-sub-chunk preparation, shared by both kernels.  Ends with M and M^T in
+// LDS, every operand stored, and (wave 0) KK in `kk` (accumulator layout:
+// lane r + 16g holds KK[4g + i][r]).
+template <typename TI, int DK, int DV, bool FULL>
+__device__ __forceinline__ void prep(const BArgs<TI>& a, char* smem, int h, int64_t t0, int L, int tid, int w,
+                                     floatx4& kk) {
+    typedef BCfg<TI, DK, DV, FULL> P;
+    typedef typename Two<TI>::type T2;
+    typedef Mma<TI> M;
+    const int H = a.H;
+    const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+    float* sG = reinterpret_cast<float*>(smem + P::OFF_G);
+    float* sML = reinterpret_cast<float*>(smem + P::OFF_ML);
+    float* sEM = reinterpret_cast<float*>(smem + P::OFF_EM);
+    float* sFF = reinterpret_cast<float*>(smem + P::OFF_FF);
+    float* sGAM = reinterpret_cast<float*>(smem + P::OFF_GAM);
+    float* sBETA = reinterpret_cast<float*>(smem + P::OFF_BETA);
+    TI* sKN = reinterpret_cast<TI*>(smem + P::OFF_KN);
+    TI* sHN = reinterpret_cast<TI*>(smem + P::OFF_HN);
+    TI* sHT = reinterpret_cast<TI*>(smem + P::OFF_HT);
+    TI* sQN = reinterpret_cast<TI*>(smem + P::OFF_QN);
+    TI* sKT = reinterpret_cast<TI*>(smem + P::OFF_KT);
+    TI* sQT = reinterpret_cast<TI*>(smem + P::OFF_QT);
+    TI* sDO = reinterpret_cast<TI*>(smem + P::OFF_DO);
+    float* sN = reinterpret_cast<float*>(smem + P::OFF_N);
+    float* sMI = reinterpret_cast<float*>(smem + P::OFF_MI);
+    float* sMT = reinterpret_cast<float*>(smem + P::OFF_MT);
+    const size_t row0 = (size_t)t0 * H + h;  // (token, head) row of the sub-chunk's first token
+
+    // 1. cumulative log-decay of each key channel (rows past L read g = 0)
+    if (tid < DK) {
+        const float* gp = a.g + row0 * DK + tid;
+        float G = 0.f, m = 0.f;
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            const float x = t < L ? gp[(size_t)t * H * DK] : 0.f;
+            G = __builtin_fmaf(x, LOG2E_B, G);
+            sG[t * DK + tid] = G;
+            if (t == 7) m = G;
+        }
+        sML[tid] = m;
+        sEM[tid] = __builtin_amdgcn_exp2f(m);
+        sFF[tid] = __builtin_amdgcn_exp2f(G - m);
+        sGAM[tid] = __builtin_amdgcn_exp2f(G);
+    }
+    if (tid >= DK && tid < DK + CB) {
+        const int t = tid - DK;
+        sBETA[t] = t < L ? a.beta[row0 + (size_t)t * H] : 0.f;
+    }
+    if constexpr (FULL) {
+        // dO rows into LDS (16-byte pieces; rows past L are zero)
+        constexpr int PER = 16 / P::ES, NPR = DV / PER;
+        for (int i = tid; i < CB * NPR; i += P::NT) {
+            const int t = i / NPR, c = (i % NPR) * PER;
+            floatx4 x = zero4();
+            if (t < L) x = *reinterpret_cast<const floatx4*>(a.dO + (row0 + (size_t)t * H) * DV + c);
+            *reinterpret_cast<floatx4*>(sDO + t * P::SV + c) = x;
+        }
+    }
+    __syncthreads();
+
+    // 2. operands: (token pair tp, channel pair cp) per item
+    for (int i = tid; i < 4 * DK; i += P::NT) {
+        const int cp = i % (DK / 2), tp = i / (DK / 2), c0 = 2 * cp;
+        const floatx2 ml = *reinterpret_cast<const floatx2*>(sML + c0);
+        floatx2 kt[2], kh[2], qt[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = 2 * tp + u;
+            const size_t off = (row0 + (size_t)t * H) * DK + c0;
+            floatx2 kk2 = floatx2{0.f, 0.f}, qq2 = floatx2{0.f, 0.f};
+            if (t < L) {
+                kk2 = Two<TI>::f(*reinterpret_cast<const T2*>(a.k + off));
+                if constexpr (FULL) qq2 = Two<TI>::f(*reinterpret_cast<const T2*>(a.q + off));
+            }
+            const floatx2 G = *reinterpret_cast<const floatx2*>(sG + t * DK + c0);
+            const floatx2 e = exp2v(G - ml), ei = exp2v(ml - G);
+            kt[u] = kk2 * e;
+            kh[u] = kk2 * ei;
+            *reinterpret_cast<T2*>(sKN + t * P::SK + c0) = Two<TI>::t(kt[u]);
+            *reinterpret_cast<T2*>(sHN + t * P::SK + c0) = Two<TI>::t(kh[u]);
+            if constexpr (FULL) {
+                qt[u] = qq2 * e;
+                *reinterpret_cast<T2*>(sQN + t * P::SK + c0) = Two<TI>::t(qt[u]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = c0 + j;
+            *reinterpret_cast<T2*>(sHT + c * CB + 2 * tp) = Two<TI>::t(floatx2{kh[0][j], kh[1][j]});
+            if constexpr (FULL) {
+                *reinterpret_cast<T2*>(sKT + c * CB + 2 * tp) = Two<TI>::t(floatx2{kt[0][j], kt[1][j]});
+                *reinterpret_cast<T2*>(sQT + c * CB + 2 * tp) = Two<TI>::t(floatx2{qt[0][j], qt[1][j]});
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3. (wave 0) KK = k~ k^T, the unit lower-triangular I + diag(b) KK and its inverse M
+    if (w == 0) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int mm = 0; mm < P::KM; ++mm)
+            acc = M::mma(lds_nat(sKN + r * P::SK, mm, g), lds_nat(sHN + r * P::SK, mm, g), acc);
+        // lane r + 16g: KK[t = 4g + i][s = r]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            acc[i] = r < t ? acc[i] : 0.f;
+            sN[t * 16 + r] = -sBETA[t] * acc[i];
+        }
+        kk = acc;
+        // forward substitution, rows in order: lane r + 16g carries M[r][4g .. 4g+3];
+        // row j of M is final once rows < j are applied.
+        const floatx4 n0 = *reinterpret_cast<const floatx4*>(sN + r * 16);
+        const floatx4 n1 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 4);
+        const floatx4 n2 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 8);
+        const floatx4 n3 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 12);
+        const float nr[16] = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                              n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+        floatx4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = r == 4 * g + e ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+            floatx4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = __shfl(x[e], j + 16 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(nr[j], y[e], x[e]);
+        }
+        *reinterpret_cast<floatx4*>(sMI + r * 16 + 4 * g) = x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sMT[(4 * g + e) * 16 + r] = x[e];
+    }
+    __syncthreads();
+}
+
+// Forward pass storing checkpoints: one workgroup per (sequence, head).
+template <typename TI, int DK, int DV>
+__global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
+    typedef BCfg<TI, DK, DV, false> P;
+    typedef Mma<TI> M;
+    typedef K16<TI> K;
+    __shared__ __attribute__((aligned(16))) char smem[P::LDS];
+    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const int n = blockIdx.x / H, h = blockIdx.x - n * H;
+    const int64_t tb = a.cu[n], te = a.cu[n + 1];
+    const int col0 = 16 * w;
+    const float* sEM = reinterpret_cast<const float*>(smem + P::OFF_EM);
+    const float* sFF = reinterpret_cast<const float*>(smem + P::OFF_FF);
+    const float* sGAM = reinterpret_cast<const float*>(smem + P::OFF_GAM);
+    const float* sBETA = reinterpret_cast<const float*>(smem + P::OFF_BETA);
+    const TI* sKN = reinterpret_cast<const TI*>(smem + P::OFF_KN);
+    const TI* sHT = reinterpret_cast<const TI*>(smem + P::OFF_HT);
+    const float* sMI = reinterpret_cast<const float*>(smem + P::OFF_MI);
+
+    // state, own columns: S[rt][i] = S[16 rt + 4g + i][col0 + r]
+    floatx4 S[P::RT];
+    const float* s0 = a.S0 ? a.S0 + (size_t)blockIdx.x * DK * DV : nullptr;
+#pragma unroll
+    for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[(16 * rt + 4 * g + i) * DV + col0 + r] : 0.f;
+
+    TI* ck = a.ck + (((size_t)(tb >> 4) + n) * H + h) * DK * DV;
+    for (int64_t t0 = tb; t0 < te; t0 += CB, ck += (size_t)H * DK * DV) {
+        const int L = (int)(te - t0 < CB ? te - t0 : CB);
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ck[(16 * rt + 4 * g + i) * DV + col0 + r] = from_f32<TI>(S[rt][i]);
+        __syncthreads();  // the previous sub-chunk is done with LDS
+        floatx4 kk;
+        prep<TI, DK, DV, false>(a, smem, h, t0, L, tid, w, kk);
+
+        // R = V - k~ (E S), own columns
+        floatx4 es[P::RT];
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt) es[rt] = S[rt] * *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int mm = 0; mm < P::KM; ++mm)
+            acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
+        floatx4 br;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            const float vv = t < L ? to_f32(a.v[((size_t)(t0 + t) * H + h) * DV + col0 + r]) : 0.f;
+            br[i] = sBETA[t] * (vv - acc[i]);
+        }
+        // U = M diag(b) R
+        const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
+        const typename K::frag bu = K::cvt(U);
+        // S <- gamma S + F (k^T U)
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt) {
+            const floatx4 d = K::mma(K::load(sHT + (16 * rt + r) * CB + 4 * g), bu, zero4());
+            const floatx4 gm = *reinterpret_cast<const floatx4*>(sGAM + 16 * rt + 4 * g);
+            const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
+            S[rt] = gm * S[rt] + ff * d;
+        }
+    }
+}
+
+// Reverse pass: one workgroup per (sequence, head), sub-chunks last to first.
+template <typename TI, int DK, int DV>
+__global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
+    typedef BCfg<TI, DK, DV, true> P;
+    typedef Mma<TI> M;
+    typedef typename M::frag frag;
+    typedef K16<TI> K;
+    typedef Four<TI> F4;
+    __shared__ __attribute__((aligned(16))) char smem[P::LDS];
+    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const int n = blockIdx.x / H, h = blockIdx.x - n * H;
+    const int64_t tb = a.cu[n], te = a.cu[n + 1];
+    const int col0 = 16 * w;
+    const float* sG = reinterpret_cast<const float*>(smem + P::OFF_G);
+    const float* sML = reinterpret_cast<const float*>(smem + P::OFF_ML);
+    const float* sEM = reinterpret_cast<const float*>(smem + P::OFF_EM);
+    const float* sFF = reinterpret_cast<const float*>(smem + P::OFF_FF);
+    const float* sGAM = reinterpret_cast<const float*>(smem + P::OFF_GAM);
+    float* sDG15 = reinterpret_cast<float*>(smem + P::OFF_DG15);
+    const float* sBETA = reinterpret_cast<const float*>(smem + P::OFF_BETA);
+    float* sDB = reinterpret_cast<float*>(smem + P::OFF_DB);
+    const TI* sKN = reinterpret_cast<const TI*>(smem + P::OFF_KN);
+    const TI* sHN = reinterpret_cast<const TI*>(smem + P::OFF_HN);
+    const TI* sQN = reinterpret_cast<const TI*>(smem + P::OFF_QN);
+    const TI* sKT = reinterpret_cast<const TI*>(smem + P::OFF_KT);
+    const TI* sHT = reinterpret_cast<const TI*>(smem + P::OFF_HT);
+    const TI* sQT = reinterpret_cast<const TI*>(smem + P::OFF_QT);
+    TI* sDO = reinterpret_cast<TI*>(smem + P::OFF_DO);
+    TI* sU = reinterpret_cast<TI*>(smem + P::OFF_U);
+    TI* sDR = reinterpret_cast<TI*>(smem + P::OFF_DR);
+    TI* sFS = reinterpret_cast<TI*>(smem + P::OFF_FS);
+    const float* sMI = reinterpret_cast<const float*>(smem + P::OFF_MI);
+    const float* sMT = reinterpret_cast<const float*>(smem + P::OFF_MT);
+
+    // dS = dL/d(state at the end of the current sub-chunk), own columns
+    floatx4 dS[P::RT];
+    const float* dsf = a.dSf ? a.dSf + (size_t)blockIdx.x * DK * DV : nullptr;
+#pragma unroll
+    for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[rt][i] = dsf ? dsf[(16 * rt + 4 * g + i) * DV + col0 + r] : 0.f;
+
+    const int64_t nsub = (te - tb + CB - 1) / CB;
+    for (int64_t c = nsub - 1; c >= 0; --c) {
+        const int64_t t0 = tb + CB * c;
+        const int L = (int)(te - t0 < CB ? te - t0 : CB);
+        const size_t row0 = (size_t)t0 * H + h;
+        const TI* ck = a.ck + ((((size_t)(tb >> 4) + n + (size_t)c) * H + h) * DK * DV);
+        // start state of the sub-chunk, own columns
+        floatx4 es[P::RT];
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) es[rt][i] = to_f32(ck[(16 * rt + 4 * g + i) * DV + col0 + r]);
+        floatx4 vv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            vv[i] = t < L ? to_f32(a.v[(row0 + (size_t)t * H) * DV + col0 + r]) : 0.f;
+        }
+        __syncthreads();  // the previous sub-chunk is done with LDS
+        floatx4 kk = zero4();
+        prep<TI, DK, DV, true>(a, smem, h, t0, L, tid, w, kk);
+
+        // ---- 3. value-column steps (own columns) -------------------------------
+        // P = lower(q~ k^T): lane r + 16g holds P[t = 4g + i][s = r]
+        floatx4 Pa = zero4();
+#pragma unroll
+        for (int mm = 0; mm < P::KM; ++mm)
+            Pa = M::mma(lds_nat(sQN + r * P::SK, mm, g), lds_nat(sHN + r * P::SK, mm, g), Pa);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Pa[i] = r <= 4 * g + i ? Pa[i] : 0.f;
+        // R = V - k~ (E S0)
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt) es[rt] *= *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int mm = 0; mm < P::KM; ++mm)
+            acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
+        floatx4 R, br;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            R[i] = vv[i] - acc[i];
+            br[i] = sBETA[4 * g + i] * R[i];
+        }
+        const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
+        // own columns of dO
+        floatx4 dOc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dOc[i] = to_f32(sDO[(4 * g + i) * P::SV + col0 + r]);
+        // F dS
+        floatx4 fds[P::RT];
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt) fds[rt] = dS[rt] * *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
+        // dU = P^T dO + k^ (F dS)
+        floatx4 dU = K::mma(K::cvt(Pa), K::cvt(dOc), zero4());
+#pragma unroll
+        for (int mm = 0; mm < P::KM; ++mm)
+            dU = M::mma(lds_perm(sHN + r * P::SK, mm, g), acc_perm<TI>(fds, mm, P::RT), dU);
+        // dRm = M^T dU, dR = diag(b) dRm = dv
+        const floatx4 dRm = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMT + r * 16 + 4 * g)), K::cvt(dU), zero4());
+        floatx4 dR, ndR;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            dR[i] = sBETA[t] * dRm[i];
+            ndR[i] = -dR[i];
+            if (t < L) a.dv[(row0 + (size_t)t * H) * DV + col0 + r] = from_f32<TI>(dR[i]);
+            const float p = sum16(R[i] * dRm[i]);
+            if (r == 0) sDB[w * CB + t] = p;
+        }
+        // exchange: F dS, U, dRm (natural layouts) for the key-channel products
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sFS[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(fds[rt][i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sU[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(U[i]);
+            sDR[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(dRm[i]);
+        }
+        // dS <- gamma dS + E (q~^T dO - k~^T dR)
+        {
+            const typename K::frag bo = K::cvt(dOc), br2 = K::cvt(ndR);
+#pragma unroll
+            for (int rt = 0; rt < P::RT; ++rt) {
+                floatx4 x = K::mma(K::load(sQT + (16 * rt + r) * CB + 4 * g), bo, zero4());
+                x = K::mma(K::load(sKT + (16 * rt + r) * CB + 4 * g), br2, x);
+                const floatx4 gm = *reinterpret_cast<const floatx4*>(sGAM + 16 * rt + 4 * g);
+                const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
+                dS[rt] = gm * dS[rt] + em * x;
+            }
+        }
+        __syncthreads();
+
+        // ---- 4. key-channel outputs ------------------------------------------
+        // token-pair matrices over d_v (same in every wave)
+        floatx4 dPT = zero4(), dPa = zero4(), dAa = zero4(), dAT = zero4();
+#pragma unroll
+        for (int mm = 0; mm < P::KV; ++mm) {
+            const frag fo = lds_nat(sDO + r * P::SV, mm, g);
+            const frag fu = lds_nat(sU + r * P::SV, mm, g);
+            const frag fr = lds_nat(sDR + r * P::SV, mm, g);
+            dPT = M::mma(fu, fo, dPT);  // dP[t = r][s = 4g + i]
+            dPa = M::mma(fo, fu, dPa);  // dP[t = 4g + i][s = r]
+            dAa = M::mma(fr, fu, dAa);  // -dA[t = 4g + i][s = r]
+            dAT = M::mma(fu, fr, dAT);  // -dA[t = r][s = 4g + i]
+        }
+        floatx4 dKKa, dKKT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ti = 4 * g + i;
+            dPT[i] = ti <= r ? dPT[i] : 0.f;
+            dPa[i] = r <= ti ? dPa[i] : 0.f;
+            dAa[i] = r < ti ? -dAa[i] : 0.f;
+            dAT[i] = ti < r ? -dAT[i] : 0.f;
+            dKKa[i] = sBETA[ti] * dAa[i];
+            dKKT[i] = sBETA[r] * dAT[i];
+        }
+        if (w == 0) {
+            // dbeta_t = R_t . dRm_t + sum_s dA_ts KK_ts,  t = 4g + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g + i;
+                float p = sum16(dAa[i] * kk[i]);
+                if (r == 0 && t < L) {
+                    for (int ww = 0; ww < P::NW; ++ww) p += sDB[ww * CB + t];
+                    a.dbeta[row0 + (size_t)t * H] = p;
+                }
+            }
+        }
+        const typename K::frag bPT = K::cvt(dPT), bKKT = K::cvt(dKKT), bKKa = K::cvt(dKKa), bPa = K::cvt(dPa);
+        for (int it = w; it < P::RT; it += P::NW) {
+            const int i0 = 16 * it;
+            // state rows i0 + r, from the checkpoint (Z, X) and from LDS (Y)
+            const TI* ckrow = ck + (size_t)(i0 + r) * DV;
+            floatx4 z1 = zero4(), x1 = zero4(), y1 = zero4();
+            float d1 = 0.f;  // sum_j (F dS)[i0 + r][j] S0[i0 + r][j] over this lane's j
+#pragma unroll
+            for (int mm = 0; mm < P::KV; ++mm) {
+                const frag fs0 = *reinterpret_cast<const frag*>(ckrow + mm * P::KSTEP + g * P::KW);
+                const frag ffs = lds_nat(sFS + (i0 + r) * P::SV, mm, g);
+                z1 = M::mma(fs0, lds_nat(sDO + r * P::SV, mm, g), z1);
+                x1 = M::mma(fs0, lds_nat(sDR + r * P::SV, mm, g), x1);
+                y1 = M::mma(ffs, lds_nat(sU + r * P::SV, mm, g), y1);
+                if constexpr (P::KW == 1) {
+                    d1 += (float)fs0 * (float)ffs;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < P::KW; ++e) d1 += (float)fs0[e] * (float)ffs[e];
+                }
+            }
+            d1 += __shfl_xor(d1, 16);
+            d1 += __shfl_xor(d1, 32);
+            if (g == 0) sDG15[i0 + r] = d1 * sEM[i0 + r];
+            // lane r + 16g: key channel i = i0 + 4g + e, token t = r
+            const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + i0 + 4 * g);
+            const float bt = sBETA[r];
+            floatx4 Z = em * z1, X = -(bt * em) * x1;
+            Z = K::mma(K::load(sHT + (i0 + r) * CB + 4 * g), bPT, Z);
+            X = K::mma(K::load(sHT + (i0 + r) * CB + 4 * g), bKKT, X);
+            floatx4 Y = K::mma(K::load(sKT + (i0 + r) * CB + 4 * g), bKKa, y1);
+            Y = K::mma(K::load(sQT + (i0 + r) * CB + 4 * g), bPa, Y);
+            const floatx4 khat = F4::f(*reinterpret_cast<const typename F4::type*>(sHN + r * P::SK + i0 + 4 * g));
+            const floatx4 ktil = F4::f(*reinterpret_cast<const typename F4::type*>(sKN + r * P::SK + i0 + 4 * g));
+            const floatx4 qtil = F4::f(*reinterpret_cast<const typename F4::type*>(sQN + r * P::SK + i0 + 4 * g));
+            const floatx4 Gl = *reinterpret_cast<const floatx4*>(sG + r * DK + i0 + 4 * g);
+            const floatx4 ml = *reinterpret_cast<const floatx4*>(sML + i0 + 4 * g);
+            const floatx4 ef = exp2v(Gl - ml), eb = exp2v(ml - Gl);
+            const floatx4 dq = ef * Z, dk = ef * X + eb * Y;
+            floatx4 dG = qtil * Z + ktil * X - khat * Y;
+            floatx4 d2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d2[e] = sum16(khat[e] * y1[e]);
+            const floatx4 d15 = *reinterpret_cast<const floatx4*>(sDG15 + i0 + 4 * g) + d2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dG[e] = suffix16(dG[e], r) + d15[e];
+            if (r < L) {
+                const size_t off = (row0 + (size_t)r * H) * DK + i0 + 4 * g;
+                *reinterpret_cast<typename F4::type*>(a.dq + off) = F4::t(dq);
+                *reinterpret_cast<typename F4::type*>(a.dk + off) = F4::t(dk);
+                *reinterpret_cast<floatx4*>(a.dg + off) = dG;
+            }
+        }
+    }
+    if (a.dS0) {
+        float* dst = a.dS0 + (size_t)blockIdx.x * DK * DV;
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g + i) * DV + col0 + r] = dS[rt][i];
+    }
+}
+
+template <typename TI, int DK, int DV>
+hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
+    BArgs<TI> a;
+    a.q = static_cast<const TI*>(p.q);
+    a.k = static_cast<const TI*>(p.k);
+    a.v = static_cast<const TI*>(p.v);
+    a.g = p.g;
+    a.beta = p.beta;
+    a.cu = p.cu_seqlens;
+    a.S0 = p.initial_state;
+    a.dO = static_cast<const TI*>(p.d_o);
+    a.dSf = p.d_final_state;
+    a.dq = static_cast<TI*>(p.dq);
+    a.dk = static_cast<TI*>(p.dk);
+    a.dv = static_cast<TI*>(p.dv);
+    a.dg = p.dg;
+    a.dbeta = p.dbeta;
+    a.dS0 = p.d_initial_state;
+    a.ck = static_cast<TI*>(p.workspace);
+    a.H = p.H;
+    const unsigned blocks = (unsigned)((int64_t)p.num_seqs * p.H);
+    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename TI>
+hipError_t run_bwd_t(const BackwardLaunch& p, hipStream_t s) {
+    if (p.dk_dim == 128 && p.dv_dim == 128) return run_bwd<TI, 128, 128>(p, s);
+    if (p.dk_dim == 128 && p.dv_dim == 64) return run_bwd<TI, 128, 64>(p, s);
+    if (p.dk_dim == 64 && p.dv_dim == 128) return run_bwd<TI, 64, 128>(p, s);
+    return run_bwd<TI, 64, 64>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardLaunch& p, hipStream_t s) {
+    if (p.num_seqs == 0) return hipSuccess;
+    return p.bf16 ? run_bwd_t<bf16>(p, s) : run_bwd_t<float>(p, s);
+}
+
+}  // namespace gdn

@@ -8,6 +8,8 @@ returns.  The draw order is fixed so a seed names one input set:
   2. q, k, v, the beta logits, the decay logits,
   3. the initial states (when asked for),
   4. decode draws, one block per step, in step order.
+The backward pass's incoming gradients (make_cotangents) come from a
+generator of their own.
 
 Distributions
   q, k   N(0, 1) per element, L2-normalised over the key channels of each
@@ -144,6 +146,22 @@ def make_decode_steps(N: int, H: int, dk: int, dv: int, steps: int, dtype=torch.
         beta, g, z = _draw_gates(gen, (N, H), (N, H) if head_gate else (N, H, dk), gate, a_min, device)
         out.append(DecodeStep(q, k, v, g, beta, z.to(torch.bfloat16) if logits else None))
     return S0, out
+
+
+def make_cotangents(T: int, num_seqs: int, H: int, dk: int, dv: int, dtype=torch.bfloat16,
+                    final_state: bool = True, seed: int = 0, device="cpu",
+                    gen: Optional[torch.Generator] = None):
+    """Gradients flowing into the layer's outputs, for the backward pass:
+    dL/do ~ N(0, 1) [T, H, dv] cast to dtype (RNE), and dL/d(final state)
+    ~ 0.02 * N(0, 1) [num_seqs, H, dk, dv] fp32 (None when final_state is False),
+    drawn in that order."""
+    if gen is None:
+        gen = make_generator(seed, device)
+    d_o = torch.randn((T, H, dv), generator=gen, device=device, dtype=torch.float32).to(dtype)
+    dSf = None
+    if final_state:
+        dSf = 0.02 * torch.randn((num_seqs, H, dk, dv), generator=gen, device=device, dtype=torch.float32)
+    return d_o, dSf
 
 
 # Named workloads.  Each entry: how to build its inputs from a generator.

@@ -192,6 +192,57 @@ int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const voi
                           float gate_param, const float* beta, float* state, void* o, int32_t N, int32_t H,
                           int32_t d_k, int32_t d_v, int32_t dtype, void* stream);
 
+/* Device scratch bytes gdn_prefill_backward needs: one state per 16-token
+ * sub-chunk and head in the input dtype, (T_total / 16 + num_seqs) * H * d_k
+ * * d_v * (2 for GDN_BF16, 4 for GDN_F32).  Depends on the arguments only; 0
+ * for invalid arguments. */
+size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k,
+                                            int32_t d_v, int32_t dtype);
+
+/* Gradients of gdn_prefill.  The method is trained by back-propagation
+ * ("Architecture Evolution and Training Engineering for Trillion-Scale Sparse
+ * Multimodal Models", section 3.3; "What a Trillion-Parameter MoE Model
+ * Reveals About the Next Stage of LLM Scaling", section 3.2); given the
+ * gradient of a loss with respect to every output o and to the final states,
+ * this returns its gradient with respect to q, k, v, g, beta and the initial
+ * states: the exact adjoint of the recurrence above, up to rounding.
+ *
+ *   q, k, v, g, beta, cu_seqlens, num_seqs, T_total, initial_state, H, d_k,
+ *   d_v, dtype     as for gdn_prefill (the forward inputs; initial_state may
+ *                  be NULL for zeros)
+ *   d_o            device, [T_total, H, d_v], dtype: dL/do
+ *   d_final_state  device, [num_seqs, H, d_k, d_v] fp32: dL/d(final state),
+ *                  or NULL for zero
+ *   dq, dk         device, [T_total, H, d_k], dtype (written)
+ *   dv             device, [T_total, H, d_v], dtype (written)
+ *   dg             device, [T_total, H, d_k] fp32 (written)
+ *   dbeta          device, [T_total, H] fp32, 4-byte aligned (written)
+ *   d_initial_state  device, [num_seqs, H, d_k, d_v] fp32 (written), or NULL
+ *                  when not wanted; written also when initial_state is NULL
+ *                  (the gradient at a zero initial state)
+ *   workspace      device scratch of at least
+ *                  gdn_prefill_backward_workspace_bytes(...) bytes, 16-byte
+ *                  aligned, owned by the caller; contents on entry ignored,
+ *                  on return unspecified.  Two calls in flight at once need
+ *                  two workspaces.
+ * Outputs must not alias inputs.  Alignment and validation (GDN_VALIDATE=1)
+ * as for gdn_prefill.
+ *
+ * Method: a forward sweep stores the state at the start of every 16-token
+ * sub-chunk; a reverse sweep carries dL/dS from the last sub-chunk to the
+ * first and forms each sub-chunk's gradients from its start state with
+ * dense matrix-core tiles.  The cumulative decay inside a 16-token window is
+ * referred to the window's middle token, so every factor stays within
+ * e^-40 .. e^40 for g in [-5, 0] (the 16-token tile bound of
+ * "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate the New
+ * Generation", section 3.1). */
+int32_t gdn_prefill_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
+                             const float* initial_state, const void* d_o, const float* d_final_state, void* dq,
+                             void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state, int32_t H,
+                             int32_t d_k, int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

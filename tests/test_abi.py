@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(lib):
     names = gdn.exported_symbols_in_header()
     assert set(names) == {"gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free",
                           "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_prefill_logits",
-                          "gdn_decode_logits", "gdn_prefill_head_gate", "gdn_decode_head_gate"}
+                          "gdn_decode_logits", "gdn_prefill_head_gate", "gdn_decode_head_gate",
+                          "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -159,3 +160,29 @@ def test_head_gate_argument_errors(lib):
     assert dec() == INVALID
     assert dec(q=P, g=NUL) == INVALID
     assert dec(N=0) == OK
+
+
+def _backward(lib, p=NUL, cu=NUL, n=1, T=10, H=4, dk=64, dv=64, dt=1, ws=NUL, wsb=0):
+    return lib.gdn_prefill_backward(p, p, p, p, p, cu, n, T, NUL, p, NUL, p, p, p, p, p, NUL, H, dk, dv, dt, ws, wsb,
+                                    None)
+
+
+def test_backward_workspace_bytes(lib):
+    f = lib.gdn_prefill_backward_workspace_bytes
+    # one state per 16-token sub-chunk and head, in the input dtype
+    assert f(1024, 2, 4, 128, 128, 1) == (1024 // 16 + 2) * 4 * 128 * 128 * 2
+    assert f(1000, 3, 2, 64, 128, 0) == (1000 // 16 + 3) * 2 * 64 * 128 * 4
+    assert f(-1, 1, 1, 64, 64, 1) == 0
+    assert f(16, 1, 1, 64, 64, 9) == 0
+
+
+def test_backward_argument_errors(lib):
+    assert _backward(lib) == INVALID                      # null pointers with T > 0
+    assert _backward(lib, dk=96) == UNSUPPORTED
+    assert _backward(lib, dv=32) == UNSUPPORTED
+    assert _backward(lib, dt=7) == UNSUPPORTED
+    assert _backward(lib, n=-1) == INVALID
+    assert _backward(lib, H=0) == INVALID
+    assert _backward(lib, n=0, T=3) == INVALID
+    assert _backward(lib, p=BAD, cu=BAD) == INVALID       # misaligned
+    assert _backward(lib, n=0, T=0) == OK                 # nothing to do

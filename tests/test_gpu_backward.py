@@ -1,0 +1,121 @@
+"""GPU parity of gdn_prefill_backward: dq, dk, dv, dg, dbeta and the initial
+state's gradient through the C-ABI against the fp64 oracle's reverse-mode
+recurrence (oracle.backward, pinned by finite differences and hand-derived
+cases in test_oracle_backward_pins.py), element by element on seeded inputs.
+Sizes span several 16-token sub-chunks and ragged tails."""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_linear_amd as gdn
+import oracle
+from gated_delta_rule_linear_amd import inputs
+from helpers import TOL, assert_close, log, np64, to_device
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+
+
+def _oracle_grads(x, d_o, dSf):
+    cu = x.cu_seqlens.cpu().numpy().astype(np.int32)
+    return oracle.backward(np64(x.q), np64(x.k), np64(x.v), np64(x.g), np64(x.beta), cu, np64(d_o),
+                           initial_state=None if x.initial_state is None else np64(x.initial_state),
+                           d_final_state=None if dSf is None else np64(dSf))
+
+
+def _run(x, d_o, dSf):
+    out = gdn.gdn_prefill_backward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, d_o, initial_state=x.initial_state,
+                                   d_final_state=dSf)
+    torch.cuda.synchronize()
+    return dict(zip(NAMES, out))
+
+
+def _check(got, ref, tol):
+    for name in NAMES:
+        assert_close(name, np64(got[name]), ref[name], tol)
+
+
+def _case(lengths, H, dk, dv, dtype, gate="amin", init=True, final=True, seed=0, x=None):
+    log(f"backward case lengths={lengths} H={H} dk={dk} dv={dv} {dtype} gate={gate} init={init} final={final}")
+    if x is None:
+        x = inputs.make_prefill_inputs(lengths, H, dk, dv, dtype=dtype, gate=gate, init_state=init, seed=seed)
+    d_o, dSf = inputs.make_cotangents(x.T_total, x.num_seqs, H, dk, dv, dtype=dtype, final_state=final,
+                                      seed=seed + 100)
+    ref = _oracle_grads(x, d_o, dSf)
+    to_device(x)
+    d_o = d_o.cuda()
+    dSf = None if dSf is None else dSf.cuda()
+    got = _run(x, d_o, dSf)
+    _check(got, ref, TOL[dtype])
+    return x, d_o, dSf, got
+
+
+def test_small_fp32():
+    # one 256-token sequence, 2 heads, d = 64, fp32, zero initial state
+    _case([256], 2, 64, 64, torch.float32, init=False)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_bf16_ragged(dk, dv):
+    _case([1, 15, 16, 17, 63, 0, 130], 3, dk, dv, torch.bfloat16, seed=1)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_fp32_ragged(dk, dv):
+    _case([1, 15, 16, 17, 63, 0, 130], 2, dk, dv, torch.float32, seed=2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_pages_gate(dtype):
+    # g = -5 sigmoid(z): about -40 per 16 tokens, the range the window reference is built for
+    _case([320, 100], 2, 128, 128, dtype, gate="pages", seed=3)
+
+
+def test_no_initial_state_no_final_gradient():
+    _case([200, 33], 2, 128, 128, torch.bfloat16, init=False, final=False, seed=4)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gate_endpoints_and_beta_extremes(dtype):
+    # g exactly -5 and exactly 0 on alternating 16-token blocks, beta in {0, 1}
+    lengths = [96, 50]
+    x = inputs.make_prefill_inputs(lengths, 2, 64, 64, dtype=dtype, gate="pages", init_state=True, seed=5)
+    T = x.T_total
+    blk = (torch.arange(T) // 16) % 2
+    x.g = torch.where(blk[:, None, None] == 0, torch.tensor(-5.0), torch.tensor(0.0)).expand(T, 2, 64).contiguous()
+    x.beta = (torch.arange(T * 2).reshape(T, 2) % 3 != 0).to(torch.float32)
+    _case(lengths, 2, 64, 64, dtype, x=x, seed=5)
+
+
+def test_deterministic():
+    x = inputs.make_prefill_inputs([300, 77], 2, 128, 128, dtype=torch.bfloat16, init_state=True, seed=6)
+    d_o, dSf = inputs.make_cotangents(x.T_total, x.num_seqs, 2, 128, 128, seed=106)
+    to_device(x)
+    d_o, dSf = d_o.cuda(), dSf.cuda()
+    a = _run(x, d_o, dSf)
+    b = _run(x, d_o, dSf)
+    for name in NAMES:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_without_initial_state_gradient_output():
+    x = inputs.make_prefill_inputs([40], 1, 64, 64, dtype=torch.bfloat16, init_state=True, seed=7)
+    d_o, dSf = inputs.make_cotangents(x.T_total, 1, 1, 64, 64, seed=107)
+    ref = _oracle_grads(x, d_o, dSf)
+    to_device(x)
+    out = gdn.gdn_prefill_backward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, d_o.cuda(),
+                                   initial_state=x.initial_state, d_final_state=dSf.cuda(),
+                                   want_d_initial_state=False)
+    torch.cuda.synchronize()
+    assert out[5] is None
+    for name, t in zip(NAMES[:5], out[:5]):
+        assert_close(name, np64(t), ref[name], TOL[torch.bfloat16])
