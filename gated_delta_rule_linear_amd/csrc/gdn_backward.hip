@@ -116,6 +116,7 @@ struct Four<float> {
     __device__ __forceinline__ static floatx4 t(floatx4 x) { return x; }
 };
 
+
 __device__ __forceinline__ floatx4 exp2v(floatx4 x) {
     return floatx4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]), __builtin_amdgcn_exp2f(x[2]),
                    __builtin_amdgcn_exp2f(x[3])};
@@ -123,22 +124,49 @@ __device__ __forceinline__ floatx4 exp2v(floatx4 x) {
 __device__ __forceinline__ floatx2 exp2v(floatx2 x) {
     return floatx2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])};
 }
-// Sum over the 16 lanes of a lane group (lanes 16g .. 16g+15); every lane gets it.
+
+// Cross-lane moves inside a 16-lane row (lanes 16g .. 16g+15) with DPP.
+// row_newbcast:J: every lane reads lane J of its row; row_ror:N: lane i reads
+// lane (i + N) mod 16; row_shl:N: lane i reads lane i + N, 0 past the row end.
+template <int CTRL, bool ZERO>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, ZERO));
+}
+// Sum over the 16 lanes of a row; every lane of the row gets it.
 __device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 1, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 8, 16);
+    x += dpp<0x128, false>(x);
+    x += dpp<0x124, false>(x);
+    x += dpp<0x122, false>(x);
+    x += dpp<0x121, false>(x);
     return x;
 }
-// Suffix sum inside a lane group: lane r gets the sum over lanes r .. 15.
-__device__ __forceinline__ float suffix16(float x, int r) {
-#pragma unroll
-    for (int d = 1; d < 16; d *= 2) {
-        const float y = __shfl_down(x, d, 16);
-        if (r + d < 16) x += y;
-    }
+// Suffix sum inside a row: lane r gets the sum over lanes r .. 15.
+__device__ __forceinline__ float suffix16(float x) {
+    x += dpp<0x101, true>(x);
+    x += dpp<0x102, true>(x);
+    x += dpp<0x104, true>(x);
+    x += dpp<0x108, true>(x);
     return x;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Workgroup barrier for LDS traffic only: each wave waits for its own LDS
+// operations, not for its outstanding global memory operations, so a copy
+// into LDS issued earlier (global_load_lds) stays in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ const __attribute__((address_space(1))) void* as_global(const void* p) {
+    return (const __attribute__((address_space(1))) void*)p;
+}
+__device__ __forceinline__ __attribute__((address_space(3))) void* as_lds(void* p) {
+    return (__attribute__((address_space(3))) void*)p;
 }
 
 template <typename TI>
@@ -165,14 +193,20 @@ struct BArgs {
 // LDS layout.  "Natural" matrices are row-major over the contraction index
 // with one 16-byte pad per row; "transposed" ones hold 16 tokens per key
 // channel.  FULL: the gradient kernel's buffers; otherwise the forward one's.
+// With bf16 inputs (STAGE) the next sub-chunk's raw inputs, and in the
+// gradient kernel its checkpoint, are copied into a staging area by DMA
+// while the current one is processed.
 template <typename TI, int DK, int DV, bool FULL>
 struct BCfg {
     typedef Mma<TI> M;
+    static constexpr bool STAGE = sizeof(TI) == 2;
     static constexpr int NW = DV / 16, NT = 64 * NW;
     static constexpr int ES = (int)sizeof(TI);
     static constexpr int KSTEP = M::KSTEP, KW = M::KW;
     static constexpr int KM = DK / KSTEP, KV = DV / KSTEP;  // MFMA steps over d_k, d_v
     static constexpr int RT = DK / 16;                      // 16-row tiles of d_k
+    static constexpr int TPW = (RT + NW - 1) / NW;          // key-channel tiles per wave
+    static constexpr int UNR = KW == 8 ? 8 : 4;             // unroll of the contraction loops
     static constexpr int SK = DK + 16 / ES, SV = DV + 16 / ES;
     static constexpr int B_NK = CB * SK * ES, B_TK = DK * CB * ES, B_NV = CB * SV * ES, B_FS = DK * SV * ES;
     static constexpr int OFF_KN = 0;                                   // k~ natural [16][SK]
@@ -196,20 +230,66 @@ struct BCfg {
     static constexpr int OFF_N = OFF_DB + NW * CB * 4;                 // -diag(b) KK [16][16]
     static constexpr int OFF_MI = OFF_N + 256 * 4;                     // M [16][16]
     static constexpr int OFF_MT = OFF_MI + 256 * 4;                    // M^T [16][16]
-    static constexpr int LDS = OFF_MT + 256 * 4;
+    // staging (rows packed back to back, as the DMA writes them)
+    static constexpr int OFF_STG = OFF_MT + 256 * 4;
+    static constexpr int ST_G = OFF_STG;                               // g [16][DK] fp32
+    static constexpr int ST_K = ST_G + CB * DK * 4;                    // k [16][DK]
+    static constexpr int ST_Q = ST_K + CB * DK * ES;                   // q [16][DK]   (FULL)
+    static constexpr int ST_O = ST_Q + (FULL ? CB * DK * ES : 0);      // dO [16][DV]  (FULL)
+    static constexpr int ST_V = ST_O + (FULL ? CB * DV * ES : 0);      // v [16][DV]
+    static constexpr int ST_B = ST_V + CB * DV * ES;                   // beta [64] (lanes past 16 repeat the last row)
+    static constexpr int ST_C = ST_B + 256;                            // checkpoint [DK][DV]  (FULL)
+    static constexpr int LDS = STAGE ? ST_C + (FULL ? DK * DV * ES : 0) : OFF_STG;
     static_assert(B_NK % 16 == 0 && B_TK % 16 == 0 && B_NV % 16 == 0 && B_FS % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Per-sub-chunk preparation, shared by both kernels.  Ends with M and M^T in
-// LDS, every operand stored, and (wave 0) KK in `kk` (accumulator layout:
-// lane r + 16g holds KK[4g + i][r]).
+// DMA of ROWS rows of RB bytes (row t at src + t * stride, t clamped to
+// L - 1) into LDS rows packed back to back at dst; one wave instruction moves
+// 1 KiB, and wave w issues instructions w, w + NW, ...
+template <int RB, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(const void* src, size_t stride, int L, char* dst, int w, int lane) {
+    constexpr int LPR = RB / 16, RPI = 64 / LPR, NI = ROWS * RB / 1024;
+    static_assert(RB % 16 == 0 && RB <= 1024 && (ROWS * RB) % 1024 == 0, "copy shape");
+#pragma unroll
+    for (int i0 = 0; i0 < NI; i0 += NW) {
+        const int i = i0 + w;
+        if (NI % NW == 0 || i < NI) {
+            const int t = min(i * RPI + lane / LPR, L - 1);
+            __builtin_amdgcn_global_load_lds(
+                as_global(static_cast<const char*>(src) + (size_t)t * stride + (lane % LPR) * 16),
+                as_lds(dst + i * 1024), 16, 0, 0);
+        }
+    }
+}
+
+// Copy of one sub-chunk's raw inputs (t0: first token, L tokens) into the staging area.
 template <typename TI, int DK, int DV, bool FULL>
-__device__ __forceinline__ void prep(const BArgs<TI>& a, char* smem, int h, int64_t t0, int L, int tid, int w,
-                                     floatx4& kk) {
+__device__ __forceinline__ void dma_inputs(const BArgs<TI>& a, char* smem, int h, int64_t t0, int L, int w,
+                                           int lane) {
+    typedef BCfg<TI, DK, DV, FULL> P;
+    const int H = a.H;
+    const size_t row0 = (size_t)t0 * H + h;
+    dma_rows<DK * 4, CB, P::NW>(a.g + row0 * DK, (size_t)H * DK * 4, L, smem + P::ST_G, w, lane);
+    dma_rows<DK * P::ES, CB, P::NW>(a.k + row0 * DK, (size_t)H * DK * P::ES, L, smem + P::ST_K, w, lane);
+    if constexpr (FULL) {
+        dma_rows<DK * P::ES, CB, P::NW>(a.q + row0 * DK, (size_t)H * DK * P::ES, L, smem + P::ST_Q, w, lane);
+        dma_rows<DV * P::ES, CB, P::NW>(a.dO + row0 * DV, (size_t)H * DV * P::ES, L, smem + P::ST_O, w, lane);
+    }
+    dma_rows<DV * P::ES, CB, P::NW>(a.v + row0 * DV, (size_t)H * DV * P::ES, L, smem + P::ST_V, w, lane);
+    if (w == P::NW - 1)
+        __builtin_amdgcn_global_load_lds(as_global(a.beta + row0 + (size_t)min(lane, L - 1) * H),
+                                         as_lds(smem + P::ST_B), 4, 0, 0);
+}
+
+// Steps 1 and 2 of a sub-chunk (both kernels): cumulative log-decay, the
+// per-channel vectors, beta, the operands; dO into its padded layout (FULL);
+// this lane's 4 values of v (rows 4g + i, column col0 + r).  Ends with an
+// LDS barrier after the operands.
+template <typename TI, int DK, int DV, bool FULL>
+__device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, int64_t t0, int L, int tid, int col0) {
     typedef BCfg<TI, DK, DV, FULL> P;
     typedef typename Two<TI>::type T2;
-    typedef Mma<TI> M;
     const int H = a.H;
     const int lane = tid & 63, r = lane & 15, g = lane >> 4;
     float* sG = reinterpret_cast<float*>(smem + P::OFF_G);
@@ -225,19 +305,27 @@ __device__ __forceinline__ void prep(const BArgs<TI>& a, char* smem, int h, int6
     TI* sKT = reinterpret_cast<TI*>(smem + P::OFF_KT);
     TI* sQT = reinterpret_cast<TI*>(smem + P::OFF_QT);
     TI* sDO = reinterpret_cast<TI*>(smem + P::OFF_DO);
-    float* sN = reinterpret_cast<float*>(smem + P::OFF_N);
-    float* sMI = reinterpret_cast<float*>(smem + P::OFF_MI);
-    float* sMT = reinterpret_cast<float*>(smem + P::OFF_MT);
+    const float* stg_g = reinterpret_cast<const float*>(smem + P::ST_G);
+    const TI* stg_k = reinterpret_cast<const TI*>(smem + P::ST_K);
+    const TI* stg_q = reinterpret_cast<const TI*>(smem + P::ST_Q);
+    const TI* stg_o = reinterpret_cast<const TI*>(smem + P::ST_O);
+    const TI* stg_v = reinterpret_cast<const TI*>(smem + P::ST_V);
+    const float* stg_b = reinterpret_cast<const float*>(smem + P::ST_B);
     const size_t row0 = (size_t)t0 * H + h;  // (token, head) row of the sub-chunk's first token
+    auto clampt = [&](int t) { return t < L ? t : L - 1; };
 
-    // 1. cumulative log-decay of each key channel (rows past L read g = 0)
+    // 1. cumulative log-decay of each key channel (rows past L count as g = 0)
     if (tid < DK) {
-        const float* gp = a.g + row0 * DK + tid;
+        float x[CB];
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            if constexpr (P::STAGE) x[t] = stg_g[t * DK + tid];
+            else x[t] = a.g[(row0 + (size_t)clampt(t) * H) * DK + tid];
+        }
         float G = 0.f, m = 0.f;
 #pragma unroll
         for (int t = 0; t < CB; ++t) {
-            const float x = t < L ? gp[(size_t)t * H * DK] : 0.f;
-            G = __builtin_fmaf(x, LOG2E_B, G);
+            G = __builtin_fmaf(t < L ? x[t] : 0.f, LOG2E_B, G);
             sG[t * DK + tid] = G;
             if (t == 7) m = G;
         }
@@ -248,34 +336,58 @@ __device__ __forceinline__ void prep(const BArgs<TI>& a, char* smem, int h, int6
     }
     if (tid >= DK && tid < DK + CB) {
         const int t = tid - DK;
-        sBETA[t] = t < L ? a.beta[row0 + (size_t)t * H] : 0.f;
+        float b;
+        if constexpr (P::STAGE) b = stg_b[t];
+        else b = a.beta[row0 + (size_t)clampt(t) * H];
+        sBETA[t] = t < L ? b : 0.f;
     }
     if constexpr (FULL) {
-        // dO rows into LDS (16-byte pieces; rows past L are zero)
+        // dO rows into the padded layout (16-byte pieces; rows past L are zero)
         constexpr int PER = 16 / P::ES, NPR = DV / PER;
-        for (int i = tid; i < CB * NPR; i += P::NT) {
-            const int t = i / NPR, c = (i % NPR) * PER;
-            floatx4 x = zero4();
-            if (t < L) x = *reinterpret_cast<const floatx4*>(a.dO + (row0 + (size_t)t * H) * DV + c);
-            *reinterpret_cast<floatx4*>(sDO + t * P::SV + c) = x;
+#pragma unroll
+        for (int i0 = 0; i0 < CB * NPR; i0 += P::NT) {
+            const int i = i0 + tid;
+            if ((CB * NPR) % P::NT == 0 || i < CB * NPR) {
+                const int t = i / NPR, c = (i % NPR) * PER;
+                floatx4 x;
+                if constexpr (P::STAGE) x = *reinterpret_cast<const floatx4*>(stg_o + t * DV + c);
+                else x = *reinterpret_cast<const floatx4*>(a.dO + (row0 + (size_t)clampt(t) * H) * DV + c);
+                *reinterpret_cast<floatx4*>(sDO + t * P::SV + c) = t < L ? x : zero4();
+            }
         }
     }
-    __syncthreads();
+    floatx4 vv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        float x;
+        if constexpr (P::STAGE) x = to_f32(stg_v[t * DV + col0 + r]);
+        else x = to_f32(a.v[(row0 + (size_t)clampt(t) * H) * DV + col0 + r]);
+        vv[i] = t < L ? x : 0.f;
+    }
+    lds_barrier();
 
     // 2. operands: (token pair tp, channel pair cp) per item
-    for (int i = tid; i < 4 * DK; i += P::NT) {
+#pragma unroll
+    for (int i0 = 0; i0 < 4 * DK; i0 += P::NT) {
+        const int i = i0 + tid;
+        if ((4 * DK) % P::NT != 0 && i >= 4 * DK) break;
         const int cp = i % (DK / 2), tp = i / (DK / 2), c0 = 2 * cp;
         const floatx2 ml = *reinterpret_cast<const floatx2*>(sML + c0);
         floatx2 kt[2], kh[2], qt[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int t = 2 * tp + u;
-            const size_t off = (row0 + (size_t)t * H) * DK + c0;
-            floatx2 kk2 = floatx2{0.f, 0.f}, qq2 = floatx2{0.f, 0.f};
-            if (t < L) {
+            floatx2 kk2, qq2 = floatx2{0.f, 0.f};
+            if constexpr (P::STAGE) {
+                kk2 = Two<TI>::f(*reinterpret_cast<const T2*>(stg_k + t * DK + c0));
+                if constexpr (FULL) qq2 = Two<TI>::f(*reinterpret_cast<const T2*>(stg_q + t * DK + c0));
+            } else {
+                const size_t off = (row0 + (size_t)clampt(t) * H) * DK + c0;
                 kk2 = Two<TI>::f(*reinterpret_cast<const T2*>(a.k + off));
                 if constexpr (FULL) qq2 = Two<TI>::f(*reinterpret_cast<const T2*>(a.q + off));
             }
+            if (t >= L) kk2 = qq2 = floatx2{0.f, 0.f};
             const floatx2 G = *reinterpret_cast<const floatx2*>(sG + t * DK + c0);
             const floatx2 e = exp2v(G - ml), ei = exp2v(ml - G);
             kt[u] = kk2 * e;
@@ -297,46 +409,55 @@ __device__ __forceinline__ void prep(const BArgs<TI>& a, char* smem, int h, int6
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
+    return vv;
+}
 
-    // 3. (wave 0) KK = k~ k^T, the unit lower-triangular I + diag(b) KK and its inverse M
-    if (w == 0) {
-        floatx4 acc = zero4();
+// Step 3 of a sub-chunk (one wave): KK = k~ k^T (returned in accumulator
+// layout, lane r + 16g holding KK[4g + i][r], strictly lower part), the unit
+// lower-triangular I + diag(b) KK and its inverse M by forward substitution
+// (lane r + 16g carries M[r][4g .. 4g+3]; row j of M is final once rows < j
+// are applied, and is read from lane j of the row with a DPP broadcast), then
+// M and M^T into LDS.
+template <typename TI, int DK, int DV, bool FULL>
+__device__ __forceinline__ floatx4 gram_inverse(char* smem, int lane) {
+    typedef BCfg<TI, DK, DV, FULL> P;
+    typedef Mma<TI> M;
+    const int r = lane & 15, g = lane >> 4;
+    const TI* sKN = reinterpret_cast<const TI*>(smem + P::OFF_KN);
+    const TI* sHN = reinterpret_cast<const TI*>(smem + P::OFF_HN);
+    const float* sBETA = reinterpret_cast<const float*>(smem + P::OFF_BETA);
+    float* sN = reinterpret_cast<float*>(smem + P::OFF_N);
+    float* sMI = reinterpret_cast<float*>(smem + P::OFF_MI);
+    float* sMT = reinterpret_cast<float*>(smem + P::OFF_MT);
+    floatx4 kk = zero4();
+#pragma unroll(P::UNR)
+    for (int mm = 0; mm < P::KM; ++mm) kk = M::mma(lds_nat(sKN + r * P::SK, mm, g), lds_nat(sHN + r * P::SK, mm, g), kk);
 #pragma unroll
-        for (int mm = 0; mm < P::KM; ++mm)
-            acc = M::mma(lds_nat(sKN + r * P::SK, mm, g), lds_nat(sHN + r * P::SK, mm, g), acc);
-        // lane r + 16g: KK[t = 4g + i][s = r]
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * g + i;
-            acc[i] = r < t ? acc[i] : 0.f;
-            sN[t * 16 + r] = -sBETA[t] * acc[i];
-        }
-        kk = acc;
-        // forward substitution, rows in order: lane r + 16g carries M[r][4g .. 4g+3];
-        // row j of M is final once rows < j are applied.
-        const floatx4 n0 = *reinterpret_cast<const floatx4*>(sN + r * 16);
-        const floatx4 n1 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 4);
-        const floatx4 n2 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 8);
-        const floatx4 n3 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 12);
-        const float nr[16] = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
-                              n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
-        floatx4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = r == 4 * g + e ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < 15; ++j) {
-            floatx4 y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = __shfl(x[e], j + 16 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(nr[j], y[e], x[e]);
-        }
-        *reinterpret_cast<floatx4*>(sMI + r * 16 + 4 * g) = x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sMT[(4 * g + e) * 16 + r] = x[e];
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        kk[i] = r < t ? kk[i] : 0.f;
+        sN[t * 16 + r] = -sBETA[t] * kk[i];
     }
-    __syncthreads();
+    // (lanes of this wave read what other lanes wrote: LDS operations of one wave complete in order)
+    const floatx4 n0 = *reinterpret_cast<const floatx4*>(sN + r * 16);
+    const floatx4 n1 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 4);
+    const floatx4 n2 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 8);
+    const floatx4 n3 = *reinterpret_cast<const floatx4*>(sN + r * 16 + 12);
+    const float nr[16] = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                          n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+    floatx4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = r == 4 * g + e ? 1.f : 0.f;
+    static_for<0, 15>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(nr[j], dpp<0x150 + j, false>(x[e]), x[e]);
+    });
+    *reinterpret_cast<floatx4*>(sMI + r * 16 + 4 * g) = x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sMT[(4 * g + e) * 16 + r] = x[e];
+    return kk;
 }
 
 // Forward pass storing checkpoints: one workgroup per (sequence, head).
@@ -345,9 +466,9 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
     typedef BCfg<TI, DK, DV, false> P;
     typedef Mma<TI> M;
     typedef K16<TI> K;
-    __shared__ __attribute__((aligned(16))) char smem[P::LDS];
-    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
+    const int tid0 = threadIdx.x, g0 = (tid0 & 63) >> 4, r0 = tid0 & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
     const int n = blockIdx.x / H, h = blockIdx.x - n * H;
     const int64_t tb = a.cu[n], te = a.cu[n + 1];
@@ -366,34 +487,44 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[(16 * rt + 4 * g + i) * DV + col0 + r] : 0.f;
+        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[(16 * rt + 4 * g0 + i) * DV + col0 + r0] : 0.f;
 
+    if constexpr (P::STAGE)
+        if (te > tb) dma_inputs<TI, DK, DV, false>(a, smem, h, tb, (int)(te - tb < CB ? te - tb : CB), w, tid0 & 63);
     TI* ck = a.ck + (((size_t)(tb >> 4) + n) * H + h) * DK * DV;
     for (int64_t t0 = tb; t0 < te; t0 += CB, ck += (size_t)H * DK * DV) {
         const int L = (int)(te - t0 < CB ? te - t0 : CB);
+        // lane-derived values are recomputed every iteration (opaque to the
+        // compiler), so addresses built from them are not hoisted out of the
+        // loop and held in registers for its whole length
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+        if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of the sub-chunk has landed
+        lds_barrier();  // ... and every wave's; the previous sub-chunk is done with LDS
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) ck[(16 * rt + 4 * g + i) * DV + col0 + r] = from_f32<TI>(S[rt][i]);
-        __syncthreads();  // the previous sub-chunk is done with LDS
-        floatx4 kk;
-        prep<TI, DK, DV, false>(a, smem, h, t0, L, tid, w, kk);
-
+        const floatx4 vv = prep<TI, DK, DV, false>(a, smem, h, t0, L, tid, col0);
+        if constexpr (P::STAGE) {
+            const int64_t t1 = t0 + CB;
+            if (t1 < te) dma_inputs<TI, DK, DV, false>(a, smem, h, t1, (int)(te - t1 < CB ? te - t1 : CB), w, lane);
+        }
+        if (w == 0) (void)gram_inverse<TI, DK, DV, false>(smem, lane);
         // R = V - k~ (E S), own columns
-        floatx4 es[P::RT];
-#pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt) es[rt] = S[rt] * *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
         floatx4 acc = zero4();
+#pragma unroll(P::UNR)
+        for (int mm = 0; mm < P::KM; ++mm) {
+            floatx4 es[P::RT];
 #pragma unroll
-        for (int mm = 0; mm < P::KM; ++mm)
+            for (int rt = 0; rt < P::RT; ++rt) es[rt] = S[rt] * *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
             acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
+        }
         floatx4 br;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * g + i;
-            const float vv = t < L ? to_f32(a.v[((size_t)(t0 + t) * H + h) * DV + col0 + r]) : 0.f;
-            br[i] = sBETA[t] * (vv - acc[i]);
-        }
+        for (int i = 0; i < 4; ++i) br[i] = sBETA[4 * g + i] * (vv[i] - acc[i]);
+        lds_barrier();  // M is ready
         // U = M diag(b) R
         const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
         const typename K::frag bu = K::cvt(U);
@@ -409,6 +540,8 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
 }
 
 // Reverse pass: one workgroup per (sequence, head), sub-chunks last to first.
+// A sub-chunk's outputs are stored at the start of the next iteration, after
+// its wait for the copies in flight, so that wait does not include them.
 template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
     typedef BCfg<TI, DK, DV, true> P;
@@ -416,9 +549,9 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
     typedef typename M::frag frag;
     typedef K16<TI> K;
     typedef Four<TI> F4;
-    __shared__ __attribute__((aligned(16))) char smem[P::LDS];
-    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
+    const int tid0 = threadIdx.x, g0 = (tid0 & 63) >> 4, r0 = tid0 & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
     const int n = blockIdx.x / H, h = blockIdx.x - n * H;
     const int64_t tb = a.cu[n], te = a.cu[n + 1];
@@ -437,12 +570,13 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
     const TI* sKT = reinterpret_cast<const TI*>(smem + P::OFF_KT);
     const TI* sHT = reinterpret_cast<const TI*>(smem + P::OFF_HT);
     const TI* sQT = reinterpret_cast<const TI*>(smem + P::OFF_QT);
-    TI* sDO = reinterpret_cast<TI*>(smem + P::OFF_DO);
+    const TI* sDO = reinterpret_cast<const TI*>(smem + P::OFF_DO);
     TI* sU = reinterpret_cast<TI*>(smem + P::OFF_U);
     TI* sDR = reinterpret_cast<TI*>(smem + P::OFF_DR);
     TI* sFS = reinterpret_cast<TI*>(smem + P::OFF_FS);
     const float* sMI = reinterpret_cast<const float*>(smem + P::OFF_MI);
     const float* sMT = reinterpret_cast<const float*>(smem + P::OFF_MT);
+    const TI* stg_c = reinterpret_cast<const TI*>(smem + P::ST_C);
 
     // dS = dL/d(state at the end of the current sub-chunk), own columns
     floatx4 dS[P::RT];
@@ -450,65 +584,118 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dS[rt][i] = dsf ? dsf[(16 * rt + 4 * g + i) * DV + col0 + r] : 0.f;
+        for (int i = 0; i < 4; ++i) dS[rt][i] = dsf ? dsf[(16 * rt + 4 * g0 + i) * DV + col0 + r0] : 0.f;
 
-    const int64_t nsub = (te - tb + CB - 1) / CB;
-    for (int64_t c = nsub - 1; c >= 0; --c) {
-        const int64_t t0 = tb + CB * c;
-        const int L = (int)(te - t0 < CB ? te - t0 : CB);
-        const size_t row0 = (size_t)t0 * H + h;
-        const TI* ck = a.ck + ((((size_t)(tb >> 4) + n + (size_t)c) * H + h) * DK * DV);
-        // start state of the sub-chunk, own columns
-        floatx4 es[P::RT];
+    // outputs of the previous iteration, stored at the start of the next one
+    floatx4 o_dv = zero4(), o_db = zero4();
+    floatx4 o_dq[P::TPW], o_dk[P::TPW], o_dg[P::TPW];
 #pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) es[rt][i] = to_f32(ck[(16 * rt + 4 * g + i) * DV + col0 + r]);
-        floatx4 vv;
+    for (int j = 0; j < P::TPW; ++j) o_dq[j] = o_dk[j] = o_dg[j] = zero4();
+    size_t o_row0 = 0;
+    int o_L = 0;  // 0: nothing pending
+    auto flush = [&](int r, int g) {
+        if (o_L == 0) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
-            vv[i] = t < L ? to_f32(a.v[(row0 + (size_t)t * H) * DV + col0 + r]) : 0.f;
+            if (t < o_L) a.dv[(o_row0 + (size_t)t * H) * DV + col0 + r] = from_f32<TI>(o_dv[i]);
+            if (w == 0 && r == 0 && t < o_L) a.dbeta[o_row0 + (size_t)t * H] = o_db[i];
         }
-        __syncthreads();  // the previous sub-chunk is done with LDS
+#pragma unroll
+        for (int j = 0; j < P::TPW; ++j) {
+            const int it = w + P::NW * j;
+            if (it < P::RT && r < o_L) {
+                const size_t off = (o_row0 + (size_t)r * H) * DK + 16 * it + 4 * g;
+                *reinterpret_cast<typename F4::type*>(a.dq + off) = F4::t(o_dq[j]);
+                *reinterpret_cast<typename F4::type*>(a.dk + off) = F4::t(o_dk[j]);
+                *reinterpret_cast<floatx4*>(a.dg + off) = o_dg[j];
+            }
+        }
+    };
+    auto slot = [&](int64_t c) { return a.ck + ((((size_t)(tb >> 4) + n + (size_t)c) * H + h) * DK * DV); };
+    auto sub_len = [&](int64_t c) { return (int)(te - (tb + CB * c) < CB ? te - (tb + CB * c) : CB); };
+
+    const int64_t nsub = (te - tb + CB - 1) / CB;
+    if constexpr (P::STAGE) {
+        if (nsub > 0) {
+            dma_inputs<TI, DK, DV, true>(a, smem, h, tb + CB * (nsub - 1), sub_len(nsub - 1), w, tid0 & 63);
+            dma_rows<DV * P::ES, DK, P::NW>(slot(nsub - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w, tid0 & 63);
+        }
+    }
+    for (int64_t c = nsub - 1; c >= 0; --c) {
+        const int64_t t0 = tb + CB * c;
+        const int L = sub_len(c);
+        const size_t row0 = (size_t)t0 * H + h;
+        const TI* ck = slot(c);
+        // lane-derived values are recomputed every iteration (opaque to the
+        // compiler), so addresses built from them are not hoisted out of the
+        // loop and held in registers for its whole length
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+        if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
+        lds_barrier();  // ... and every wave's; the previous sub-chunk is done with LDS
+        flush(r, g);
+        const floatx4 vv = prep<TI, DK, DV, true>(a, smem, h, t0, L, tid, col0);
+        if constexpr (P::STAGE)
+            if (c > 0) dma_inputs<TI, DK, DV, true>(a, smem, h, t0 - CB, sub_len(c - 1), w, lane);
         floatx4 kk = zero4();
-        prep<TI, DK, DV, true>(a, smem, h, t0, L, tid, w, kk);
+        if (w == 0) kk = gram_inverse<TI, DK, DV, true>(smem, lane);
 
         // ---- 3. value-column steps (own columns) -------------------------------
         // P = lower(q~ k^T): lane r + 16g holds P[t = 4g + i][s = r]
         floatx4 Pa = zero4();
-#pragma unroll
+#pragma unroll(P::UNR)
         for (int mm = 0; mm < P::KM; ++mm)
             Pa = M::mma(lds_nat(sQN + r * P::SK, mm, g), lds_nat(sHN + r * P::SK, mm, g), Pa);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Pa[i] = r <= 4 * g + i ? Pa[i] : 0.f;
-        // R = V - k~ (E S0)
-#pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt) es[rt] *= *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
+        // R = V - k~ (E S0), S0 from the checkpoint
         floatx4 acc = zero4();
+#pragma unroll(P::UNR)
+        for (int mm = 0; mm < P::KM; ++mm) {
+            // only the accumulator tiles this step reads are loaded (bf16: tiles 2mm, 2mm + 1; fp32: tile mm / 4)
+            floatx4 es[P::RT];
 #pragma unroll
-        for (int mm = 0; mm < P::KM; ++mm)
+            for (int rt = 0; rt < P::RT; ++rt) es[rt] = zero4();
+#pragma unroll
+            for (int rt = 0; rt < P::RT; ++rt) {
+                const bool used = P::KW == 8 ? (rt >> 1) == mm : (rt == (mm >> 2));
+                if (used) {
+                    const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * rt + 4 * g + i;
+                        const float s = P::STAGE ? to_f32(stg_c[row * DV + col0 + r]) : to_f32(ck[row * DV + col0 + r]);
+                        es[rt][i] = em[i] * s;
+                    }
+                }
+            }
             acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
+        }
         floatx4 R, br;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             R[i] = vv[i] - acc[i];
             br[i] = sBETA[4 * g + i] * R[i];
         }
-        const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
         // own columns of dO
         floatx4 dOc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dOc[i] = to_f32(sDO[(4 * g + i) * P::SV + col0 + r]);
-        // F dS
-        floatx4 fds[P::RT];
-#pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt) fds[rt] = dS[rt] * *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
         // dU = P^T dO + k^ (F dS)
         floatx4 dU = K::mma(K::cvt(Pa), K::cvt(dOc), zero4());
+#pragma unroll(P::UNR)
+        for (int mm = 0; mm < P::KM; ++mm) {
+            floatx4 fds[P::RT];
 #pragma unroll
-        for (int mm = 0; mm < P::KM; ++mm)
+            for (int rt = 0; rt < P::RT; ++rt) fds[rt] = dS[rt] * *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
             dU = M::mma(lds_perm(sHN + r * P::SK, mm, g), acc_perm<TI>(fds, mm, P::RT), dU);
+        }
+        lds_barrier();  // M is ready; every read of the staged checkpoint is done
+        if constexpr (P::STAGE)
+            if (c > 0) dma_rows<DV * P::ES, DK, P::NW>(slot(c - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w, lane);
+        const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
         // dRm = M^T dU, dR = diag(b) dRm = dv
         const floatx4 dRm = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMT + r * 16 + 4 * g)), K::cvt(dU), zero4());
         floatx4 dR, ndR;
@@ -517,15 +704,17 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             const int t = 4 * g + i;
             dR[i] = sBETA[t] * dRm[i];
             ndR[i] = -dR[i];
-            if (t < L) a.dv[(row0 + (size_t)t * H) * DV + col0 + r] = from_f32<TI>(dR[i]);
             const float p = sum16(R[i] * dRm[i]);
             if (r == 0) sDB[w * CB + t] = p;
         }
+        o_dv = dR;
         // exchange: F dS, U, dRm (natural layouts) for the key-channel products
 #pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt)
+        for (int rt = 0; rt < P::RT; ++rt) {
+            const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sFS[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(fds[rt][i]);
+            for (int i = 0; i < 4; ++i) sFS[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(ff[i] * dS[rt][i]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sU[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(U[i]);
@@ -543,12 +732,12 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
                 dS[rt] = gm * dS[rt] + em * x;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 4. key-channel outputs ------------------------------------------
-        // token-pair matrices over d_v (same in every wave)
+        // token-pair matrices over d_v (the same in every wave)
         floatx4 dPT = zero4(), dPa = zero4(), dAa = zero4(), dAT = zero4();
-#pragma unroll
+#pragma unroll(P::UNR)
         for (int mm = 0; mm < P::KV; ++mm) {
             const frag fo = lds_nat(sDO + r * P::SV, mm, g);
             const frag fu = lds_nat(sU + r * P::SV, mm, g);
@@ -575,20 +764,23 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             for (int i = 0; i < 4; ++i) {
                 const int t = 4 * g + i;
                 float p = sum16(dAa[i] * kk[i]);
-                if (r == 0 && t < L) {
-                    for (int ww = 0; ww < P::NW; ++ww) p += sDB[ww * CB + t];
-                    a.dbeta[row0 + (size_t)t * H] = p;
-                }
+#pragma unroll
+                for (int ww = 0; ww < P::NW; ++ww) p += sDB[ww * CB + t];
+                o_db[i] = p;
             }
         }
         const typename K::frag bPT = K::cvt(dPT), bKKT = K::cvt(dKKT), bKKa = K::cvt(dKKa), bPa = K::cvt(dPa);
-        for (int it = w; it < P::RT; it += P::NW) {
+#pragma unroll
+        for (int j = 0; j < P::TPW; ++j) {
+            const int it = w + P::NW * j;
+            if (P::RT % P::NW != 0 && it >= P::RT) break;
             const int i0 = 16 * it;
-            // state rows i0 + r, from the checkpoint (Z, X) and from LDS (Y)
+            // state rows i0 + r: the checkpoint (Z, X; from global memory, where its
+            // copy into LDS left it in the cache) and F dS (Y)
             const TI* ckrow = ck + (size_t)(i0 + r) * DV;
             floatx4 z1 = zero4(), x1 = zero4(), y1 = zero4();
             float d1 = 0.f;  // sum_j (F dS)[i0 + r][j] S0[i0 + r][j] over this lane's j
-#pragma unroll
+#pragma unroll(P::UNR)
             for (int mm = 0; mm < P::KV; ++mm) {
                 const frag fs0 = *reinterpret_cast<const frag*>(ckrow + mm * P::KSTEP + g * P::KW);
                 const frag ffs = lds_nat(sFS + (i0 + r) * P::SV, mm, g);
@@ -619,28 +811,27 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             const floatx4 Gl = *reinterpret_cast<const floatx4*>(sG + r * DK + i0 + 4 * g);
             const floatx4 ml = *reinterpret_cast<const floatx4*>(sML + i0 + 4 * g);
             const floatx4 ef = exp2v(Gl - ml), eb = exp2v(ml - Gl);
-            const floatx4 dq = ef * Z, dk = ef * X + eb * Y;
+            o_dq[j] = ef * Z;
+            o_dk[j] = ef * X + eb * Y;
             floatx4 dG = qtil * Z + ktil * X - khat * Y;
             floatx4 d2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) d2[e] = sum16(khat[e] * y1[e]);
             const floatx4 d15 = *reinterpret_cast<const floatx4*>(sDG15 + i0 + 4 * g) + d2;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dG[e] = suffix16(dG[e], r) + d15[e];
-            if (r < L) {
-                const size_t off = (row0 + (size_t)r * H) * DK + i0 + 4 * g;
-                *reinterpret_cast<typename F4::type*>(a.dq + off) = F4::t(dq);
-                *reinterpret_cast<typename F4::type*>(a.dk + off) = F4::t(dk);
-                *reinterpret_cast<floatx4*>(a.dg + off) = dG;
-            }
+            for (int e = 0; e < 4; ++e) dG[e] = suffix16(dG[e]) + d15[e];
+            o_dg[j] = dG;
         }
+        o_row0 = row0;
+        o_L = L;
     }
+    flush(r0, g0);
     if (a.dS0) {
         float* dst = a.dS0 + (size_t)blockIdx.x * DK * DV;
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g + i) * DV + col0 + r] = dS[rt][i];
+            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g0 + i) * DV + col0 + r0] = dS[rt][i];
     }
 }
 
