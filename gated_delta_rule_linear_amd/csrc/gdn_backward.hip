@@ -207,6 +207,7 @@ struct BCfg {
     static constexpr int RT = DK / 16;                      // 16-row tiles of d_k
     static constexpr int TPW = (RT + NW - 1) / NW;          // key-channel tiles per wave
     static constexpr int UNR = KW == 8 ? 8 : 4;             // unroll of the contraction loops
+    static constexpr int UNR4 = KW == 8 ? 2 : 4;            // ... of the key-channel outputs' pass over d_v
     static constexpr int SK = DK + 16 / ES, SV = DV + 16 / ES;
     static constexpr int B_NK = CB * SK * ES, B_TK = DK * CB * ES, B_NV = CB * SV * ES, B_FS = DK * SV * ES;
     static constexpr int OFF_KN = 0;                                   // k~ natural [16][SK]
@@ -230,8 +231,9 @@ struct BCfg {
     static constexpr int OFF_N = OFF_DB + NW * CB * 4;                 // -diag(b) KK [16][16]
     static constexpr int OFF_MI = OFF_N + 256 * 4;                     // M [16][16]
     static constexpr int OFF_MT = OFF_MI + 256 * 4;                    // M^T [16][16]
+    static constexpr int OFF_P = OFF_MT + 256 * 4;                     // P, accumulator layout by lane (FULL)
     // staging (rows packed back to back, as the DMA writes them)
-    static constexpr int OFF_STG = OFF_MT + 256 * 4;
+    static constexpr int OFF_STG = OFF_P + (FULL ? 256 * 4 : 0);
     static constexpr int ST_G = OFF_STG;                               // g [16][DK] fp32
     static constexpr int ST_K = ST_G + CB * DK * 4;                    // k [16][DK]
     static constexpr int ST_Q = ST_K + CB * DK * ES;                   // q [16][DK]   (FULL)
@@ -239,7 +241,10 @@ struct BCfg {
     static constexpr int ST_V = ST_O + (FULL ? CB * DV * ES : 0);      // v [16][DV]
     static constexpr int ST_B = ST_V + CB * DV * ES;                   // beta [64] (lanes past 16 repeat the last row)
     static constexpr int ST_C = ST_B + 256;                            // checkpoint [DK][DV]  (FULL)
-    static constexpr int LDS = STAGE ? ST_C + (FULL ? DK * DV * ES : 0) : OFF_STG;
+    static constexpr int STG_END = STAGE ? ST_C + (FULL ? DK * DV * ES : 0) : OFF_STG;
+    // forward kernel: the state in the input dtype, rows padded, for coalesced checkpoint stores
+    static constexpr int OFF_CK = STG_END;
+    static constexpr int LDS = OFF_CK + (FULL ? 0 : DK * SV * ES);
     static_assert(B_NK % 16 == 0 && B_TK % 16 == 0 && B_NV % 16 == 0 && B_FS % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -247,7 +252,10 @@ struct BCfg {
 // DMA of ROWS rows of RB bytes (row t at src + t * stride, t clamped to
 // L - 1) into LDS rows packed back to back at dst; one wave instruction moves
 // 1 KiB, and wave w issues instructions w, w + NW, ...
-template <int RB, int ROWS, int NW>
+// With SWZ the 16-byte pieces of each row are permuted, piece p of row t landing
+// in slot p ^ (t mod LPR) (see swz_off): reads of one column down 16 rows, and
+// of the same piece of 16 rows, then fall in different LDS banks.
+template <int RB, int ROWS, int NW, bool SWZ = false>
 __device__ __forceinline__ void dma_rows(const void* src, size_t stride, int L, char* dst, int w, int lane) {
     constexpr int LPR = RB / 16, RPI = 64 / LPR, NI = ROWS * RB / 1024;
     static_assert(RB % 16 == 0 && RB <= 1024 && (ROWS * RB) % 1024 == 0, "copy shape");
@@ -255,12 +263,19 @@ __device__ __forceinline__ void dma_rows(const void* src, size_t stride, int L, 
     for (int i0 = 0; i0 < NI; i0 += NW) {
         const int i = i0 + w;
         if (NI % NW == 0 || i < NI) {
-            const int t = min(i * RPI + lane / LPR, L - 1);
+            const int row = i * RPI + lane / LPR, t = min(row, L - 1);
+            const int piece = SWZ ? (lane % LPR) ^ (row % LPR) : lane % LPR;
             __builtin_amdgcn_global_load_lds(
-                as_global(static_cast<const char*>(src) + (size_t)t * stride + (lane % LPR) * 16),
+                as_global(static_cast<const char*>(src) + (size_t)t * stride + piece * 16),
                 as_lds(dst + i * 1024), 16, 0, 0);
         }
     }
+}
+// Byte offset of element `col` of row `row` in a swizzled copy of rows of RB bytes (elements of ES bytes).
+template <int RB, int ES>
+__device__ __forceinline__ int swz_off(int row, int col) {
+    constexpr int LPR = RB / 16, PER = 16 / ES;
+    return row * RB + (((col / PER) ^ (row % LPR)) * 16) + (col % PER) * ES;
 }
 
 // Copy of one sub-chunk's raw inputs (t0: first token, L tokens) into the staging area.
@@ -480,6 +495,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
     const TI* sKN = reinterpret_cast<const TI*>(smem + P::OFF_KN);
     const TI* sHT = reinterpret_cast<const TI*>(smem + P::OFF_HT);
     const float* sMI = reinterpret_cast<const float*>(smem + P::OFF_MI);
+    TI* sCK = reinterpret_cast<TI*>(smem + P::OFF_CK);
 
     // state, own columns: S[rt][i] = S[16 rt + 4g + i][col0 + r]
     floatx4 S[P::RT];
@@ -502,14 +518,24 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
         if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of the sub-chunk has landed
         lds_barrier();  // ... and every wave's; the previous sub-chunk is done with LDS
+        // the checkpoint: own columns into LDS, then whole rows out in 16-byte pieces
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ck[(16 * rt + 4 * g + i) * DV + col0 + r] = from_f32<TI>(S[rt][i]);
+            for (int i = 0; i < 4; ++i) sCK[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(S[rt][i]);
         const floatx4 vv = prep<TI, DK, DV, false>(a, smem, h, t0, L, tid, col0);
         if constexpr (P::STAGE) {
             const int64_t t1 = t0 + CB;
             if (t1 < te) dma_inputs<TI, DK, DV, false>(a, smem, h, t1, (int)(te - t1 < CB ? te - t1 : CB), w, lane);
+        }
+        {
+            constexpr int PER = 16 / P::ES, NPR = DV / PER;
+#pragma unroll
+            for (int k = 0; k < DK * NPR / P::NT; ++k) {
+                const int id = tid + P::NT * k, row = id / NPR, pc = id % NPR;
+                *reinterpret_cast<floatx4*>(ck + row * DV + pc * PER) =
+                    *reinterpret_cast<const floatx4*>(sCK + row * P::SV + pc * PER);
+            }
         }
         if (w == 0) (void)gram_inverse<TI, DK, DV, false>(smem, lane);
         // R = V - k~ (E S), own columns
@@ -576,6 +602,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
     TI* sFS = reinterpret_cast<TI*>(smem + P::OFF_FS);
     const float* sMI = reinterpret_cast<const float*>(smem + P::OFF_MI);
     const float* sMT = reinterpret_cast<const float*>(smem + P::OFF_MT);
+    float* sP = reinterpret_cast<float*>(smem + P::OFF_P);
     const TI* stg_c = reinterpret_cast<const TI*>(smem + P::ST_C);
 
     // dS = dL/d(state at the end of the current sub-chunk), own columns
@@ -619,7 +646,8 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
     if constexpr (P::STAGE) {
         if (nsub > 0) {
             dma_inputs<TI, DK, DV, true>(a, smem, h, tb + CB * (nsub - 1), sub_len(nsub - 1), w, tid0 & 63);
-            dma_rows<DV * P::ES, DK, P::NW>(slot(nsub - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w, tid0 & 63);
+            dma_rows<DV * P::ES, DK, P::NW, true>(slot(nsub - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w,
+                                                  tid0 & 63);
         }
     }
     for (int64_t c = nsub - 1; c >= 0; --c) {
@@ -643,13 +671,16 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         if (w == 0) kk = gram_inverse<TI, DK, DV, true>(smem, lane);
 
         // ---- 3. value-column steps (own columns) -------------------------------
-        // P = lower(q~ k^T): lane r + 16g holds P[t = 4g + i][s = r]
-        floatx4 Pa = zero4();
+        // (wave 1) P = lower(q~ k^T): lane r + 16g holds P[t = 4g + i][s = r]; shared through LDS
+        if (w == 1) {
+            floatx4 Pa = zero4();
 #pragma unroll(P::UNR)
-        for (int mm = 0; mm < P::KM; ++mm)
-            Pa = M::mma(lds_nat(sQN + r * P::SK, mm, g), lds_nat(sHN + r * P::SK, mm, g), Pa);
+            for (int mm = 0; mm < P::KM; ++mm)
+                Pa = M::mma(lds_nat(sQN + r * P::SK, mm, g), lds_nat(sHN + r * P::SK, mm, g), Pa);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Pa[i] = r <= 4 * g + i ? Pa[i] : 0.f;
+            for (int i = 0; i < 4; ++i) Pa[i] = r <= 4 * g + i ? Pa[i] : 0.f;
+            *reinterpret_cast<floatx4*>(sP + 4 * lane) = Pa;
+        }
         // R = V - k~ (E S0), S0 from the checkpoint
         floatx4 acc = zero4();
 #pragma unroll(P::UNR)
@@ -666,7 +697,12 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int row = 16 * rt + 4 * g + i;
-                        const float s = P::STAGE ? to_f32(stg_c[row * DV + col0 + r]) : to_f32(ck[row * DV + col0 + r]);
+                        float s;
+                        if constexpr (P::STAGE)
+                            s = to_f32(*reinterpret_cast<const TI*>(reinterpret_cast<const char*>(stg_c) +
+                                                                     swz_off<DV * P::ES, P::ES>(row, col0 + r)));
+                        else
+                            s = to_f32(ck[row * DV + col0 + r]);
                         es[rt][i] = em[i] * s;
                     }
                 }
@@ -683,8 +719,8 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         floatx4 dOc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dOc[i] = to_f32(sDO[(4 * g + i) * P::SV + col0 + r]);
-        // dU = P^T dO + k^ (F dS)
-        floatx4 dU = K::mma(K::cvt(Pa), K::cvt(dOc), zero4());
+        // dU = k^ (F dS) + P^T dO (the second term once P is shared)
+        floatx4 dU = zero4();
 #pragma unroll(P::UNR)
         for (int mm = 0; mm < P::KM; ++mm) {
             floatx4 fds[P::RT];
@@ -694,8 +730,10 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         }
         lds_barrier();  // M is ready; every read of the staged checkpoint is done
         if constexpr (P::STAGE)
-            if (c > 0) dma_rows<DV * P::ES, DK, P::NW>(slot(c - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w, lane);
+            if (c > 0)
+                dma_rows<DV * P::ES, DK, P::NW, true>(slot(c - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w, lane);
         const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
+        dU = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sP + 4 * lane)), K::cvt(dOc), dU);
         // dRm = M^T dU, dR = diag(b) dRm = dv
         const floatx4 dRm = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMT + r * 16 + 4 * g)), K::cvt(dU), zero4());
         floatx4 dR, ndR;
@@ -735,9 +773,20 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         lds_barrier();
 
         // ---- 4. key-channel outputs ------------------------------------------
-        // token-pair matrices over d_v (the same in every wave)
+        // Contractions over d_v, one pass over the value rows: the token-pair
+        // matrices (the same in every wave) and, for each of this wave's
+        // key-channel tiles i0 = 16 it, the products with state rows i0 + r (the
+        // checkpoint, from global memory where its copy into LDS left it in the
+        // cache, and F dS).
         floatx4 dPT = zero4(), dPa = zero4(), dAa = zero4(), dAT = zero4();
-#pragma unroll(P::UNR)
+        floatx4 z1[P::TPW], x1[P::TPW], y1[P::TPW];
+        float d1[P::TPW];  // sum_j (F dS)[i0 + r][j] S0[i0 + r][j] over this lane's j
+#pragma unroll
+        for (int j = 0; j < P::TPW; ++j) {
+            z1[j] = x1[j] = y1[j] = zero4();
+            d1[j] = 0.f;
+        }
+#pragma unroll(P::UNR4)
         for (int mm = 0; mm < P::KV; ++mm) {
             const frag fo = lds_nat(sDO + r * P::SV, mm, g);
             const frag fu = lds_nat(sU + r * P::SV, mm, g);
@@ -746,6 +795,23 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             dPa = M::mma(fo, fu, dPa);  // dP[t = 4g + i][s = r]
             dAa = M::mma(fr, fu, dAa);  // -dA[t = 4g + i][s = r]
             dAT = M::mma(fu, fr, dAT);  // -dA[t = r][s = 4g + i]
+#pragma unroll
+            for (int j = 0; j < P::TPW; ++j) {
+                const int it = w + P::NW * j;
+                if (P::RT % P::NW != 0 && it >= P::RT) break;
+                const int i0 = 16 * it;
+                const frag fs0 = *reinterpret_cast<const frag*>(ck + (size_t)(i0 + r) * DV + mm * P::KSTEP + g * P::KW);
+                const frag ffs = lds_nat(sFS + (i0 + r) * P::SV, mm, g);
+                z1[j] = M::mma(fs0, fo, z1[j]);
+                x1[j] = M::mma(fs0, fr, x1[j]);
+                y1[j] = M::mma(ffs, fu, y1[j]);
+                if constexpr (P::KW == 1) {
+                    d1[j] += (float)fs0 * (float)ffs;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < P::KW; ++e) d1[j] += (float)fs0[e] * (float)ffs[e];
+                }
+            }
         }
         floatx4 dKKa, dKKT;
 #pragma unroll
@@ -775,35 +841,17 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             const int it = w + P::NW * j;
             if (P::RT % P::NW != 0 && it >= P::RT) break;
             const int i0 = 16 * it;
-            // state rows i0 + r: the checkpoint (Z, X; from global memory, where its
-            // copy into LDS left it in the cache) and F dS (Y)
-            const TI* ckrow = ck + (size_t)(i0 + r) * DV;
-            floatx4 z1 = zero4(), x1 = zero4(), y1 = zero4();
-            float d1 = 0.f;  // sum_j (F dS)[i0 + r][j] S0[i0 + r][j] over this lane's j
-#pragma unroll(P::UNR)
-            for (int mm = 0; mm < P::KV; ++mm) {
-                const frag fs0 = *reinterpret_cast<const frag*>(ckrow + mm * P::KSTEP + g * P::KW);
-                const frag ffs = lds_nat(sFS + (i0 + r) * P::SV, mm, g);
-                z1 = M::mma(fs0, lds_nat(sDO + r * P::SV, mm, g), z1);
-                x1 = M::mma(fs0, lds_nat(sDR + r * P::SV, mm, g), x1);
-                y1 = M::mma(ffs, lds_nat(sU + r * P::SV, mm, g), y1);
-                if constexpr (P::KW == 1) {
-                    d1 += (float)fs0 * (float)ffs;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < P::KW; ++e) d1 += (float)fs0[e] * (float)ffs[e];
-                }
-            }
-            d1 += __shfl_xor(d1, 16);
-            d1 += __shfl_xor(d1, 32);
-            if (g == 0) sDG15[i0 + r] = d1 * sEM[i0 + r];
+            float dd = d1[j];
+            dd += __shfl_xor(dd, 16);
+            dd += __shfl_xor(dd, 32);
+            if (g == 0) sDG15[i0 + r] = dd * sEM[i0 + r];
             // lane r + 16g: key channel i = i0 + 4g + e, token t = r
             const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + i0 + 4 * g);
             const float bt = sBETA[r];
-            floatx4 Z = em * z1, X = -(bt * em) * x1;
+            floatx4 Z = em * z1[j], X = -(bt * em) * x1[j];
             Z = K::mma(K::load(sHT + (i0 + r) * CB + 4 * g), bPT, Z);
             X = K::mma(K::load(sHT + (i0 + r) * CB + 4 * g), bKKT, X);
-            floatx4 Y = K::mma(K::load(sKT + (i0 + r) * CB + 4 * g), bKKa, y1);
+            floatx4 Y = K::mma(K::load(sKT + (i0 + r) * CB + 4 * g), bKKa, y1[j]);
             Y = K::mma(K::load(sQT + (i0 + r) * CB + 4 * g), bPa, Y);
             const floatx4 khat = F4::f(*reinterpret_cast<const typename F4::type*>(sHN + r * P::SK + i0 + 4 * g));
             const floatx4 ktil = F4::f(*reinterpret_cast<const typename F4::type*>(sKN + r * P::SK + i0 + 4 * g));
@@ -816,7 +864,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             floatx4 dG = qtil * Z + ktil * X - khat * Y;
             floatx4 d2;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) d2[e] = sum16(khat[e] * y1[e]);
+            for (int e = 0; e < 4; ++e) d2[e] = sum16(khat[e] * y1[j][e]);
             const floatx4 d15 = *reinterpret_cast<const floatx4*>(sDG15 + i0 + 4 * g) + d2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dG[e] = suffix16(dG[e]) + d15[e];
