@@ -50,6 +50,7 @@ METRIC = "prefill tokens/s (H=32,d=128,T=64K bf16) + decode HBM GB/s; % of roofl
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published (no sparsity)
 KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp", "gdn_kernels.h"]
+BACKWARD_SOURCES = ["gdn_backward.hip", "gdn_backward.h", "gdn_mfma.h", "gdn_device.h", "gdn_api_backward.cpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -68,15 +69,34 @@ def prefill_flops(T_tokens: int, H: int, dk: int, dv: int, C: int = 64):
     return T_tokens * H * per
 
 
+def backward_bytes(T_tokens: int, H: int, dk: int, dv: int, n_seqs: int, elt: int = 2, init_state: bool = False,
+                   d_final: bool = True):
+    """Algorithmic HBM bytes of one backward launch: q, k, v, dL/do, g, beta read once; dq, dk, dv, dg,
+    dbeta written once; per (sequence, head) the initial state and dL/d(final state) read and the initial
+    state's gradient written.  (The checkpoints the kernels keep are the implementation's, not counted.)"""
+    per_head_token = elt * (2 * dk + 2 * dv) + 4 * dk + 4 + elt * (2 * dk + dv) + 4 * dk + 4
+    states = n_seqs * H * dk * dv * 4 * (1 + (1 if init_state else 0) + (1 if d_final else 0))
+    return T_tokens * H * per_head_token + states
+
+
+def backward_flops(T_tokens: int, H: int, dk: int, dv: int, C: int = 16):
+    """Matrix-core flops of one backward launch as the kernels form it, per 16-token sub-chunk: nine
+    state-sized products (forward replay k~ S and k^T U; in the gradient pass k~ S, k^ dS, q~^T dO,
+    k~^T dR, and the three key-channel products with the state rows) and twelve token-pair products
+    (16 x 16 over d_k or d_v, or over the 16 tokens), spread over C tokens."""
+    per = 9 * 2 * dk * dv + 12 * 2 * C * max(dk, dv)
+    return T_tokens * H * per
+
+
 def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int = 2):
     """Algorithmic HBM bytes of one decode launch: state read and written, token vectors read, o written."""
     per = 8 * dk * dv + elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv
     return N * H * per
 
 
-def source_hash() -> str:
+def source_hash(files=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "gated_delta_rule_linear_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -91,7 +111,7 @@ def measured_traffic(kernel: str):
     except (OSError, ValueError):
         return None
     e = t.get(kernel)
-    if not e or e.get("source_hash") != source_hash():
+    if not e or e.get("source_hash") != source_hash(BACKWARD_SOURCES if kernel == "backward" else None):
         return None
     return e.get("bytes_per_launch")
 
@@ -144,6 +164,26 @@ def cpu_baseline(x, tokens: int):
                       f"host {model or 'unknown CPU'}, {os.cpu_count()} logical CPUs visible"}
 
 
+def cpu_backward_baseline(x, d_o, dSf, tokens: int, heads: int):
+    """The oracle's reverse-mode recurrence (fp64, OpenMP over heads) on the host for the first
+    `tokens` tokens of the first `heads` heads of sequence 0."""
+    import oracle
+
+    oracle.build(force=False)
+    sl = lambda t: t[:tokens, :heads].to("cpu", torch.float64).numpy()
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    threads = max(1, min(os.cpu_count() or 1, heads, share))
+    t0 = time.perf_counter()
+    oracle.backward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), np.array([0, tokens], np.int32), sl(d_o),
+                    d_final_state=dSf[:1, :heads].to("cpu", torch.float64).numpy(), threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": tokens * heads / dt / x.q.shape[1], "unit": "tokens/s (all heads)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {tokens} tokens of sequence 0, {heads} of {x.q.shape[1]} heads, fp64 reverse-mode "
+                      f"recurrence (checkpoints every 64 tokens, OpenMP over heads), {dt:.2f} s wall; value is "
+                      f"head-tokens/s divided by the {x.q.shape[1]} heads"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +192,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=10)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
@@ -173,6 +215,7 @@ def main():
     # ---- prefill workload
     T, H, d = 65536, 32, 128
     x = inputs.make_workload("prefill_64k", seed=0, device=dev)
+    xf = x
     o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
     S = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
     ws_bytes = gdn.gdn_prefill_workspace_bytes(T, 1, H, d, d)
@@ -213,6 +256,52 @@ def main():
     dbytes = decode_bytes(N, Hd, d, d)
     dgbs = dbytes / (dms / 1e3) / 1e9
 
+    # ---- backward workload: four 8192-token sequences, 32 heads (a training batch)
+    bwd = None
+    if not args.no_backward:
+        del o
+        torch.cuda.empty_cache()
+        xb = inputs.make_workload("batch4_t8k", seed=0, device=dev)
+        Tb, nb = xb.T_total, xb.num_seqs
+        d_o, dSf = inputs.make_cotangents(Tb, nb, H, d, d, dtype=torch.bfloat16, seed=1, device=dev)
+        grads = [torch.empty_like(t) for t in (xb.q, xb.k, xb.v, xb.g, xb.beta)]
+        dS0 = torch.empty((nb, H, d, d), dtype=torch.float32, device=dev)
+        bws = torch.empty(gdn.gdn_prefill_backward_workspace_bytes(Tb, nb, H, d, d, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        lib = gdn.load_library()
+        ptr = lambda t: t.data_ptr()
+
+        def bstep():
+            st = lib.gdn_prefill_backward(ptr(xb.q), ptr(xb.k), ptr(xb.v), ptr(xb.g), ptr(xb.beta),
+                                          ptr(xb.cu_seqlens), nb, Tb, None, ptr(d_o), ptr(dSf), ptr(grads[0]),
+                                          ptr(grads[1]), ptr(grads[2]), ptr(grads[3]), ptr(grads[4]), ptr(dS0),
+                                          H, d, d, gdn.GDN_BF16, ptr(bws), bws.numel(), stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"gdn_prefill_backward: {st}")
+
+        bms = time_loop(bstep, args.backward_steps, 3, stream)
+        bbytes = backward_bytes(Tb, H, d, d, nb)
+        bflops = backward_flops(Tb, H, d, d)
+        bgbs = bbytes / (bms / 1e3) / 1e9
+        # sampled parity: sequence 0, head 0, whole sequence (a gradient depends on every later token)
+        su = lambda t: t[:8192, :1].to("cpu", torch.float64).numpy()
+        ref = oracle.backward(su(xb.q), su(xb.k), su(xb.v), su(xb.g), su(xb.beta), np.array([0, 8192], np.int32),
+                              su(d_o), d_final_state=dSf[:1, :1].to("cpu", torch.float64).numpy())
+        bpar = max(oracle.rel_err(su(gt), ref[nm]) for gt, nm in zip(grads, ("dq", "dk", "dv", "dg", "dbeta")))
+        bwd = {"workload": "batch4_t8k backward", "num_seqs": nb, "T": Tb, "H": H, "d_k": d, "d_v": d,
+               "ms_per_step": bms, "steps": args.backward_steps, "warmup": 3, "tokens_per_s": Tb / (bms / 1e3),
+               "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": bgbs / HBM_PEAK_GBS, "traffic": measured_traffic("backward"),
+                            "kernel": "gdn_prefill_backward call (bwd_states_kernel<bf16,128,128>, "
+                                      "bwd_grad_kernel<bf16,128,128>)",
+                            "algorithmic_bytes_per_launch": bbytes},
+               "mfma": {"flops_per_launch": bflops, "achieved": bflops / (bms / 1e3) / 1e12,
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": bflops / (bms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+               "parity_max_rel_err_seq0_head0": bpar}
+        if not args.no_cpu:
+            bwd["cpu_baseline"] = cpu_backward_baseline(xb, d_o, dSf, 2048, 16)
+
     traffic = measured_traffic("prefill")
     res = {
         "metric": METRIC,
@@ -245,8 +334,10 @@ def main():
                                     / (ms / 1e3),
         "parity": {"prefill_o_rel_err_head0_first2048": parity},
     }
+    if bwd is not None:
+        res["backward"] = bwd
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(x, min(args.cpu_tokens, T))
+        res["cpu_baseline"] = cpu_baseline(xf, min(args.cpu_tokens, T))
     print(json.dumps(res), flush=True)
 
 

@@ -129,3 +129,30 @@ def test_decode_512x32_steps():
         ref_o, ref_S = oracle.decode_step(pick(dr.q), pick(dr.k), pick(dr.v), pick(dr.g), pick(dr.beta), ref_S)
         assert_close(f"step {st}: o", np64(o[sample]), ref_o, 1e-2)
     assert_close("state", np64(state[sample]), ref_S, 1e-5)
+
+
+@pytest.mark.parametrize("name", ["batch4_t8k", "varlen64"])
+def test_backward_full_size_sampled_units(name):
+    # the whole workload through gdn_prefill_backward; two (sequence, head) units
+    # recomputed by the fp64 oracle's reverse-mode recurrence and compared in full
+    log(f"backward full size {name}")
+    x = inputs.make_workload(name, seed=0, device="cuda")
+    H, dk, dv = x.q.shape[1], x.q.shape[2], x.v.shape[2]
+    d_o, dSf = inputs.make_cotangents(x.T_total, x.num_seqs, H, dk, dv, dtype=x.q.dtype, seed=1, device="cuda")
+    out = gdn.gdn_prefill_backward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, d_o, initial_state=x.initial_state,
+                                   d_final_state=dSf)
+    torch.cuda.synchronize()
+    cu = x.cu_seqlens.cpu().numpy()
+    units = [(0, 0), (x.num_seqs - 1, H - 1)]
+    for n, h in units:
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = lambda t: np64(t[a:b, h:h + 1])
+        S0 = None if x.initial_state is None else np64(x.initial_state[n:n + 1, h:h + 1])
+        ref = oracle.backward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), np64(x.beta[a:b, h:h + 1]),
+                              np.array([0, b - a], np.int32), sl(d_o), initial_state=S0,
+                              d_final_state=np64(dSf[n:n + 1, h:h + 1]))
+        got = {"dq": sl(out[0]), "dk": sl(out[1]), "dv": sl(out[2]), "dg": sl(out[3]),
+               "dbeta": np64(out[4][a:b, h:h + 1]), "d_initial_state": np64(out[5][n:n + 1, h:h + 1])}
+        log(f"  unit (seq {n}, head {h}), {b - a} tokens")
+        for k in got:
+            assert_close(k, got[k], ref[k], TOL_BF16)
