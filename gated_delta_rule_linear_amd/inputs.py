@@ -23,6 +23,10 @@ Distributions
                     ("Lower-Bounded Decay Parameterization", eq. 1 of
                     "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate the
                     New Generation", section 3.1).
+           "softplus": g = -softplus(s * N(0,1)), the unbounded negative-softplus
+                    gate the bounded form replaces (same articles); s = softplus_scale
+                    (1 by default; larger values give steep decays, down to about
+                    -4s per token)
   S0     0.02 * N(0, 1), fp32, layout [num_seqs, H, d_k, d_v].
   g      (head_gate=True) one log-decay per (token, head), [T_total, H], same recipes.
   z      (logits=True) the decay logits N(0,1) themselves, cast to bf16 (RNE),
@@ -98,7 +102,7 @@ def _draw_qkv(gen, shape_k, shape_v, dtype, device):
     return q, k, v
 
 
-def _draw_gates(gen, shape_beta, shape_g, gate: str, a_min: float, device):
+def _draw_gates(gen, shape_beta, shape_g, gate: str, a_min: float, device, softplus_scale: float = 1.0):
     beta = torch.sigmoid(torch.randn(shape_beta, generator=gen, device=device, dtype=torch.float32))
     z = torch.randn(shape_g, generator=gen, device=device, dtype=torch.float32)
     if gate == "amin":
@@ -106,6 +110,8 @@ def _draw_gates(gen, shape_beta, shape_g, gate: str, a_min: float, device):
         g = torch.log(alpha)
     elif gate == "pages":
         g = G_MIN * torch.sigmoid(z)
+    elif gate == "softplus":
+        g = -torch.nn.functional.softplus(softplus_scale * z)
     else:
         raise ValueError(f"unknown gate recipe {gate!r}")
     return beta, g.contiguous(), z
@@ -114,14 +120,16 @@ def _draw_gates(gen, shape_beta, shape_g, gate: str, a_min: float, device):
 def make_prefill_inputs(lengths: Sequence[int], H: int, dk: int, dv: int, dtype=torch.bfloat16,
                         gate: str = "amin", a_min: float = 0.9, init_state: bool = False,
                         seed: int = 0, device="cpu", gen: Optional[torch.Generator] = None,
-                        logits: bool = False, head_gate: bool = False) -> PrefillInputs:
+                        logits: bool = False, head_gate: bool = False,
+                        softplus_scale: float = 1.0) -> PrefillInputs:
     """Packed prefill inputs for the given sequence lengths (draw order above)."""
     if gen is None:
         gen = make_generator(seed, device)
     lengths = [int(x) for x in lengths]
     T = sum(lengths)
     q, k, v = _draw_qkv(gen, (T, H, dk), (T, H, dv), dtype, device)
-    beta, g, z = _draw_gates(gen, (T, H), (T, H) if head_gate else (T, H, dk), gate, a_min, device)
+    beta, g, z = _draw_gates(gen, (T, H), (T, H) if head_gate else (T, H, dk), gate, a_min, device,
+                             softplus_scale)
     zb = z.to(torch.bfloat16) if logits else None
     del z
     S0 = None

@@ -243,6 +243,39 @@ int32_t gdn_prefill_backward(const void* q, const void* k, const void* v, const 
                              int32_t d_k, int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* The two ways of forming the intra-tile ("diagonal tile") pair terms that
+ * gdn_prefill_tiles offers (see there). */
+typedef enum gdn_tile_path { GDN_TILES_DENSE = 0, GDN_TILES_PAIRS = 1 } gdn_tile_path;
+
+/* Prefill in 16-token windows with a choice of diagonal-tile path: the
+ * comparison the pages describe between a bounded and an unbounded log-decay
+ * ("How to Think About Trillion-Parameter Sparse Multimodal LLMs", section 3;
+ * "What a Trillion-Parameter MoE Model Reveals About the Next Stage of LLM
+ * Scaling", section 3.2).  Inside a window the pair terms carry the decay
+ * e^{G_t - G_s} between two of its tokens (G the window's cumulative
+ * log-decay).
+ *   GDN_TILES_DENSE  the decay is split into a row factor e^{G_t - m} and a
+ *       column factor e^{m - G_s} about the window's middle token m and the
+ *       pair terms are dense matrix-core products.  Needs g in [-5, 0] (the
+ *       lower-bounded gate of "Trillion-Parameter MoE Multimodal LLMs: How to
+ *       Evaluate the New Generation", section 3.1, which keeps both factors
+ *       within e^-40 .. e^40); with a steeper gate the factors overflow and
+ *       the results are not finite.
+ *   GDN_TILES_PAIRS  each pair's decay is formed position by position on the
+ *       vector units: valid for any finite g <= 0, e.g. the unbounded
+ *       negative-softplus gate the pages replace.
+ * Arguments, layouts and the result are as for gdn_prefill (no workspace;
+ * final_state may alias initial_state), except g's domain: [-5, 0] for
+ * GDN_TILES_DENSE, any finite g <= 0 for GDN_TILES_PAIRS (checked under
+ * GDN_VALIDATE=1, GDN_ERR_DOMAIN).  An unknown tile_path is
+ * GDN_ERR_INVALID_ARG.  For bounded gates gdn_prefill is the faster path;
+ * this call exists for unbounded gates and for measuring what the
+ * position-pair path costs. */
+int32_t gdn_prefill_tiles(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
+                          const float* initial_state, float* final_state, void* o, int32_t H, int32_t d_k,
+                          int32_t d_v, int32_t dtype, int32_t tile_path, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

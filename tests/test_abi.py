@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free",
                           "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_prefill_logits",
                           "gdn_decode_logits", "gdn_prefill_head_gate", "gdn_decode_head_gate",
-                          "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward"}
+                          "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward", "gdn_prefill_tiles"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -186,3 +186,17 @@ def test_backward_argument_errors(lib):
     assert _backward(lib, n=0, T=3) == INVALID
     assert _backward(lib, p=BAD, cu=BAD) == INVALID       # misaligned
     assert _backward(lib, n=0, T=0) == OK                 # nothing to do
+
+
+def _tiles(lib, p=NUL, cu=NUL, n=1, T=10, H=4, dk=64, dv=64, dt=1, path=0):
+    return lib.gdn_prefill_tiles(p, p, p, p, p, cu, n, T, NUL, NUL, p, H, dk, dv, dt, path, None)
+
+
+def test_tiles_argument_errors(lib):
+    assert _tiles(lib) == INVALID                         # null pointers with T > 0
+    assert _tiles(lib, path=2) == INVALID                 # unknown tile path
+    assert _tiles(lib, dk=96) == UNSUPPORTED
+    assert _tiles(lib, dt=7) == UNSUPPORTED
+    assert _tiles(lib, H=0) == INVALID
+    assert _tiles(lib, p=BAD, cu=BAD, path=1) == INVALID  # misaligned
+    assert _tiles(lib, n=0, T=0, path=1) == OK

@@ -397,3 +397,44 @@ def test_generator_logits_match_its_gates():
         assert x.z.dtype == torch.bfloat16 and x.z.shape == x.g.shape
         g = oracle.gates_from_logits(_np(x.z), kind, p)
         assert np.max(np.abs(g - _np(x.g))) < 0.02 * abs(p if kind == oracle.GATE_SCALED_SIGMOID else math.log(p))
+
+
+def test_unbounded_softplus_gate_window_factors_leave_fp32_range():
+    # The pages' point about the unbounded negative-softplus gate: a 16-token
+    # window's split of e^{G_t - G_s} into e^{G_t - m} e^{m - G_s} (m the window's
+    # middle token) needs factors beyond fp32's range (e^88.72) once the decay is
+    # steep, while the pair decays themselves never exceed 1.
+    from gated_delta_rule_linear_amd import inputs
+
+    x = inputs.make_prefill_inputs([256], 2, 64, 64, dtype=torch.float32, gate="softplus", softplus_scale=8.0,
+                                   seed=3)
+    g = x.g.double().numpy()[:, 0, :]                      # [T, d_k], head 0
+    worst = 0.0
+    for w0 in range(0, 256, 16):
+        G = np.cumsum(g[w0:w0 + 16], axis=0)
+        worst = max(worst, float(np.max(np.abs(G - G[7]))))
+        pair = G[:, None, :] - G[None, :, :]               # G_t - G_s
+        assert np.all(pair[np.tril_indices(16)] <= 1e-12)  # s <= t: decay factor <= 1
+    assert worst > 88.72
+    # the bounded gate of the pages never does: |G_t - m| <= 8 * 5
+    xb = inputs.make_prefill_inputs([256], 2, 64, 64, dtype=torch.float32, gate="pages", seed=3)
+    gb = xb.g.double().numpy()[:, 0, :]
+    for w0 in range(0, 256, 16):
+        G = np.cumsum(gb[w0:w0 + 16], axis=0)
+        assert np.max(np.abs(G - G[7])) <= 40.0 + 1e-9
+
+
+def test_chunked_form_matches_recurrence_for_unbounded_gates():
+    # the oracle's chunked form uses only exponentials of differences (the
+    # position-pair decays); it must reproduce the token recurrence for steep
+    # negative-softplus gates too
+    from gated_delta_rule_linear_amd import inputs
+
+    x = inputs.make_prefill_inputs([80, 3, 16], 2, 8, 6, dtype=torch.float32, gate="softplus", softplus_scale=8.0,
+                                   init_state=True, seed=4)
+    f = lambda t: t.double().numpy()
+    cu = x.cu_seqlens.numpy()
+    o1, S1 = oracle.recurrent(f(x.q), f(x.k), f(x.v), f(x.g), f(x.beta), cu, initial_state=f(x.initial_state))
+    o2, S2 = oracle.chunked(f(x.q), f(x.k), f(x.v), f(x.g), f(x.beta), cu, initial_state=f(x.initial_state),
+                            chunk=16)
+    assert oracle.rel_err(o2, o1) < 1e-12 and oracle.rel_err(S2, S1) < 1e-12
