@@ -28,6 +28,13 @@ same workload.  One JSON line is printed.
 
 runs only a device-to-device copy of that many bytes (three times), the
 reference for scaling the counters.
+
+Two more legs follow in the same run, each on four 8,192-token sequences x
+32 heads and reported in objects of their own: "tile_paths" times
+gdn_prefill_tiles with dense window products and with position-pair decays
+(the diagonal-tile comparison), and "backward" times gdn_prefill_backward
+with its own roofline, sampled parity and host-oracle baseline.
+--no-tiles / --no-backward skip them.
 """
 
 from __future__ import annotations
@@ -194,6 +201,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=10)
+    ap.add_argument("--no-tiles", action="store_true")
+    ap.add_argument("--tiles-steps", type=int, default=10)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
@@ -256,13 +265,44 @@ def main():
     dbytes = decode_bytes(N, Hd, d, d)
     dgbs = dbytes / (dms / 1e3) / 1e9
 
+    del o
+    torch.cuda.empty_cache()
+    xb = inputs.make_workload("batch4_t8k", seed=0, device=dev)
+    Tb, nb = xb.T_total, xb.num_seqs
+
+    # ---- diagonal-tile paths: the same batch through gdn_prefill_tiles with dense window products and
+    # with position-pair decays (bounded gates, so both are valid), then gdn_prefill; and the pair path on
+    # the unbounded negative-softplus gate
+    tiles = None
+    if not args.no_tiles:
+        ob = torch.empty_like(xb.v)
+        tbytes = prefill_bytes(Tb, H, d, d, nb)
+
+        def tiles_step(path, xx):
+            return lambda: gdn.gdn_prefill_tiles(xx.q, xx.k, xx.v, xx.g, xx.beta, xx.cu_seqlens, path, o=ob,
+                                                 output_final_state=False, stream=stream)
+
+        tms_dense = time_loop(tiles_step(gdn.GDN_TILES_DENSE, xb), args.tiles_steps, 3, stream)
+        tms_pairs = time_loop(tiles_step(gdn.GDN_TILES_PAIRS, xb), args.tiles_steps, 3, stream)
+        tms_prefill = time_loop(lambda: gdn.gdn_prefill(xb.q, xb.k, xb.v, xb.g, xb.beta, xb.cu_seqlens, o=ob,
+                                                        output_final_state=False, stream=stream),
+                                args.tiles_steps, 3, stream)
+        xs = inputs.make_prefill_inputs([8192] * 4, H, d, d, dtype=torch.bfloat16, gate="softplus", seed=0,
+                                        device=dev)
+        tms_soft = time_loop(tiles_step(gdn.GDN_TILES_PAIRS, xs), args.tiles_steps, 3, stream)
+        del xs
+        frac = lambda ms: tbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
+        tiles = {"workload": "batch4_t8k forward, 16-token windows", "steps": args.tiles_steps, "warmup": 3,
+                 "dense_window_products_ms": tms_dense, "position_pairs_ms": tms_pairs,
+                 "position_pairs_over_dense": tms_pairs / tms_dense,
+                 "position_pairs_softplus_gate_ms": tms_soft, "gdn_prefill_ms": tms_prefill,
+                 "hbm_frac": {"dense": frac(tms_dense), "pairs": frac(tms_pairs), "gdn_prefill": frac(tms_prefill)},
+                 "algorithmic_bytes_per_launch": tbytes}
+        del ob
+
     # ---- backward workload: four 8192-token sequences, 32 heads (a training batch)
     bwd = None
     if not args.no_backward:
-        del o
-        torch.cuda.empty_cache()
-        xb = inputs.make_workload("batch4_t8k", seed=0, device=dev)
-        Tb, nb = xb.T_total, xb.num_seqs
         d_o, dSf = inputs.make_cotangents(Tb, nb, H, d, d, dtype=torch.bfloat16, seed=1, device=dev)
         grads = [torch.empty_like(t) for t in (xb.q, xb.k, xb.v, xb.g, xb.beta)]
         dS0 = torch.empty((nb, H, d, d), dtype=torch.float32, device=dev)
@@ -334,6 +374,8 @@ def main():
                                     / (ms / 1e3),
         "parity": {"prefill_o_rel_err_head0_first2048": parity},
     }
+    if tiles is not None:
+        res["tile_paths"] = tiles
     if bwd is not None:
         res["backward"] = bwd
     if not args.no_cpu:
