@@ -159,16 +159,27 @@ __device__ __forceinline__ int swz_off(int row, int col) {
 // by forward substitution.  Lane r + 16g holds row r of N in nr[0..15] and
 // returns M[r][4g .. 4g+3] of M = (I - N)^-1; row j of M is final once rows < j
 // are applied, and is read from lane j of the row with a DPP broadcast.
+// Step j updates the four columns with one v_fmac_f32 each whose first source
+// is lane j of the row (DPP row_newbcast).  A DPP read of a register needs two
+// wait states after a VALU write of it: each step starts with s_nop 1, so
+// whatever the compiler places between steps (a copy of x included) cannot
+// break that, and inside a step the four chains are independent.
+template <int J>
+__device__ __forceinline__ void fmac4_row_newbcast(float a, float& x0, float& x1, float& x2, float& x3) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+        : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)
+        : "v"(a), "n"(J));
+}
 __device__ __forceinline__ floatx4 unit_lower_inverse16(const float (&nr)[16], int r, int g) {
-    floatx4 x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = r == 4 * g + e ? 1.f : 0.f;
-    static_for<0, 15>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(nr[j], dpp<0x150 + j, false>(x[e]), x[e]);
-    });
-    return x;
+    float x0 = r == 4 * g ? 1.f : 0.f, x1 = r == 4 * g + 1 ? 1.f : 0.f;
+    float x2 = r == 4 * g + 2 ? 1.f : 0.f, x3 = r == 4 * g + 3 ? 1.f : 0.f;
+    static_for<0, 15>([&](auto jc) { fmac4_row_newbcast<decltype(jc)::value>(nr[jc], x0, x1, x2, x3); });
+    return floatx4{x0, x1, x2, x3};
 }
 
 }  // namespace t16
