@@ -119,3 +119,14 @@ def test_without_initial_state_gradient_output():
     assert out[5] is None
     for name, t in zip(NAMES[:5], out[:5]):
         assert_close(name, np64(t), ref[name], TOL[torch.bfloat16])
+
+
+def test_pages_gate_long_sequences():
+    # the pages' gate g = -5 sigmoid(z) over a few thousand tokens: every window
+    # needs its middle reference (about -40 per 16 tokens)
+    _case([2048, 1000], 4, 128, 128, torch.bfloat16, gate="pages", seed=8)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_bf16_rectangular_longer(dk, dv):
+    _case([777, 64, 1300], 3, dk, dv, torch.bfloat16, seed=9)

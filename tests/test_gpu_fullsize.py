@@ -156,3 +156,19 @@ def test_backward_full_size_sampled_units(name):
         log(f"  unit (seq {n}, head {h}), {b - a} tokens")
         for k in got:
             assert_close(k, got[k], ref[k], TOL_BF16)
+
+
+def test_tiles_pairs_full_size_sampled_units():
+    # the position-pair path over the whole four-sequence batch, two units against the oracle
+    log("tiles pairs full size batch4_t8k")
+    x = inputs.make_workload("batch4_t8k", seed=0, device="cuda")
+    o, S = gdn.gdn_prefill_tiles(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, gdn.GDN_TILES_PAIRS)
+    torch.cuda.synchronize()
+    H = x.q.shape[1]
+    units = [(0, 0), (x.num_seqs - 1, H - 1)]
+    ref = _oracle_units(x, units)
+    cu = x.cu_seqlens.cpu().numpy()
+    for (n, h), (ro, rS) in ref.items():
+        a, b = int(cu[n]), int(cu[n + 1])
+        assert_close(f"o unit ({n},{h})", np64(o[a:b, h]), ro, TOL_BF16)
+        assert_close(f"S unit ({n},{h})", np64(S[n, h]), rS, TOL_BF16)
