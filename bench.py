@@ -330,11 +330,14 @@ def main():
                               su(d_o), d_final_state=dSf[:1, :1].to("cpu", torch.float64).numpy())
         bpar = max(oracle.rel_err(su(gt), ref[nm]) for gt, nm in zip(grads, ("dq", "dk", "dv", "dg", "dbeta")))
         bwd = {"workload": "batch4_t8k backward", "num_seqs": nb, "T": Tb, "H": H, "d_k": d, "d_v": d,
+               "workspace_bytes": bws.numel(),
                "ms_per_step": bms, "steps": args.backward_steps, "warmup": 3, "tokens_per_s": Tb / (bms / 1e3),
                "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": bgbs / HBM_PEAK_GBS, "traffic": measured_traffic("backward"),
-                            "kernel": "gdn_prefill_backward call (bwd_states_kernel<bf16,128,128>, "
-                                      "bwd_grad_kernel<bf16,128,128>)",
+                            "kernel": "gdn_prefill_backward call (time split planned for 128 units: "
+                                      "bwd_states_kernel<bf16,128,128,M|N|checkpoints>, "
+                                      "bwd_grad_kernel<bf16,128,128,adjoint-only|full>, "
+                                      "bwd_fold_fwd_kernel, bwd_fold_rev_kernel)",
                             "algorithmic_bytes_per_launch": bbytes},
                "mfma": {"flops_per_launch": bflops, "achieved": bflops / (bms / 1e3) / 1e12,
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

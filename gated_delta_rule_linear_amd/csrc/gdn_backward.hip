@@ -37,7 +37,7 @@
 // Every product is a 16 x 16 matrix-core tile (bf16 operands and fp32
 // accumulation for bf16 inputs, fp32 throughout for fp32 inputs).
 //
-// Two kernels per call, one workgroup per (sequence, head) each:
+// Two sweeps per call, one workgroup per (sequence, head) each:
 //  1. bwd_states_kernel walks the sub-chunks forward and stores every
 //     sub-chunk's start state (a checkpoint, in the input dtype) in the
 //     caller's workspace;
@@ -46,6 +46,17 @@
 // The workgroup has d_v / 16 waves; for state-shaped quantities wave w owns
 // the 16 value columns [16w, 16w + 16), for the key-channel outputs the
 // 16-channel tiles w, w + d_v/16, ...
+//
+// Time split (few (sequence, head) pairs, long sequences): each sequence is
+// cut into segments of seg tokens and every sweep runs one workgroup per
+// (segment, head).  The forward map of a segment is affine in its start
+// state, S_end = M S_start + N, and the reverse map of its state gradient is
+// dS_start = M^T dS_end + D (D: the reverse sweep's result for dS_end = 0).
+//  a. bwd_states_kernel<MAP_M>, <MAP_N>: M (from I, v = 0) and N (from 0) of
+//     every segment; bwd_grad_kernel<DONLY>: D of every segment but the first;
+//  b. bwd_fold_fwd_kernel: S_start(j + 1) = M_j S_start(j) + N_j in order;
+//     bwd_fold_rev_kernel: dS_end(j - 1) = M_j^T dS_end(j) + D_j in reverse;
+//  c. sweeps 1 and 2 per segment, from S_start(j) and dS_end(j).
 #include <type_traits>
 
 #include "gdn_backward.h"
@@ -75,19 +86,77 @@ struct BArgs {
     float* dS0;        // [num_seqs, H, DK, DV] or null (not wanted)
     TI* ck;            // checkpoints: slot (cu[n] / 16 + n + c, h) is the start state of sub-chunk c of sequence n
     int H;
+    // Time split (seg > 0, a multiple of 16): sequence n is cut into segments of
+    // seg tokens, segment j using slot cu[n] / seg + n + j of the areas below
+    // (d_k x d_k or d_k x d_v fp32 per slot and head):
+    //   wsM  the segment's transition M (S_end = M S_start + N)
+    //   wsN  its offset N, replaced by the next segment's start state (forward fold)
+    //   wsD  D, the state gradient at its start for a zero end gradient, replaced
+    //        by the previous segment's end gradient (reverse fold)
+    int num_seqs;
+    int64_t seg;
+    float* wsM;
+    float* wsN;
+    float* wsD;
 };
+
+// What one workgroup of a sweep works on: head h of sequence n (tokens
+// [tb, te)), its segment j of P (tokens [sb, se)), slot the segment's slot.
+struct BUnit {
+    int n, h, j, P, slot;
+    int64_t tb, te, sb, se;
+    bool valid;
+};
+template <typename TI>
+__device__ __forceinline__ BUnit bwd_unit(const BArgs<TI>& a, int b) {
+    BUnit u;
+    const int H = a.H;
+    if (a.seg == 0) {
+        u.n = b / H;
+        u.h = b - u.n * H;
+        u.tb = a.cu[u.n];
+        u.te = a.cu[u.n + 1];
+        u.j = u.slot = 0;
+        u.P = 1;
+        u.sb = u.tb;
+        u.se = u.te;
+        u.valid = true;
+        return u;
+    }
+    const int s = b / H;
+    u.h = b - s * H;
+    // the last sequence whose first slot is at or before s (first slots increase with n)
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)a.cu[mid] / a.seg + mid <= s) lo = mid;
+        else hi = mid - 1;
+    }
+    u.n = lo;
+    u.tb = a.cu[lo];
+    u.te = a.cu[lo + 1];
+    u.j = s - (int)(u.tb / a.seg + lo);
+    u.P = max(1, (int)((u.te - u.tb + a.seg - 1) / a.seg));
+    u.slot = s;
+    u.valid = u.j >= 0 && u.j < u.P;
+    u.sb = u.tb + (int64_t)u.j * a.seg;
+    u.se = u.sb + a.seg < u.te ? u.sb + a.seg : u.te;
+    return u;
+}
 
 // LDS layout.  "Natural" matrices are row-major over the contraction index
 // with one 16-byte pad per row; "transposed" ones hold 16 tokens per key
 // channel.  FULL: the gradient kernel's buffers; otherwise the forward one's.
 // With bf16 inputs (STAGE) the next sub-chunk's raw inputs, and in the
 // gradient kernel its checkpoint, are copied into a staging area by DMA
-// while the current one is processed.
-template <typename TI, int DK, int DV, bool FULL>
+// while the current one is processed.  LITE: without what only the outputs
+// or the checkpoints need (FULL: U, dRm, F dS, the staged v and checkpoint;
+// otherwise the checkpoint tile), so that two workgroups share a compute unit.
+template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false>
 struct BCfg {
     typedef Mma<TI> M;
     static constexpr bool STAGE = sizeof(TI) == 2;
-    static constexpr int NW = DV / 16, NT = 64 * NW;
+    static constexpr int NW = NWX, NT = 64 * NW;
     static constexpr int ES = (int)sizeof(TI);
     static constexpr int KSTEP = M::KSTEP, KW = M::KW;
     static constexpr int KM = DK / KSTEP, KV = DV / KSTEP;  // MFMA steps over d_k, d_v
@@ -104,10 +173,11 @@ struct BCfg {
     static constexpr int OFF_KT = OFF_QN + (FULL ? B_NK : 0);          // k~ transposed   (FULL)
     static constexpr int OFF_QT = OFF_KT + (FULL ? B_TK : 0);          // q~ transposed   (FULL)
     static constexpr int OFF_DO = OFF_QT + (FULL ? B_TK : 0);          // dO natural [16][SV]   (FULL)
-    static constexpr int OFF_U = OFF_DO + (FULL ? B_NV : 0);           // U natural       (FULL)
-    static constexpr int OFF_DR = OFF_U + (FULL ? B_NV : 0);           // dRm natural     (FULL)
-    static constexpr int OFF_FS = OFF_DR + (FULL ? B_NV : 0);          // F dS [DK][SV]   (FULL)
-    static constexpr int OFF_G = OFF_FS + (FULL ? B_FS : 0);           // G (log2) [16][DK] fp32
+    static constexpr bool GX = FULL && !LITE;                          // the outputs' buffers
+    static constexpr int OFF_U = OFF_DO + (FULL ? B_NV : 0);           // U natural       (GX)
+    static constexpr int OFF_DR = OFF_U + (GX ? B_NV : 0);             // dRm natural     (GX)
+    static constexpr int OFF_FS = OFF_DR + (GX ? B_NV : 0);            // F dS [DK][SV]   (GX)
+    static constexpr int OFF_G = OFF_FS + (GX ? B_FS : 0);             // G (log2) [16][DK] fp32
     static constexpr int OFF_ML = OFF_G + CB * DK * 4;                 // m (log2) [DK]
     static constexpr int OFF_EM = OFF_ML + DK * 4;                     // e^m [DK]
     static constexpr int OFF_FF = OFF_EM + DK * 4;                     // e^{G_15 - m} [DK]
@@ -125,22 +195,22 @@ struct BCfg {
     static constexpr int ST_K = ST_G + CB * DK * 4;                    // k [16][DK]
     static constexpr int ST_Q = ST_K + CB * DK * ES;                   // q [16][DK]   (FULL)
     static constexpr int ST_O = ST_Q + (FULL ? CB * DK * ES : 0);      // dO [16][DV]  (FULL)
-    static constexpr int ST_V = ST_O + (FULL ? CB * DV * ES : 0);      // v [16][DV]
-    static constexpr int ST_B = ST_V + CB * DV * ES;                   // beta [64] (lanes past 16 repeat the last row)
-    static constexpr int ST_C = ST_B + 256;                            // checkpoint [DK][DV]  (FULL)
-    static constexpr int STG_END = STAGE ? ST_C + (FULL ? DK * DV * ES : 0) : OFF_STG;
+    static constexpr int ST_V = ST_O + (FULL ? CB * DV * ES : 0);      // v [16][DV]   (not FULL && LITE)
+    static constexpr int ST_B = ST_V + (FULL && LITE ? 0 : CB * DV * ES);  // beta [64] (lanes past 16 repeat the last row)
+    static constexpr int ST_C = ST_B + 256;                            // checkpoint [DK][DV]  (GX)
+    static constexpr int STG_END = STAGE ? ST_C + (GX ? DK * DV * ES : 0) : OFF_STG;
     // forward kernel: the state in the input dtype, rows padded, for coalesced checkpoint stores
     static constexpr int OFF_CK = STG_END;
-    static constexpr int LDS = OFF_CK + (FULL ? 0 : DK * SV * ES);
+    static constexpr int LDS = OFF_CK + (FULL || LITE ? 0 : DK * SV * ES);
     static_assert(B_NK % 16 == 0 && B_TK % 16 == 0 && B_NV % 16 == 0 && B_FS % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // Copy of one sub-chunk's raw inputs (t0: first token, L tokens) into the staging area.
-template <typename TI, int DK, int DV, bool FULL>
+template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false, bool WITH_V = true>
 __device__ __forceinline__ void dma_inputs(const BArgs<TI>& a, char* smem, int h, int64_t t0, int L, int w,
                                            int lane) {
-    typedef BCfg<TI, DK, DV, FULL> P;
+    typedef BCfg<TI, DK, DV, FULL, NWX, LITE> P;
     const int H = a.H;
     const size_t row0 = (size_t)t0 * H + h;
     dma_rows<DK * 4, CB, P::NW>(a.g + row0 * DK, (size_t)H * DK * 4, L, smem + P::ST_G, w, lane);
@@ -149,7 +219,8 @@ __device__ __forceinline__ void dma_inputs(const BArgs<TI>& a, char* smem, int h
         dma_rows<DK * P::ES, CB, P::NW>(a.q + row0 * DK, (size_t)H * DK * P::ES, L, smem + P::ST_Q, w, lane);
         dma_rows<DV * P::ES, CB, P::NW>(a.dO + row0 * DV, (size_t)H * DV * P::ES, L, smem + P::ST_O, w, lane);
     }
-    dma_rows<DV * P::ES, CB, P::NW>(a.v + row0 * DV, (size_t)H * DV * P::ES, L, smem + P::ST_V, w, lane);
+    if constexpr (WITH_V && !(FULL && LITE))
+        dma_rows<DV * P::ES, CB, P::NW>(a.v + row0 * DV, (size_t)H * DV * P::ES, L, smem + P::ST_V, w, lane);
     if (w == P::NW - 1)
         __builtin_amdgcn_global_load_lds(as_global(a.beta + row0 + (size_t)min(lane, L - 1) * H),
                                          as_lds(smem + P::ST_B), 4, 0, 0);
@@ -157,11 +228,11 @@ __device__ __forceinline__ void dma_inputs(const BArgs<TI>& a, char* smem, int h
 
 // Steps 1 and 2 of a sub-chunk (both kernels): cumulative log-decay, the
 // per-channel vectors, beta, the operands; dO into its padded layout (FULL);
-// this lane's 4 values of v (rows 4g + i, column col0 + r).  Ends with an
-// LDS barrier after the operands.
-template <typename TI, int DK, int DV, bool FULL>
+// this lane's 4 values of v (rows 4g + i, column col0 + r; zero for a FULL
+// LITE layout, which has no v).  Ends with an LDS barrier after the operands.
+template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false>
 __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, int64_t t0, int L, int tid, int col0) {
-    typedef BCfg<TI, DK, DV, FULL> P;
+    typedef BCfg<TI, DK, DV, FULL, NWX, LITE> P;
     typedef typename Two<TI>::type T2;
     const int H = a.H;
     const int lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -229,9 +300,9 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
             }
         }
     }
-    floatx4 vv;
+    floatx4 vv = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4 && !(FULL && LITE); ++i) {
         const int t = 4 * g + i;
         float x;
         if constexpr (P::STAGE) x = to_f32(stg_v[t * DV + col0 + r]);
@@ -292,9 +363,9 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
 // (lane r + 16g carries M[r][4g .. 4g+3]; row j of M is final once rows < j
 // are applied, and is read from lane j of the row with a DPP broadcast), then
 // M and M^T into LDS.
-template <typename TI, int DK, int DV, bool FULL>
+template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false>
 __device__ __forceinline__ floatx4 gram_inverse(char* smem, int lane) {
-    typedef BCfg<TI, DK, DV, FULL> P;
+    typedef BCfg<TI, DK, DV, FULL, NWX, LITE> P;
     typedef Mma<TI> M;
     const int r = lane & 15, g = lane >> 4;
     const TI* sKN = reinterpret_cast<const TI*>(smem + P::OFF_KN);
@@ -326,18 +397,35 @@ __device__ __forceinline__ floatx4 gram_inverse(char* smem, int lane) {
     return kk;
 }
 
-// Forward pass storing checkpoints: one workgroup per (sequence, head).
-template <typename TI, int DK, int DV>
-__global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
-    typedef BCfg<TI, DK, DV, false> P;
+// Forward sweep over the sub-chunks of one (sequence, head), or with a time
+// split of one (segment, head).
+//  CK:  stores every sub-chunk's start state (its checkpoint), starting from
+//       the initial state, or from the segment's start state left by the
+//       forward fold.
+//  MAP_M, MAP_N: the segment's transition (time split, sequences of two or
+//       more segments), written to the segment's slot at the end: M from the
+//       start state I with v = 0 (d_k / 16 waves, wave w carrying columns
+//       [16w, 16w + 16) of M), or N from the start state 0 (not for the last
+//       segment, which the forward fold does not use).
+constexpr int SWEEP_CK = 0, MAP_M = 1, MAP_N = 2;
+// (The second launch bound is waves per SIMD: two workgroups of NW waves per
+// compute unit need NW / 2.)
+template <typename TI, int DK, int DV, int MODE>
+__global__ __launch_bounds__(MODE == MAP_M ? DK * 4 : DV * 4, MODE == SWEEP_CK ? 1 : (MODE == MAP_M ? DK : DV) / 32)
+void bwd_states_kernel(BArgs<TI> a) {
+    constexpr bool CK = MODE == SWEEP_CK, mcol = MODE == MAP_M;
+    constexpr int NWX = mcol ? DK / 16 : DV / 16;
+    typedef BCfg<TI, DK, DV, false, NWX, !CK> P;
     typedef Mma<TI> M;
     typedef K16<TI> K;
     __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
     const int tid0 = threadIdx.x, g0 = (tid0 & 63) >> 4, r0 = tid0 & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
-    const int n = blockIdx.x / H, h = blockIdx.x - n * H;
-    const int64_t tb = a.cu[n], te = a.cu[n + 1];
+    const BUnit u = bwd_unit(a, blockIdx.x);
+    if (!u.valid || (!CK && u.P < 2) || (MODE == MAP_N && u.j == u.P - 1)) return;
+    const int n = u.n, h = u.h;
+    const int64_t sb = u.sb, se = u.se;
     const int col0 = 16 * w;
     const float* sEM = reinterpret_cast<const float*>(smem + P::OFF_EM);
     const float* sFF = reinterpret_cast<const float*>(smem + P::OFF_FF);
@@ -350,17 +438,26 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
 
     // state, own columns: S[rt][i] = S[16 rt + 4g + i][col0 + r]
     floatx4 S[P::RT];
-    const float* s0 = a.S0 ? a.S0 + (size_t)blockIdx.x * DK * DV : nullptr;
+    const float* s0 = nullptr;
+    if (CK) {
+        if (u.j == 0) s0 = a.S0 ? a.S0 + ((size_t)n * H + h) * DK * DV : nullptr;
+        else s0 = a.wsN + ((size_t)(u.slot - 1) * H + h) * DK * DV;
+    }
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[(16 * rt + 4 * g0 + i) * DV + col0 + r0] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g0 + i;
+            S[rt][i] = mcol ? (row == col0 + r0 ? 1.f : 0.f) : s0 ? s0[row * DV + col0 + r0] : 0.f;
+        }
 
     if constexpr (P::STAGE)
-        if (te > tb) dma_inputs<TI, DK, DV, false>(a, smem, h, tb, (int)(te - tb < CB ? te - tb : CB), w, tid0 & 63);
-    TI* ck = a.ck + (((size_t)(tb >> 4) + n) * H + h) * DK * DV;
-    for (int64_t t0 = tb; t0 < te; t0 += CB, ck += (size_t)H * DK * DV) {
-        const int L = (int)(te - t0 < CB ? te - t0 : CB);
+        if (se > sb)
+            dma_inputs<TI, DK, DV, false, NWX, !CK, !mcol>(a, smem, h, sb, (int)(se - sb < CB ? se - sb : CB), w,
+                                                          tid0 & 63);
+    TI* ck = a.ck + (((size_t)(u.tb >> 4) + n + (size_t)((sb - u.tb) >> 4)) * H + h) * DK * DV;
+    for (int64_t t0 = sb; t0 < se; t0 += CB, ck += (size_t)H * DK * DV) {
+        const int L = (int)(se - t0 < CB ? se - t0 : CB);
         // lane-derived values are recomputed every iteration (opaque to the
         // compiler), so addresses built from them are not hoisted out of the
         // loop and held in registers for its whole length
@@ -370,16 +467,21 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
         if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of the sub-chunk has landed
         lds_barrier();  // ... and every wave's; the previous sub-chunk is done with LDS
         // the checkpoint: own columns into LDS, then whole rows out in 16-byte pieces
+        if constexpr (CK) {
 #pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt)
+            for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sCK[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(S[rt][i]);
-        const floatx4 vv = prep<TI, DK, DV, false>(a, smem, h, t0, L, tid, col0);
+                for (int i = 0; i < 4; ++i) sCK[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(S[rt][i]);
+        }
+        floatx4 vv = prep<TI, DK, DV, false, NWX, !CK>(a, smem, h, t0, L, tid, mcol ? 0 : col0);
+        if constexpr (mcol) vv = zero4();
         if constexpr (P::STAGE) {
             const int64_t t1 = t0 + CB;
-            if (t1 < te) dma_inputs<TI, DK, DV, false>(a, smem, h, t1, (int)(te - t1 < CB ? te - t1 : CB), w, lane);
+            if (t1 < se)
+                dma_inputs<TI, DK, DV, false, NWX, !CK, !mcol>(a, smem, h, t1, (int)(se - t1 < CB ? se - t1 : CB),
+                                                               w, lane);
         }
-        {
+        if constexpr (CK) {
             constexpr int PER = 16 / P::ES, NPR = DV / PER;
 #pragma unroll
             for (int k = 0; k < DK * NPR / P::NT; ++k) {
@@ -388,7 +490,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
                     *reinterpret_cast<const floatx4*>(sCK + row * P::SV + pc * PER);
             }
         }
-        if (w == 0) (void)gram_inverse<TI, DK, DV, false>(smem, lane);
+        if (w == 0) (void)gram_inverse<TI, DK, DV, false, NWX, !CK>(smem, lane);
         // R = V - k~ (E S), own columns
         floatx4 acc = zero4();
 #pragma unroll(P::UNR)
@@ -414,14 +516,110 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
             S[rt] = gm * S[rt] + ff * d;
         }
     }
+    if constexpr (!CK) {
+        constexpr int LD = mcol ? DK : DV;
+        float* dst = (mcol ? a.wsM : a.wsN) + ((size_t)u.slot * H + h) * DK * LD;
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g0 + i) * LD + col0 + r0] = S[rt][i];
+    }
 }
 
-// Reverse pass: one workgroup per (sequence, head), sub-chunks last to first.
-// A sub-chunk's outputs are stored at the start of the next iteration, after
-// its wait for the copies in flight, so that wait does not include them.
-template <typename TI, int DK, int DV>
-__global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
-    typedef BCfg<TI, DK, DV, true> P;
+// Time split, forward fold, per (sequence, head) and 16 state columns: the
+// start state of segment j + 1 is M_j S_start(j) + N_j, written over N_j.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_fold_fwd_kernel(const int32_t* cu, int H, int64_t seg, const float* S0,
+                                                           const float* wsM, float* wsN) {
+    constexpr int TPR = 256 / DK, CPT = 16 / TPR;
+    __shared__ float sx[DK][16];
+    const int unit = blockIdx.x, n = unit / H, h = unit - n * H, c0 = 16 * blockIdx.y;
+    const int64_t tb = cu[n], len = cu[n + 1] - tb;
+    const int P = (int)((len + seg - 1) / seg);
+    if (P < 2) return;
+    const int64_t base = tb / seg + n;
+    const int tid = threadIdx.x, i = tid / TPR, cc = (tid % TPR) * CPT;
+    for (int e = tid; e < DK * 16; e += 256)
+        sx[e >> 4][e & 15] = S0 ? S0[((size_t)unit * DK + (e >> 4)) * DV + c0 + (e & 15)] : 0.f;
+    __syncthreads();
+    for (int j = 0; j + 1 < P; ++j) {
+        const size_t sl = (size_t)(base + j) * H + h;
+        const float* Mi = wsM + sl * DK * DK + (size_t)i * DK;  // row i of M_j
+        float* Nj = wsN + sl * DK * DV + (size_t)i * DV + c0 + cc;
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = Nj[c];
+#pragma unroll 8
+        for (int k = 0; k < DK; k += 4) {
+            const floatx4 m = *reinterpret_cast<const floatx4*>(Mi + k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) acc[c] = __builtin_fmaf(m[e], sx[k + e][cc + c], acc[c]);
+        }
+        __syncthreads();  // every read of x is done
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            sx[i][cc + c] = acc[c];
+            Nj[c] = acc[c];
+        }
+        __syncthreads();
+    }
+}
+
+// Time split, reverse fold, per (sequence, head) and 16 state columns: from
+// x = dL/d(final state), for j = P-1 down to 1, x <- M_j^T x + D_j (the state
+// gradient at the start of segment j, i.e. at the end of segment j - 1),
+// written over D_j.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_fold_rev_kernel(const int32_t* cu, int H, int64_t seg, const float* dSf,
+                                                           const float* wsM, float* wsD) {
+    constexpr int TPR = 256 / DK, CPT = 16 / TPR;
+    __shared__ float sx[DK][16];
+    const int unit = blockIdx.x, n = unit / H, h = unit - n * H, c0 = 16 * blockIdx.y;
+    const int64_t tb = cu[n], len = cu[n + 1] - tb;
+    const int P = (int)((len + seg - 1) / seg);
+    if (P < 2) return;
+    const int64_t base = tb / seg + n;
+    const int tid = threadIdx.x, i = tid / TPR, cc = (tid % TPR) * CPT;
+    for (int e = tid; e < DK * 16; e += 256)
+        sx[e >> 4][e & 15] = dSf ? dSf[((size_t)unit * DK + (e >> 4)) * DV + c0 + (e & 15)] : 0.f;
+    __syncthreads();
+    for (int j = P - 1; j >= 1; --j) {
+        const size_t sl = (size_t)(base + j) * H + h;
+        const float* Mc = wsM + sl * DK * DK + i;  // column i of M_j
+        float* Dj = wsD + sl * DK * DV + (size_t)i * DV + c0 + cc;
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = Dj[c];
+#pragma unroll 16
+        for (int k = 0; k < DK; ++k) {
+            const float m = Mc[(size_t)k * DK];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] = __builtin_fmaf(m, sx[k][cc + c], acc[c]);
+        }
+        __syncthreads();  // every read of x is done
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            sx[i][cc + c] = acc[c];
+            Dj[c] = acc[c];
+        }
+        __syncthreads();
+    }
+}
+
+// Reverse sweep over the sub-chunks of one (sequence, head), or with a time
+// split of one (segment, head), last to first, from the gradient of the state
+// at its end: that of the final state, or for a non-last segment the one the
+// reverse fold left.  A sub-chunk's outputs are stored at the start of the next
+// iteration, after its wait for the copies in flight, so that wait does not
+// include them.
+// DONLY (time split, segments after the first): only the state-gradient
+// recursion, from a zero end gradient; its result D is written to the
+// segment's slot for the reverse fold.  It needs neither the checkpoints nor v.
+template <typename TI, int DK, int DV, bool DONLY>
+__global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(BArgs<TI> a) {
+    typedef BCfg<TI, DK, DV, true, DV / 16, DONLY> P;
     typedef Mma<TI> M;
     typedef typename M::frag frag;
     typedef K16<TI> K;
@@ -430,8 +628,10 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
     const int tid0 = threadIdx.x, g0 = (tid0 & 63) >> 4, r0 = tid0 & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
-    const int n = blockIdx.x / H, h = blockIdx.x - n * H;
-    const int64_t tb = a.cu[n], te = a.cu[n + 1];
+    const BUnit u = bwd_unit(a, blockIdx.x);
+    if (!u.valid || (DONLY && u.j == 0)) return;
+    const int n = u.n, h = u.h;
+    const int64_t tb = u.tb, sb = u.sb, se = u.se;
     const int col0 = 16 * w;
     const float* sG = reinterpret_cast<const float*>(smem + P::OFF_G);
     const float* sML = reinterpret_cast<const float*>(smem + P::OFF_ML);
@@ -458,7 +658,11 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
 
     // dS = dL/d(state at the end of the current sub-chunk), own columns
     floatx4 dS[P::RT];
-    const float* dsf = a.dSf ? a.dSf + (size_t)blockIdx.x * DK * DV : nullptr;
+    const float* dsf = nullptr;
+    if (!DONLY) {
+        if (u.j == u.P - 1) dsf = a.dSf ? a.dSf + ((size_t)n * H + h) * DK * DV : nullptr;
+        else dsf = a.wsD + ((size_t)(u.slot + 1) * H + h) * DK * DV;
+    }
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
@@ -490,19 +694,23 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             }
         }
     };
-    auto slot = [&](int64_t c) { return a.ck + ((((size_t)(tb >> 4) + n + (size_t)c) * H + h) * DK * DV); };
-    auto sub_len = [&](int64_t c) { return (int)(te - (tb + CB * c) < CB ? te - (tb + CB * c) : CB); };
+    // sub-chunk c of the segment: checkpoint slot and length
+    const size_t cbase = (size_t)(tb >> 4) + n + (size_t)((sb - tb) >> 4);
+    auto slot = [&](int64_t c) { return a.ck + (((cbase + (size_t)c) * H + h) * DK * DV); };
+    auto sub_len = [&](int64_t c) { return (int)(se - (sb + CB * c) < CB ? se - (sb + CB * c) : CB); };
 
-    const int64_t nsub = (te - tb + CB - 1) / CB;
+    const int64_t nsub = (se - sb + CB - 1) / CB;
     if constexpr (P::STAGE) {
         if (nsub > 0) {
-            dma_inputs<TI, DK, DV, true>(a, smem, h, tb + CB * (nsub - 1), sub_len(nsub - 1), w, tid0 & 63);
-            dma_rows<DV * P::ES, DK, P::NW, true>(slot(nsub - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w,
-                                                  tid0 & 63);
+            dma_inputs<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, sb + CB * (nsub - 1), sub_len(nsub - 1), w,
+                                                         tid0 & 63);
+            if constexpr (!DONLY)
+                dma_rows<DV * P::ES, DK, P::NW, true>(slot(nsub - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w,
+                                                      tid0 & 63);
         }
     }
     for (int64_t c = nsub - 1; c >= 0; --c) {
-        const int64_t t0 = tb + CB * c;
+        const int64_t t0 = sb + CB * c;
         const int L = sub_len(c);
         const size_t row0 = (size_t)t0 * H + h;
         const TI* ck = slot(c);
@@ -514,12 +722,12 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
         if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
         lds_barrier();  // ... and every wave's; the previous sub-chunk is done with LDS
-        flush(r, g);
-        const floatx4 vv = prep<TI, DK, DV, true>(a, smem, h, t0, L, tid, col0);
+        if constexpr (!DONLY) flush(r, g);
+        const floatx4 vv = prep<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0, L, tid, col0);
         if constexpr (P::STAGE)
-            if (c > 0) dma_inputs<TI, DK, DV, true>(a, smem, h, t0 - CB, sub_len(c - 1), w, lane);
+            if (c > 0) dma_inputs<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0 - CB, sub_len(c - 1), w, lane);
         floatx4 kk = zero4();
-        if (w == 0) kk = gram_inverse<TI, DK, DV, true>(smem, lane);
+        if (w == 0) kk = gram_inverse<TI, DK, DV, true, DV / 16, DONLY>(smem, lane);
 
         // ---- 3. value-column steps (own columns) -------------------------------
         // (wave 1) P = lower(q~ k^T): lane r + 16g holds P[t = 4g + i][s = r]; shared through LDS
@@ -534,6 +742,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         }
         // R = V - k~ (E S0), S0 from the checkpoint
         floatx4 acc = zero4();
+        if constexpr (!DONLY) {
 #pragma unroll(P::UNR)
         for (int mm = 0; mm < P::KM; ++mm) {
             // only the accumulator tiles this step reads are loaded (bf16: tiles 2mm, 2mm + 1; fp32: tile mm / 4)
@@ -560,6 +769,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             }
             acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
         }
+        }
         floatx4 R, br;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -580,7 +790,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             dU = M::mma(lds_perm(sHN + r * P::SK, mm, g), acc_perm<TI>(fds, mm, P::RT), dU);
         }
         lds_barrier();  // M is ready; every read of the staged checkpoint is done
-        if constexpr (P::STAGE)
+        if constexpr (P::STAGE && !DONLY)
             if (c > 0)
                 dma_rows<DV * P::ES, DK, P::NW, true>(slot(c - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w, lane);
         const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
@@ -593,11 +803,14 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
             const int t = 4 * g + i;
             dR[i] = sBETA[t] * dRm[i];
             ndR[i] = -dR[i];
-            const float p = sum16(R[i] * dRm[i]);
-            if (r == 0) sDB[w * CB + t] = p;
+            if constexpr (!DONLY) {
+                const float p = sum16(R[i] * dRm[i]);
+                if (r == 0) sDB[w * CB + t] = p;
+            }
         }
         o_dv = dR;
         // exchange: F dS, U, dRm (natural layouts) for the key-channel products
+        if constexpr (!DONLY) {
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt) {
             const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
@@ -608,6 +821,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         for (int i = 0; i < 4; ++i) {
             sU[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(U[i]);
             sDR[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(dRm[i]);
+        }
         }
         // dS <- gamma dS + E (q~^T dO - k~^T dR)
         {
@@ -621,6 +835,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
                 dS[rt] = gm * dS[rt] + em * x;
             }
         }
+        if constexpr (DONLY) continue;
         lds_barrier();
 
         // ---- 4. key-channel outputs ------------------------------------------
@@ -724,9 +939,17 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_grad_kernel(BArgs<TI> a) {
         o_row0 = row0;
         o_L = L;
     }
+    if constexpr (DONLY) {
+        float* dst = a.wsD + ((size_t)u.slot * H + h) * DK * DV;
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g0 + i) * DV + col0 + r0] = dS[rt][i];
+        return;
+    }
     flush(r0, g0);
-    if (a.dS0) {
-        float* dst = a.dS0 + (size_t)blockIdx.x * DK * DV;
+    if (u.j == 0 && a.dS0) {
+        float* dst = a.dS0 + ((size_t)n * H + h) * DK * DV;
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
@@ -754,11 +977,41 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     a.dS0 = p.d_initial_state;
     a.ck = static_cast<TI*>(p.workspace);
     a.H = p.H;
-    const unsigned blocks = (unsigned)((int64_t)p.num_seqs * p.H);
-    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    a.num_seqs = p.num_seqs;
+    a.seg = p.seg;
+    a.wsM = a.wsN = a.wsD = nullptr;
+    if (p.seg <= 0) {
+        const unsigned blocks = (unsigned)((int64_t)p.num_seqs * p.H);
+        hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, SWEEP_CK>), dim3(blocks), dim3(DV * 4), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
+        return hipGetLastError();
+    }
+    // time split: transitions and end-gradient-free adjoints per segment, the
+    // two folds, then both sweeps per segment from the folded boundary values
+    const BackwardWorkspace ws = backward_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.bf16, p.seg);
+    char* base = static_cast<char*>(p.workspace);
+    a.wsM = reinterpret_cast<float*>(base + ws.m_off);
+    a.wsN = reinterpret_cast<float*>(base + ws.n_off);
+    a.wsD = reinterpret_cast<float*>(base + ws.d_off);
+    const unsigned blocks = (unsigned)(ws.slots * p.H);
+    const dim3 fold_grid((unsigned)((int64_t)p.num_seqs * p.H), DV / 16);
+    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, MAP_M>), dim3(blocks), dim3(DK * 4), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, MAP_N>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, true>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_fold_fwd_kernel<DK, DV>), fold_grid, dim3(256), 0, s, a.cu, p.H, p.seg, a.S0, a.wsM, a.wsN);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_fold_rev_kernel<DK, DV>), fold_grid, dim3(256), 0, s, a.cu, p.H, p.seg, a.dSf, a.wsM,
+                       a.wsD);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, SWEEP_CK>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
     return hipGetLastError();
 }
 

@@ -194,8 +194,11 @@ int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const voi
 
 /* Device scratch bytes gdn_prefill_backward needs: one state per 16-token
  * sub-chunk and head in the input dtype, (T_total / 16 + num_seqs) * H * d_k
- * * d_v * (2 for GDN_BF16, 4 for GDN_F32).  Depends on the arguments only; 0
- * for invalid arguments. */
+ * * d_v * (2 for GDN_BF16, 4 for GDN_F32), rounded up to 256; with a time
+ * split of segment length L (below), (T_total / L + num_seqs) * H * (d_k * d_k
+ * + 2 * d_k * d_v) * 4 more, each of the three areas rounded up to 256.
+ * Depends on the arguments and on GDN_BACKWARD_SEGMENT only; 0 for invalid
+ * arguments. */
 size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k,
                                             int32_t d_v, int32_t dtype);
 
@@ -235,7 +238,17 @@ size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, i
  * referred to the window's middle token, so every factor stays within
  * e^-40 .. e^40 for g in [-5, 0] (the 16-token tile bound of
  * "Trillion-Parameter MoE Multimodal LLMs: How to Evaluate the New
- * Generation", section 3.1). */
+ * Generation", section 3.1).
+ * Time split: when few (sequence, head) pairs leave compute units idle
+ * (num_seqs * H <= 144) and sequences are long, each sequence is cut into
+ * segments of L tokens (a multiple of 16) swept in parallel.  The state map
+ * of a segment is affine, S_end = M S_start + N, and its adjoint
+ * dS_start = M^T dS_end + D; M, N and D of every segment come from
+ * per-segment sweeps, two sequential folds give every segment's start state
+ * and end gradient, then both sweeps run per segment.  Same results up to
+ * rounding.  GDN_BACKWARD_SEGMENT=L forces the length (rounded up to a
+ * multiple of 16), 0 turns the split off; it must not change between the
+ * workspace query and the call. */
 int32_t gdn_prefill_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
                              const float* initial_state, const void* d_o, const float* d_final_state, void* dq,

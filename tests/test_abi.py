@@ -176,6 +176,34 @@ def test_backward_workspace_bytes(lib):
     assert f(16, 1, 1, 64, 64, 9) == 0
 
 
+def _backward_ws(T, n, H, dk, dv, bf16, seg):
+    # checkpoints, then with a time split of segment length seg the per-segment
+    # transition M (d_k x d_k fp32) and the two d_k x d_v fp32 boundary areas
+    al = lambda x: (x + 255) // 256 * 256
+    ck = al((T // 16 + n) * H * dk * dv * (2 if bf16 else 4))
+    if seg == 0:
+        return ck
+    slots = T // seg + n
+    return ck + al(slots * H * dk * dk * 4) + 2 * al(slots * H * dk * dv * 4)
+
+
+def test_backward_workspace_bytes_split(lib, monkeypatch):
+    f = lib.gdn_prefill_backward_workspace_bytes
+    monkeypatch.delenv("GDN_BACKWARD_SEGMENT", raising=False)
+    # few (sequence, head) units over long sequences: segments for about 512 workgroups
+    assert f(32768, 4, 32, 128, 128, 1) == _backward_ws(32768, 4, 32, 128, 128, True, 2048)
+    assert f(65536, 1, 16, 128, 128, 1) == _backward_ws(65536, 1, 16, 128, 128, True, 2048)
+    assert f(1 << 20, 1, 16, 128, 128, 1) == _backward_ws(1 << 20, 1, 16, 128, 128, True, 32768)
+    # enough units to fill the chip, or sequences too short for three segments: no split
+    assert f(65536, 8, 32, 128, 128, 1) == _backward_ws(65536, 8, 32, 128, 128, True, 0)
+    assert f(1024, 4, 32, 128, 128, 1) == _backward_ws(1024, 4, 32, 128, 128, True, 0)
+    # forced length, rounded up to a multiple of 16; 0 turns the split off
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "250")
+    assert f(1000, 3, 2, 64, 128, 0) == _backward_ws(1000, 3, 2, 64, 128, False, 256)
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "0")
+    assert f(32768, 4, 32, 128, 128, 1) == _backward_ws(32768, 4, 32, 128, 128, True, 0)
+
+
 def test_backward_argument_errors(lib):
     assert _backward(lib) == INVALID                      # null pointers with T > 0
     assert _backward(lib, dk=96) == UNSUPPORTED

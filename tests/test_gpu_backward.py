@@ -121,12 +121,52 @@ def test_without_initial_state_gradient_output():
         assert_close(name, np64(t), ref[name], TOL[torch.bfloat16])
 
 
-def test_pages_gate_long_sequences():
+def test_pages_gate_long_sequences(monkeypatch):
     # the pages' gate g = -5 sigmoid(z) over a few thousand tokens: every window
-    # needs its middle reference (about -40 per 16 tokens)
+    # needs its middle reference (about -40 per 16 tokens); one sweep per
+    # (sequence, head) (the planner would split these few units)
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "0")
     _case([2048, 1000], 4, 128, 128, torch.bfloat16, gate="pages", seed=8)
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
 def test_bf16_rectangular_longer(dk, dv):
     _case([777, 64, 1300], 3, dk, dv, torch.bfloat16, seed=9)
+
+
+# ---- time split: each sequence cut into segments of GDN_BACKWARD_SEGMENT
+# tokens, with the transitions, both folds and the per-segment sweeps
+
+
+@pytest.mark.parametrize("seg,dk,dv,dtype", [(48, 128, 128, torch.bfloat16), (32, 64, 64, torch.float32),
+                                             (64, 64, 128, torch.bfloat16), (64, 128, 64, torch.bfloat16),
+                                             (16, 128, 128, torch.float32)])
+def test_split_ragged(monkeypatch, seg, dk, dv, dtype):
+    # empty sequences, sequences shorter than a segment, ragged last segments
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", str(seg))
+    _case([1, 15, 16, 17, 63, 0, 130, 700], 3, dk, dv, dtype, seed=10)
+
+
+def test_split_pages_gate_long(monkeypatch):
+    # eight segments per sequence under the pages' steep gate
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "256")
+    _case([2048, 1000], 4, 128, 128, torch.bfloat16, gate="pages", seed=11)
+
+
+def test_split_no_initial_state_no_final_gradient(monkeypatch):
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "64")
+    _case([200, 0, 33], 2, 128, 128, torch.bfloat16, init=False, final=False, seed=12)
+
+
+def test_split_matches_unsplit(monkeypatch):
+    # the same call with and without the split agrees to rounding (fp32)
+    x = inputs.make_prefill_inputs([900, 300], 2, 64, 64, dtype=torch.float32, init_state=True, seed=13)
+    d_o, dSf = inputs.make_cotangents(x.T_total, x.num_seqs, 2, 64, 64, dtype=torch.float32, seed=113)
+    to_device(x)
+    d_o, dSf = d_o.cuda(), dSf.cuda()
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "0")
+    a = _run(x, d_o, dSf)
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "128")
+    b = _run(x, d_o, dSf)
+    for name in NAMES:
+        assert_close(name, np64(b[name]), np64(a[name]), TOL[torch.float32])
