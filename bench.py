@@ -58,7 +58,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published (no sparsity)
 KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp", "gdn_kernels.h"]
 BACKWARD_SOURCES = ["gdn_backward.hip", "gdn_backward.h", "gdn_tile16.h", "gdn_mfma.h", "gdn_device.h",
-                    "gdn_api_backward.cpp"]
+                    "gdn_api_backward.cpp", "gdn_prefill.hip", "gdn_kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -335,9 +335,9 @@ def main():
                "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": bgbs / HBM_PEAK_GBS, "traffic": measured_traffic("backward"),
                             "kernel": "gdn_prefill_backward call (time split planned for 128 units: "
-                                      "bwd_states_kernel<bf16,128,128,M|N|checkpoints>, "
-                                      "bwd_grad_kernel<bf16,128,128,adjoint-only|full>, "
-                                      "bwd_fold_fwd_kernel, bwd_fold_rev_kernel)",
+                                      "seg_table, prefill_ws_kernel<128,128,map>, seg_fold, "
+                                      "bwd_grad_kernel<bf16,128,128,adjoint-only>, bwd_fold_rev_kernel, "
+                                      "bwd_states_kernel<bf16,128,128>, bwd_grad_kernel<bf16,128,128,full>)",
                             "algorithmic_bytes_per_launch": bbytes},
                "mfma": {"flops_per_launch": bflops, "achieved": bflops / (bms / 1e3) / 1e12,
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -36,27 +36,27 @@ int32_t validate_backward_inputs(const int32_t* cu_dev, int32_t num_seqs, int64_
 
 namespace gdn {
 
-// The split adds two transition sweeps (M and N), an adjoint sweep without
-// outputs and two folds: on MI355X (bf16, d = 128) the split call runs at
-// about 190 M head-tokens/s against 310 M for the unsplit one with every
-// compute unit busy, so it pays only when the (sequence, head) units leave
-// enough of the 256 compute units idle: up to 144 units.  Segments are cut so
-// that about 512 workgroups run (two per compute unit for the forward sweeps),
-// no shorter than 512 tokens and at least three per sequence.  Measured
-// (ms, unsplit -> split): 4 x 8192 tokens x 32 heads 6.43 -> 5.49 (2048-token
-// segments); 1 x 65536 x 16 heads 49.5 -> 5.99; 1 x 262144 x 16 198 -> 22.0.
+// The split adds the forward pass's map pass and fold, an adjoint sweep
+// without outputs and a reverse fold: on MI355X (bf16, d = 128) the split call
+// over 256 (sequence, head) units of 8192 tokens takes 8.05 ms against 6.68
+// unsplit, so it pays only when the units leave compute units idle: up to
+// 144 units.  Segments (a multiple of 64 tokens, the forward's chunk) are cut
+// so that about 512 workgroups run, no shorter than 512 tokens and at least
+// three per sequence.  Measured (ms, unsplit -> split): 4 x 8192 tokens x 32
+// heads 6.37 -> 4.40 (2048-token segments); 1 x 65536 x 16 heads 49.5 -> 4.85;
+// 1 x 262144 x 16 198 -> 17.5; 4 x 2048 x 32 1.60 -> 1.20.
 int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H) {
     if (const char* e = std::getenv("GDN_BACKWARD_SEGMENT")) {
         if (*e) {
             const long long v = std::strtoll(e, nullptr, 10);
-            return v <= 0 ? 0 : (int64_t)((v + 15) / 16 * 16);
+            return v <= 0 ? 0 : (int64_t)((v + 63) / 64 * 64);
         }
     }
     if (num_seqs <= 0 || T_total <= 0 || H <= 0) return 0;
     const int64_t units = (int64_t)num_seqs * H;
     if (units > 144) return 0;
     const int64_t P = std::max<int64_t>(3, 512 / units), len = (T_total + num_seqs - 1) / num_seqs;
-    const int64_t seg = std::max<int64_t>(512, ((len + P - 1) / P + 15) / 16 * 16);
+    const int64_t seg = std::max<int64_t>(512, ((len + P - 1) / P + 63) / 64 * 64);
     return (len + seg - 1) / seg >= 3 ? seg : 0;
 }
 

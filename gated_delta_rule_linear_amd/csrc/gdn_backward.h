@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gdn_kernels.h"
+
 namespace gdn {
 
 struct BackwardLaunch {
@@ -30,11 +32,11 @@ struct BackwardLaunch {
     bool bf16;
     int64_t T_total;
     void* workspace;             // backward_workspace_bytes(...) bytes
-    int64_t seg = 0;             // time split segment length (tokens, multiple of 16); 0: none
+    int64_t seg = 0;             // time split segment length (tokens, multiple of 64); 0: none
 };
 
 // Segment length of the backward's time split for these sizes (tokens, a
-// multiple of 16; 0: every (sequence, head) walked by one workgroup).  Depends
+// multiple of 64; 0: every (sequence, head) walked by one workgroup).  Depends
 // on the arguments only, and on the environment variable GDN_BACKWARD_SEGMENT,
 // which forces a length (0 = never split).
 int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H);
@@ -44,26 +46,24 @@ int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H);
 //    dtype.  Sequence n's sub-chunk c uses slot cu[n] / 16 + n + c (slots never
 //    overlap: a sequence of len tokens needs ceil(len / 16) of them and the next
 //    one starts at least that far on), so T_total / 16 + num_seqs slots per head.
-//  - With a time split of segment length seg, per segment slot and head (slot
+//  - With a time split of segment length seg: at pre_off, the forward pass's
+//    split workspace (prefill_workspace_layout: the maps M, N of the non-last
+//    segments and the segment table); at d_off, per segment slot and head (slot
 //    cu[n] / seg + n + j for segment j of sequence n, T_total / seg + num_seqs
-//    slots): the segment's transition M (d_k x d_k fp32), its offset N (d_k x d_v
-//    fp32, replaced by the next segment's start state) and D (d_k x d_v fp32: the
-//    state gradient at the segment's start from a zero end gradient, replaced by
-//    the previous segment's end gradient).
+//    slots) the d_k x d_v fp32 state gradient D of the reverse fold.
 struct BackwardWorkspace {
     int64_t slots = 0;
-    size_t m_off = 0, n_off = 0, d_off = 0, bytes = 0;
+    size_t pre_off = 0, d_off = 0, bytes = 0;
 };
 inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_seqs, int32_t H, int32_t dk,
                                                    int32_t dv, bool bf16, int64_t seg) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     BackwardWorkspace w;
-    w.m_off = al(((size_t)(T_total / 16) + (size_t)num_seqs) * (size_t)H * (size_t)dk * (size_t)dv * (bf16 ? 2 : 4));
-    w.bytes = w.m_off;
+    w.pre_off = al(((size_t)(T_total / 16) + (size_t)num_seqs) * (size_t)H * (size_t)dk * (size_t)dv * (bf16 ? 2 : 4));
+    w.bytes = w.pre_off;
     if (seg > 0) {
         w.slots = T_total / seg + num_seqs;
-        w.n_off = w.m_off + al((size_t)w.slots * H * dk * dk * sizeof(float));
-        w.d_off = w.n_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
+        w.d_off = w.pre_off + al(prefill_workspace_layout(T_total, num_seqs, H, dk, dv, seg).bytes);
         w.bytes = w.d_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
     }
     return w;

@@ -52,10 +52,11 @@
 // (segment, head).  The forward map of a segment is affine in its start
 // state, S_end = M S_start + N, and the reverse map of its state gradient is
 // dS_start = M^T dS_end + D (D: the reverse sweep's result for dS_end = 0).
-//  a. bwd_states_kernel<MAP_M>, <MAP_N>: M (from I, v = 0) and N (from 0) of
-//     every segment; bwd_grad_kernel<DONLY>: D of every segment but the first;
-//  b. bwd_fold_fwd_kernel: S_start(j + 1) = M_j S_start(j) + N_j in order;
-//     bwd_fold_rev_kernel: dS_end(j - 1) = M_j^T dS_end(j) + D_j in reverse;
+//  a. the forward pass's own time split (launch_prefill_maps): M_j and N_j of
+//     every non-last segment and the fold S_start(j + 1) = M_j S_start(j) + N_j;
+//     bwd_grad_kernel<DONLY>: D_j of every segment but the first, the last one
+//     started from dL/d(final state), which makes it dS_end of the one before;
+//  b. bwd_fold_rev_kernel: dS_end(j - 1) = M_j^T dS_end(j) + D_j in reverse;
 //  c. sweeps 1 and 2 per segment, from S_start(j) and dS_end(j).
 #include <type_traits>
 
@@ -86,17 +87,20 @@ struct BArgs {
     float* dS0;        // [num_seqs, H, DK, DV] or null (not wanted)
     TI* ck;            // checkpoints: slot (cu[n] / 16 + n + c, h) is the start state of sub-chunk c of sequence n
     int H;
-    // Time split (seg > 0, a multiple of 16): sequence n is cut into segments of
-    // seg tokens, segment j using slot cu[n] / seg + n + j of the areas below
-    // (d_k x d_k or d_k x d_v fp32 per slot and head):
-    //   wsM  the segment's transition M (S_end = M S_start + N)
-    //   wsN  its offset N, replaced by the next segment's start state (forward fold)
-    //   wsD  D, the state gradient at its start for a zero end gradient, replaced
-    //        by the previous segment's end gradient (reverse fold)
+    // Time split (seg > 0, a multiple of 64): sequence n is cut into segments of
+    // seg tokens.  From the forward pass's split, for segment j < last of
+    // sequence n, slot nl[n] + j of
+    //   fM  its transition M_j (d_k x d_k fp32; S_end = M_j S_start + N_j)
+    //   fN  the start state of segment j + 1 (d_k x d_v fp32)
+    // and segment j's slot cu[n] / seg + n + j of
+    //   wsD  D_j, the state gradient at its start for a zero end gradient (the
+    //        last segment's from dL/d(final state)), replaced by the previous
+    //        segment's end gradient in the reverse fold (d_k x d_v fp32)
     int num_seqs;
     int64_t seg;
-    float* wsM;
-    float* wsN;
+    const int32_t* nl;
+    const float* fM;
+    const float* fN;
     float* wsD;
 };
 
@@ -149,9 +153,9 @@ __device__ __forceinline__ BUnit bwd_unit(const BArgs<TI>& a, int b) {
 // channel.  FULL: the gradient kernel's buffers; otherwise the forward one's.
 // With bf16 inputs (STAGE) the next sub-chunk's raw inputs, and in the
 // gradient kernel its checkpoint, are copied into a staging area by DMA
-// while the current one is processed.  LITE: without what only the outputs
-// or the checkpoints need (FULL: U, dRm, F dS, the staged v and checkpoint;
-// otherwise the checkpoint tile), so that two workgroups share a compute unit.
+// while the current one is processed.  LITE (FULL only): without what only
+// the outputs need (U, dRm, F dS, the staged v and checkpoint), so that two
+// workgroups share a compute unit.
 template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false>
 struct BCfg {
     typedef Mma<TI> M;
@@ -201,13 +205,13 @@ struct BCfg {
     static constexpr int STG_END = STAGE ? ST_C + (GX ? DK * DV * ES : 0) : OFF_STG;
     // forward kernel: the state in the input dtype, rows padded, for coalesced checkpoint stores
     static constexpr int OFF_CK = STG_END;
-    static constexpr int LDS = OFF_CK + (FULL || LITE ? 0 : DK * SV * ES);
+    static constexpr int LDS = OFF_CK + (FULL ? 0 : DK * SV * ES);
     static_assert(B_NK % 16 == 0 && B_TK % 16 == 0 && B_NV % 16 == 0 && B_FS % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // Copy of one sub-chunk's raw inputs (t0: first token, L tokens) into the staging area.
-template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false, bool WITH_V = true>
+template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false>
 __device__ __forceinline__ void dma_inputs(const BArgs<TI>& a, char* smem, int h, int64_t t0, int L, int w,
                                            int lane) {
     typedef BCfg<TI, DK, DV, FULL, NWX, LITE> P;
@@ -219,7 +223,7 @@ __device__ __forceinline__ void dma_inputs(const BArgs<TI>& a, char* smem, int h
         dma_rows<DK * P::ES, CB, P::NW>(a.q + row0 * DK, (size_t)H * DK * P::ES, L, smem + P::ST_Q, w, lane);
         dma_rows<DV * P::ES, CB, P::NW>(a.dO + row0 * DV, (size_t)H * DV * P::ES, L, smem + P::ST_O, w, lane);
     }
-    if constexpr (WITH_V && !(FULL && LITE))
+    if constexpr (!(FULL && LITE))
         dma_rows<DV * P::ES, CB, P::NW>(a.v + row0 * DV, (size_t)H * DV * P::ES, L, smem + P::ST_V, w, lane);
     if (w == P::NW - 1)
         __builtin_amdgcn_global_load_lds(as_global(a.beta + row0 + (size_t)min(lane, L - 1) * H),
@@ -398,24 +402,12 @@ __device__ __forceinline__ floatx4 gram_inverse(char* smem, int lane) {
 }
 
 // Forward sweep over the sub-chunks of one (sequence, head), or with a time
-// split of one (segment, head).
-//  CK:  stores every sub-chunk's start state (its checkpoint), starting from
-//       the initial state, or from the segment's start state left by the
-//       forward fold.
-//  MAP_M, MAP_N: the segment's transition (time split, sequences of two or
-//       more segments), written to the segment's slot at the end: M from the
-//       start state I with v = 0 (d_k / 16 waves, wave w carrying columns
-//       [16w, 16w + 16) of M), or N from the start state 0 (not for the last
-//       segment, which the forward fold does not use).
-constexpr int SWEEP_CK = 0, MAP_M = 1, MAP_N = 2;
-// (The second launch bound is waves per SIMD: two workgroups of NW waves per
-// compute unit need NW / 2.)
-template <typename TI, int DK, int DV, int MODE>
-__global__ __launch_bounds__(MODE == MAP_M ? DK * 4 : DV * 4, MODE == SWEEP_CK ? 1 : (MODE == MAP_M ? DK : DV) / 32)
-void bwd_states_kernel(BArgs<TI> a) {
-    constexpr bool CK = MODE == SWEEP_CK, mcol = MODE == MAP_M;
-    constexpr int NWX = mcol ? DK / 16 : DV / 16;
-    typedef BCfg<TI, DK, DV, false, NWX, !CK> P;
+// split of one (segment, head), storing every sub-chunk's start state (its
+// checkpoint), from the initial state or from the segment's start state left
+// by the forward fold.
+template <typename TI, int DK, int DV>
+__global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
+    typedef BCfg<TI, DK, DV, false> P;
     typedef Mma<TI> M;
     typedef K16<TI> K;
     __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
@@ -423,7 +415,7 @@ void bwd_states_kernel(BArgs<TI> a) {
     const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int H = a.H;
     const BUnit u = bwd_unit(a, blockIdx.x);
-    if (!u.valid || (!CK && u.P < 2) || (MODE == MAP_N && u.j == u.P - 1)) return;
+    if (!u.valid) return;
     const int n = u.n, h = u.h;
     const int64_t sb = u.sb, se = u.se;
     const int col0 = 16 * w;
@@ -438,23 +430,16 @@ void bwd_states_kernel(BArgs<TI> a) {
 
     // state, own columns: S[rt][i] = S[16 rt + 4g + i][col0 + r]
     floatx4 S[P::RT];
-    const float* s0 = nullptr;
-    if (CK) {
-        if (u.j == 0) s0 = a.S0 ? a.S0 + ((size_t)n * H + h) * DK * DV : nullptr;
-        else s0 = a.wsN + ((size_t)(u.slot - 1) * H + h) * DK * DV;
-    }
+    const float* s0;
+    if (u.j == 0) s0 = a.S0 ? a.S0 + ((size_t)n * H + h) * DK * DV : nullptr;
+    else s0 = a.fN + ((size_t)(a.nl[n] + u.j - 1) * H + h) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * rt + 4 * g0 + i;
-            S[rt][i] = mcol ? (row == col0 + r0 ? 1.f : 0.f) : s0 ? s0[row * DV + col0 + r0] : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[(16 * rt + 4 * g0 + i) * DV + col0 + r0] : 0.f;
 
     if constexpr (P::STAGE)
-        if (se > sb)
-            dma_inputs<TI, DK, DV, false, NWX, !CK, !mcol>(a, smem, h, sb, (int)(se - sb < CB ? se - sb : CB), w,
-                                                          tid0 & 63);
+        if (se > sb) dma_inputs<TI, DK, DV, false>(a, smem, h, sb, (int)(se - sb < CB ? se - sb : CB), w, tid0 & 63);
     TI* ck = a.ck + (((size_t)(u.tb >> 4) + n + (size_t)((sb - u.tb) >> 4)) * H + h) * DK * DV;
     for (int64_t t0 = sb; t0 < se; t0 += CB, ck += (size_t)H * DK * DV) {
         const int L = (int)(se - t0 < CB ? se - t0 : CB);
@@ -467,21 +452,16 @@ void bwd_states_kernel(BArgs<TI> a) {
         if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's copy of the sub-chunk has landed
         lds_barrier();  // ... and every wave's; the previous sub-chunk is done with LDS
         // the checkpoint: own columns into LDS, then whole rows out in 16-byte pieces
-        if constexpr (CK) {
 #pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt)
+        for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sCK[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(S[rt][i]);
-        }
-        floatx4 vv = prep<TI, DK, DV, false, NWX, !CK>(a, smem, h, t0, L, tid, mcol ? 0 : col0);
-        if constexpr (mcol) vv = zero4();
+            for (int i = 0; i < 4; ++i) sCK[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(S[rt][i]);
+        const floatx4 vv = prep<TI, DK, DV, false>(a, smem, h, t0, L, tid, col0);
         if constexpr (P::STAGE) {
             const int64_t t1 = t0 + CB;
-            if (t1 < se)
-                dma_inputs<TI, DK, DV, false, NWX, !CK, !mcol>(a, smem, h, t1, (int)(se - t1 < CB ? se - t1 : CB),
-                                                               w, lane);
+            if (t1 < se) dma_inputs<TI, DK, DV, false>(a, smem, h, t1, (int)(se - t1 < CB ? se - t1 : CB), w, lane);
         }
-        if constexpr (CK) {
+        {
             constexpr int PER = 16 / P::ES, NPR = DV / PER;
 #pragma unroll
             for (int k = 0; k < DK * NPR / P::NT; ++k) {
@@ -490,7 +470,7 @@ void bwd_states_kernel(BArgs<TI> a) {
                     *reinterpret_cast<const floatx4*>(sCK + row * P::SV + pc * PER);
             }
         }
-        if (w == 0) (void)gram_inverse<TI, DK, DV, false, NWX, !CK>(smem, lane);
+        if (w == 0) (void)gram_inverse<TI, DK, DV, false>(smem, lane);
         // R = V - k~ (E S), own columns
         floatx4 acc = zero4();
 #pragma unroll(P::UNR)
@@ -516,79 +496,29 @@ void bwd_states_kernel(BArgs<TI> a) {
             S[rt] = gm * S[rt] + ff * d;
         }
     }
-    if constexpr (!CK) {
-        constexpr int LD = mcol ? DK : DV;
-        float* dst = (mcol ? a.wsM : a.wsN) + ((size_t)u.slot * H + h) * DK * LD;
-#pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g0 + i) * LD + col0 + r0] = S[rt][i];
-    }
-}
-
-// Time split, forward fold, per (sequence, head) and 16 state columns: the
-// start state of segment j + 1 is M_j S_start(j) + N_j, written over N_j.
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_fold_fwd_kernel(const int32_t* cu, int H, int64_t seg, const float* S0,
-                                                           const float* wsM, float* wsN) {
-    constexpr int TPR = 256 / DK, CPT = 16 / TPR;
-    __shared__ float sx[DK][16];
-    const int unit = blockIdx.x, n = unit / H, h = unit - n * H, c0 = 16 * blockIdx.y;
-    const int64_t tb = cu[n], len = cu[n + 1] - tb;
-    const int P = (int)((len + seg - 1) / seg);
-    if (P < 2) return;
-    const int64_t base = tb / seg + n;
-    const int tid = threadIdx.x, i = tid / TPR, cc = (tid % TPR) * CPT;
-    for (int e = tid; e < DK * 16; e += 256)
-        sx[e >> 4][e & 15] = S0 ? S0[((size_t)unit * DK + (e >> 4)) * DV + c0 + (e & 15)] : 0.f;
-    __syncthreads();
-    for (int j = 0; j + 1 < P; ++j) {
-        const size_t sl = (size_t)(base + j) * H + h;
-        const float* Mi = wsM + sl * DK * DK + (size_t)i * DK;  // row i of M_j
-        float* Nj = wsN + sl * DK * DV + (size_t)i * DV + c0 + cc;
-        float acc[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = Nj[c];
-#pragma unroll 8
-        for (int k = 0; k < DK; k += 4) {
-            const floatx4 m = *reinterpret_cast<const floatx4*>(Mi + k);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) acc[c] = __builtin_fmaf(m[e], sx[k + e][cc + c], acc[c]);
-        }
-        __syncthreads();  // every read of x is done
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            sx[i][cc + c] = acc[c];
-            Nj[c] = acc[c];
-        }
-        __syncthreads();
-    }
 }
 
 // Time split, reverse fold, per (sequence, head) and 16 state columns: from
-// x = dL/d(final state), for j = P-1 down to 1, x <- M_j^T x + D_j (the state
-// gradient at the start of segment j, i.e. at the end of segment j - 1),
-// written over D_j.
+// x = dS_end of the second-to-last segment (the last segment's adjoint-only
+// sweep, started from dL/d(final state)), for j = P-2 down to 1,
+// x <- M_j^T x + D_j, the gradient at the end of segment j - 1, written over D_j.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_fold_rev_kernel(const int32_t* cu, int H, int64_t seg, const float* dSf,
-                                                           const float* wsM, float* wsD) {
+__global__ __launch_bounds__(256) void bwd_fold_rev_kernel(const int32_t* cu, const int32_t* nl, int H, int64_t seg,
+                                                           const float* fM, float* wsD) {
     constexpr int TPR = 256 / DK, CPT = 16 / TPR;
     __shared__ float sx[DK][16];
     const int unit = blockIdx.x, n = unit / H, h = unit - n * H, c0 = 16 * blockIdx.y;
     const int64_t tb = cu[n], len = cu[n + 1] - tb;
     const int P = (int)((len + seg - 1) / seg);
-    if (P < 2) return;
+    if (P < 3) return;
     const int64_t base = tb / seg + n;
     const int tid = threadIdx.x, i = tid / TPR, cc = (tid % TPR) * CPT;
-    for (int e = tid; e < DK * 16; e += 256)
-        sx[e >> 4][e & 15] = dSf ? dSf[((size_t)unit * DK + (e >> 4)) * DV + c0 + (e & 15)] : 0.f;
+    const float* x0 = wsD + ((size_t)(base + P - 1) * H + h) * DK * DV;
+    for (int e = tid; e < DK * 16; e += 256) sx[e >> 4][e & 15] = x0[(size_t)(e >> 4) * DV + c0 + (e & 15)];
     __syncthreads();
-    for (int j = P - 1; j >= 1; --j) {
-        const size_t sl = (size_t)(base + j) * H + h;
-        const float* Mc = wsM + sl * DK * DK + i;  // column i of M_j
-        float* Dj = wsD + sl * DK * DV + (size_t)i * DV + c0 + cc;
+    for (int j = P - 2; j >= 1; --j) {
+        const float* Mc = fM + ((size_t)(nl[n] + j) * H + h) * DK * DK + i;  // column i of M_j
+        float* Dj = wsD + ((size_t)(base + j) * H + h) * DK * DV + (size_t)i * DV + c0 + cc;
         float acc[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) acc[c] = Dj[c];
@@ -615,8 +545,10 @@ __global__ __launch_bounds__(256) void bwd_fold_rev_kernel(const int32_t* cu, in
 // iteration, after its wait for the copies in flight, so that wait does not
 // include them.
 // DONLY (time split, segments after the first): only the state-gradient
-// recursion, from a zero end gradient; its result D is written to the
-// segment's slot for the reverse fold.  It needs neither the checkpoints nor v.
+// recursion, from a zero end gradient (the last segment: from dL/d(final
+// state)); its result is written to the segment's slot for the reverse fold.
+// It needs neither the checkpoints nor v.
+// (DONLY: two workgroups per compute unit, i.e. d_v / 32 waves per SIMD.)
 template <typename TI, int DK, int DV, bool DONLY>
 __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(BArgs<TI> a) {
     typedef BCfg<TI, DK, DV, true, DV / 16, DONLY> P;
@@ -658,11 +590,9 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
 
     // dS = dL/d(state at the end of the current sub-chunk), own columns
     floatx4 dS[P::RT];
-    const float* dsf = nullptr;
-    if (!DONLY) {
-        if (u.j == u.P - 1) dsf = a.dSf ? a.dSf + ((size_t)n * H + h) * DK * DV : nullptr;
-        else dsf = a.wsD + ((size_t)(u.slot + 1) * H + h) * DK * DV;
-    }
+    const float* dsf;
+    if (u.j == u.P - 1) dsf = a.dSf ? a.dSf + ((size_t)n * H + h) * DK * DV : nullptr;
+    else dsf = DONLY ? nullptr : a.wsD + ((size_t)(u.slot + 1) * H + h) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
@@ -979,37 +909,54 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     a.H = p.H;
     a.num_seqs = p.num_seqs;
     a.seg = p.seg;
-    a.wsM = a.wsN = a.wsD = nullptr;
+    a.nl = nullptr;
+    a.fM = a.fN = nullptr;
+    a.wsD = nullptr;
     if (p.seg <= 0) {
         const unsigned blocks = (unsigned)((int64_t)p.num_seqs * p.H);
-        hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, SWEEP_CK>), dim3(blocks), dim3(DV * 4), 0, s, a);
+        hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
         return hipGetLastError();
     }
-    // time split: transitions and end-gradient-free adjoints per segment, the
-    // two folds, then both sweeps per segment from the folded boundary values
+    // time split: the forward's maps and fold, the adjoint-only sweeps, the
+    // reverse fold, then both sweeps per segment from the folded boundary values
     const BackwardWorkspace ws = backward_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.bf16, p.seg);
     char* base = static_cast<char*>(p.workspace);
-    a.wsM = reinterpret_cast<float*>(base + ws.m_off);
-    a.wsN = reinterpret_cast<float*>(base + ws.n_off);
+    const PrefillWorkspace pw = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
+    a.nl = reinterpret_cast<const int32_t*>(base + ws.pre_off + pw.nl_off);
+    a.fM = reinterpret_cast<const float*>(base + ws.pre_off + pw.m_off);
+    a.fN = reinterpret_cast<const float*>(base + ws.pre_off + pw.n_off);
     a.wsD = reinterpret_cast<float*>(base + ws.d_off);
-    const unsigned blocks = (unsigned)(ws.slots * p.H);
-    const dim3 fold_grid((unsigned)((int64_t)p.num_seqs * p.H), DV / 16);
-    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, MAP_M>), dim3(blocks), dim3(DK * 4), 0, s, a);
-    hipError_t e = hipGetLastError();
+    PrefillLaunch f;
+    f.q = p.q;
+    f.k = p.k;
+    f.v = p.v;
+    f.g = p.g;
+    f.beta = p.beta;
+    f.cu_seqlens = p.cu_seqlens;
+    f.initial_state = p.initial_state;
+    f.final_state = nullptr;
+    f.o = nullptr;
+    f.num_seqs = p.num_seqs;
+    f.H = p.H;
+    f.dk = DK;
+    f.dv = DV;
+    f.bf16 = p.bf16;
+    f.T_total = p.T_total;
+    f.seg = p.seg;
+    f.workspace = base + ws.pre_off;
+    f.legacy = false;
+    hipError_t e = launch_prefill_maps(f, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, MAP_N>), dim3(blocks), dim3(DV * 4), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned blocks = (unsigned)(ws.slots * p.H);
     hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, true>), dim3(blocks), dim3(DV * 4), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_fold_fwd_kernel<DK, DV>), fold_grid, dim3(256), 0, s, a.cu, p.H, p.seg, a.S0, a.wsM, a.wsN);
+    hipLaunchKernelGGL((bwd_fold_rev_kernel<DK, DV>), dim3((unsigned)((int64_t)p.num_seqs * p.H), DV / 16),
+                       dim3(256), 0, s, a.cu, a.nl, p.H, p.seg, a.fM, a.wsD);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_fold_rev_kernel<DK, DV>), fold_grid, dim3(256), 0, s, a.cu, p.H, p.seg, a.dSf, a.wsM,
-                       a.wsD);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV, SWEEP_CK>), dim3(blocks), dim3(DV * 4), 0, s, a);
+    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
     return hipGetLastError();

@@ -124,6 +124,13 @@ struct DecodeLaunch {
 
 // Each returns hipSuccess or the launch error.  Sizes are validated by the caller.
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+// The first half of the time split alone (p.seg > 0, workspace laid out by
+// prefill_workspace_layout): the segment table nl, the maps of every non-last
+// segment and the fold.  On return, for segment j of sequence n that is not
+// its last, slot nl[n] + j of wsM holds its transition M_j and slot
+// nl[n] + j of wsN the start state of segment j + 1.  o and final_state are
+// not used.
+hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
 
 }  // namespace gdn

@@ -1837,8 +1837,8 @@ hipError_t launch_seq(const Args<TI>& a, int64_t blocks, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename TI, int DK, int DV>
-hipError_t run(const PrefillLaunch& p, hipStream_t s) {
+template <typename TI>
+Args<TI> make_args(const PrefillLaunch& p) {
     Args<TI> a;
     a.q = static_cast<const TI*>(p.q);
     a.k = static_cast<const TI*>(p.k);
@@ -1860,10 +1860,14 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     a.z = static_cast<const bf16*>(p.z);
     a.gate = p.gate;
     a.gate_param = p.gate_param;
-    const int64_t units = (int64_t)p.num_seqs * p.H;
-    if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
+    return a;
+}
 
-    // Time split: maps of the non-last segments, fold, then every segment.
+// Time split, first half: the segment table, the maps of the non-last
+// segments and the fold (a.seg, a.nl, a.wsM, a.wsN set here).
+template <typename TI, int DK, int DV>
+hipError_t run_maps(const PrefillLaunch& p, Args<TI>& a, hipStream_t s) {
+    const int64_t units = (int64_t)p.num_seqs * p.H;
     const PrefillWorkspace ws = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
     char* w = static_cast<char*>(p.workspace);
     a.seg = p.seg;
@@ -1906,8 +1910,21 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
                            a.nl, p.H, p.initial_state, a.wsM, a.wsN);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = launch_seq<TI, DK, DV, false>(a, ((int64_t)p.num_seqs + ws.slots) * p.H, s);
-    if (e != hipSuccess || !a.final_to_slot || map_blocks == 0) return e;
+    return hipSuccess;
+}
+
+template <typename TI, int DK, int DV>
+hipError_t run(const PrefillLaunch& p, hipStream_t s) {
+    Args<TI> a = make_args<TI>(p);
+    const int64_t units = (int64_t)p.num_seqs * p.H;
+    if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
+
+    // Time split: maps of the non-last segments, fold, then every segment.
+    hipError_t e = run_maps<TI, DK, DV>(p, a, s);
+    if (e != hipSuccess) return e;
+    const int64_t slots = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg).slots;
+    e = launch_seq<TI, DK, DV, false>(a, ((int64_t)p.num_seqs + slots) * p.H, s);
+    if (e != hipSuccess || !a.final_to_slot || slots * p.H == 0) return e;
     hipLaunchKernelGGL((seg_final_kernel<DK, DV>), dim3((unsigned)units), dim3(256), 0, s, a.nl, p.H, a.wsN,
                        p.final_state);
     return hipGetLastError();
@@ -1922,11 +1939,26 @@ hipError_t run_t(const PrefillLaunch& p, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+template <typename TI>
+hipError_t run_maps_t(const PrefillLaunch& p, hipStream_t s) {
+    Args<TI> a = make_args<TI>(p);
+    if (p.dk == 128 && p.dv == 128) return run_maps<TI, 128, 128>(p, a, s);
+    if (p.dk == 128 && p.dv == 64) return run_maps<TI, 128, 64>(p, a, s);
+    if (p.dk == 64 && p.dv == 128) return run_maps<TI, 64, 128>(p, a, s);
+    if (p.dk == 64 && p.dv == 64) return run_maps<TI, 64, 64>(p, a, s);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s) {
     if ((int64_t)p.num_seqs * p.H == 0) return hipSuccess;
     return p.bf16 ? run_t<bf16>(p, s) : run_t<float>(p, s);
+}
+
+hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t s) {
+    if ((int64_t)p.num_seqs * p.H == 0 || p.seg <= 0) return hipSuccess;
+    return p.bf16 ? run_maps_t<bf16>(p, s) : run_maps_t<float>(p, s);
 }
 
 }  // namespace gdn

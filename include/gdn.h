@@ -195,10 +195,10 @@ int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const voi
 /* Device scratch bytes gdn_prefill_backward needs: one state per 16-token
  * sub-chunk and head in the input dtype, (T_total / 16 + num_seqs) * H * d_k
  * * d_v * (2 for GDN_BF16, 4 for GDN_F32), rounded up to 256; with a time
- * split of segment length L (below), (T_total / L + num_seqs) * H * (d_k * d_k
- * + 2 * d_k * d_v) * 4 more, each of the three areas rounded up to 256.
- * Depends on the arguments and on GDN_BACKWARD_SEGMENT only; 0 for invalid
- * arguments. */
+ * split of segment length L (below), also gdn_prefill's split workspace for
+ * segments of L tokens and (T_total / L + num_seqs) * H * d_k * d_v * 4 bytes,
+ * each rounded up to 256.  Depends on the arguments and on
+ * GDN_BACKWARD_SEGMENT only; 0 for invalid arguments. */
 size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k,
                                             int32_t d_v, int32_t dtype);
 
@@ -241,14 +241,14 @@ size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, i
  * Generation", section 3.1).
  * Time split: when few (sequence, head) pairs leave compute units idle
  * (num_seqs * H <= 144) and sequences are long, each sequence is cut into
- * segments of L tokens (a multiple of 16) swept in parallel.  The state map
+ * segments of L tokens (a multiple of 64) swept in parallel.  The state map
  * of a segment is affine, S_end = M S_start + N, and its adjoint
- * dS_start = M^T dS_end + D; M, N and D of every segment come from
- * per-segment sweeps, two sequential folds give every segment's start state
- * and end gradient, then both sweeps run per segment.  Same results up to
- * rounding.  GDN_BACKWARD_SEGMENT=L forces the length (rounded up to a
- * multiple of 16), 0 turns the split off; it must not change between the
- * workspace query and the call. */
+ * dS_start = M^T dS_end + D.  gdn_prefill's own time split gives M, N and
+ * every segment's start state; per-segment sweeps give D and a sequential
+ * fold every segment's end gradient; then both sweeps run per segment.
+ * Same results up to rounding.  GDN_BACKWARD_SEGMENT=L forces the length
+ * (rounded up to a multiple of 64), 0 turns the split off; it must not
+ * change between the workspace query and the call. */
 int32_t gdn_prefill_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
                              const float* initial_state, const void* d_o, const float* d_final_state, void* dq,

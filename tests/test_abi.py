@@ -177,14 +177,16 @@ def test_backward_workspace_bytes(lib):
 
 
 def _backward_ws(T, n, H, dk, dv, bf16, seg):
-    # checkpoints, then with a time split of segment length seg the per-segment
-    # transition M (d_k x d_k fp32) and the two d_k x d_v fp32 boundary areas
+    # checkpoints, then with a time split of segment length seg the forward
+    # pass's split workspace (M, N of the T // seg non-last segment slots, the
+    # segment table) and one d_k x d_v fp32 gradient per segment slot
     al = lambda x: (x + 255) // 256 * 256
     ck = al((T // 16 + n) * H * dk * dv * (2 if bf16 else 4))
     if seg == 0:
         return ck
-    slots = T // seg + n
-    return ck + al(slots * H * dk * dk * 4) + 2 * al(slots * H * dk * dv * 4)
+    fs = T // seg
+    pre = al(fs * H * dk * dk * 4) + al(fs * H * dk * dv * 4) + al((n + 1) * 4)
+    return ck + al(pre) + al((T // seg + n) * H * dk * dv * 4)
 
 
 def test_backward_workspace_bytes_split(lib, monkeypatch):
@@ -197,8 +199,8 @@ def test_backward_workspace_bytes_split(lib, monkeypatch):
     # enough units to fill the chip, or sequences too short for three segments: no split
     assert f(65536, 8, 32, 128, 128, 1) == _backward_ws(65536, 8, 32, 128, 128, True, 0)
     assert f(1024, 4, 32, 128, 128, 1) == _backward_ws(1024, 4, 32, 128, 128, True, 0)
-    # forced length, rounded up to a multiple of 16; 0 turns the split off
-    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "250")
+    # forced length, rounded up to a multiple of 64; 0 turns the split off
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "200")
     assert f(1000, 3, 2, 64, 128, 0) == _backward_ws(1000, 3, 2, 64, 128, False, 256)
     monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "0")
     assert f(32768, 4, 32, 128, 128, 1) == _backward_ws(32768, 4, 32, 128, 128, True, 0)

@@ -138,13 +138,13 @@ def test_bf16_rectangular_longer(dk, dv):
 # tokens, with the transitions, both folds and the per-segment sweeps
 
 
-@pytest.mark.parametrize("seg,dk,dv,dtype", [(48, 128, 128, torch.bfloat16), (32, 64, 64, torch.float32),
-                                             (64, 64, 128, torch.bfloat16), (64, 128, 64, torch.bfloat16),
-                                             (16, 128, 128, torch.float32)])
+@pytest.mark.parametrize("seg,dk,dv,dtype", [(64, 128, 128, torch.bfloat16), (64, 64, 64, torch.float32),
+                                             (128, 64, 128, torch.bfloat16), (64, 128, 64, torch.bfloat16),
+                                             (192, 128, 128, torch.float32)])
 def test_split_ragged(monkeypatch, seg, dk, dv, dtype):
-    # empty sequences, sequences shorter than a segment, ragged last segments
+    # empty sequences, sequences of one, two and many segments, ragged last segments
     monkeypatch.setenv("GDN_BACKWARD_SEGMENT", str(seg))
-    _case([1, 15, 16, 17, 63, 0, 130, 700], 3, dk, dv, dtype, seed=10)
+    _case([1, 15, 16, 17, 63, 0, 130, 700, 128, 129], 3, dk, dv, dtype, seed=10)
 
 
 def test_split_pages_gate_long(monkeypatch):
