@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -71,10 +72,18 @@ int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32
     const double whole = K::rounds(units) * (std::ceil(len / 64.0) + K::START);
     double best = whole;
     int64_t best_seg = 0;
-    for (int64_t ls = 1024; ls < len; ls += 512) {
+    // Split of P segments: the output pass of segment 0 beside the maps of
+    // segments 1 .. P-2 (one pass: its critical path is the longer of the two,
+    // counted as output chunks in rounds of all their workgroups), the fold
+    // from segment 1, then the output pass of segments 1 .. P-1.
+    const int64_t step = std::max<int64_t>(64, len / 2048 / 64 * 64);
+    for (int64_t ls = 1024; ls < len; ls += step) {
         const double P = std::ceil((double)len / ls), ch = ls / 64.0;
-        const double t = K::maps_pass(units * (P - 1), ch, share, nullptr) +
-                         K::fold_pass(P - 1, units * (d_v / 16)) + K::rounds(units * P) * (ch + K::START);
+        bool both = false;
+        const double maps = K::maps_pass(units * (P - 2), ch, share, &both);
+        const double first = K::rounds(units + (both ? 1 : 2) * units * (P - 2)) * (ch + K::START);
+        const double t = std::max(first, maps) + K::fold_pass(P - 2, units * (d_v / 16)) +
+                         K::rounds(units * (P - 1)) * (ch + K::START);
         if (t < best) {
             best = t;
             best_seg = ls;

@@ -50,6 +50,8 @@
 //
 // This restates, chunk by chunk, the token recurrence
 //   S_t = diag(a_t) S_{t-1} + b_t k_t (v_t - (diag(a_t) S_{t-1})^T k_t)^T, o_t = S_t^T q_t.
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_kernels.h"
@@ -125,7 +127,9 @@ struct Args {
     float* wsM;
     float* wsN;
     int m_blocks;       // map launches: blocks [0, m_blocks) compute M, the rest N
-    int final_to_slot;  // final state of a split sequence goes to its last slot (final_state aliases S0)
+    int map_from;       // map launches: first segment of a sequence that gets a map (0 or 1)
+    int phase;          // split output launches: 0 every segment; 1 segment 0 only (one workgroup per
+                        // (sequence, head), its end state to slot nl[n] when more segments follow); 2 the rest
     int legacy;         // bf16: use the single-role kernel instead of the warp-specialised one
     // gate != GATE_LOG: g is not read; the log-decay comes from the bf16 logits
     // z in the same layout (warp-specialised kernel only)
@@ -374,6 +378,10 @@ __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
             return u;
         }
         const int n = seq_of(a.nl, a.num_seqs, k, 0);
+        if (k - a.nl[n] < a.map_from) {
+            u.valid = false;
+            return u;
+        }
         u.tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
         u.te = u.tb + a.seg;
         u.eye = true;
@@ -389,10 +397,23 @@ __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
             return u;
         }
         const int n = seq_of(a.nl, a.num_seqs, k, 0);
+        if (k - a.nl[n] < a.map_from) {
+            u.valid = false;
+            return u;
+        }
         u.tb = a.cu[n] + (int64_t)(k - a.nl[n]) * a.seg;
         u.te = u.tb + a.seg;
         u.eye = u.vzero = kindM;
         u.sf = kindM ? a.wsM + ((size_t)k * H + u.h) * DK * DK : a.wsN + ((size_t)k * H + u.h) * DK * DV;
+    } else if (a.seg > 0 && a.phase == 1) {
+        const int n = b / H;
+        u.h = b - n * H;
+        const size_t unit = (size_t)b;
+        u.tb = a.cu[n];
+        u.te = u.tb + a.seg < a.cu[n + 1] ? u.tb + a.seg : a.cu[n + 1];
+        u.s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
+        if (a.nl[n + 1] > a.nl[n]) u.sf = a.wsN + ((size_t)a.nl[n] * H + u.h) * DK * DV;
+        else u.sf = a.Sf ? a.Sf + unit * DK * DV : nullptr;
     } else if (a.seg > 0) {
         const int q = b / H;
         u.h = b - q * H;
@@ -402,12 +423,16 @@ __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
         }
         const int n = seq_of(a.nl, a.num_seqs, q, 1);
         const int j = q - (a.nl[n] + n), last = a.nl[n + 1] - a.nl[n];
+        if (a.phase == 2 && j == 0) {
+            u.valid = false;
+            return u;
+        }
         const size_t unit = (size_t)n * H + u.h;
         u.tb = a.cu[n] + (int64_t)j * a.seg;
         u.te = u.tb + a.seg < a.cu[n + 1] ? u.tb + a.seg : a.cu[n + 1];
         if (j == 0) u.s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
         else u.s0 = a.wsN + ((size_t)(a.nl[n] + j - 1) * H + u.h) * DK * DV;
-        if (j == last && a.Sf) u.sf = (j > 0 && a.final_to_slot) ? const_cast<float*>(u.s0) : a.Sf + unit * DK * DV;
+        if (j == last && a.Sf) u.sf = a.Sf + unit * DK * DV;
     } else {
         const int n = b / H;
         u.h = b - n * H;
@@ -1751,23 +1776,26 @@ __global__ __launch_bounds__(256) void seg_table_kernel(const int32_t* __restric
 
 // Serial fold over the segments of one (sequence, head), 16 state columns per
 // workgroup (columns of the state evolve independently):
-//   S_start(j + 1) = M_j S_start(j) + N_j,  S_start(0) = S0 (or zero),
-// written over N_j.  fp32 FMA; M_j is staged in LDS, S in LDS.
+//   S_start(j + 1) = M_j S_start(j) + N_j,  j >= first,
+// written over N_j, from S_start(0) = S0 (or zero) when first = 0, or from
+// S_start(1) already in slot N_0 (segment 0's own end state) when first = 1.
+// fp32 FMA; M_j is staged in LDS, S in LDS.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void seg_fold_kernel(const int32_t* __restrict__ nl, int H,
                                                        const float* __restrict__ S0, const float* __restrict__ wsM,
-                                                       float* __restrict__ wsN) {
+                                                       float* __restrict__ wsN, int first) {
     constexpr int NCB = DV / 16, RPT = DK / 16, LDM = DK + 4;
     extern __shared__ __attribute__((aligned(16))) float fsm[];
     float* Ms = fsm;              // [DK][LDM]
     float* Ss = fsm + DK * LDM;  // [DK][16]
     const int bid = blockIdx.x, cb = bid % NCB, unit = bid / NCB, n = unit / H, h = unit - n * H;
     const int k0 = nl[n], cnt = nl[n + 1] - k0;
-    if (cnt == 0) return;
+    if (cnt <= first) return;
     const int t = threadIdx.x, c = t & 15, rg = t >> 4;  // column c, rows rg + 16 r
     const int col = 16 * cb + c;
-    for (int i = rg; i < DK; i += 16) Ss[i * 16 + c] = S0 ? S0[((size_t)unit * DK + i) * DV + col] : 0.f;
-    for (int j = 0; j < cnt; ++j) {
+    const float* x0 = first ? wsN + ((size_t)k0 * H + h) * DK * DV : S0 ? S0 + (size_t)unit * DK * DV : nullptr;
+    for (int i = rg; i < DK; i += 16) Ss[i * 16 + c] = x0 ? x0[(size_t)i * DV + col] : 0.f;
+    for (int j = first; j < cnt; ++j) {
         const size_t slot = (size_t)(k0 + j) * H + h;
         const floatx4* M = reinterpret_cast<const floatx4*>(wsM + slot * DK * DK);
         float* N = wsN + slot * DK * DV;
@@ -1796,18 +1824,6 @@ __global__ __launch_bounds__(256) void seg_fold_kernel(const int32_t* __restrict
             N[(rg + 16 * r) * DV + col] = acc[r];
         }
     }
-}
-
-// final_state of every split sequence, from its last slot (used when
-// final_state aliases the initial state, which segment 0 still reads).
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void seg_final_kernel(const int32_t* __restrict__ nl, int H,
-                                                        const float* __restrict__ wsN, float* __restrict__ Sf) {
-    const int unit = blockIdx.x, n = unit / H, h = unit - n * H;
-    if (nl[n + 1] == nl[n]) return;  // one segment: written by its own workgroup
-    const floatx4* src = reinterpret_cast<const floatx4*>(wsN + ((size_t)(nl[n + 1] - 1) * H + h) * DK * DV);
-    floatx4* dst = reinterpret_cast<floatx4*>(Sf + (size_t)unit * DK * DV);
-    for (int e = threadIdx.x; e < DK * DV / 4; e += 256) dst[e] = src[e];
 }
 
 template <int DK, int DV, bool MAP, int NCB = 1>
@@ -1855,7 +1871,8 @@ Args<TI> make_args(const PrefillLaunch& p) {
     a.nl = nullptr;
     a.wsM = a.wsN = nullptr;
     a.m_blocks = 0;
-    a.final_to_slot = 0;
+    a.map_from = 0;
+    a.phase = 0;
     a.legacy = p.legacy;
     a.z = static_cast<const bf16*>(p.z);
     a.gate = p.gate;
@@ -1863,29 +1880,34 @@ Args<TI> make_args(const PrefillLaunch& p) {
     return a;
 }
 
-// Time split, first half: the segment table, the maps of the non-last
-// segments and the fold (a.seg, a.nl, a.wsM, a.wsN set here).
+// Time split: the workspace pointers and the segment table.
 template <typename TI, int DK, int DV>
-hipError_t run_maps(const PrefillLaunch& p, Args<TI>& a, hipStream_t s) {
-    const int64_t units = (int64_t)p.num_seqs * p.H;
+hipError_t run_table(const PrefillLaunch& p, Args<TI>& a, hipStream_t s) {
     const PrefillWorkspace ws = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
     char* w = static_cast<char*>(p.workspace);
     a.seg = p.seg;
     a.nl = reinterpret_cast<int32_t*>(w + ws.nl_off);
     a.wsM = reinterpret_cast<float*>(w + ws.m_off);
     a.wsN = reinterpret_cast<float*>(w + ws.n_off);
-    a.final_to_slot = p.final_state && p.final_state == p.initial_state;
     hipLaunchKernelGGL(seg_table_kernel, dim3(1), dim3(256), 0, s, p.cu_seqlens, p.num_seqs, p.seg,
                        const_cast<int32_t*>(a.nl));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+// Time split: the maps of the non-last segments from segment a.map_from on,
+// then the fold from there (after run_table).
+template <typename TI, int DK, int DV>
+hipError_t run_maps_fold(const PrefillLaunch& p, Args<TI>& a, hipStream_t s, hipEvent_t before_fold) {
+    const int64_t units = (int64_t)p.num_seqs * p.H;
+    const PrefillWorkspace ws = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
+    hipError_t e = hipSuccess;
     const int64_t map_blocks = ws.slots * p.H;
     if (map_blocks > 0) {
         // M and N in one workgroup or in two: decided for the number of
         // transitions that sequences of the mean length would have (the grid
         // is sized for the bound; surplus workgroups exit at once)
         const int64_t len = (p.T_total + p.num_seqs - 1) / p.num_seqs;
-        const double maps = (double)p.num_seqs * p.H * (len > 0 ? (len - 1) / p.seg : 0);
+        const double maps = (double)p.num_seqs * p.H * (len > 0 ? std::max<int64_t>(0, (len - 1) / p.seg - a.map_from) : 0);
         bool both = false;
         SplitCost::maps_pass(maps, p.seg / 64.0, DK == DV && sizeof(TI) == 2, &both);
         if constexpr (DK == DV && sizeof(TI) == 2) {
@@ -1902,14 +1924,32 @@ hipError_t run_maps(const PrefillLaunch& p, Args<TI>& a, hipStream_t s) {
             if (e == hipSuccess) e = launch_seq<TI, DK, DV, true>(a, map_blocks, s);
         }
         if (e != hipSuccess) return e;
+        if (before_fold && (e = hipStreamWaitEvent(s, before_fold, 0)) != hipSuccess) return e;
         constexpr int FOLD_LDS = (DK * (DK + 4) + DK * 16) * 4;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(seg_fold_kernel<DK, DV>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, FOLD_LDS);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((seg_fold_kernel<DK, DV>), dim3((unsigned)(units * (DV / 16))), dim3(256), FOLD_LDS, s,
-                           a.nl, p.H, p.initial_state, a.wsM, a.wsN);
+                           a.nl, p.H, p.initial_state, a.wsM, a.wsN, a.map_from);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (before_fold) {
+        e = hipStreamWaitEvent(s, before_fold, 0);
     }
+    return e;
+}
+
+// A second stream per device (default priority), for the output pass of every
+// sequence's first segment, which runs beside the maps of the later ones.
+hipError_t side_stream(hipStream_t* out) {
+    static std::mutex mu;
+    static hipStream_t st[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!st[dev] && (e = hipStreamCreateWithFlags(&st[dev], hipStreamNonBlocking)) != hipSuccess) return e;
+    *out = st[dev];
     return hipSuccess;
 }
 
@@ -1919,15 +1959,39 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     const int64_t units = (int64_t)p.num_seqs * p.H;
     if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
 
-    // Time split: maps of the non-last segments, fold, then every segment.
-    hipError_t e = run_maps<TI, DK, DV>(p, a, s);
+    // Time split.  Segment 0 of every sequence needs no map: its own output
+    // pass (on a side stream, after the table) gives the start state of
+    // segment 1 while the maps of segments 1 .. last-1 run on the caller's
+    // stream; the fold then starts at segment 1 and the output pass of the
+    // remaining segments follows.  Segment 0 is done before any later segment
+    // writes a final state, so a final state that aliases the initial state
+    // needs no copy.
+    hipStream_t s2;
+    hipError_t e = side_stream(&s2);
     if (e != hipSuccess) return e;
-    const int64_t slots = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg).slots;
-    e = launch_seq<TI, DK, DV, false>(a, ((int64_t)p.num_seqs + slots) * p.H, s);
-    if (e != hipSuccess || !a.final_to_slot || slots * p.H == 0) return e;
-    hipLaunchKernelGGL((seg_final_kernel<DK, DV>), dim3((unsigned)units), dim3(256), 0, s, a.nl, p.H, a.wsN,
-                       p.final_state);
-    return hipGetLastError();
+    hipEvent_t table_done, first_done;
+    if ((e = hipEventCreateWithFlags(&table_done, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&first_done, hipEventDisableTiming)) != hipSuccess) {
+        (void)hipEventDestroy(table_done);
+        return e;
+    }
+    auto body = [&]() -> hipError_t {
+        hipError_t r = run_table<TI, DK, DV>(p, a, s);
+        if (r != hipSuccess) return r;
+        if ((r = hipEventRecord(table_done, s)) != hipSuccess) return r;
+        if ((r = hipStreamWaitEvent(s2, table_done, 0)) != hipSuccess) return r;
+        a.phase = 1;
+        if ((r = launch_seq<TI, DK, DV, false>(a, units, s2)) != hipSuccess) return r;
+        if ((r = hipEventRecord(first_done, s2)) != hipSuccess) return r;
+        a.map_from = 1;
+        if ((r = run_maps_fold<TI, DK, DV>(p, a, s, first_done)) != hipSuccess) return r;
+        a.phase = 2;
+        const int64_t slots = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg).slots;
+        return launch_seq<TI, DK, DV, false>(a, ((int64_t)p.num_seqs + slots) * p.H, s);
+    };
+    e = body();
+    const hipError_t e1 = hipEventDestroy(table_done), e2 = hipEventDestroy(first_done);
+    return e != hipSuccess ? e : e1 != hipSuccess ? e1 : e2;
 }
 
 template <typename TI>
@@ -1939,13 +2003,19 @@ hipError_t run_t(const PrefillLaunch& p, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+template <typename TI, int DK, int DV>
+hipError_t run_maps(const PrefillLaunch& p, hipStream_t s) {
+    Args<TI> a = make_args<TI>(p);
+    const hipError_t e = run_table<TI, DK, DV>(p, a, s);
+    return e != hipSuccess ? e : run_maps_fold<TI, DK, DV>(p, a, s, nullptr);
+}
+
 template <typename TI>
 hipError_t run_maps_t(const PrefillLaunch& p, hipStream_t s) {
-    Args<TI> a = make_args<TI>(p);
-    if (p.dk == 128 && p.dv == 128) return run_maps<TI, 128, 128>(p, a, s);
-    if (p.dk == 128 && p.dv == 64) return run_maps<TI, 128, 64>(p, a, s);
-    if (p.dk == 64 && p.dv == 128) return run_maps<TI, 64, 128>(p, a, s);
-    if (p.dk == 64 && p.dv == 64) return run_maps<TI, 64, 64>(p, a, s);
+    if (p.dk == 128 && p.dv == 128) return run_maps<TI, 128, 128>(p, s);
+    if (p.dk == 128 && p.dv == 64) return run_maps<TI, 128, 64>(p, s);
+    if (p.dk == 64 && p.dv == 128) return run_maps<TI, 64, 128>(p, s);
+    if (p.dk == 64 && p.dv == 64) return run_maps<TI, 64, 64>(p, s);
     return hipErrorInvalidValue;
 }
 

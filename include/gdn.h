@@ -122,7 +122,10 @@ size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H,
  *
  * Method: each sequence is cut into chunks (32 tokens with GDN_BF16, 64 with
  * GDN_F32), long sequences also into segments run in parallel and joined
- * through the affine map of the state.  Inside a chunk the decay
+ * through the affine map of the state.  A split call runs the first segment's
+ * output pass on a second stream the library keeps per device (default
+ * priority), forked from and joined back into `stream` by events, so the
+ * call stays ordered on `stream`.  Inside a chunk the decay
  * is carried as a local cumulative log-decay (the cumulative decay factor of
  * "Architecture Evolution and Training Engineering for Trillion-Scale Sparse
  * Multimodal Models", section 3.2), the causal intra-chunk products run as
