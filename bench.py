@@ -365,8 +365,9 @@ def main():
                    "chunk": 32, "workspace_bytes": ws_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn_prefill call (seg_table, prefill_ws_kernel<128,128,map>, seg_fold, "
-                               "prefill_ws_kernel<128,128,out>)",
+                     "kernel": "gdn_prefill call (seg_table; prefill_ws_kernel<128,128,out> of segment 0 on a side "
+                               "stream beside prefill_ws_kernel<128,128,map>; seg_fold; "
+                               "prefill_ws_kernel<128,128,out> of segments 1-8)",
                      "algorithmic_bytes_per_launch": pbytes},
         "decode": {"workload": "decode_512x32", "N": N, "H": Hd, "d_k": d, "d_v": d, "ms_per_step": dms,
                    "tokens_per_s": N / (dms / 1e3), "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
