@@ -674,31 +674,31 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         floatx4 acc = zero4();
         if constexpr (!DONLY) {
 #pragma unroll(P::UNR)
-        for (int mm = 0; mm < P::KM; ++mm) {
-            // only the accumulator tiles this step reads are loaded (bf16: tiles 2mm, 2mm + 1; fp32: tile mm / 4)
-            floatx4 es[P::RT];
+            for (int mm = 0; mm < P::KM; ++mm) {
+                // only the accumulator tiles this step reads are loaded (bf16: tiles 2mm, 2mm + 1; fp32: tile mm / 4)
+                floatx4 es[P::RT];
 #pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt) es[rt] = zero4();
+                for (int rt = 0; rt < P::RT; ++rt) es[rt] = zero4();
 #pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt) {
-                const bool used = P::KW == 8 ? (rt >> 1) == mm : (rt == (mm >> 2));
-                if (used) {
-                    const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
+                for (int rt = 0; rt < P::RT; ++rt) {
+                    const bool used = P::KW == 8 ? (rt >> 1) == mm : (rt == (mm >> 2));
+                    if (used) {
+                        const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * rt + 4 * g + i;
-                        float s;
-                        if constexpr (P::STAGE)
-                            s = to_f32(*reinterpret_cast<const TI*>(reinterpret_cast<const char*>(stg_c) +
-                                                                     swz_off<DV * P::ES, P::ES>(row, col0 + r)));
-                        else
-                            s = to_f32(ck[row * DV + col0 + r]);
-                        es[rt][i] = em[i] * s;
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = 16 * rt + 4 * g + i;
+                            float s;
+                            if constexpr (P::STAGE)
+                                s = to_f32(*reinterpret_cast<const TI*>(reinterpret_cast<const char*>(stg_c) +
+                                                                         swz_off<DV * P::ES, P::ES>(row, col0 + r)));
+                            else
+                                s = to_f32(ck[row * DV + col0 + r]);
+                            es[rt][i] = em[i] * s;
+                        }
                     }
                 }
+                acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
             }
-            acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
-        }
         }
         floatx4 R, br;
 #pragma unroll
@@ -742,16 +742,17 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         // exchange: F dS, U, dRm (natural layouts) for the key-channel products
         if constexpr (!DONLY) {
 #pragma unroll
-        for (int rt = 0; rt < P::RT; ++rt) {
-            const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
+            for (int rt = 0; rt < P::RT; ++rt) {
+                const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sFS[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(ff[i] * dS[rt][i]);
-        }
+                for (int i = 0; i < 4; ++i)
+                    sFS[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(ff[i] * dS[rt][i]);
+            }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sU[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(U[i]);
-            sDR[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(dRm[i]);
-        }
+            for (int i = 0; i < 4; ++i) {
+                sU[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(U[i]);
+                sDR[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(dRm[i]);
+            }
         }
         // dS <- gamma dS + E (q~^T dO - k~^T dR)
         {
