@@ -68,7 +68,7 @@ struct SplitCost {
     static constexpr double MAP_ONE = 0.76;  // a transition workgroup computing M or N
     static constexpr double MAP_BOTH = 0.87; // one computing M and N together (bf16, d_k = d_v)
     static constexpr double START = 0.7;     // fixed cost per workgroup
-    static constexpr double FOLD = 1.8;      // per fold step and round of 256 fold workgroups
+    static constexpr double FOLD = 0.6;      // per fold step and round of 256 fold workgroups
     // Relative time of a round in which a fraction `occ` of the CUs is busy: a
     // chunk runs faster when fewer workgroups share HBM and the power budget
     // (measured 0.79 with 1/8 of the CUs busy, 0.80 at 1/4, 0.85 at 1/2).
