@@ -56,9 +56,10 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s (H=32,d=128,T=64K bf16) + decode HBM GB/s; % of roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published (no sparsity)
-KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp", "gdn_kernels.h"]
+KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp", "gdn_kernels.h",
+                  "gdn_fold.h"]
 BACKWARD_SOURCES = ["gdn_backward.hip", "gdn_backward.h", "gdn_tile16.h", "gdn_mfma.h", "gdn_device.h",
-                    "gdn_api_backward.cpp", "gdn_prefill.hip", "gdn_kernels.h"]
+                    "gdn_api_backward.cpp", "gdn_prefill.hip", "gdn_kernels.h", "gdn_fold.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

@@ -61,6 +61,7 @@
 #include <type_traits>
 
 #include "gdn_backward.h"
+#include "gdn_fold.h"
 #include "gdn_tile16.h"
 
 namespace gdn {
@@ -503,39 +504,20 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
 // sweep, started from dL/d(final state)), for j = P-2 down to 1,
 // x <- M_j^T x + D_j, the gradient at the end of segment j - 1, written over D_j.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_fold_rev_kernel(const int32_t* cu, const int32_t* nl, int H, int64_t seg,
-                                                           const float* fM, float* wsD) {
-    constexpr int TPR = 256 / DK, CPT = 16 / TPR;
-    __shared__ float sx[DK][16];
-    const int unit = blockIdx.x, n = unit / H, h = unit - n * H, c0 = 16 * blockIdx.y;
+__global__ __launch_bounds__(64 * (DK / 16)) void bwd_fold_rev_kernel(const int32_t* cu, const int32_t* nl, int H,
+                                                                      int64_t seg, const float* fM, float* wsD) {
+    // grid (units, DV / 16): the column blocks of a unit are launched one grid
+    // row apart, on one XCD when the number of units is a multiple of 8
+    const int unit = blockIdx.x, n = unit / H, h = unit - n * H;
     const int64_t tb = cu[n], len = cu[n + 1] - tb;
     const int P = (int)((len + seg - 1) / seg);
     if (P < 3) return;
     const int64_t base = tb / seg + n;
-    const int tid = threadIdx.x, i = tid / TPR, cc = (tid % TPR) * CPT;
     const float* x0 = wsD + ((size_t)(base + P - 1) * H + h) * DK * DV;
-    for (int e = tid; e < DK * 16; e += 256) sx[e >> 4][e & 15] = x0[(size_t)(e >> 4) * DV + c0 + (e & 15)];
-    __syncthreads();
-    for (int j = P - 2; j >= 1; --j) {
-        const float* Mc = fM + ((size_t)(nl[n] + j) * H + h) * DK * DK + i;  // column i of M_j
-        float* Dj = wsD + ((size_t)(base + j) * H + h) * DK * DV + (size_t)i * DV + c0 + cc;
-        float acc[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = Dj[c];
-#pragma unroll 16
-        for (int k = 0; k < DK; ++k) {
-            const float m = Mc[(size_t)k * DK];
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) acc[c] = __builtin_fmaf(m, sx[k][cc + c], acc[c]);
-        }
-        __syncthreads();  // every read of x is done
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            sx[i][cc + c] = acc[c];
-            Dj[c] = acc[c];
-        }
-        __syncthreads();
-    }
+    // step i takes segment j = P - 2 - i
+    fold_columns<DK, DV, true>(
+        x0, P - 2, blockIdx.y, [&](int i) { return fM + ((size_t)(nl[n] + P - 2 - i) * H + h) * DK * DK; },
+        [&](int i) { return wsD + ((size_t)(base + P - 2 - i) * H + h) * DK * DV; });
 }
 
 // Reverse sweep over the sub-chunks of one (sequence, head), or with a time
@@ -955,7 +937,7 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, true>), dim3(blocks), dim3(DV * 4), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_fold_rev_kernel<DK, DV>), dim3((unsigned)((int64_t)p.num_seqs * p.H), DV / 16),
-                       dim3(256), 0, s, a.cu, a.nl, p.H, p.seg, a.fM, a.wsD);
+                       dim3(64 * (DK / 16)), 0, s, a.cu, a.nl, p.H, p.seg, a.fM, a.wsD);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -54,6 +54,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "gdn_fold.h"
 #include "gdn_kernels.h"
 #include "gdn_mfma.h"
 
@@ -1778,24 +1779,14 @@ __global__ __launch_bounds__(256) void seg_table_kernel(const int32_t* __restric
 // workgroup (columns of the state evolve independently):
 //   S_start(j + 1) = M_j S_start(j) + N_j,  j >= first,
 // written over N_j, from S_start(0) = S0 (or zero) when first = 0, or from
-// S_start(1) already in slot N_0 (segment 0's own end state) when first = 1.
+// S_start(1) already in slot N_0 (segment 0's own end state) when first = 1;
+// fp32 matrix-core steps (fold_columns), one wave per 16-row tile.
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 16)) void seg_fold_kernel(const int32_t* __restrict__ nl, int H,
                                                                   const float* __restrict__ S0,
                                                                   const float* __restrict__ wsM,
                                                                   float* __restrict__ wsN, int first) {
-    // One workgroup per (sequence, head, 16-column block of the state), one
-    // wave per 16-row tile; x_{j+1} = M_j x_j + N_j on the fp32 matrix cores
-    // (v_mfma_f32_16x16x4_f32).  The contraction index runs in a permuted
-    // order: in instruction (b, s) lane group g supplies k = 16b + 4g + s, so
-    // a lane's A values for four instructions are four adjacent entries of
-    // one row of M (one 16-byte load straight from memory) and its B values
-    // are the rows 16b + 4g + s of tile b that lane group g of that tile's
-    // accumulator holds.  x passes between the waves through LDS in the
-    // accumulator layout; each wave loads the next map's rows and N tile
-    // while the current step runs.
-    constexpr int RT = DK / 16, NCB = DV / 16;
-    __shared__ floatx4 xs[RT][64];  // xs[t][l] = x[16t + 4g + i][16cb + r], lane l = r + 16g
+    constexpr int NCB = DV / 16;
     int bid = blockIdx.x, cb, unit;
     if ((gridDim.x / NCB) % 8 == 0) {
         // workgroups go to the eight XCDs in turn: keep the NCB column blocks
@@ -1810,55 +1801,10 @@ __global__ __launch_bounds__(64 * (DK / 16)) void seg_fold_kernel(const int32_t*
     const int n = unit / H, h = unit - n * H;
     const int k0 = nl[n], cnt = nl[n + 1] - k0;
     if (cnt <= first) return;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-    const int col = 16 * cb + r;
-    const size_t my_row = (size_t)(16 * w + 4 * g) * DV + col;  // element (16w + 4g, col) of a d_k x d_v matrix
-    {
-        const float* x0 = first ? wsN + ((size_t)k0 * H + h) * DK * DV : S0 ? S0 + (size_t)unit * DK * DV : nullptr;
-        floatx4 x = zero4();
-        if (x0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = x0[my_row + (size_t)i * DV];
-        }
-        xs[w][l] = x;
-    }
-    auto load = [&](int j, floatx4(&m)[RT], floatx4& nn) {
-        const size_t slot = (size_t)(k0 + j) * H + h;
-        const float* M = wsM + slot * DK * DK + (size_t)(16 * w + r) * DK + 4 * g;
-#pragma unroll
-        for (int b = 0; b < RT; ++b) m[b] = *reinterpret_cast<const floatx4*>(M + 16 * b);
-        const float* N = wsN + slot * DK * DV + my_row;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nn[i] = N[(size_t)i * DV];
-    };
-    // step j with its operands in (m, nn); the operands of step j + 1 go to (m2, n2)
-    auto step = [&](int j, const floatx4(&m)[RT], const floatx4& nn, floatx4(&m2)[RT], floatx4& n2) {
-        if (j + 1 < cnt) load(j + 1, m2, n2);
-        __syncthreads();  // xs holds x_j
-        floatx4 xb[RT];
-#pragma unroll
-        for (int b = 0; b < RT; ++b) xb[b] = xs[b][l];
-        floatx4 acc0 = nn, acc1 = zero4();
-#pragma unroll
-        for (int b = 0; b < RT; ++b)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if (b & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[b][s], xb[b][s], acc1, 0, 0, 0);
-                else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[b][s], xb[b][s], acc0, 0, 0, 0);
-            }
-        const floatx4 acc = acc0 + acc1;
-        __syncthreads();  // every wave has read x_j
-        xs[w][l] = acc;
-        float* N = wsN + ((size_t)(k0 + j) * H + h) * DK * DV + my_row;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) N[(size_t)i * DV] = acc[i];
-    };
-    floatx4 ma[RT], mb[RT], na, nb;
-    load(first, ma, na);
-    for (int j = first; j < cnt; j += 2) {
-        step(j, ma, na, mb, nb);
-        if (j + 1 < cnt) step(j + 1, mb, nb, ma, na);
-    }
+    const float* x0 = first ? wsN + ((size_t)k0 * H + h) * DK * DV : S0 ? S0 + (size_t)unit * DK * DV : nullptr;
+    fold_columns<DK, DV, false>(
+        x0, cnt - first, cb, [&](int j) { return wsM + ((size_t)(k0 + first + j) * H + h) * DK * DK; },
+        [&](int j) { return wsN + ((size_t)(k0 + first + j) * H + h) * DK * DV; });
 }
 
 template <int DK, int DV, bool MAP, int NCB = 1>
