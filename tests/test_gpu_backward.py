@@ -153,6 +153,12 @@ def test_split_pages_gate_long(monkeypatch):
     _case([2048, 1000], 4, 128, 128, torch.bfloat16, gate="pages", seed=11)
 
 
+def test_split_units_multiple_of_eight_rectangular(monkeypatch):
+    # 16 units, d_k != d_v: both folds with the column blocks of a unit together
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "128")
+    _case([700, 257], 8, 64, 128, torch.bfloat16, seed=14)
+
+
 def test_split_no_initial_state_no_final_gradient(monkeypatch):
     monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "64")
     _case([200, 0, 33], 2, 128, 128, torch.bfloat16, init=False, final=False, seed=12)

@@ -48,6 +48,13 @@ def test_split_bf16_ragged(monkeypatch):
     _case(monkeypatch, [1, 255, 256, 257, 0, 700, 64], 3, 128, 128, torch.bfloat16, 256, seed=20)
 
 
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (64, 64, torch.float32)])
+def test_split_units_multiple_of_eight(monkeypatch, dk, dv, dtype):
+    # 16 (sequence, head) units with initial states: the fold keeps the column
+    # blocks of a unit together (the block order for unit counts divisible by 8)
+    _case(monkeypatch, [900, 333], 8, dk, dv, dtype, 128, seed=24)
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
 def test_split_head_dims(monkeypatch, dk, dv):
     _case(monkeypatch, [300, 5, 129], 2, dk, dv, torch.bfloat16, 128, seed=21)
