@@ -10,6 +10,7 @@ The submodule `inputs` (seeded synthetic inputs) does not need the library.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -18,7 +19,11 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_HOST_SANITIZE=1 loads the build whose host code (validation, planning,
+# launch set-up) carries AddressSanitizer and UndefinedBehaviorSanitizer; its
+# kernels are the same.  It needs the sanitizer runtime preloaded
+# (tests/run_host_sanitizers.sh).
+LIB_PATH = os.path.join(_HERE, "libgdn_hostsan.so" if os.environ.get("GDN_HOST_SANITIZE") == "1" else "libgdn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_DOMAIN, GDN_ERR_OOM, GDN_ERR_HIP = range(6)
@@ -109,6 +114,13 @@ def _stream(stream) -> Optional[ctypes.c_void_p]:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context for the tensors a call allocates (outputs, workspace): the stream
+    the kernels run on.  The caching allocator then gives a block released here
+    back only to later work ordered after those kernels on that stream."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return GDN_BF16
@@ -170,21 +182,22 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=No
         _need(initial_state, "initial_state", torch.float32, 4)
         if initial_state.shape != (n, H, dk, dv):
             raise ValueError("initial_state must be [num_seqs, H, dk, dv]")
-    if o is None:
-        o = torch.empty((T, H, dv), dtype=dt, device=q.device)
-    _need(o, "o", dt, 3)
-    if final_state is None and output_final_state:
-        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
-    if final_state is not None:
-        _need(final_state, "final_state", torch.float32, 4)
-    need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _load().gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
-                         _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
-                         _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "gdn_prefill")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((T, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        if final_state is None and output_final_state:
+            final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+        if final_state is not None:
+            _need(final_state, "final_state", torch.float32, 4)
+        need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = _load().gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                             _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+        _check(st, "gdn_prefill")
     return o, final_state
 
 
@@ -207,21 +220,22 @@ def gdn_prefill_head_gate(q, k, v, g, beta, cu_seqlens, initial_state=None, fina
         _need(initial_state, "initial_state", torch.float32, 4)
         if initial_state.shape != (n, H, dk, dv):
             raise ValueError("initial_state must be [num_seqs, H, dk, dv]")
-    if o is None:
-        o = torch.empty((T, H, dv), dtype=dt, device=q.device)
-    _need(o, "o", dt, 3)
-    if final_state is None and output_final_state:
-        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
-    if final_state is not None:
-        _need(final_state, "final_state", torch.float32, 4)
-    need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _load().gdn_prefill_head_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
-                                       _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
-                                       _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "gdn_prefill_head_gate")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((T, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        if final_state is None and output_final_state:
+            final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+        if final_state is not None:
+            _need(final_state, "final_state", torch.float32, 4)
+        need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = _load().gdn_prefill_head_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                           _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
+                                           _ptr(workspace), ws_bytes, _stream(stream))
+        _check(st, "gdn_prefill_head_gate")
     return o, final_state
 
 
@@ -238,12 +252,13 @@ def gdn_decode_head_gate(q, k, v, g, beta, state, o=None, stream=None):
     _need(state, "state", torch.float32, 4)
     if state.shape != (N, H, dk, dv) or k.shape != (N, H, dk) or g.shape != (N, H) or beta.shape != (N, H):
         raise ValueError("inconsistent shapes")
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
-    _need(o, "o", dt, 3)
-    st = _load().gdn_decode_head_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H,
-                                      dk, dv, _dtype_code(q), _stream(stream))
-    _check(st, "gdn_decode_head_gate")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        st = _load().gdn_decode_head_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H,
+                                          dk, dv, _dtype_code(q), _stream(stream))
+        _check(st, "gdn_decode_head_gate")
     return o
 
 
@@ -267,21 +282,22 @@ def gdn_prefill_logits(q, k, v, z, gate, gate_param, beta, cu_seqlens, initial_s
         _need(initial_state, "initial_state", torch.float32, 4)
         if initial_state.shape != (n, H, dk, dv):
             raise ValueError("initial_state must be [num_seqs, H, dk, dv]")
-    if o is None:
-        o = torch.empty((T, H, dv), dtype=dt, device=q.device)
-    _need(o, "o", dt, 3)
-    if final_state is None and output_final_state:
-        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
-    if final_state is not None:
-        _need(final_state, "final_state", torch.float32, 4)
-    need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _load().gdn_prefill_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(z), int(gate), float(gate_param), _ptr(beta),
-                                    _ptr(cu_seqlens), n, T, _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk,
-                                    dv, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "gdn_prefill_logits")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((T, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        if final_state is None and output_final_state:
+            final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+        if final_state is not None:
+            _need(final_state, "final_state", torch.float32, 4)
+        need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = _load().gdn_prefill_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(z), int(gate), float(gate_param), _ptr(beta),
+                                        _ptr(cu_seqlens), n, T, _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk,
+                                        dv, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream))
+        _check(st, "gdn_prefill_logits")
     return o, final_state
 
 
@@ -298,12 +314,13 @@ def gdn_decode_logits(q, k, v, z, gate, gate_param, beta, state, o=None, stream=
     _need(state, "state", torch.float32, 4)
     if state.shape != (N, H, dk, dv) or k.shape != (N, H, dk) or z.shape != (N, H, dk) or beta.shape != (N, H):
         raise ValueError("inconsistent shapes")
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
-    _need(o, "o", dt, 3)
-    st = _load().gdn_decode_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(z), int(gate), float(gate_param), _ptr(beta),
-                                   _ptr(state), _ptr(o), N, H, dk, dv, _dtype_code(q), _stream(stream))
-    _check(st, "gdn_decode_logits")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        st = _load().gdn_decode_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(z), int(gate), float(gate_param), _ptr(beta),
+                                       _ptr(state), _ptr(o), N, H, dk, dv, _dtype_code(q), _stream(stream))
+        _check(st, "gdn_decode_logits")
     return o
 
 
@@ -320,12 +337,13 @@ def gdn_decode(q, k, v, g, beta, state, o=None, stream=None):
     _need(state, "state", torch.float32, 4)
     if state.shape != (N, H, dk, dv) or k.shape != (N, H, dk) or g.shape != (N, H, dk) or beta.shape != (N, H):
         raise ValueError("inconsistent shapes")
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=q.device)
-    _need(o, "o", dt, 3)
-    st = _load().gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, dk, dv,
-                        _dtype_code(q), _stream(stream))
-    _check(st, "gdn_decode")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((N, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        st = _load().gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, dk, dv,
+                            _dtype_code(q), _stream(stream))
+        _check(st, "gdn_decode")
     return o
 
 
@@ -360,21 +378,22 @@ def gdn_prefill_backward(q, k, v, g, beta, cu_seqlens, d_o, initial_state=None, 
             _need(s, name, torch.float32, 4)
             if s.shape != (n, H, dk, dv):
                 raise ValueError(f"{name} must be [num_seqs, H, dk, dv]")
-    dq = torch.empty_like(q)
-    dkk = torch.empty_like(k)
-    dvv = torch.empty_like(v)
-    dg = torch.empty_like(g)
-    db = torch.empty_like(beta)
-    dS0 = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device) if want_d_initial_state else None
-    need = gdn_prefill_backward_workspace_bytes(T, n, H, dk, dv, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    st = _load().gdn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
-                                      _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dkk),
-                                      _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dS0), H, dk, dv, _dtype_code(q),
-                                      _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "gdn_prefill_backward")
+    with _on(stream):
+        dq = torch.empty_like(q)
+        dkk = torch.empty_like(k)
+        dvv = torch.empty_like(v)
+        dg = torch.empty_like(g)
+        db = torch.empty_like(beta)
+        dS0 = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device) if want_d_initial_state else None
+        need = gdn_prefill_backward_workspace_bytes(T, n, H, dk, dv, dt)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        st = _load().gdn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                          _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dkk),
+                                          _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dS0), H, dk, dv, _dtype_code(q),
+                                          _ptr(workspace), ws_bytes, _stream(stream))
+        _check(st, "gdn_prefill_backward")
     return dq, dkk, dvv, dg, db, dS0
 
 
@@ -398,17 +417,18 @@ def gdn_prefill_tiles(q, k, v, g, beta, cu_seqlens, tile_path, initial_state=Non
         _need(initial_state, "initial_state", torch.float32, 4)
         if initial_state.shape != (n, H, dk, dv):
             raise ValueError("initial_state must be [num_seqs, H, dk, dv]")
-    if o is None:
-        o = torch.empty((T, H, dv), dtype=dt, device=q.device)
-    _need(o, "o", dt, 3)
-    if final_state is None and output_final_state:
-        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
-    if final_state is not None:
-        _need(final_state, "final_state", torch.float32, 4)
-    st = _load().gdn_prefill_tiles(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
-                                   _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
-                                   int(tile_path), _stream(stream))
-    _check(st, "gdn_prefill_tiles")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((T, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        if final_state is None and output_final_state:
+            final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+        if final_state is not None:
+            _need(final_state, "final_state", torch.float32, 4)
+        st = _load().gdn_prefill_tiles(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                       _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
+                                       int(tile_path), _stream(stream))
+        _check(st, "gdn_prefill_tiles")
     return o, final_state
 
 

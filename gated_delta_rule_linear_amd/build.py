@@ -35,22 +35,34 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libgdn.so; returns its path."""
+# The host-sanitizer build (libgdn_hostsan.so): the host code compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the kernels are not), for the
+# CPU test tier under tests/run_host_sanitizers.sh.
+LIB_HOSTSAN = os.path.join(HERE, "libgdn_hostsan.so")
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, host_sanitize: bool = False) -> str:
+    """Compile every source and link libgdn.so (host_sanitize: libgdn_hostsan.so);
+    returns its path."""
+    lib = LIB_HOSTSAN if host_sanitize else LIB
+    extra = HOSTSAN_FLAGS if host_sanitize else []
     with tempfile.TemporaryDirectory(prefix="gdn_build_") as tmp:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            out = _run([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+            out = _run([HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
             if verbose and out.strip():
                 print(out)
             objs.append(obj)
-        tmp_lib = LIB + f".tmp{os.getpid()}"
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs])
-        os.replace(tmp_lib, LIB)
-    return LIB
+        tmp_lib = lib + f".tmp{os.getpid()}"
+        link = ["-Xarch_host", "-fsanitize=address,undefined", "-shared-libsan"] if host_sanitize else []
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link, "-o", tmp_lib, *objs])
+        os.replace(tmp_lib, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_sanitize="--host-sanitize" in sys.argv))

@@ -118,7 +118,10 @@ const char* gdn_status_string(int32_t status) {
 
 size_t gdn_state_bytes(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v) {
     if (num_seqs < 0 || H < 0 || d_k < 0 || d_v < 0) return 0;
-    return (size_t)num_seqs * (size_t)H * (size_t)d_k * (size_t)d_v * sizeof(float);
+    size_t b = sizeof(float);
+    for (const size_t f : {(size_t)num_seqs, (size_t)H, (size_t)d_k, (size_t)d_v})
+        if (__builtin_mul_overflow(b, f, &b)) return SIZE_MAX;  // not addressable: saturate
+    return b;
 }
 
 int32_t gdn_state_alloc(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, float** out, void* stream) {
@@ -127,7 +130,7 @@ int32_t gdn_state_alloc(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, f
     *out = nullptr;
     const size_t bytes = gdn_state_bytes(num_seqs, H, d_k, d_v);
     if (bytes == 0) return GDN_OK;
-    if (num_seqs > (int64_t)(SIZE_MAX / 4 / (size_t)H / (size_t)d_k / (size_t)d_v)) return GDN_ERR_OOM;
+    if (bytes == SIZE_MAX) return GDN_ERR_OOM;  // the size does not fit size_t: no device call is made
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* p = nullptr;
     if (hipMallocAsync(&p, bytes, s) != hipSuccess || !p) {

@@ -51,8 +51,10 @@
 // This restates, chunk by chunk, the token recurrence
 //   S_t = diag(a_t) S_{t-1} + b_t k_t (v_t - (diag(a_t) S_{t-1})^T k_t)^T, o_t = S_t^T q_t.
 #include <algorithm>
+#include <memory>
 #include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "gdn_fold.h"
 #include "gdn_kernels.h"
@@ -1915,19 +1917,82 @@ hipError_t run_maps_fold(const PrefillLaunch& p, Args<TI>& a, hipStream_t s, hip
     return e;
 }
 
-// A second stream per device (default priority), for the output pass of every
-// sequence's first segment, which runs beside the maps of the later ones.
-hipError_t side_stream(hipStream_t* out) {
-    static std::mutex mu;
-    static hipStream_t st[64] = {};
+// Side lanes of the time split.  The output pass of every sequence's first
+// segment runs on a second stream beside the maps of the later segments.  Each
+// caller stream gets its own lane: a side stream (default priority) and the
+// two events that fork it from and join it back into the caller's stream, all
+// kept for the life of the process.  A lane is held by one call while that call
+// enqueues; a call takes the idle lane already keyed to its stream, else a new
+// lane while a device has fewer than kLanesKept, else the idle lane used least
+// recently whose side stream is not inside a graph capture, else a new lane.
+// Calls on different caller streams therefore do not share a side stream unless
+// more than kLanesKept caller streams are in use, and a side stream that joined
+// one thread's capture is never handed to another call until that capture ends.
+struct SideLane {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!st[dev] && (e = hipStreamCreateWithFlags(&st[dev], hipStreamNonBlocking)) != hipSuccess) return e;
-    *out = st[dev];
-    return hipSuccess;
+    hipStream_t caller = nullptr;
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool busy = false;
+    uint64_t last_use = 0;
+};
+
+constexpr int kLanesKept = 16;
+
+class SideLanes {
+  public:
+    hipError_t acquire(hipStream_t caller, SideLane** out) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        std::lock_guard<std::mutex> lock(mu_);
+        SideLane* pick = nullptr;
+        int on_dev = 0;
+        for (auto& l : lanes_) {
+            if (l->dev != dev) continue;
+            ++on_dev;
+            if (!l->busy && l->caller == caller) { pick = l.get(); break; }
+        }
+        if (!pick && on_dev >= kLanesKept) {
+            for (auto& l : lanes_) {
+                if (l->dev != dev || l->busy || (pick && l->last_use >= pick->last_use)) continue;
+                hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+                if (hipStreamIsCapturing(l->side, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) pick = l.get();
+            }
+        }
+        if (!pick) {
+            auto l = std::make_unique<SideLane>();
+            l->dev = dev;
+            if ((e = hipStreamCreateWithFlags(&l->side, hipStreamNonBlocking)) != hipSuccess) return e;
+            if ((e = hipEventCreateWithFlags(&l->fork, hipEventDisableTiming)) != hipSuccess ||
+                (e = hipEventCreateWithFlags(&l->join, hipEventDisableTiming)) != hipSuccess) {
+                if (l->fork) (void)hipEventDestroy(l->fork);
+                (void)hipStreamDestroy(l->side);
+                return e;
+            }
+            pick = l.get();
+            lanes_.push_back(std::move(l));
+        }
+        pick->caller = caller;
+        pick->busy = true;
+        pick->last_use = ++clock_;
+        *out = pick;
+        return hipSuccess;
+    }
+    void release(SideLane* l) {
+        std::lock_guard<std::mutex> lock(mu_);
+        l->busy = false;
+    }
+
+  private:
+    std::mutex mu_;
+    std::vector<std::unique_ptr<SideLane>> lanes_;
+    uint64_t clock_ = 0;
+};
+
+SideLanes& side_lanes() {
+    static SideLanes* lanes = new SideLanes();  // never destroyed: streams may still run at exit
+    return *lanes;
 }
 
 template <typename TI, int DK, int DV>
@@ -1937,38 +2002,50 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
 
     // Time split.  Segment 0 of every sequence needs no map: its own output
-    // pass (on a side stream, after the table) gives the start state of
+    // pass (on the side stream, after the table) gives the start state of
     // segment 1 while the maps of segments 1 .. last-1 run on the caller's
     // stream; the fold then starts at segment 1 and the output pass of the
     // remaining segments follows.  Segment 0 is done before any later segment
     // writes a final state, so a final state that aliases the initial state
     // needs no copy.
-    hipStream_t s2;
-    hipError_t e = side_stream(&s2);
+    SideLane* lane = nullptr;
+    hipError_t e = side_lanes().acquire(s, &lane);
     if (e != hipSuccess) return e;
-    hipEvent_t table_done, first_done;
-    if ((e = hipEventCreateWithFlags(&table_done, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&first_done, hipEventDisableTiming)) != hipSuccess) {
-        (void)hipEventDestroy(table_done);
-        return e;
-    }
+    hipStream_t s2 = lane->side;
+    bool forked = false, joined = false;
     auto body = [&]() -> hipError_t {
         hipError_t r = run_table<TI, DK, DV>(p, a, s);
         if (r != hipSuccess) return r;
-        if ((r = hipEventRecord(table_done, s)) != hipSuccess) return r;
-        if ((r = hipStreamWaitEvent(s2, table_done, 0)) != hipSuccess) return r;
+        if ((r = hipEventRecord(lane->fork, s)) != hipSuccess) return r;
+        if ((r = hipStreamWaitEvent(s2, lane->fork, 0)) != hipSuccess) return r;
+        forked = true;
         a.phase = 1;
         if ((r = launch_seq<TI, DK, DV, false>(a, units, s2)) != hipSuccess) return r;
-        if ((r = hipEventRecord(first_done, s2)) != hipSuccess) return r;
+        if ((r = hipEventRecord(lane->join, s2)) != hipSuccess) return r;
         a.map_from = 1;
-        if ((r = run_maps_fold<TI, DK, DV>(p, a, s, first_done)) != hipSuccess) return r;
+        r = run_maps_fold<TI, DK, DV>(p, a, s, lane->join);
+        joined = r == hipSuccess;  // the fold (or its absence) waited for the join event
+        if (r != hipSuccess) return r;
         a.phase = 2;
         const int64_t slots = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg).slots;
         return launch_seq<TI, DK, DV, false>(a, ((int64_t)p.num_seqs + slots) * p.H, s);
     };
     e = body();
-    const hipError_t e1 = hipEventDestroy(table_done), e2 = hipEventDestroy(first_done);
-    return e != hipSuccess ? e : e1 != hipSuccess ? e1 : e2;
+    if (forked && !joined) {
+        // A step after the fork failed: join the side stream back into the
+        // caller's stream all the same, so that nothing enqueued on it can
+        // outlive the call's buffers in the caller's stream order (and a
+        // capture is not left with an unjoined fork).  Should the event path
+        // fail too, wait for the side stream on the host, unless it is being
+        // captured (the capture is then invalid anyway).
+        if (hipEventRecord(lane->join, s2) != hipSuccess || hipStreamWaitEvent(s, lane->join, 0) != hipSuccess) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(s2, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+                (void)hipStreamSynchronize(s2);
+        }
+    }
+    side_lanes().release(lane);
+    return e;
 }
 
 template <typename TI>

@@ -20,8 +20,9 @@
  *     HIP device; pointers named as host pointers must address host memory.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued on it and the call returns without waiting; results are ready
- *     when the stream reaches that point.  The library keeps no state between
- *     calls, frees no caller memory and prints nothing.
+ *     when the stream reaches that point.  Apart from the side streams of the
+ *     time split (see gdn_prefill), the library keeps no state between calls;
+ *     it frees no caller memory and prints nothing.
  *   - Every call returns a gdn_status.  Argument errors are reported before any
  *     memory is touched or any work is enqueued.  GDN_ERR_HIP means a HIP call
  *     (allocation aside) or a kernel launch failed; a fault inside a kernel
@@ -72,28 +73,35 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * gdn_decode take. */
 typedef enum gdn_gate { GDN_GATE_LOG = 0, GDN_GATE_SCALED_SIGMOID = 1, GDN_GATE_ALPHA_MIN = 2 } gdn_gate;
 
-/* Static English description of a status code (never NULL). */
+/* Static English description of a status code (never NULL).  A utility of
+ * this library: no passage of the pages defines it. */
 const char* gdn_status_string(int32_t status);
 
 /* Bytes of a state tensor [num_seqs, H, d_k, d_v] fp32 (d_v fastest); 0 for
- * negative arguments. */
+ * negative arguments, SIZE_MAX when the product does not fit a size_t.  A
+ * utility of this library: the pages define the state (see gdn_state_alloc)
+ * but no such call. */
 size_t gdn_state_bytes(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v);
 
 /* Allocates a zero-filled state tensor [num_seqs, H, d_k, d_v] fp32 on the
  * current device, ordered on `stream` (the zero fill is enqueued there).
- * *out receives the device pointer; the caller releases it with
- * gdn_state_free.  GDN_ERR_OOM when the device cannot provide the memory.
- * The fixed-size state replaces a key-value cache: its size does not depend
- * on the sequence length (section 5.3 of "Trillion-Parameter MoE Multimodal
- * LLMs: How to Evaluate the New Generation"). */
+ * *out receives the device pointer (NULL when the size is 0); the caller
+ * releases it with gdn_state_free.  GDN_ERR_OOM when the device cannot
+ * provide the memory, or when the size does not fit a size_t (then no device
+ * call is made).  The fixed-size state replaces a key-value cache: its size
+ * does not depend on the sequence length (section 5.3 of "Trillion-Parameter
+ * MoE Multimodal LLMs: How to Evaluate the New Generation"). */
 int32_t gdn_state_alloc(int64_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, float** out, void* stream);
 
-/* Releases memory from gdn_state_alloc, ordered on `stream`.  NULL is a no-op. */
+/* Releases memory from gdn_state_alloc, ordered on `stream`.  NULL is a no-op.
+ * A utility of this library: no passage of the pages defines it. */
 int32_t gdn_state_free(float* state, void* stream);
 
 /* Device scratch bytes gdn_prefill needs for these sizes (may be 0).  The
  * bound depends only on the arguments, never on the lengths inside
- * cu_seqlens, so no device-to-host copy is needed to size it. */
+ * cu_seqlens, so no device-to-host copy is needed to size it.  The scratch
+ * holds the time split's segment maps, which are this library's design: no
+ * passage of the pages defines this call. */
 size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v);
 
 /* Chunked prefill over packed variable-length sequences.
@@ -123,9 +131,16 @@ size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H,
  * Method: each sequence is cut into chunks (32 tokens with GDN_BF16, 64 with
  * GDN_F32), long sequences also into segments run in parallel and joined
  * through the affine map of the state.  A split call runs the first segment's
- * output pass on a second stream the library keeps per device (default
- * priority), forked from and joined back into `stream` by events, so the
- * call stays ordered on `stream`.  Inside a chunk the decay
+ * output pass on a side stream, forked from and joined back into `stream` by
+ * events (also when a later step of the call fails), so the call stays
+ * ordered on `stream` and can be captured into a graph.  The library creates
+ * one side stream (default priority) and two events per caller stream, on
+ * first use, and keeps them until the process ends: calls on different caller
+ * streams do not serialise on a shared side stream while at most 16 caller
+ * streams per device are in use (beyond that an idle side stream that is not
+ * being captured is reused, or a new one is made).  Host threads may call
+ * concurrently, on different streams; two captures in progress at once use
+ * different side streams.  Inside a chunk the decay
  * is carried as a local cumulative log-decay (the cumulative decay factor of
  * "Architecture Evolution and Training Engineering for Trillion-Scale Sparse
  * Multimodal Models", section 3.2), the causal intra-chunk products run as
@@ -201,7 +216,9 @@ int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const voi
  * split of segment length L (below), also gdn_prefill's split workspace for
  * segments of L tokens and (T_total / L + num_seqs) * H * d_k * d_v * 4 bytes,
  * each rounded up to 256.  Depends on the arguments and on
- * GDN_BACKWARD_SEGMENT only; 0 for invalid arguments. */
+ * GDN_BACKWARD_SEGMENT only; 0 for invalid arguments.  The checkpoints and
+ * the split are this library's design: no passage of the pages defines this
+ * call. */
 size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k,
                                             int32_t d_v, int32_t dtype);
 

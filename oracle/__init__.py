@@ -24,27 +24,45 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
 _SRC_BWD = os.path.join(_HERE, "gdn_oracle_backward.c")
 _LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
+# With GDN_HOST_SANITIZE=1 the oracle is the AddressSanitizer + UndefinedBehavior-
+# Sanitizer build (clang, the runtime of the sanitized libgdn build; see
+# tests/run_host_sanitizers.sh).
+_SAN_PATH = os.path.join(_HERE, "libgdn_oracle_hostsan.so")
+CLANG = "/opt/rocm/llvm/bin/clang"
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile gdn_oracle.c and gdn_oracle_backward.c with gcc into oracle/libgdn_oracle.so."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
+def _sanitized() -> bool:
+    return os.environ.get("GDN_HOST_SANITIZE") == "1"
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile gdn_oracle.c and gdn_oracle_backward.c with gcc into
+    oracle/libgdn_oracle.so (sanitize: with clang, AddressSanitizer and
+    UndefinedBehaviorSanitizer, into oracle/libgdn_oracle_hostsan.so)."""
+    path = _SAN_PATH if sanitize else _LIB_PATH
+    if force or not os.path.exists(path):
+        tmp = path + f".tmp{os.getpid()}"
+        if sanitize:
+            cmd = [CLANG, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                   "-fno-sanitize-recover=undefined", "-shared-libsan", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                   "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
+        else:
+            cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                   "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
         subprocess.run(cmd, check=True, cwd=_HERE)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, path)
+    return path
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build(force=False)
-    lib = ctypes.CDLL(_LIB_PATH)
+    path = _SAN_PATH if _sanitized() else _LIB_PATH
+    if not os.path.exists(path):
+        build(force=False, sanitize=_sanitized())
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32 = ctypes.c_int32
     lib.gdn_oracle_recurrent_f64.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, P, i32]
@@ -151,11 +169,11 @@ def backward(q, k, v, g, beta, cu_seqlens, d_o, initial_state=None, d_final_stat
     return out
 
 
-def decode_step(q, k, v, g, beta, state, dtype=np.float64):
+def decode_step(q, k, v, g, beta, state, dtype=np.float64, threads=None):
     """One token per sequence ([N,H,*] inputs) from `state` [N,H,dk,dv]: returns (o, new_state)."""
     N = np.asarray(q).shape[0]
     cu = np.arange(N + 1, dtype=np.int32)
-    return recurrent(q, k, v, g, beta, cu, initial_state=state, dtype=dtype)
+    return recurrent(q, k, v, g, beta, cu, initial_state=state, dtype=dtype, threads=threads)
 
 
 # Gate parameterisations computed from logits (the values of gdn_gate).

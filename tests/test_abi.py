@@ -41,6 +41,8 @@ def test_state_bytes():
     assert gdn.gdn_state_bytes(512, 32, 128, 128) == 512 * 32 * 128 * 128 * 4
     assert gdn.gdn_state_bytes(0, 32, 128, 128) == 0
     assert gdn.gdn_state_bytes(-1, 32, 128, 128) == 0
+    # 2^62 * 32 * 128 * 128 * 4 = 2^83 bytes: saturates instead of wrapping to 0
+    assert gdn.gdn_state_bytes(1 << 62, 32, 128, 128) == 2 ** 64 - 1
 
 
 def _prefill(lib, q=NUL, cu=NUL, n=1, T=10, H=4, dk=64, dv=64, dt=1, o=NUL, S0=NUL, Sf=NUL, ws=NUL, wsb=0):
@@ -79,6 +81,14 @@ def test_state_alloc_argument_errors(lib):
     assert lib.gdn_state_alloc(-1, 2, 64, 64, ctypes.byref(out), None) == INVALID
     assert lib.gdn_state_alloc(0, 2, 64, 64, ctypes.byref(out), None) == OK and not out.value
     assert lib.gdn_state_free(None, None) == OK
+
+
+def test_state_alloc_overflowing_size_is_oom_without_a_device_call(lib):
+    # the size check comes before any HIP call, so this runs without a GPU
+    out = ctypes.c_void_p(1234)
+    assert lib.gdn_state_alloc(1 << 62, 32, 128, 128, ctypes.byref(out), None) == OOM
+    assert not out.value
+    assert lib.gdn_state_alloc((1 << 63) - 1, 1, 64, 64, ctypes.byref(out), None) == OOM
 
 
 def test_workspace_bound_needs_no_lengths():

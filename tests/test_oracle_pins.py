@@ -438,3 +438,61 @@ def test_chunked_form_matches_recurrence_for_unbounded_gates():
     o2, S2 = oracle.chunked(f(x.q), f(x.k), f(x.v), f(x.g), f(x.beta), cu, initial_state=f(x.initial_state),
                             chunk=16)
     assert oracle.rel_err(o2, o1) < 1e-12 and oracle.rel_err(S2, S1) < 1e-12
+
+
+# ---------------------------------------------------------------- the error metric and the decode step
+
+def test_rel_err_hand_cases():
+    # max|x - ref| / max|ref| over the whole tensor: one largest deviation over one
+    # largest reference magnitude, not a per-element ratio and not over max|x|
+    assert oracle.rel_err([1.0, 2.0], [1.0, 3.0]) == pytest.approx(1.0 / 3.0, abs=1e-15)
+    # per-element relative error would give 1 here (0.1 against 0.1); the metric gives 0.1 / 10
+    assert oracle.rel_err([10.0, 0.2], [10.0, 0.1]) == pytest.approx(0.01, abs=1e-15)
+    # dividing by max|x| instead would give 2 / 4; signs count through the absolute values
+    assert oracle.rel_err([-4.0, 0.0], [-2.0, 1.0]) == pytest.approx(1.0, abs=1e-15)
+    # 2-D tensors are taken whole
+    assert oracle.rel_err([[1.0, 5.0], [0.0, 0.0]], [[1.0, 4.0], [0.0, -8.0]]) == pytest.approx(
+        8.0 / 8.0, abs=1e-15)
+    # an all-zero reference falls back to the absolute deviation; an exact match is 0
+    assert oracle.rel_err([0.0, 0.5], [0.0, 0.0]) == 0.5
+    assert oracle.rel_err([0.0, 0.0], [0.0, 0.0]) == 0.0
+    assert oracle.rel_err(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
+    # a NaN anywhere in x is not finite in the metric (the tests require a finite value)
+    assert not np.isfinite(oracle.rel_err([np.nan, 1.0], [1.0, 1.0]))
+
+
+def test_decode_step_hand_case_two_sequences():
+    # the one-token hand case of test_hand_one_token_with_initial_state for sequence 0,
+    # and sequence 1 with beta = 0 (pure decay): each sequence reads its own state
+    q = np.array([[[1.0, 1.0]], [[1.0, 0.0]]])
+    k = np.array([[[0.0, 1.0]], [[0.0, 1.0]]])
+    v = np.array([[[10.0, 20.0]], [[7.0, 7.0]]])
+    g = np.array([[[math.log(0.5), 0.0]], [[0.0, math.log(0.25)]]])
+    beta = np.array([[0.25], [0.0]])
+    S0 = np.array([[[[1.0, 2.0], [3.0, 4.0]]], [[[1.0, 2.0], [8.0, 4.0]]]])
+    o, S = oracle.decode_step(q, k, v, g, beta, S0)
+    np.testing.assert_allclose(o[0, 0], [5.25, 9.0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S[0, 0], [[0.5, 1.0], [4.75, 8.0]], rtol=0, atol=1e-14)
+    # sequence 1: S' = diag(1, 1/4) S0 = [[1, 2], [2, 1]]; beta = 0 keeps S'; o = S'^T (1, 0) = (1, 2)
+    np.testing.assert_allclose(S[1, 0], [[1.0, 2.0], [2.0, 1.0]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[1, 0], [1.0, 2.0], rtol=0, atol=1e-14)
+
+
+def test_decode_steps_equal_the_recurrence_over_the_same_tokens():
+    # T successive one-token steps over N sequences must reproduce the recurrence run
+    # over each sequence's T tokens packed back to back, from the same initial states
+    N, H, dk, dv, T = 3, 2, 8, 6, 5
+    S0, draws = inputs.make_decode_steps(N, H, dk, dv, T, dtype=torch.float32, seed=21)
+    S = _np(S0)
+    outs = []
+    for dr in draws:
+        o, S = oracle.decode_step(*[_np(t) for t in (dr.q, dr.k, dr.v, dr.g, dr.beta)], S)
+        outs.append(o)
+    # pack sequence n's tokens as rows [n T, (n + 1) T)
+    pack = lambda name: np.concatenate([np.stack([_np(getattr(dr, name))[n] for dr in draws]) for n in range(N)])
+    cu = np.arange(0, N * T + 1, T, dtype=np.int32)
+    o_ref, S_ref = oracle.recurrent(pack("q"), pack("k"), pack("v"), pack("g"), pack("beta"), cu,
+                                    initial_state=_np(S0))
+    o_steps = np.concatenate([np.stack([outs[t][n] for t in range(T)]) for n in range(N)])
+    np.testing.assert_allclose(o_steps, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(S, S_ref, rtol=0, atol=1e-13)
