@@ -26,7 +26,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_hostsan.so" if os.environ.get("GDN_HOST_SANITIZE") == "1" else "libgdn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
 
-GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_DOMAIN, GDN_ERR_OOM, GDN_ERR_HIP = range(6)
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_DOMAIN, GDN_ERR_OOM, GDN_ERR_HIP, GDN_ERR_SCRATCH_LIMIT = range(7)
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_LOG, GDN_GATE_SCALED_SIGMOID, GDN_GATE_ALPHA_MIN = 0, 1, 2
 GDN_TILES_DENSE, GDN_TILES_PAIRS = 0, 1
@@ -61,6 +62,8 @@ def _load():
     lib.gdn_prefill_workspace_bytes.restype = sz
     lib.gdn_prefill.argtypes = [P, P, P, P, P, P, i32, i64, P, P, P, i32, i32, i32, i32, P, sz, P]
     lib.gdn_prefill.restype = i32
+    lib.gdn_prefill_noalloc.argtypes = [P, P, P, P, P, P, i32, i64, P, P, P, i32, i32, i32, i32, P]
+    lib.gdn_prefill_noalloc.restype = i32
     lib.gdn_decode.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
     lib.gdn_decode.restype = i32
     f32 = ctypes.c_float
@@ -198,6 +201,43 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=No
                              _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
                              _ptr(workspace), ws_bytes, _stream(stream))
         _check(st, "gdn_prefill")
+    return o, final_state
+
+
+def gdn_prefill_noalloc(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=None, o=None,
+                        output_final_state: bool = True, stream=None):
+    """gdn_prefill with its scratch in the library's fixed device array (no
+    workspace, no device allocation by the library).  Pass o (and final_state)
+    to allocate nothing here either; calls that overlap on one GPU race on the
+    shared array."""
+    _need(q, "q", dims=3)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(k, "k", dt, 3)
+    _need(v, "v", dt, 3)
+    _need(g, "g", torch.float32, 3)
+    _need(beta, "beta", torch.float32, 2)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if k.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes")
+    n = cu_seqlens.shape[0] - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, 4)
+        if initial_state.shape != (n, H, dk, dv):
+            raise ValueError("initial_state must be [num_seqs, H, dk, dv]")
+    with _on(stream):
+        if o is None:
+            o = torch.empty((T, H, dv), dtype=dt, device=q.device)
+        _need(o, "o", dt, 3)
+        if final_state is None and output_final_state:
+            final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+        if final_state is not None:
+            _need(final_state, "final_state", torch.float32, 4)
+        st = _load().gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                         _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv,
+                                         _dtype_code(q), _stream(stream))
+        _check(st, "gdn_prefill_noalloc")
     return o, final_state
 
 
@@ -434,7 +474,7 @@ def gdn_prefill_tiles(q, k, v, g, beta, cu_seqlens, tile_path, initial_state=Non
 
 __all__ = [
     "gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free", "gdn_prefill_workspace_bytes",
-    "gdn_prefill", "gdn_decode", "gdn_prefill_logits", "gdn_decode_logits", "gdn_prefill_head_gate",
+    "gdn_prefill", "gdn_prefill_noalloc", "gdn_decode", "gdn_prefill_logits", "gdn_decode_logits", "gdn_prefill_head_gate",
     "gdn_decode_head_gate", "gdn_prefill_backward", "gdn_prefill_backward_workspace_bytes", "gdn_prefill_tiles", "GdnError", "load_library", "LIB_PATH",
     "GDN_GATE_LOG", "GDN_GATE_SCALED_SIGMOID", "GDN_GATE_ALPHA_MIN", "GDN_TILES_DENSE", "GDN_TILES_PAIRS",
 ]

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_api_backward.cpp", "gdn_api_tiles.cpp", "gdn_prefill.hip", "gdn_decode.hip",
-           "gdn_backward.hip", "gdn_tiles.hip"]
+           "gdn_backward.hip", "gdn_tiles.hip", "gdn_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -112,6 +112,7 @@ const char* gdn_status_string(int32_t status) {
         case GDN_ERR_DOMAIN: return "input outside the domain (g not in [-5, 0] or malformed cu_seqlens)";
         case GDN_ERR_OOM: return "device allocation failed";
         case GDN_ERR_HIP: return "HIP runtime error";
+        case GDN_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }

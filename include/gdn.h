@@ -52,7 +52,9 @@ typedef enum gdn_status {
     GDN_ERR_UNSUPPORTED = 2, /* d_k or d_v not in {64, 128}, unknown dtype */
     GDN_ERR_DOMAIN = 3,      /* validation mode only: g outside [-5, 0], bad cu_seqlens */
     GDN_ERR_OOM = 4,         /* device allocation failed */
-    GDN_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+    GDN_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
+    GDN_ERR_SCRATCH_LIMIT = 6 /* gdn_prefill_noalloc: the call needs more scratch
+                                 than GDN_NOALLOC_SCRATCH_BYTES */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -151,6 +153,33 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
                     const float* initial_state, float* final_state, void* o,
                     int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the fixed device scratch of gdn_prefill_noalloc (64 MiB). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gdn_prefill that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The arguments and the result are gdn_prefill's, without
+ * the workspace: its scratch is a device array of GDN_NOALLOC_SCRATCH_BYTES
+ * inside the library, which each GPU the library runs on holds from the first
+ * call until the process ends.
+ *   - Returns GDN_ERR_SCRATCH_LIMIT, before any work is enqueued, when
+ *     gdn_prefill_workspace_bytes(T_total, num_seqs, H, d_k, d_v) exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES (one 65,536-token sequence x 32 heads at
+ *     d = 128 needs 32 MiB; four 8,192-token sequences x 32 heads, 44 MiB).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (on different streams, or from different host threads)
+ *     race on it and their results are undefined.  Calls ordered on one
+ *     stream, or separated by synchronisation, are safe.
+ *   - It calls no hipMalloc or hipFree.  The first call on a device looks up
+ *     the array's address; a split call on a caller stream the library has not
+ *     seen creates that stream's side stream and events (see gdn_prefill), as
+ *     gdn_prefill does.  GDN_VALIDATE=1 adds host buffers and a
+ *     synchronisation, as for gdn_prefill. */
+int32_t gdn_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total,
+                            const float* initial_state, float* final_state, void* o,
+                            int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void* stream);
 
 /* gdn_prefill with one log-decay per (token, head), shared by the key
  * channels: the gate g_th of "How to Think About Trillion-Parameter Sparse

@@ -23,14 +23,15 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free",
                           "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_prefill_logits",
                           "gdn_decode_logits", "gdn_prefill_head_gate", "gdn_decode_head_gate",
-                          "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward", "gdn_prefill_tiles"}
+                          "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward", "gdn_prefill_tiles",
+                          "gdn_prefill_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
     seen = set()
-    for code in range(6):
+    for code in range(7):
         s = gdn.gdn_status_string(code)
         assert s and s not in seen
         seen.add(s)
@@ -240,3 +241,16 @@ def test_tiles_argument_errors(lib):
     assert _tiles(lib, H=0) == INVALID
     assert _tiles(lib, p=BAD, cu=BAD, path=1) == INVALID  # misaligned
     assert _tiles(lib, n=0, T=0, path=1) == OK
+
+
+def test_noalloc_rejects_a_call_beyond_its_scratch(lib, monkeypatch):
+    # 2^22 tokens in 64-token segments x 32 heads: the split maps need far more than the fixed
+    # scratch, so the call is refused before any device call (the pointers are never read)
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "64")
+    T, n, H = 1 << 22, 1, 32
+    assert gdn.gdn_prefill_workspace_bytes(T, n, H, 128, 128) > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(0x10000)
+    st = lib.gdn_prefill_noalloc(p, p, p, p, p, p, n, T, None, p, p, H, 128, 128, 1, None)
+    assert st == gdn.GDN_ERR_SCRATCH_LIMIT
+    assert "scratch" in gdn.gdn_status_string(st)
+    assert lib.gdn_prefill_noalloc(p, p, p, p, p, p, -1, T, None, p, p, H, 128, 128, 1, None) == INVALID
