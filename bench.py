@@ -29,12 +29,24 @@ same workload.  One JSON line is printed.
 runs only a device-to-device copy of that many bytes (three times), the
 reference for scaling the counters.
 
+    python bench.py --summarize-pmc <dir>/bench_counter_collection.csv ...
+
+summarises rocprofv3 --pmc output per kernel and grid (matrix-core and VALU
+busy, LDS bank conflicts, instruction counts, clock) without a GPU.
+
 Two more legs follow in the same run, each on four 8,192-token sequences x
 32 heads and reported in objects of their own: "tile_paths" times
 gdn_prefill_tiles with dense window products and with position-pair decays
 (the diagonal-tile comparison), and "backward" times gdn_prefill_backward
 with its own roofline, sampled parity and host-oracle baseline.
 --no-tiles / --no-backward skip them.
+
+"workloads" times gdn_prefill on the other prefill shapes: 64 packed
+sequences of 512..16,384 tokens with random initial states (varlen64) and one
+2^20-token sequence x 16 heads (long_1m), each with its roofline, sampled
+parity and a host-oracle baseline on a stated sample.  --no-workloads skips
+them.  "device" gives the GPU's compute-unit count and clock as the runtime
+reports them, beside the published peaks the fractions use.
 """
 
 from __future__ import annotations
@@ -43,6 +55,8 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -61,6 +75,11 @@ KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device
 BACKWARD_SOURCES = ["gdn_backward.hip", "gdn_backward.h", "gdn_tile16.h", "gdn_mfma.h", "gdn_device.h",
                     "gdn_api_backward.cpp", "gdn_prefill.hip", "gdn_kernels.h", "gdn_fold.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+BF16_CHUNK = 32  # the bf16 prefill kernel's chunk length (tokens)
+# dense bf16 matrix-core flops per clock and CU on CDNA4: the published 2.5 PFLOP/s
+# at 256 CUs and 2.4 GHz (2.5e15 / (256 * 2.4e9) = 4069, i.e. 2048 FMA)
+BF16_FLOP_PER_CLK_CU = 4096
 
 
 def prefill_bytes(T_tokens: int, H: int, dk: int, dv: int, n_seqs: int, elt: int = 2, init_state: bool = False):
@@ -70,7 +89,7 @@ def prefill_bytes(T_tokens: int, H: int, dk: int, dv: int, n_seqs: int, elt: int
     return T_tokens * H * per_head_token + states
 
 
-def prefill_flops(T_tokens: int, H: int, dk: int, dv: int, C: int = 64):
+def prefill_flops(T_tokens: int, H: int, dk: int, dv: int, C: int = BF16_CHUNK):
     """Algorithmic flops of one prefill launch with the causal intra-chunk tiles counted dense:
     three d_k x d_v state contractions per token (Q~S, W S, K_dec^T U), the two Gram products and
     the P U and W, U~ products inside the chunk, and the C^3/3 triangular solve spread over C tokens."""
@@ -111,6 +130,44 @@ def source_hash(files=None) -> str:
     return h.hexdigest()[:16]
 
 
+def device_info():
+    """The GPU as the runtime reports it: name, architecture, compute units, peak
+    engine clock (rocminfo), memory; and the dense bf16 matrix peak those imply."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "hbm_bytes": props.total_memory, "max_clock_mhz": None}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=120).stdout
+        arch = props.gcnArchName.split(":")[0]
+        for block in out.split("*******"):
+            if re.search(rf"Name:\s+{arch}\b", block):
+                m = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", block)
+                if m:
+                    info["max_clock_mhz"] = int(m.group(1))
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if info["max_clock_mhz"]:
+        info["bf16_mfma_peak_tflops_from_cus_and_clock"] = (
+            info["compute_units"] * info["max_clock_mhz"] * 1e6 * BF16_FLOP_PER_CLK_CU / 1e12)
+    info["published_peaks"] = {"hbm_gbs": HBM_PEAK_GBS, "bf16_mfma_tflops": MFMA_BF16_PEAK_TFLOPS}
+    return info
+
+
+def measured_counters(kernel: str):
+    """Matrix-core and VALU busy fractions of `kernel` from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return {k: v for k, v in e.items() if k != "source_hash"}
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -139,6 +196,50 @@ def time_loop(fn, steps: int, warmup: int, stream):
     return start.elapsed_time(stop) / steps  # ms per call
 
 
+def summarize_pmc(paths):
+    """Per (kernel, grid size): mean duration and counters of a rocprofv3 --pmc
+    run (counter_collection.csv files), with MI355X's derived figures:
+    matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x
+    1024 SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / (256 CUs x GRBM_GUI_ACTIVE per
+    XCD); LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / (256 x the same);
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs in the CSV, so it is divided by 8;
+    clock = those cycles / duration."""
+    import csv
+    import collections
+
+    def short(n):
+        m = re.search(r"(prefill_ws_kernel|prefill_seq_kernel|seg_fold_kernel|seg_table_kernel|decode_kernel|"
+                      r"bwd_\w+_kernel|tile_prefill_kernel)", n)
+        return m.group(0) if m else n[:40]
+
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                k = (short(r["Kernel_Name"]), int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+                per[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                dur[k][(p, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = {}
+    for k in sorted(per, key=lambda k: -sum(dur[k].values())):
+        c = {n: sum(v) / len(v) for n, v in per[k].items()}
+        ns = sum(dur[k].values()) / len(dur[k])
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8
+        e = {"dispatches": len(dur[k]), "mean_us": ns / 1e3, "clock_ghz": cyc / ns if ns else None}
+        if cyc:
+            for name, ctr, den in (("mfma_busy", "SQ_VALU_MFMA_BUSY_CYCLES", 1024), ("valu_busy", "SQ_ACTIVE_INST_VALU", 256),
+                                   ("lds_bank_conflict", "SQ_LDS_BANK_CONFLICT", 256)):
+                if ctr in c:
+                    e[name] = c[ctr] / (den * cyc)
+        for n in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES"):
+            if n in c:
+                e[n] = c[n]
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            e["mfma_bf16_flops"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        out[f"{k[0]} workgroups={k[1]}"] = e
+    print(json.dumps(out, indent=1))
+
+
 def copy_calibration(nbytes: int):
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -148,29 +249,88 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "calls": 3}), flush=True)
 
 
-def cpu_baseline(x, tokens: int):
-    """fp32 oracle on the host over the first `tokens` tokens of every head."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def cpu_baseline(x, n_seqs: int, what: str):
+    """fp32 oracle on the host over the first `n_seqs` sequences of x (every head):
+    tokens/s of that sample."""
     import oracle
 
     oracle.build(force=False)
     H = x.q.shape[1]
+    cu = x.cu_seqlens[:n_seqs + 1].to("cpu", torch.int64).numpy()
+    tokens = int(cu[-1])
     sl = lambda t: t[:tokens].to("cpu", torch.float32).numpy()
-    args = [sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), np.array([0, tokens], np.int32)]
+    S0 = None if x.initial_state is None else x.initial_state[:n_seqs].to("cpu", torch.float32).numpy()
+    units = n_seqs * H
     share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
-    threads = max(1, min(os.cpu_count() or 1, H, share))
+    threads = max(1, min(os.cpu_count() or 1, units, share))
     t0 = time.perf_counter()
-    oracle.recurrent(*args, dtype=np.float32, threads=threads)
+    oracle.recurrent(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), cu.astype(np.int32), initial_state=S0,
+                     dtype=np.float32, threads=threads)
     dt = time.perf_counter() - t0
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
-    except OSError:
-        pass
-    whole = "the whole 65536-token sequence" if tokens >= x.q.shape[0] else f"the first {tokens} tokens"
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{whole}, all {H} heads, fp32 sequential recurrence (OpenMP over heads), {dt:.2f} s wall; "
-                      f"host {model or 'unknown CPU'}, {os.cpu_count()} logical CPUs visible"}
+            "sample": f"{what}: {tokens} tokens x {H} heads, fp32 sequential recurrence (OpenMP over "
+                      f"(sequence, head) units), {dt:.2f} s wall; host {_cpu_model() or 'unknown CPU'}, "
+                      f"{os.cpu_count()} logical CPUs visible"}
+
+
+def prefix_view(x, tokens: int):
+    """The first `tokens` tokens of a one-sequence workload, as a one-sequence workload."""
+    from gated_delta_rule_linear_amd.inputs import PrefillInputs
+
+    cu = torch.tensor([0, tokens], dtype=torch.int32)
+    return PrefillInputs(x.q[:tokens], x.k[:tokens], x.v[:tokens], x.g[:tokens], x.beta[:tokens], cu, [tokens],
+                         x.initial_state, None)
+
+
+def prefill_leg(gdn, name, x, steps, warmup, stream, cpu: bool, cpu_seqs: int, cpu_what: str, cpu_x=None):
+    """Time gdn_prefill over the workload x (every output written, final state included);
+    sampled parity of sequence 0, head 0 (first 2048 tokens) against the fp64 oracle."""
+    import oracle
+
+    T, H, dk = x.q.shape
+    dv = x.v.shape[2]
+    n = x.num_seqs
+    o = torch.empty((T, H, dv), dtype=x.q.dtype, device=x.q.device)
+    S = torch.empty((n, H, dk, dv), dtype=torch.float32, device=x.q.device)
+    ws_bytes = gdn.gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.q.device) if ws_bytes else None
+
+    def step():
+        gdn.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state, final_state=S,
+                        o=o, workspace=ws, stream=stream)
+
+    ms = time_loop(step, steps, warmup, stream)
+    init = x.initial_state is not None
+    pbytes = prefill_bytes(T, H, dk, dv, n, init_state=init)
+    pflops = prefill_flops(T, H, dk, dv)
+    gbs = pbytes / (ms / 1e3) / 1e9
+    cu = x.cu_seqlens.to("cpu", torch.int64).numpy()
+    tk = int(min(2048, cu[1]))
+    s0 = None if not init else x.initial_state[:1, :1].to("cpu", torch.float64).numpy()
+    ro, _ = oracle.recurrent(*(t[:tk, :1].to("cpu", torch.float64).numpy() for t in (x.q, x.k, x.v, x.g)),
+                             x.beta[:tk, :1].to("cpu", torch.float64).numpy(), np.array([0, tk], np.int32),
+                             initial_state=s0)
+    leg = {"workload": name, "num_seqs": n, "T": T, "H": H, "d_k": dk, "d_v": dv, "initial_state": init,
+           "workspace_bytes": ws_bytes, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+           "tokens_per_s": T / (ms / 1e3),
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": pbytes},
+           "mfma": {"algorithmic_flops_per_launch": pflops, "chunk": BF16_CHUNK,
+                    "frac": pflops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+           "parity": {"o_rel_err_seq0_head0_first_tokens": oracle.rel_err(
+               o[:tk, :1].to("cpu", torch.float64).numpy(), ro), "tokens": tk}}
+    del o, S, ws
+    if cpu:
+        leg["cpu_baseline"] = cpu_baseline(cpu_x if cpu_x is not None else x, cpu_seqs, cpu_what)
+    return leg
 
 
 def cpu_backward_baseline(x, d_o, dSf, tokens: int, heads: int):
@@ -205,12 +365,18 @@ def main():
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--no-tiles", action="store_true")
     ap.add_argument("--tiles-steps", type=int, default=10)
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV", help="summarise rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--no-workloads", action="store_true")
+    ap.add_argument("--workload-steps", type=int, default=10)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
               f"(asked for --gpus {args.gpus}); sharding across GPUs is described in DESIGN.md.", file=sys.stderr)
         sys.exit(2)
 
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -347,6 +513,27 @@ def main():
         if not args.no_cpu:
             bwd["cpu_baseline"] = cpu_backward_baseline(xb, d_o, dSf, 2048, 16)
 
+    # ---- the other prefill workloads: varlen64 and long_1m
+    workloads = None
+    if not args.no_workloads:
+        del xb
+        torch.cuda.empty_cache()
+        workloads = {}
+        xv = inputs.make_workload("varlen64", seed=0, device=dev)
+        # host sample: the first sequences up to ~65,536 tokens (whole sequences, their initial states)
+        cuv = xv.cu_seqlens.to("cpu", torch.int64).numpy()
+        nv = max(1, int(np.searchsorted(cuv, 65536, side="right")) - 1)
+        workloads["varlen64"] = prefill_leg(gdn, "varlen64", xv, args.workload_steps, 3, stream, not args.no_cpu,
+                                            nv, f"the first {nv} of 64 sequences")
+        del xv
+        torch.cuda.empty_cache()
+        xl = inputs.make_workload("long_1m", seed=0, device=dev)
+        workloads["long_1m"] = prefill_leg(gdn, "long_1m", xl, max(3, args.workload_steps // 2), 2, stream,
+                                           not args.no_cpu, 1, "the first 131072 of 1048576 tokens",
+                                           cpu_x=prefix_view(xl, 131072))
+        del xl
+        torch.cuda.empty_cache()
+
     traffic = measured_traffic("prefill")
     res = {
         "metric": METRIC,
@@ -374,8 +561,9 @@ def main():
                    "tokens_per_s": N / (dms / 1e3), "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": dgbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": dbytes,
                    "traffic": measured_traffic("decode")},
-        "mfma": {"algorithmic_flops_per_launch": pflops, "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS},
+        "mfma": {"algorithmic_flops_per_launch": pflops, "chunk": BF16_CHUNK, "achieved": tflops,
+                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                 "counters": measured_counters("prefill")},
         "attainable_roofline_frac": max(pflops / (MFMA_BF16_PEAK_TFLOPS * 1e12), pbytes / (HBM_PEAK_GBS * 1e9))
                                     / (ms / 1e3),
         "parity": {"prefill_o_rel_err_head0_first2048": parity},
@@ -384,8 +572,13 @@ def main():
         res["tile_paths"] = tiles
     if bwd is not None:
         res["backward"] = bwd
+    if workloads is not None:
+        res["workloads"] = workloads
+    res["device"] = device_info()
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(xf, min(args.cpu_tokens, T))
+        xc = xf if args.cpu_tokens >= T else prefix_view(xf, args.cpu_tokens)
+        what = "the whole 65536-token sequence" if args.cpu_tokens >= T else f"the first {args.cpu_tokens} tokens"
+        res["cpu_baseline"] = cpu_baseline(xc, 1, what)
     print(json.dumps(res), flush=True)
 
 
