@@ -8,6 +8,8 @@
 # CPU only: nothing here runs a kernel.
 set -euo pipefail
 cd "$(dirname "$0")/.."
+# the sanitizer builds are for this run only
+trap 'rm -f gated_delta_rule_linear_amd/libgdn_hostsan.so oracle/libgdn_oracle_hostsan.so' EXIT
 python -m gated_delta_rule_linear_amd.build --host-sanitize
 python -c "import oracle; oracle.build(force=True, sanitize=True)"
 RT=$(/opt/rocm/llvm/bin/clang -print-file-name=libclang_rt.asan-x86_64.so)
