@@ -853,11 +853,15 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         o_L = L;
     }
     if constexpr (DONLY) {
+        // lane indices recomputed here, so that nothing lane-derived stays live across the loop
+        int te = threadIdx.x;
+        asm volatile("" : "+v"(te));
+        const int ge = (te & 63) >> 4, re = te & 15;
         float* dst = a.wsD + ((size_t)u.slot * H + h) * DK * DV;
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g0 + i) * DV + col0 + r0] = dS[rt][i];
+            for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * ge + i) * DV + col0 + re] = dS[rt][i];
         return;
     }
     flush(r0, g0);
