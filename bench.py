@@ -42,10 +42,11 @@ with its own roofline, sampled parity and host-oracle baseline.
 --no-tiles / --no-backward skip them.
 
 "workloads" times gdn_prefill on the other prefill shapes: 64 packed
-sequences of 512..16,384 tokens with random initial states (varlen64) and one
-2^20-token sequence x 16 heads (long_1m), each with its roofline, sampled
-parity and a host-oracle baseline on a stated sample.  --no-workloads skips
-them.  "device" gives the GPU's compute-unit count and clock as the runtime
+sequences of 512..16,384 tokens with random initial states (varlen64), one
+2^20-token sequence x 16 heads (long_1m), and a skewed batch of 63 sequences
+of 1,024 tokens plus one of 262,144 (skewed64, with and without the bound on
+the lengths of gdn_prefill_maxlen), each with its roofline, sampled parity and
+a host-oracle baseline on a stated sample.  --no-workloads skips them.  "device" gives the GPU's compute-unit count and clock as the runtime
 reports them, beside the published peaks the fractions use.
 """
 
@@ -290,9 +291,11 @@ def prefix_view(x, tokens: int):
                          x.initial_state, None)
 
 
-def prefill_leg(gdn, name, x, steps, warmup, stream, cpu: bool, cpu_seqs: int, cpu_what: str, cpu_x=None):
-    """Time gdn_prefill over the workload x (every output written, final state included);
-    sampled parity of sequence 0, head 0 (first 2048 tokens) against the fp64 oracle."""
+def prefill_leg(gdn, name, x, steps, warmup, stream, cpu: bool, cpu_seqs: int, cpu_what: str, cpu_x=None,
+                max_seqlen: int = 0):
+    """Time gdn_prefill over the workload x (every output written, final state included;
+    max_seqlen > 0: gdn_prefill_maxlen with that bound); sampled parity of sequence 0,
+    head 0 (first 2048 tokens) against the fp64 oracle."""
     import oracle
 
     T, H, dk = x.q.shape
@@ -300,12 +303,12 @@ def prefill_leg(gdn, name, x, steps, warmup, stream, cpu: bool, cpu_seqs: int, c
     n = x.num_seqs
     o = torch.empty((T, H, dv), dtype=x.q.dtype, device=x.q.device)
     S = torch.empty((n, H, dk, dv), dtype=torch.float32, device=x.q.device)
-    ws_bytes = gdn.gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+    ws_bytes = gdn.gdn_prefill_workspace_bytes(T, n, H, dk, dv, max_seqlen)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.q.device) if ws_bytes else None
 
     def step():
         gdn.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state, final_state=S,
-                        o=o, workspace=ws, stream=stream)
+                        o=o, workspace=ws, stream=stream, max_seqlen=max_seqlen)
 
     ms = time_loop(step, steps, warmup, stream)
     init = x.initial_state is not None
@@ -319,7 +322,8 @@ def prefill_leg(gdn, name, x, steps, warmup, stream, cpu: bool, cpu_seqs: int, c
                              x.beta[:tk, :1].to("cpu", torch.float64).numpy(), np.array([0, tk], np.int32),
                              initial_state=s0)
     leg = {"workload": name, "num_seqs": n, "T": T, "H": H, "d_k": dk, "d_v": dv, "initial_state": init,
-           "workspace_bytes": ws_bytes, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+           "max_seqlen_hint": max_seqlen, "workspace_bytes": ws_bytes, "steps": steps, "warmup": warmup,
+           "ms_per_step": ms,
            "tokens_per_s": T / (ms / 1e3),
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": pbytes},
@@ -532,6 +536,19 @@ def main():
                                            not args.no_cpu, 1, "the first 131072 of 1048576 tokens",
                                            cpu_x=prefix_view(xl, 131072))
         del xl
+        torch.cuda.empty_cache()
+        # a skewed packed batch: 63 sequences of 1,024 tokens and one of 262,144, 32 heads;
+        # gdn_prefill plans from the mean length, gdn_prefill_maxlen from the bound on the lengths
+        lens = [1024] * 63 + [262144]
+        xs = inputs.make_prefill_inputs(lens, 32, d, d, dtype=torch.bfloat16, seed=5, device=dev)
+        plain = prefill_leg(gdn, "skewed64", xs, args.workload_steps, 3, stream, False, 0, "")
+        hinted = prefill_leg(gdn, "skewed64", xs, args.workload_steps, 3, stream, not args.no_cpu, 63,
+                             "the 63 sequences of 1,024 tokens", max_seqlen=max(lens))
+        hinted["without_hint_ms_per_step"] = plain["ms_per_step"]
+        hinted["without_hint_roofline_frac"] = plain["roofline"]["frac"]
+        hinted["speedup_from_hint"] = plain["ms_per_step"] / hinted["ms_per_step"]
+        workloads["skewed64"] = hinted
+        del xs
         torch.cuda.empty_cache()
 
     traffic = measured_traffic("prefill")

@@ -62,6 +62,10 @@ def _load():
     lib.gdn_prefill_workspace_bytes.restype = sz
     lib.gdn_prefill.argtypes = [P, P, P, P, P, P, i32, i64, P, P, P, i32, i32, i32, i32, P, sz, P]
     lib.gdn_prefill.restype = i32
+    lib.gdn_prefill_maxlen.argtypes = [P, P, P, P, P, P, i32, i64, i64, P, P, P, i32, i32, i32, i32, P, sz, P]
+    lib.gdn_prefill_maxlen.restype = i32
+    lib.gdn_prefill_workspace_bytes_maxlen.argtypes = [i64, i32, i64, i32, i32, i32]
+    lib.gdn_prefill_workspace_bytes_maxlen.restype = sz
     lib.gdn_prefill_noalloc.argtypes = [P, P, P, P, P, P, i32, i64, P, P, P, i32, i32, i32, i32, P]
     lib.gdn_prefill_noalloc.restype = i32
     lib.gdn_decode.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
@@ -147,7 +151,10 @@ def gdn_state_bytes(num_seqs: int, H: int, dk: int, dv: int) -> int:
     return int(_load().gdn_state_bytes(num_seqs, H, dk, dv))
 
 
-def gdn_prefill_workspace_bytes(T_total: int, num_seqs: int, H: int, dk: int, dv: int) -> int:
+def gdn_prefill_workspace_bytes(T_total: int, num_seqs: int, H: int, dk: int, dv: int, max_seqlen: int = 0) -> int:
+    """Scratch bytes of gdn_prefill (max_seqlen > 0: of gdn_prefill with that bound on the lengths)."""
+    if max_seqlen:
+        return int(_load().gdn_prefill_workspace_bytes_maxlen(T_total, num_seqs, int(max_seqlen), H, dk, dv))
     return int(_load().gdn_prefill_workspace_bytes(T_total, num_seqs, H, dk, dv))
 
 
@@ -163,12 +170,13 @@ def gdn_state_free(address: int, stream=None) -> None:
 
 
 def gdn_prefill(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=None, o=None, workspace=None,
-                output_final_state: bool = True, stream=None):
+                output_final_state: bool = True, stream=None, max_seqlen: int = 0):
     """Chunked prefill; returns (o, final_state or None).
 
     q, k [T, H, dk] and v [T, H, dv] in bf16 or fp32; g [T, H, dk] and beta [T, H]
     in fp32; cu_seqlens int32 [num_seqs + 1] on the device.  final_state may be
-    initial_state itself (updated in place)."""
+    initial_state itself (updated in place).  max_seqlen > 0, a host-side bound on
+    the sequence lengths, calls gdn_prefill_maxlen (planning for skewed batches)."""
     _need(q, "q", dims=3)
     T, H, dk = q.shape
     dv = v.shape[-1]
@@ -193,15 +201,35 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=No
             final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
         if final_state is not None:
             _need(final_state, "final_state", torch.float32, 4)
-        need = gdn_prefill_workspace_bytes(T, n, H, dk, dv)
+        need = gdn_prefill_workspace_bytes(T, n, H, dk, dv, max_seqlen)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        st = _load().gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
-                             _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
-                             _ptr(workspace), ws_bytes, _stream(stream))
-        _check(st, "gdn_prefill")
+        if max_seqlen:
+            st = _load().gdn_prefill_maxlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                            int(max_seqlen), _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk,
+                                            dv, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream))
+            _check(st, "gdn_prefill_maxlen")
+        else:
+            st = _load().gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+                                     _ptr(initial_state), _ptr(final_state), _ptr(o), H, dk, dv, _dtype_code(q),
+                                     _ptr(workspace), ws_bytes, _stream(stream))
+            _check(st, "gdn_prefill")
     return o, final_state
+
+
+def gdn_prefill_workspace_bytes_maxlen(T_total: int, num_seqs: int, max_seqlen: int, H: int, dk: int, dv: int) -> int:
+    return int(_load().gdn_prefill_workspace_bytes_maxlen(T_total, num_seqs, int(max_seqlen), H, dk, dv))
+
+
+def gdn_prefill_maxlen(q, k, v, g, beta, cu_seqlens, max_seqlen: int, initial_state=None, final_state=None, o=None,
+                       workspace=None, output_final_state: bool = True, stream=None):
+    """gdn_prefill with a host-side bound max_seqlen on the sequence lengths (see gdn_prefill)."""
+    if max_seqlen < 0:
+        raise ValueError("max_seqlen must be >= 0")
+    return gdn_prefill(q, k, v, g, beta, cu_seqlens, initial_state=initial_state, final_state=final_state, o=o,
+                       workspace=workspace, output_final_state=output_final_state, stream=stream,
+                       max_seqlen=max_seqlen)
 
 
 def gdn_prefill_noalloc(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=None, o=None,
@@ -474,7 +502,7 @@ def gdn_prefill_tiles(q, k, v, g, beta, cu_seqlens, tile_path, initial_state=Non
 
 __all__ = [
     "gdn_status_string", "gdn_state_bytes", "gdn_state_alloc", "gdn_state_free", "gdn_prefill_workspace_bytes",
-    "gdn_prefill", "gdn_prefill_noalloc", "gdn_decode", "gdn_prefill_logits", "gdn_decode_logits", "gdn_prefill_head_gate",
+    "gdn_prefill", "gdn_prefill_maxlen", "gdn_prefill_workspace_bytes_maxlen", "gdn_prefill_noalloc", "gdn_decode", "gdn_prefill_logits", "gdn_decode_logits", "gdn_prefill_head_gate",
     "gdn_decode_head_gate", "gdn_prefill_backward", "gdn_prefill_backward_workspace_bytes", "gdn_prefill_tiles", "GdnError", "load_library", "LIB_PATH",
     "GDN_GATE_LOG", "GDN_GATE_SCALED_SIGMOID", "GDN_GATE_ALPHA_MIN", "GDN_TILES_DENSE", "GDN_TILES_PAIRS",
 ]

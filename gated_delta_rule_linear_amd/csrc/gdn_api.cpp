@@ -24,7 +24,7 @@ bool validate_mode() {
 // Host-side check of cu_seqlens and of the log-decay domain (g_dev may be
 // null); synchronous.
 int32_t validate_inputs(const int32_t* cu_dev, int32_t num_seqs, int64_t T_total, const float* g_dev, int64_t ng,
-                        hipStream_t s) {
+                        hipStream_t s, int64_t max_seqlen = 0) {
     std::vector<int32_t> cu((size_t)num_seqs + 1);
     if (hipMemcpyAsync(cu.data(), cu_dev, sizeof(int32_t) * cu.size(), hipMemcpyDeviceToHost, s) != hipSuccess)
         return GDN_ERR_HIP;
@@ -33,8 +33,10 @@ int32_t validate_inputs(const int32_t* cu_dev, int32_t num_seqs, int64_t T_total
         return GDN_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
     if (cu[0] != 0 || cu[(size_t)num_seqs] != T_total) return GDN_ERR_DOMAIN;
-    for (int32_t n = 0; n < num_seqs; ++n)
+    for (int32_t n = 0; n < num_seqs; ++n) {
         if (cu[(size_t)n + 1] < cu[(size_t)n]) return GDN_ERR_DOMAIN;
+        if (max_seqlen > 0 && cu[(size_t)n + 1] - cu[(size_t)n] > max_seqlen) return GDN_ERR_DOMAIN;
+    }
     for (float x : g)
         if (!(x >= -5.0f && x <= 0.0f)) return GDN_ERR_DOMAIN;
     return GDN_OK;
@@ -57,7 +59,47 @@ namespace gdn {
 // where rounds() weights a partly filled round by its occupancy, and splits
 // when that saves at least 5%.  The workspace bound, and so the
 // plan, depends on the arguments only.
-int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
+// With a host-side bound max_seqlen on the lengths (a skewed batch: one long
+// sequence packed with short ones), the plan assumes the most skewed batch the
+// bound allows -- n_long = T_total / max_seqlen sequences of max_seqlen tokens,
+// the other tokens spread evenly over the rest -- and compares
+//   whole sequences:  max(chain of the longest, total work / CUS)
+//   split (length Ls, only the long sequences have more than one segment):
+//     phase 1 = max(Ls chain, (long units' first segments + every short unit
+//               + the maps of segments 1 .. P-2) / CUS)
+//     + fold_pass(P - 2, long units d_v/16) + rounds(long units (P - 1)) (Ls chunks + START)
+// in the same chunk-time units, and splits when that saves at least 5%.  When
+// every sequence can be of max_seqlen tokens, the mean-length plan is used.
+static int64_t plan_prefill_skewed(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_v, bool share,
+                                   int64_t max_len) {
+    typedef SplitCost K;
+    const double n_long = (double)std::max<int64_t>(1, std::min<int64_t>(num_seqs, T_total / max_len));
+    const double n_short = num_seqs - n_long, short_tokens = (double)T_total - n_long * (double)max_len;
+    const double len_s = n_short > 0 ? short_tokens / n_short : 0.0;
+    const double Ul = n_long * H, Us = n_short * H, chain = std::ceil(max_len / 64.0) + K::START;
+    const double short_work = Us * (std::ceil(len_s / 64.0) + K::START);
+    const double whole = std::max(chain, (Ul * chain + short_work) / K::CUS);
+    double best = whole;
+    int64_t best_seg = 0;
+    const int64_t step = std::max<int64_t>(64, max_len / 2048 / 64 * 64);
+    for (int64_t ls = std::max<int64_t>(1024, (int64_t)std::ceil(len_s / 64.0) * 64); ls < max_len; ls += step) {
+        const double P = std::ceil((double)max_len / ls), ch = ls / 64.0;
+        bool both = false;
+        (void)K::maps_pass(Ul * (P - 2), ch, share, &both);
+        const double map_work = (both ? Ul * (P - 2) * (ch * K::MAP_BOTH + K::START)
+                                      : 2 * Ul * (P - 2) * (ch * K::MAP_ONE + K::START));
+        const double first = std::max(ch + K::START, (Ul * (ch + K::START) + short_work + map_work) / K::CUS);
+        const double t = first + K::fold_pass(P - 2, Ul * (d_v / 16)) + K::rounds(Ul * (P - 1)) * (ch + K::START);
+        if (t < best) {
+            best = t;
+            best_seg = ls;
+        }
+    }
+    return best < 0.95 * whole ? best_seg : 0;
+}
+
+int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, bool bf16,
+                             int64_t max_seqlen) {
     if (const char* e = std::getenv("GDN_PREFILL_SEGMENT")) {
         if (*e) {
             const long long v = std::strtoll(e, nullptr, 10);
@@ -65,6 +107,8 @@ int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32
         }
     }
     if (num_seqs <= 0 || T_total <= 0 || H <= 0) return 0;
+    if (max_seqlen > 0 && max_seqlen < T_total && (int64_t)num_seqs * max_seqlen > T_total)
+        return plan_prefill_skewed(T_total, num_seqs, H, d_v, bf16 && d_k == d_v, max_seqlen);
     typedef SplitCost K;
     const bool share = bf16 && d_k == d_v;
     const double units = (double)num_seqs * H;
@@ -152,8 +196,13 @@ int32_t gdn_state_free(float* state, void* stream) {
 }
 
 size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v) {
-    if (T_total < 0 || num_seqs < 0 || H < 1 || d_k < 0 || d_v < 0) return 0;
-    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H, d_k, d_v, true);
+    return gdn_prefill_workspace_bytes_maxlen(T_total, num_seqs, 0, H, d_k, d_v);
+}
+
+size_t gdn_prefill_workspace_bytes_maxlen(int64_t T_total, int32_t num_seqs, int64_t max_seqlen, int32_t H,
+                                          int32_t d_k, int32_t d_v) {
+    if (T_total < 0 || num_seqs < 0 || max_seqlen < 0 || H < 1 || d_k < 0 || d_v < 0) return 0;
+    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H, d_k, d_v, true, max_seqlen);
     return gdn::prefill_workspace_layout(T_total, num_seqs, H, d_k, d_v, seg).bytes;
 }
 
@@ -161,8 +210,8 @@ static int32_t prefill_impl(const void* q, const void* k, const void* v, const f
                             int32_t gate, float gate_param, const float* beta, const int32_t* cu_seqlens,
                             int32_t num_seqs, int64_t T_total, const float* initial_state, float* final_state,
                             void* o, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-    if (num_seqs < 0 || T_total < 0 || H < 1) return GDN_ERR_INVALID_ARG;
+                            size_t workspace_bytes, void* stream, int64_t max_seqlen = 0) {
+    if (num_seqs < 0 || T_total < 0 || H < 1 || max_seqlen < 0) return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
     if (T_total > 0 && num_seqs == 0) return GDN_ERR_INVALID_ARG;
@@ -178,7 +227,7 @@ static int32_t prefill_impl(const void* q, const void* k, const void* v, const f
     }
     if (initial_state && !aligned(initial_state, 16)) return GDN_ERR_INVALID_ARG;
     if (final_state && !aligned(final_state, 16)) return GDN_ERR_INVALID_ARG;
-    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H, d_k, d_v, true);
+    const int64_t seg = gdn::plan_prefill_segment(T_total, num_seqs, H, d_k, d_v, true, max_seqlen);
     const size_t need = gdn::prefill_workspace_layout(T_total, num_seqs, H, d_k, d_v, seg).bytes;
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return GDN_ERR_INVALID_ARG;
     if (((int64_t)num_seqs + (seg > 0 ? T_total / seg : 0)) * H * (d_v / 16) > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
@@ -187,7 +236,7 @@ static int32_t prefill_impl(const void* q, const void* k, const void* v, const f
         // (logits: every finite or infinite z maps into the domain, so only cu_seqlens is checked)
         const bool has_g = gate == GDN_GATE_LOG || gate == gdn::GATE_HEAD;
         const int32_t st = validate_inputs(cu_seqlens, num_seqs, T_total, has_g ? g : nullptr,
-                                           T_total * H * (gate == gdn::GATE_HEAD ? 1 : d_k), s);
+                                           T_total * H * (gate == gdn::GATE_HEAD ? 1 : d_k), s, max_seqlen);
         if (st != GDN_OK) return st;
     }
     gdn::PrefillLaunch p;
@@ -211,6 +260,7 @@ static int32_t prefill_impl(const void* q, const void* k, const void* v, const f
     p.z = z;
     p.gate = gate;
     p.gate_param = gate_param;
+    p.max_seqlen = max_seqlen;
     {
         const char* e = std::getenv("GDN_PREFILL_KERNEL");
         p.legacy = e && std::strcmp(e, "seq") == 0;
@@ -224,6 +274,14 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
                     void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_impl(q, k, v, g, nullptr, GDN_GATE_LOG, 0.f, beta, cu_seqlens, num_seqs, T_total, initial_state,
                         final_state, o, H, d_k, d_v, dtype, workspace, workspace_bytes, stream);
+}
+
+int32_t gdn_prefill_maxlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total, int64_t max_seqlen,
+                           const float* initial_state, float* final_state, void* o, int32_t H, int32_t d_k,
+                           int32_t d_v, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, g, nullptr, GDN_GATE_LOG, 0.f, beta, cu_seqlens, num_seqs, T_total, initial_state,
+                        final_state, o, H, d_k, d_v, dtype, workspace, workspace_bytes, stream, max_seqlen);
 }
 
 int32_t gdn_prefill_head_gate(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -35,6 +35,7 @@ struct PrefillLaunch {
     const void* z = nullptr;  // bf16 gate logits [T_total, H, d_k] (gate != 0; g unused)
     int32_t gate = 0;         // 0: g given; 1, 2: gdn_gate parameterisation of z
     float gate_param = 0.f;
+    int64_t max_seqlen = 0;   // host-side bound on the sequence lengths (0: unknown)
 };
 
 // Workspace of the time-split prefill, for segments of `seg` tokens.  A
@@ -100,9 +101,11 @@ struct SplitCost {
 };
 
 // Segment length chosen for a batch of these sizes (0: one workgroup per whole
-// sequence and head).  Depends on the arguments only, and on the environment
-// variable GDN_PREFILL_SEGMENT, which forces a length (0 = never split).
-int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
+// sequence and head).  Depends on the arguments only (max_seqlen: a host-side
+// bound on the lengths, 0 when unknown), and on the environment variable
+// GDN_PREFILL_SEGMENT, which forces a length (0 = never split).
+int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, bool bf16,
+                             int64_t max_seqlen = 0);
 
 struct DecodeLaunch {
     const void* q;

@@ -1887,10 +1887,15 @@ hipError_t run_maps_fold(const PrefillLaunch& p, Args<TI>& a, hipStream_t s, hip
     const int64_t map_blocks = ws.slots * p.H;
     if (map_blocks > 0) {
         // M and N in one workgroup or in two: decided for the number of
-        // transitions that sequences of the mean length would have (the grid
-        // is sized for the bound; surplus workgroups exit at once)
-        const int64_t len = (p.T_total + p.num_seqs - 1) / p.num_seqs;
-        const double maps = (double)p.num_seqs * p.H * (len > 0 ? std::max<int64_t>(0, (len - 1) / p.seg - a.map_from) : 0);
+        // transitions that sequences of the mean length would have, or with a
+        // bound on the lengths the long sequences of the most skewed batch it
+        // allows (the grid is sized for the bound; surplus workgroups exit at once)
+        int64_t len = (p.T_total + p.num_seqs - 1) / p.num_seqs, nlen = p.num_seqs;
+        if (p.max_seqlen > len) {
+            len = p.max_seqlen;
+            nlen = std::max<int64_t>(1, std::min<int64_t>(p.num_seqs, p.T_total / p.max_seqlen));
+        }
+        const double maps = (double)nlen * p.H * (len > 0 ? std::max<int64_t>(0, (len - 1) / p.seg - a.map_from) : 0);
         bool both = false;
         SplitCost::maps_pass(maps, p.seg / 64.0, DK == DV && sizeof(TI) == 2, &both);
         if constexpr (DK == DV && sizeof(TI) == 2) {

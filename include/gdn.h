@@ -154,6 +154,34 @@ int32_t gdn_prefill(const void* q, const void* k, const void* v, const float* g,
                     int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* gdn_prefill for packed batches whose lengths are skewed (say one long
+ * sequence among many short ones), with a host-side bound on the lengths.
+ *   max_seqlen  >= cu_seqlens[n+1] - cu_seqlens[n] for every n; 0 = unknown
+ *               (then exactly gdn_prefill).  Negative: GDN_ERR_INVALID_ARG.
+ *               With GDN_VALIDATE=1 a sequence longer than the bound is
+ *               GDN_ERR_DOMAIN.
+ *   workspace   at least gdn_prefill_workspace_bytes_maxlen(T_total,
+ *               num_seqs, max_seqlen, H, d_k, d_v) bytes.
+ * Everything else is as for gdn_prefill.  gdn_prefill plans the time split
+ * (which sequences are cut into segments run in parallel) from the mean
+ * length, since the lengths stay on the device; a bound lets it cut the long
+ * sequences of a skewed batch, whose serial chains would otherwise be the
+ * whole call's critical path.  A bound that is too large or too small changes
+ * the plan, never the result (up to rounding).  This is this library's
+ * scheduling of the pages' chunked form: no passage of the pages defines the
+ * call. */
+int32_t gdn_prefill_maxlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const int32_t* cu_seqlens, int32_t num_seqs, int64_t T_total, int64_t max_seqlen,
+                           const float* initial_state, float* final_state, void* o,
+                           int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device scratch bytes of gdn_prefill_maxlen (0 for invalid arguments); a
+ * function of the arguments only, like gdn_prefill_workspace_bytes, which it
+ * equals for max_seqlen = 0. */
+size_t gdn_prefill_workspace_bytes_maxlen(int64_t T_total, int32_t num_seqs, int64_t max_seqlen, int32_t H,
+                                          int32_t d_k, int32_t d_v);
+
 /* Bytes of the fixed device scratch of gdn_prefill_noalloc (64 MiB). */
 #define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

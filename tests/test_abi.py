@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
                           "gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_prefill_logits",
                           "gdn_decode_logits", "gdn_prefill_head_gate", "gdn_decode_head_gate",
                           "gdn_prefill_backward_workspace_bytes", "gdn_prefill_backward", "gdn_prefill_tiles",
-                          "gdn_prefill_noalloc"}
+                          "gdn_prefill_noalloc", "gdn_prefill_maxlen", "gdn_prefill_workspace_bytes_maxlen"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -108,6 +108,30 @@ def test_time_split_plan(monkeypatch):
     # short sequences are never split
     assert gdn.gdn_prefill_workspace_bytes(256, 1, 2, 64, 64) == 0
     assert gdn.gdn_prefill_workspace_bytes(0, 3, 2, 64, 64) == 0
+
+
+def test_time_split_plan_with_a_bound_on_the_lengths(monkeypatch):
+    monkeypatch.delenv("GDN_PREFILL_SEGMENT", raising=False)
+    # one 262,144-token sequence among 63 of 1,024 tokens, 32 heads: 2,048 units, so the
+    # mean-length plan does not split; the bound on the lengths cuts the long sequence
+    T, n, H = 262144 + 63 * 1024, 64, 32
+    assert gdn.gdn_prefill_workspace_bytes(T, n, H, 128, 128) == 0
+    assert gdn.gdn_prefill_workspace_bytes_maxlen(T, n, 262144, H, 128, 128) > 0
+    # a bound of 0 is gdn_prefill's plan; balanced batches plan as without a bound
+    for args in ((65536, 1, 32), (32768, 4, 32), (540000, 64, 32), (T, n, H)):
+        assert gdn.gdn_prefill_workspace_bytes_maxlen(args[0], args[1], 0, args[2], 128, 128) == \
+            gdn.gdn_prefill_workspace_bytes(*args, 128, 128)
+    assert gdn.gdn_prefill_workspace_bytes_maxlen(32768, 4, 8192, 32, 128, 128) == \
+        gdn.gdn_prefill_workspace_bytes(32768, 4, 32, 128, 128)
+    # uniform lengths up to the bound: nothing to gain from a split
+    assert gdn.gdn_prefill_workspace_bytes_maxlen(540000, 64, 16384, 32, 128, 128) == 0
+    assert gdn.gdn_prefill_workspace_bytes_maxlen(T, n, -1, H, 128, 128) == 0
+
+
+def test_maxlen_argument_errors(lib):
+    p = ctypes.c_void_p(0x10000)
+    st = lib.gdn_prefill_maxlen(p, p, p, p, p, p, 1, 10, -1, None, None, p, 4, 64, 64, 1, None, 0, None)
+    assert st == INVALID
 
 
 def test_time_split_workspace_layout(monkeypatch):

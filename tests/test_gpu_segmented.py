@@ -152,3 +152,39 @@ def test_split_head_gate(monkeypatch, gate):
     o1, S1 = gdn.gdn_prefill_head_gate(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, initial_state=x.initial_state)
     torch.cuda.synchronize()
     assert_close("o vs unsplit", np64(o), np64(o1), TOL[torch.bfloat16])
+
+
+def test_maxlen_hint_splits_a_skewed_batch(monkeypatch):
+    # one 16,384-token sequence among 31 of 256 tokens, 4 heads: planned from the
+    # mean length the batch is not split; with the bound on the lengths the long
+    # sequence is cut into segments.  Every unit against the fp64 oracle.
+    monkeypatch.delenv("GDN_PREFILL_SEGMENT", raising=False)
+    lengths = [256] * 15 + [16384] + [256] * 16
+    H, d = 4, 128
+    T = sum(lengths)
+    assert gdn.gdn_prefill_workspace_bytes(T, len(lengths), H, d, d) == 0
+    assert gdn.gdn_prefill_workspace_bytes_maxlen(T, len(lengths), 16384, H, d, d) > 0
+    log(f"skewed batch T={T}: workspace with the bound "
+        f"{gdn.gdn_prefill_workspace_bytes_maxlen(T, len(lengths), 16384, H, d, d)} bytes")
+    x = inputs.make_prefill_inputs(lengths, H, d, d, dtype=torch.bfloat16, init_state=True, seed=26)
+    ref_o, ref_S = oracle_prefill(x)
+    to_device(x)
+    o, S = gdn.gdn_prefill_maxlen(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, 16384, initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    assert_close("o", np64(o), ref_o, TOL[torch.bfloat16])
+    assert_close("final_state", np64(S), ref_S, TOL[torch.bfloat16])
+    # a bound that is too large or too small changes the plan, not the result
+    for bound in (1 << 20, 1024):
+        ob, Sb = gdn.gdn_prefill_maxlen(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, bound,
+                                        initial_state=x.initial_state)
+        torch.cuda.synchronize()
+        assert_close(f"o, bound {bound}", np64(ob), ref_o, TOL[torch.bfloat16])
+        assert_close(f"final_state, bound {bound}", np64(Sb), ref_S, TOL[torch.bfloat16])
+    # under validation, a sequence longer than the bound is a domain error and nothing is written
+    monkeypatch.setenv("GDN_VALIDATE", "1")
+    oz = torch.full_like(o, 7.0)
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.gdn_prefill_maxlen(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, 8192, initial_state=x.initial_state, o=oz)
+    assert ei.value.status == gdn.GDN_ERR_DOMAIN
+    torch.cuda.synchronize()
+    assert torch.all(oz == 7.0)
