@@ -515,7 +515,7 @@ def main():
                         "frac": bflops / (bms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
                "parity_max_rel_err_seq0_head0": bpar}
         if not args.no_cpu:
-            bwd["cpu_baseline"] = cpu_backward_baseline(xb, d_o, dSf, 2048, 16)
+            bwd["cpu_baseline"] = cpu_backward_baseline(xb, d_o, dSf, 8192, 16)
 
     # ---- the other prefill workloads: varlen64 and long_1m
     workloads = None
