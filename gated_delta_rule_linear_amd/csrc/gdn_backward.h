@@ -63,7 +63,7 @@ inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_
     w.bytes = w.pre_off;
     if (seg > 0) {
         w.slots = T_total / seg + num_seqs;
-        w.d_off = w.pre_off + al(prefill_workspace_layout(T_total, num_seqs, H, dk, dv, seg).bytes);
+        w.d_off = w.pre_off + al(prefill_workspace_layout(T_total, num_seqs, H, dk, dv, seg, false).bytes);
         w.bytes = w.d_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
     }
     return w;

@@ -911,7 +911,7 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     // reverse fold, then both sweeps per segment from the folded boundary values
     const BackwardWorkspace ws = backward_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.bf16, p.seg);
     char* base = static_cast<char*>(p.workspace);
-    const PrefillWorkspace pw = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
+    const PrefillWorkspace pw = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg, false);
     a.nl = reinterpret_cast<const int32_t*>(base + ws.pre_off + pw.nl_off);
     a.fM = reinterpret_cast<const float*>(base + ws.pre_off + pw.m_off);
     a.fN = reinterpret_cast<const float*>(base + ws.pre_off + pw.n_off);

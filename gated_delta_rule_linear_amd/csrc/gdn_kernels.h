@@ -30,7 +30,7 @@ struct PrefillLaunch {
     bool bf16;
     int64_t T_total;
     int64_t seg;      // segment length of the time split (tokens, multiple of 64); 0: none
-    void* workspace;  // prefill_workspace_layout(...).bytes bytes when seg > 0
+    void* workspace;  // prefill_workspace_layout(...).bytes bytes (none when that is 0)
     bool legacy;      // bf16: single-role kernel (GDN_PREFILL_KERNEL=seq) instead of the warp-specialised one
     const void* z = nullptr;  // bf16 gate logits [T_total, H, d_k] (gate != 0; g unused)
     int32_t gate = 0;         // 0: g given; 1, 2: gdn_gate parameterisation of z
@@ -38,25 +38,44 @@ struct PrefillLaunch {
     int64_t max_seqlen = 0;   // host-side bound on the sequence lengths (0: unknown)
 };
 
-// Workspace of the time-split prefill, for segments of `seg` tokens.  A
-// sequence's non-last segments hold exactly seg tokens, so there are at most
-// T_total / seg of them over the batch; each (non-last segment, head) owns an
-// M slot (d_k x d_k fp32) and an N slot (d_k x d_v fp32).  nl is the int32
-// table of non-last segment counts [num_seqs + 1].
+// Compute units of the device the plans are made for (MI355X).
+constexpr int64_t kComputeUnits = 256;
+
+// Workspace of the prefill.
+// Time split, for segments of `seg` tokens: a sequence's non-last segments
+// hold exactly seg tokens, so there are at most T_total / seg of them over the
+// batch; each (non-last segment, head) owns an M slot (d_k x d_k fp32) and an
+// N slot (d_k x d_v fp32).  nl is the int32 table of non-last segment counts
+// [num_seqs + 1].
+// Unit order: with more than one sequence, the workgroups of a pass over
+// whole sequences (or over every sequence's first segment) take the sequences
+// longest first, from the int32 table ord [num_seqs] (a permutation of the
+// sequence indices that the order kernel writes at the start of the call), so
+// that the long chains start first.  It is kept when the split runs, or when
+// there are more (sequence, head) units than compute units; otherwise every
+// unit starts at once and the order changes nothing.  (with_order = false: the
+// maps and fold alone, which need no order.)
 struct PrefillWorkspace {
     int64_t slots = 0;
-    size_t m_off = 0, n_off = 0, nl_off = 0, bytes = 0;
+    size_t m_off = 0, n_off = 0, nl_off = 0, ord_off = 0, bytes = 0;
+    bool ord = false;
 };
 inline PrefillWorkspace prefill_workspace_layout(int64_t T_total, int32_t num_seqs, int32_t H, int32_t dk,
-                                                 int32_t dv, int64_t seg) {
+                                                 int32_t dv, int64_t seg, bool with_order = true) {
     PrefillWorkspace w;
-    if (seg <= 0) return w;
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    w.slots = T_total / seg;
-    w.m_off = 0;
-    w.n_off = al((size_t)w.slots * H * dk * dk * sizeof(float));
-    w.nl_off = w.n_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
-    w.bytes = w.nl_off + al(((size_t)num_seqs + 1) * sizeof(int32_t));
+    if (seg > 0) {
+        w.slots = T_total / seg;
+        w.m_off = 0;
+        w.n_off = al((size_t)w.slots * H * dk * dk * sizeof(float));
+        w.nl_off = w.n_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
+        w.bytes = w.nl_off + al(((size_t)num_seqs + 1) * sizeof(int32_t));
+    }
+    if (with_order && num_seqs > 1 && (seg > 0 || (int64_t)num_seqs * H > kComputeUnits)) {
+        w.ord = true;
+        w.ord_off = w.bytes;
+        w.bytes += al((size_t)num_seqs * sizeof(int32_t));
+    }
     return w;
 }
 
@@ -65,7 +84,7 @@ inline PrefillWorkspace prefill_workspace_layout(int64_t T_total, int32_t num_se
 struct SplitCost {
     // Costs in units of one 64-token chunk of the output pass with every CU busy
     // (fitted to kernel traces of the bf16 kernels at d = 128 on MI355X).
-    static constexpr double CUS = 256.0;     // compute units
+    static constexpr double CUS = (double)kComputeUnits;
     static constexpr double MAP_ONE = 0.76;  // a transition workgroup computing M or N
     static constexpr double MAP_BOTH = 0.87; // one computing M and N together (bf16, d_k = d_v)
     static constexpr double START = 0.7;     // fixed cost per workgroup

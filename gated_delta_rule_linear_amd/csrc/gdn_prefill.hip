@@ -139,6 +139,10 @@ struct Args {
     const bf16* z;
     int gate;
     float gate_param;
+    // passes over whole sequences (seg == 0) and over first segments (phase 1):
+    // workgroup b takes head b % H of sequence ord[b / H] (longest first), or
+    // of sequence b / H when ord is null
+    const int32_t* ord;
 };
 
 template <typename T>
@@ -409,9 +413,10 @@ __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
         u.eye = u.vzero = kindM;
         u.sf = kindM ? a.wsM + ((size_t)k * H + u.h) * DK * DK : a.wsN + ((size_t)k * H + u.h) * DK * DV;
     } else if (a.seg > 0 && a.phase == 1) {
-        const int n = b / H;
-        u.h = b - n * H;
-        const size_t unit = (size_t)b;
+        const int nb = b / H;
+        u.h = b - nb * H;
+        const int n = a.ord ? a.ord[nb] : nb;
+        const size_t unit = (size_t)n * H + u.h;
         u.tb = a.cu[n];
         u.te = u.tb + a.seg < a.cu[n + 1] ? u.tb + a.seg : a.cu[n + 1];
         u.s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
@@ -437,12 +442,14 @@ __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
         else u.s0 = a.wsN + ((size_t)(a.nl[n] + j - 1) * H + u.h) * DK * DV;
         if (j == last && a.Sf) u.sf = a.Sf + unit * DK * DV;
     } else {
-        const int n = b / H;
-        u.h = b - n * H;
+        const int nb = b / H;
+        u.h = b - nb * H;
+        const int n = a.ord ? a.ord[nb] : nb;
+        const size_t unit = (size_t)n * H + u.h;
         u.tb = a.cu[n];
         u.te = a.cu[n + 1];
-        u.s0 = a.S0 ? a.S0 + (size_t)b * DK * DV : nullptr;
-        u.sf = a.Sf ? a.Sf + (size_t)b * DK * DV : nullptr;
+        u.s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
+        u.sf = a.Sf ? a.Sf + unit * DK * DV : nullptr;
     }
     return u;
 }
@@ -1777,6 +1784,81 @@ __global__ __launch_bounds__(256) void seg_table_kernel(const int32_t* __restric
     }
 }
 
+// Order of the sequences for a pass with one workgroup per (sequence, head):
+// longest first, so that the longest chains are dispatched first (a pass over
+// many units of mixed lengths otherwise ends on a long unit that started
+// late).  The key of a sequence is the bucket of its length in 64-token chunks
+// (capped at `cap` tokens when cap > 0: a first segment is at most one
+// segment long), four buckets per octave, 0 for an empty sequence; ord lists
+// the buckets from the highest down, each in increasing sequence index, so the
+// order is deterministic.  One workgroup: a histogram of the keys, a scan over
+// the buckets, then the placement, 1024 sequences per step (the lanes of a wave
+// that share a key are found with one ballot per key bit; the waves' counts
+// per key are summed in LDS).
+constexpr int kOrderBuckets = 128;  // keys 0 .. 104 (and one value for idle lanes)
+__device__ __forceinline__ int order_key(int len, int cap) {
+    if (cap > 0 && len > cap) len = cap;
+    if (len <= 0) return 0;
+    const unsigned c = ((unsigned)len + 63u) / 64u;
+    const int e = 31 - __builtin_clz(c);
+    const int sub = e >= 2 ? (int)(c >> (e - 2)) & 3 : (int)(c << (2 - e)) & 3;
+    return 1 + 4 * e + sub;
+}
+__global__ __launch_bounds__(1024) void seq_order_kernel(const int32_t* __restrict__ cu, int num_seqs, int cap,
+                                                         int32_t* __restrict__ ord) {
+    constexpr int NB = kOrderBuckets, NWV = 16;
+    __shared__ int hist[NB], start[NB], done[NB];
+    __shared__ int cnt[NWV][NB];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    if (t < NB) {
+        hist[t] = 0;
+        done[t] = 0;
+    }
+    for (int i = t; i < NWV * NB; i += 1024) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+    for (int n = t; n < num_seqs; n += 1024) atomicAdd(&hist[order_key(cu[n + 1] - cu[n], cap)], 1);
+    __syncthreads();
+    if (t == 0) {
+        int acc = 0;
+        for (int k = NB - 1; k >= 0; --k) {
+            start[k] = acc;
+            acc += hist[k];
+        }
+    }
+    __syncthreads();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int base = 0; base < num_seqs; base += 1024) {
+        const int n = base + t;
+        const bool valid = n < num_seqs;
+        const int key = valid ? order_key(cu[n + 1] - cu[n], cap) : NB;  // NB: idle lanes, a key of their own
+        unsigned long long same = ~0ull;
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool on = (key >> bit) & 1;
+            const unsigned long long m = __ballot(on);
+            same &= on ? m : ~m;
+        }
+        const int rank = __popcll(same & below);
+        if (valid && rank == 0) cnt[w][key] = __popcll(same);
+        __syncthreads();
+        if (valid) {
+            int pos = start[key] + done[key] + rank;
+            for (int v = 0; v < w; ++v) pos += cnt[v][key];
+            ord[pos] = n;
+        }
+        __syncthreads();
+        if (t < NB) {
+            int sum = 0;
+            for (int v = 0; v < NWV; ++v) {
+                sum += cnt[v][t];
+                cnt[v][t] = 0;
+            }
+            done[t] += sum;
+        }
+        __syncthreads();
+    }
+}
+
 // Serial fold over the segments of one (sequence, head), 16 state columns per
 // workgroup (columns of the state evolve independently):
 //   S_start(j + 1) = M_j S_start(j) + N_j,  j >= first,
@@ -1860,6 +1942,7 @@ Args<TI> make_args(const PrefillLaunch& p) {
     a.z = static_cast<const bf16*>(p.z);
     a.gate = p.gate;
     a.gate_param = p.gate_param;
+    a.ord = nullptr;
     return a;
 }
 
@@ -2004,6 +2087,16 @@ template <typename TI, int DK, int DV>
 hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     Args<TI> a = make_args<TI>(p);
     const int64_t units = (int64_t)p.num_seqs * p.H;
+    const PrefillWorkspace wl = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
+    if (wl.ord) {
+        // longest sequences first (for the pass over whole sequences, or over first segments)
+        int32_t* ord = reinterpret_cast<int32_t*>(static_cast<char*>(p.workspace) + wl.ord_off);
+        hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.num_seqs,
+                           (int)std::min<int64_t>(p.seg, 0x7fffffff), ord);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        a.ord = ord;
+    }
     if (p.seg <= 0) return launch_seq<TI, DK, DV, false>(a, units, s);
 
     // Time split.  Segment 0 of every sequence needs no map: its own output

@@ -102,8 +102,11 @@ int32_t gdn_state_free(float* state, void* stream);
 /* Device scratch bytes gdn_prefill needs for these sizes (may be 0).  The
  * bound depends only on the arguments, never on the lengths inside
  * cu_seqlens, so no device-to-host copy is needed to size it.  The scratch
- * holds the time split's segment maps, which are this library's design: no
- * passage of the pages defines this call. */
+ * holds the time split's segment maps and, with more than one sequence when
+ * the split runs or when num_seqs * H exceeds the 256 compute units, an int32
+ * table of num_seqs entries: the order (longest sequence first) in which the
+ * workgroups take the sequences, written by the call itself.  Both are this
+ * library's design: no passage of the pages defines this call. */
 size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v);
 
 /* Chunked prefill over packed variable-length sequences.

@@ -92,6 +92,23 @@ def test_state_alloc_overflowing_size_is_oom_without_a_device_call(lib):
     assert lib.gdn_state_alloc((1 << 63) - 1, 1, 64, 64, ctypes.byref(out), None) == OOM
 
 
+ORDER_TABLE_64 = 256  # int32 [64], rounded up to 256 bytes
+
+
+def test_unit_order_table(monkeypatch):
+    # the order table (int32 [num_seqs], 256-byte rounded) is kept when the split
+    # runs with more than one sequence, or when (sequence, head) units outnumber
+    # the 256 compute units; a single sequence or a batch that starts at once has none
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "0")
+    assert gdn.gdn_prefill_workspace_bytes(10000, 8, 32, 128, 128) == 0      # 256 units
+    assert gdn.gdn_prefill_workspace_bytes(10000, 9, 32, 128, 128) == 256    # 288 units
+    assert gdn.gdn_prefill_workspace_bytes(10 ** 6, 65, 32, 128, 128) == 512  # int32 [65]
+    assert gdn.gdn_prefill_workspace_bytes(10 ** 6, 1, 512, 128, 128) == 0   # one sequence
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "1024")
+    one = gdn.gdn_prefill_workspace_bytes(4096, 1, 2, 64, 64)
+    assert gdn.gdn_prefill_workspace_bytes(4096, 2, 2, 64, 64) == one + 256
+
+
 def test_workspace_bound_needs_no_lengths():
     # the bound is a function of the arguments alone
     a = gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128)
@@ -103,8 +120,9 @@ def test_time_split_plan(monkeypatch):
     monkeypatch.delenv("GDN_PREFILL_SEGMENT", raising=False)
     # one 65,536-token sequence x 32 heads: 32 workgroups would leave most CUs idle -> split
     assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128) > 0
-    # 64 sequences of ~8K tokens x 32 heads: 2048 workgroups already -> no split
-    assert gdn.gdn_prefill_workspace_bytes(540000, 64, 32, 128, 128) == 0
+    # 64 sequences of ~8K tokens x 32 heads: 2048 workgroups already -> no split,
+    # only the int32 order table [64] (more units than compute units)
+    assert gdn.gdn_prefill_workspace_bytes(540000, 64, 32, 128, 128) == ORDER_TABLE_64
     # short sequences are never split
     assert gdn.gdn_prefill_workspace_bytes(256, 1, 2, 64, 64) == 0
     assert gdn.gdn_prefill_workspace_bytes(0, 3, 2, 64, 64) == 0
@@ -115,8 +133,8 @@ def test_time_split_plan_with_a_bound_on_the_lengths(monkeypatch):
     # one 262,144-token sequence among 63 of 1,024 tokens, 32 heads: 2,048 units, so the
     # mean-length plan does not split; the bound on the lengths cuts the long sequence
     T, n, H = 262144 + 63 * 1024, 64, 32
-    assert gdn.gdn_prefill_workspace_bytes(T, n, H, 128, 128) == 0
-    assert gdn.gdn_prefill_workspace_bytes_maxlen(T, n, 262144, H, 128, 128) > 0
+    assert gdn.gdn_prefill_workspace_bytes(T, n, H, 128, 128) == ORDER_TABLE_64
+    assert gdn.gdn_prefill_workspace_bytes_maxlen(T, n, 262144, H, 128, 128) > ORDER_TABLE_64
     # a bound of 0 is gdn_prefill's plan; balanced batches plan as without a bound
     for args in ((65536, 1, 32), (32768, 4, 32), (540000, 64, 32), (T, n, H)):
         assert gdn.gdn_prefill_workspace_bytes_maxlen(args[0], args[1], 0, args[2], 128, 128) == \
@@ -124,7 +142,7 @@ def test_time_split_plan_with_a_bound_on_the_lengths(monkeypatch):
     assert gdn.gdn_prefill_workspace_bytes_maxlen(32768, 4, 8192, 32, 128, 128) == \
         gdn.gdn_prefill_workspace_bytes(32768, 4, 32, 128, 128)
     # uniform lengths up to the bound: nothing to gain from a split
-    assert gdn.gdn_prefill_workspace_bytes_maxlen(540000, 64, 16384, 32, 128, 128) == 0
+    assert gdn.gdn_prefill_workspace_bytes_maxlen(540000, 64, 16384, 32, 128, 128) == ORDER_TABLE_64
     assert gdn.gdn_prefill_workspace_bytes_maxlen(T, n, -1, H, 128, 128) == 0
 
 
@@ -137,10 +155,11 @@ def test_maxlen_argument_errors(lib):
 def test_time_split_workspace_layout(monkeypatch):
     # forced 8192-token segments: 8 full segments -> at most 8 non-last ones per
     # 65,536 tokens; each (slot, head) holds M (d_k x d_k) and N (d_k x d_v) in
-    # fp32, each area rounded up to 256 bytes, then the int32 table [n + 1]
+    # fp32, each area rounded up to 256 bytes, then the int32 table [n + 1] and,
+    # with more than one sequence, the int32 order table [n]
     monkeypatch.setenv("GDN_PREFILL_SEGMENT", "8192")
     assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 64) == 8 * 32 * 128 * 128 * 4 + 8 * 32 * 128 * 64 * 4 + 256
-    assert gdn.gdn_prefill_workspace_bytes(65535, 3, 2, 64, 64) == 7 * 2 * 64 * 64 * 4 * 2 + 256
+    assert gdn.gdn_prefill_workspace_bytes(65535, 3, 2, 64, 64) == 7 * 2 * 64 * 64 * 4 * 2 + 256 + 256
     monkeypatch.setenv("GDN_PREFILL_SEGMENT", "100")  # rounded up to 128
     assert gdn.gdn_prefill_workspace_bytes(1000, 1, 1, 64, 64) == 7 * 64 * 64 * 4 * 2 + 256
     monkeypatch.setenv("GDN_PREFILL_SEGMENT", "0")

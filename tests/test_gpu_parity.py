@@ -113,6 +113,24 @@ def test_write_then_read_on_gpu():
     assert_close("o vs v", np64(o), np64(x.v), 1e-4)
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_longest_first_order_many_units(monkeypatch, dtype, d):
+    # 90 sequences of 0 .. 600 tokens x 3 heads: 270 (sequence, head) units, more
+    # than the 256 compute units, so the pass over whole sequences takes them
+    # longest first through an order table in the workspace.  Every unit
+    # against the fp64 oracle, initial and final states included (each
+    # workgroup must still read and write its own unit's states).
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", "0")
+    rng = np.random.default_rng(31)
+    lengths = [int(v) for v in rng.integers(0, 601, 90)]
+    lengths[3] = lengths[50] = 0
+    lengths[89] = 1
+    H = 3
+    assert gdn.gdn_prefill_workspace_bytes(sum(lengths), len(lengths), H, d, d) == 512  # int32 [90], rounded
+    assert gdn.gdn_prefill_workspace_bytes(sum(lengths[:85]), 85, H, d, d) == 0  # 255 units: no table
+    _prefill_case(lengths, H, d, d, dtype, seed=33)
+
+
 def test_split_prefill_equals_whole():
     x = inputs.make_prefill_inputs([300], 2, 128, 128, dtype=torch.bfloat16, init_state=True, seed=7)
     to_device(x)
