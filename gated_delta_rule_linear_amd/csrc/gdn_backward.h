@@ -51,9 +51,13 @@ int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H);
 //    segments and the segment table); at d_off, per segment slot and head (slot
 //    cu[n] / seg + n + j for segment j of sequence n, T_total / seg + num_seqs
 //    slots) the d_k x d_v fp32 state gradient D of the reverse fold.
+//  - Without the split, when (sequence, head) units outnumber the compute
+//    units and there is more than one sequence: at ord_off the int32 order of
+//    the sequences, longest first (launch_seq_order), which both sweeps follow.
 struct BackwardWorkspace {
     int64_t slots = 0;
-    size_t pre_off = 0, d_off = 0, bytes = 0;
+    size_t pre_off = 0, d_off = 0, ord_off = 0, bytes = 0;
+    bool ord = false;
 };
 inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_seqs, int32_t H, int32_t dk,
                                                    int32_t dv, bool bf16, int64_t seg) {
@@ -65,6 +69,10 @@ inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_
         w.slots = T_total / seg + num_seqs;
         w.d_off = w.pre_off + al(prefill_workspace_layout(T_total, num_seqs, H, dk, dv, seg, false).bytes);
         w.bytes = w.d_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
+    } else if (num_seqs > 1 && (int64_t)num_seqs * H > kComputeUnits) {
+        w.ord = true;
+        w.ord_off = w.bytes;
+        w.bytes += al((size_t)num_seqs * sizeof(int32_t));
     }
     return w;
 }

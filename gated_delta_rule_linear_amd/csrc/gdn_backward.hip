@@ -103,6 +103,9 @@ struct BArgs {
     const float* fM;
     const float* fN;
     float* wsD;
+    // without the split: workgroup b takes head b % H of sequence ord[b / H]
+    // (longest first), or of sequence b / H when ord is null
+    const int32_t* ord;
 };
 
 // What one workgroup of a sweep works on: head h of sequence n (tokens
@@ -117,8 +120,9 @@ __device__ __forceinline__ BUnit bwd_unit(const BArgs<TI>& a, int b) {
     BUnit u;
     const int H = a.H;
     if (a.seg == 0) {
-        u.n = b / H;
-        u.h = b - u.n * H;
+        const int nb = b / H;
+        u.h = b - nb * H;
+        u.n = a.ord ? a.ord[nb] : nb;
         u.tb = a.cu[u.n];
         u.te = a.cu[u.n + 1];
         u.j = u.slot = 0;
@@ -899,8 +903,17 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     a.nl = nullptr;
     a.fM = a.fN = nullptr;
     a.wsD = nullptr;
+    a.ord = nullptr;
     if (p.seg <= 0) {
         const unsigned blocks = (unsigned)((int64_t)p.num_seqs * p.H);
+        const BackwardWorkspace wl = backward_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.bf16, 0);
+        if (wl.ord) {
+            // longest sequences first, the same order in both sweeps
+            int32_t* ord = reinterpret_cast<int32_t*>(static_cast<char*>(p.workspace) + wl.ord_off);
+            const hipError_t e = launch_seq_order(p.cu_seqlens, p.num_seqs, 0, ord, s);
+            if (e != hipSuccess) return e;
+            a.ord = ord;
+        }
         hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -154,5 +154,9 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 // not used.
 hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
+// The unit order (see PrefillWorkspace): ord[0 .. num_seqs) receives the
+// sequence indices, longest first, lengths capped at cap tokens when cap > 0.
+hipError_t launch_seq_order(const int32_t* cu_seqlens, int32_t num_seqs, int64_t cap, int32_t* ord,
+                            hipStream_t stream);
 
 }  // namespace gdn

@@ -2091,9 +2091,7 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
     if (wl.ord) {
         // longest sequences first (for the pass over whole sequences, or over first segments)
         int32_t* ord = reinterpret_cast<int32_t*>(static_cast<char*>(p.workspace) + wl.ord_off);
-        hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.num_seqs,
-                           (int)std::min<int64_t>(p.seg, 0x7fffffff), ord);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_seq_order(p.cu_seqlens, p.num_seqs, p.seg, ord, s);
         if (e != hipSuccess) return e;
         a.ord = ord;
     }
@@ -2176,6 +2174,13 @@ hipError_t run_maps_t(const PrefillLaunch& p, hipStream_t s) {
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s) {
     if ((int64_t)p.num_seqs * p.H == 0) return hipSuccess;
     return p.bf16 ? run_t<bf16>(p, s) : run_t<float>(p, s);
+}
+
+hipError_t launch_seq_order(const int32_t* cu_seqlens, int32_t num_seqs, int64_t cap, int32_t* ord, hipStream_t s) {
+    if (num_seqs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, s, cu_seqlens, num_seqs,
+                       (int)std::min<int64_t>(std::max<int64_t>(cap, 0), 0x7fffffff), ord);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t s) {

@@ -233,11 +233,13 @@ def test_backward_workspace_bytes(lib):
 def _backward_ws(T, n, H, dk, dv, bf16, seg):
     # checkpoints, then with a time split of segment length seg the forward
     # pass's split workspace (M, N of the T // seg non-last segment slots, the
-    # segment table) and one d_k x d_v fp32 gradient per segment slot
+    # segment table) and one d_k x d_v fp32 gradient per segment slot; without
+    # it, the int32 order table [n] when more than one sequence gives more
+    # (sequence, head) units than the 256 compute units
     al = lambda x: (x + 255) // 256 * 256
     ck = al((T // 16 + n) * H * dk * dv * (2 if bf16 else 4))
     if seg == 0:
-        return ck
+        return ck + (al(n * 4) if n > 1 and n * H > 256 else 0)
     fs = T // seg
     pre = al(fs * H * dk * dk * 4) + al(fs * H * dk * dv * 4) + al((n + 1) * 4)
     return ck + al(pre) + al((T // seg + n) * H * dk * dv * 4)
@@ -252,6 +254,9 @@ def test_backward_workspace_bytes_split(lib, monkeypatch):
     assert f(1 << 20, 1, 16, 128, 128, 1) == _backward_ws(1 << 20, 1, 16, 128, 128, True, 32768)
     # enough units to fill the chip, or sequences too short for three segments: no split
     assert f(65536, 8, 32, 128, 128, 1) == _backward_ws(65536, 8, 32, 128, 128, True, 0)
+    assert f(65536, 9, 32, 128, 128, 1) == _backward_ws(65536, 9, 32, 128, 128, True, 0)
+    assert _backward_ws(65536, 9, 32, 128, 128, True, 0) == _backward_ws(65536, 8, 32, 128, 128, True, 0) \
+        + 32 * 128 * 128 * 2 + 256  # one more sequence's checkpoint slot per head, and the order table
     assert f(1024, 4, 32, 128, 128, 1) == _backward_ws(1024, 4, 32, 128, 128, True, 0)
     # forced length, rounded up to a multiple of 64; 0 turns the split off
     monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "200")

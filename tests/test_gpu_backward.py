@@ -59,6 +59,19 @@ def _case(lengths, H, dk, dv, dtype, gate="amin", init=True, final=True, seed=0,
     return x, d_o, dSf, got
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_longest_first_order_many_units(dtype, d):
+    # 90 sequences of 0 .. 300 tokens x 3 heads: 270 (sequence, head) units, more
+    # than the compute units, so both sweeps take the sequences longest first
+    # through an order table in the workspace; every gradient of every unit,
+    # the initial state's included, against the fp64 oracle
+    rng = np.random.default_rng(35)
+    lengths = [int(v) for v in rng.integers(0, 301, 90)]
+    lengths[7] = lengths[60] = 0
+    lengths[88] = 1
+    _case(lengths, 3, d, d, dtype, seed=37)
+
+
 def test_small_fp32():
     # one 256-token sequence, 2 heads, d = 64, fp32, zero initial state
     _case([256], 2, 64, 64, torch.float32, init=False)
