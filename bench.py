@@ -46,8 +46,11 @@ sequences of 512..16,384 tokens with random initial states (varlen64), one
 2^20-token sequence x 16 heads (long_1m), and a skewed batch of 63 sequences
 of 1,024 tokens plus one of 262,144 (skewed64, with and without the bound on
 the lengths of gdn_prefill_maxlen), each with its roofline, sampled parity and
-a host-oracle baseline on a stated sample.  --no-workloads skips them.  "device" gives the GPU's compute-unit count and clock as the runtime
-reports them, beside the published peaks the fractions use.
+a host-oracle baseline on a stated sample, after --workload-warmup (10)
+untimed calls; and gdn_prefill_backward on varlen64 (varlen64_backward) with
+its roofline and sampled parity.  --no-workloads skips them.  "device" gives
+the GPU's compute-unit count and clock as the runtime reports them, beside
+the published peaks the fractions use.
 """
 
 from __future__ import annotations
@@ -337,6 +340,47 @@ def prefill_leg(gdn, name, x, steps, warmup, stream, cpu: bool, cpu_seqs: int, c
     return leg
 
 
+def backward_leg(gdn, name, x, steps, warmup, stream):
+    """Time gdn_prefill_backward over the workload x (every gradient written, the initial
+    state's included; dL/do ~ N(0,1), dL/d(final state) ~ 0.02 N(0,1)); sampled parity of
+    sequence 0, head 0 (its whole length) against the fp64 oracle."""
+    import oracle
+    from gated_delta_rule_linear_amd import inputs
+
+    T, H, dk = x.q.shape
+    dv = x.v.shape[2]
+    n = x.num_seqs
+    d_o, dSf = inputs.make_cotangents(T, n, H, dk, dv, dtype=x.q.dtype, seed=1, device=x.q.device)
+    wsb = gdn.gdn_prefill_backward_workspace_bytes(T, n, H, dk, dv, x.q.dtype)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=x.q.device)
+    out = []
+
+    def step():
+        out[:] = gdn.gdn_prefill_backward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, d_o,
+                                          initial_state=x.initial_state, d_final_state=dSf, workspace=ws,
+                                          stream=stream)
+
+    ms = time_loop(step, steps, warmup, stream)
+    init = x.initial_state is not None
+    bbytes = backward_bytes(T, H, dk, dv, n, init_state=init)
+    gbs = bbytes / (ms / 1e3) / 1e9
+    cu = x.cu_seqlens.to("cpu", torch.int64).numpy()
+    L0 = int(cu[1])
+    su = lambda t: t[:L0, :1].to("cpu", torch.float64).numpy()
+    ref = oracle.backward(su(x.q), su(x.k), su(x.v), su(x.g), su(x.beta), np.array([0, L0], np.int32), su(d_o),
+                          initial_state=None if not init else x.initial_state[:1, :1].to("cpu", torch.float64).numpy(),
+                          d_final_state=dSf[:1, :1].to("cpu", torch.float64).numpy())
+    par = max(oracle.rel_err(su(gt), ref[nm]) for gt, nm in zip(out[:5], ("dq", "dk", "dv", "dg", "dbeta")))
+    leg = {"workload": name + " backward", "num_seqs": n, "T": T, "H": H, "d_k": dk, "d_v": dv,
+           "initial_state": init, "workspace_bytes": wsb, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+           "tokens_per_s": T / (ms / 1e3),
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": bbytes},
+           "parity_max_rel_err_seq0_head0": par, "parity_tokens": L0}
+    del out[:], ws, d_o, dSf
+    return leg
+
+
 def cpu_backward_baseline(x, d_o, dSf, tokens: int, heads: int):
     """The oracle's reverse-mode recurrence (fp64, OpenMP over heads) on the host for the first
     `tokens` tokens of the first `heads` heads of sequence 0."""
@@ -372,6 +416,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV", help="summarise rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--workload-steps", type=int, default=10)
+    ap.add_argument("--workload-warmup", type=int, default=10)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
@@ -527,12 +572,16 @@ def main():
         # host sample: the first sequences up to ~65,536 tokens (whole sequences, their initial states)
         cuv = xv.cu_seqlens.to("cpu", torch.int64).numpy()
         nv = max(1, int(np.searchsorted(cuv, 65536, side="right")) - 1)
-        workloads["varlen64"] = prefill_leg(gdn, "varlen64", xv, args.workload_steps, 3, stream, not args.no_cpu,
+        ww = args.workload_warmup
+        workloads["varlen64"] = prefill_leg(gdn, "varlen64", xv, args.workload_steps, ww, stream, not args.no_cpu,
                                             nv, f"the first {nv} of 64 sequences")
+        if not args.no_backward:
+            workloads["varlen64_backward"] = backward_leg(gdn, "varlen64", xv, max(3, args.workload_steps // 2),
+                                                          3, stream)
         del xv
         torch.cuda.empty_cache()
         xl = inputs.make_workload("long_1m", seed=0, device=dev)
-        workloads["long_1m"] = prefill_leg(gdn, "long_1m", xl, max(3, args.workload_steps // 2), 2, stream,
+        workloads["long_1m"] = prefill_leg(gdn, "long_1m", xl, args.workload_steps, ww, stream,
                                            not args.no_cpu, 1, "the first 131072 of 1048576 tokens",
                                            cpu_x=prefix_view(xl, 131072))
         del xl
@@ -541,8 +590,8 @@ def main():
         # gdn_prefill plans from the mean length, gdn_prefill_maxlen from the bound on the lengths
         lens = [1024] * 63 + [262144]
         xs = inputs.make_prefill_inputs(lens, 32, d, d, dtype=torch.bfloat16, seed=5, device=dev)
-        plain = prefill_leg(gdn, "skewed64", xs, args.workload_steps, 3, stream, False, 0, "")
-        hinted = prefill_leg(gdn, "skewed64", xs, args.workload_steps, 3, stream, not args.no_cpu, 63,
+        plain = prefill_leg(gdn, "skewed64", xs, args.workload_steps, ww, stream, False, 0, "")
+        hinted = prefill_leg(gdn, "skewed64", xs, args.workload_steps, ww, stream, not args.no_cpu, 63,
                              "the 63 sequences of 1,024 tokens", max_seqlen=max(lens))
         hinted["without_hint_ms_per_step"] = plain["ms_per_step"]
         hinted["without_hint_roofline_frac"] = plain["roofline"]["frac"]
