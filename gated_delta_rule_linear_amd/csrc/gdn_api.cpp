@@ -133,7 +133,24 @@ int64_t plan_prefill_segment(int64_t T_total, int32_t num_seqs, int32_t H, int32
             best_seg = ls;
         }
     }
-    return best < 0.95 * whole ? best_seg : 0;
+    if (best < 0.95 * whole) return best_seg;
+    // No split for sequences of the mean length.  With more units than compute
+    // units the lengths may still be skewed, and one sequence much longer than
+    // the rest would then be the critical path of the call.  Split, whatever
+    // the lengths turn out to be, every sequence longer than
+    //   Ls = T_total / (CUS / H + 1)
+    // tokens: a sequence that long has a chain at least the whole batch's work
+    // per compute unit, and the later segments of even one sequence of T_total
+    // tokens then fill one round of workgroups.  A batch without such a
+    // sequence runs as unsplit (its table, empty map and fold passes and an
+    // empty pass over later segments cost some tens of microseconds, so the
+    // segment must be long enough for that not to matter).
+    if (num_seqs > 1 && units > K::CUS) {
+        const int64_t pmax = (int64_t)(K::CUS / H) + 1;
+        const int64_t ls = ((T_total + pmax - 1) / pmax + 63) / 64 * 64;
+        if (pmax >= 3 && ls >= kSpeculativeMinSegment) return ls;
+    }
+    return 0;
 }
 
 }  // namespace gdn

@@ -40,13 +40,19 @@ struct PrefillLaunch {
 
 // Compute units of the device the plans are made for (MI355X).
 constexpr int64_t kComputeUnits = 256;
+// Shortest segment of the length-agnostic split of a batch that the
+// mean-length plan does not split (a segment of 512 chunks of 32 tokens).
+constexpr int64_t kSpeculativeMinSegment = 16384;
 
 // Workspace of the prefill.
 // Time split, for segments of `seg` tokens: a sequence's non-last segments
 // hold exactly seg tokens, so there are at most T_total / seg of them over the
 // batch; each (non-last segment, head) owns an M slot (d_k x d_k fp32) and an
 // N slot (d_k x d_v fp32).  nl is the int32 table of non-last segment counts
-// [num_seqs + 1].
+// [num_seqs + 1]; spl lists the sequences that have more than one segment (a
+// sequence longer than seg tokens: at most min(num_seqs, T_total / (seg + 1))
+// of them, the `splits` entries of the list, unused ones -1), so that the fold
+// runs one workgroup per split (sequence, head) only.
 // Unit order: with more than one sequence, the workgroups of a pass over
 // whole sequences (or over every sequence's first segment) take the sequences
 // longest first, from the int32 table ord [num_seqs] (a permutation of the
@@ -56,8 +62,8 @@ constexpr int64_t kComputeUnits = 256;
 // unit starts at once and the order changes nothing.  (with_order = false: the
 // maps and fold alone, which need no order.)
 struct PrefillWorkspace {
-    int64_t slots = 0;
-    size_t m_off = 0, n_off = 0, nl_off = 0, ord_off = 0, bytes = 0;
+    int64_t slots = 0, splits = 0;
+    size_t m_off = 0, n_off = 0, nl_off = 0, spl_off = 0, ord_off = 0, bytes = 0;
     bool ord = false;
 };
 inline PrefillWorkspace prefill_workspace_layout(int64_t T_total, int32_t num_seqs, int32_t H, int32_t dk,
@@ -69,7 +75,9 @@ inline PrefillWorkspace prefill_workspace_layout(int64_t T_total, int32_t num_se
         w.m_off = 0;
         w.n_off = al((size_t)w.slots * H * dk * dk * sizeof(float));
         w.nl_off = w.n_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
-        w.bytes = w.nl_off + al(((size_t)num_seqs + 1) * sizeof(int32_t));
+        w.splits = std::min<int64_t>(num_seqs, T_total / (seg + 1));
+        w.spl_off = w.nl_off + al(((size_t)num_seqs + 1) * sizeof(int32_t));
+        w.bytes = w.spl_off + al((size_t)std::max<int64_t>(w.splits, 1) * sizeof(int32_t));
     }
     if (with_order && num_seqs > 1 && (seg > 0 || (int64_t)num_seqs * H > kComputeUnits)) {
         w.ord = true;

@@ -127,12 +127,14 @@ struct Args {
     int num_seqs;
     int seg;
     const int32_t* nl;
+    const int32_t* spl;  // the sequences with more than one segment (see seg_table_kernel)
     float* wsM;
     float* wsN;
     int m_blocks;       // map launches: blocks [0, m_blocks) compute M, the rest N
     int map_from;       // map launches: first segment of a sequence that gets a map (0 or 1)
-    int phase;          // split output launches: 0 every segment; 1 segment 0 only (one workgroup per
-                        // (sequence, head), its end state to slot nl[n] when more segments follow); 2 the rest
+    int phase;          // split output launches: 1 segment 0 only (one workgroup per (sequence, head),
+                        // its end state to slot nl[n] when more segments follow); 2 the later segments (one
+                        // workgroup per (non-last segment, head): the segment after it)
     int legacy;         // bf16: use the single-role kernel instead of the warp-specialised one
     // gate != GATE_LOG: g is not read; the log-decay comes from the bf16 logits
     // z in the same layout (warp-specialised kernel only)
@@ -422,24 +424,21 @@ __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
         u.s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
         if (a.nl[n + 1] > a.nl[n]) u.sf = a.wsN + ((size_t)a.nl[n] * H + u.h) * DK * DV;
         else u.sf = a.Sf ? a.Sf + unit * DK * DV : nullptr;
-    } else if (a.seg > 0) {
-        const int q = b / H;
-        u.h = b - q * H;
-        if (q >= a.nl[a.num_seqs] + a.num_seqs) {
+    } else if (a.seg > 0) {  // phase 2
+        // non-last segment k of the batch (sequence n, its segment k - nl[n]) is
+        // followed by segment j = k - nl[n] + 1, which this workgroup runs
+        const int k = b / H;
+        u.h = b - k * H;
+        if (k >= a.nl[a.num_seqs]) {
             u.valid = false;
             return u;
         }
-        const int n = seq_of(a.nl, a.num_seqs, q, 1);
-        const int j = q - (a.nl[n] + n), last = a.nl[n + 1] - a.nl[n];
-        if (a.phase == 2 && j == 0) {
-            u.valid = false;
-            return u;
-        }
+        const int n = seq_of(a.nl, a.num_seqs, k, 0);
+        const int j = k - a.nl[n] + 1, last = a.nl[n + 1] - a.nl[n];
         const size_t unit = (size_t)n * H + u.h;
         u.tb = a.cu[n] + (int64_t)j * a.seg;
         u.te = u.tb + a.seg < a.cu[n + 1] ? u.tb + a.seg : a.cu[n + 1];
-        if (j == 0) u.s0 = a.S0 ? a.S0 + unit * DK * DV : nullptr;
-        else u.s0 = a.wsN + ((size_t)(a.nl[n] + j - 1) * H + u.h) * DK * DV;
+        u.s0 = a.wsN + ((size_t)(k) * H + u.h) * DK * DV;
         if (j == last && a.Sf) u.sf = a.Sf + unit * DK * DV;
     } else {
         const int nb = b / H;
@@ -1756,12 +1755,16 @@ __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(
 
 // nl[0] = 0, nl[n + 1] = nl[n] + (number of non-last segments of sequence n):
 // a sequence of len > 0 tokens has ceil(len / seg) segments, an empty one has
-// one (of zero tokens).  One workgroup, a block-wide scan per 256 sequences.
+// one (of zero tokens).  spl[0 .. splits): the sequences with more than one
+// segment in increasing order, then -1 (a list longer than `splits`, which
+// well-formed lengths cannot give, is cut there).  One workgroup, block-wide
+// scans per 256 sequences.
 __global__ __launch_bounds__(256) void seg_table_kernel(const int32_t* __restrict__ cu, int num_seqs, int seg,
-                                                        int32_t* __restrict__ nl) {
-    __shared__ int part[256];
+                                                        int32_t* __restrict__ nl, int32_t* __restrict__ spl,
+                                                        int splits) {
+    __shared__ int part[256], pf[256];
     const int t = threadIdx.x;
-    int carry = 0;
+    int carry = 0, carryf = 0;
     if (t == 0) nl[0] = 0;
     for (int base = 0; base < num_seqs; base += 256) {
         const int n = base + t;
@@ -1771,17 +1774,25 @@ __global__ __launch_bounds__(256) void seg_table_kernel(const int32_t* __restric
             c = len > 0 ? (len - 1) / seg : 0;
         }
         part[t] = c;
+        pf[t] = c > 0;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
-            const int x = t >= off ? part[t - off] : 0;
+            const int x = t >= off ? part[t - off] : 0, y = t >= off ? pf[t - off] : 0;
             __syncthreads();
             part[t] += x;
+            pf[t] += y;
             __syncthreads();
         }
-        if (n < num_seqs) nl[n + 1] = carry + part[t];
+        if (n < num_seqs) {
+            nl[n + 1] = carry + part[t];
+            const int pos = carryf + pf[t] - 1;
+            if (c > 0 && pos < splits) spl[pos] = n;
+        }
         carry += part[255];
+        carryf += pf[255];
         __syncthreads();
     }
+    for (int k = carryf + t; k < splits; k += 256) spl[k] = -1;
 }
 
 // Order of the sequences for a pass with one workgroup per (sequence, head):
@@ -1866,23 +1877,28 @@ __global__ __launch_bounds__(1024) void seq_order_kernel(const int32_t* __restri
 // S_start(1) already in slot N_0 (segment 0's own end state) when first = 1;
 // fp32 matrix-core steps (fold_columns), one wave per 16-row tile.
 template <int DK, int DV>
-__global__ __launch_bounds__(64 * (DK / 16)) void seg_fold_kernel(const int32_t* __restrict__ nl, int H,
+__global__ __launch_bounds__(64 * (DK / 16)) void seg_fold_kernel(const int32_t* __restrict__ nl,
+                                                                  const int32_t* __restrict__ spl, int H,
                                                                   const float* __restrict__ S0,
                                                                   const float* __restrict__ wsM,
                                                                   float* __restrict__ wsN, int first) {
+    // one workgroup per (split sequence, head, 16 columns): workgroup slot
+    // `us` = k H + h is head h of the k-th sequence in spl
     constexpr int NCB = DV / 16;
-    int bid = blockIdx.x, cb, unit;
+    int bid = blockIdx.x, cb, us;
     if ((gridDim.x / NCB) % 8 == 0) {
         // workgroups go to the eight XCDs in turn: keep the NCB column blocks
         // of a unit on one XCD, so that its L2 fetches each map once
         const int x = bid % 8, q = bid / 8;
         cb = q % NCB;
-        unit = (q / NCB) * 8 + x;
+        us = (q / NCB) * 8 + x;
     } else {
         cb = bid % NCB;
-        unit = bid / NCB;
+        us = bid / NCB;
     }
-    const int n = unit / H, h = unit - n * H;
+    const int kk = us / H, h = us - kk * H, n = spl[kk];
+    if (n < 0) return;
+    const int unit = n * H + h;
     const int k0 = nl[n], cnt = nl[n + 1] - k0;
     if (cnt <= first) return;
     const float* x0 = first ? wsN + ((size_t)k0 * H + h) * DK * DV : S0 ? S0 + (size_t)unit * DK * DV : nullptr;
@@ -1934,6 +1950,7 @@ Args<TI> make_args(const PrefillLaunch& p) {
     a.num_seqs = p.num_seqs;
     a.seg = 0;
     a.nl = nullptr;
+    a.spl = nullptr;
     a.wsM = a.wsN = nullptr;
     a.m_blocks = 0;
     a.map_from = 0;
@@ -1955,52 +1972,64 @@ hipError_t run_table(const PrefillLaunch& p, Args<TI>& a, hipStream_t s) {
     a.nl = reinterpret_cast<int32_t*>(w + ws.nl_off);
     a.wsM = reinterpret_cast<float*>(w + ws.m_off);
     a.wsN = reinterpret_cast<float*>(w + ws.n_off);
+    a.spl = reinterpret_cast<int32_t*>(w + ws.spl_off);
     hipLaunchKernelGGL(seg_table_kernel, dim3(1), dim3(256), 0, s, p.cu_seqlens, p.num_seqs, p.seg,
-                       const_cast<int32_t*>(a.nl));
+                       const_cast<int32_t*>(a.nl), const_cast<int32_t*>(a.spl), (int)ws.splits);
     return hipGetLastError();
 }
 
-// Time split: the maps of the non-last segments from segment a.map_from on,
-// then the fold from there (after run_table).
+// Time split: the maps of the non-last segments from segment a.map_from on
+// (after run_table).
 template <typename TI, int DK, int DV>
-hipError_t run_maps_fold(const PrefillLaunch& p, Args<TI>& a, hipStream_t s, hipEvent_t before_fold) {
-    const int64_t units = (int64_t)p.num_seqs * p.H;
+hipError_t run_map_pass(const PrefillLaunch& p, Args<TI>& a, hipStream_t s) {
     const PrefillWorkspace ws = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
-    hipError_t e = hipSuccess;
     const int64_t map_blocks = ws.slots * p.H;
-    if (map_blocks > 0) {
-        // M and N in one workgroup or in two: decided for the number of
-        // transitions that sequences of the mean length would have, or with a
-        // bound on the lengths the long sequences of the most skewed batch it
-        // allows (the grid is sized for the bound; surplus workgroups exit at once)
-        int64_t len = (p.T_total + p.num_seqs - 1) / p.num_seqs, nlen = p.num_seqs;
-        if (p.max_seqlen > len) {
-            len = p.max_seqlen;
-            nlen = std::max<int64_t>(1, std::min<int64_t>(p.num_seqs, p.T_total / p.max_seqlen));
-        }
-        const double maps = (double)nlen * p.H * (len > 0 ? std::max<int64_t>(0, (len - 1) / p.seg - a.map_from) : 0);
-        bool both = false;
-        SplitCost::maps_pass(maps, p.seg / 64.0, DK == DV && sizeof(TI) == 2, &both);
-        if constexpr (DK == DV && sizeof(TI) == 2) {
-            if (both) {
-                e = launch_seq<TI, DK, DV, true, 2>(a, map_blocks, s);
-            } else {
-                a.m_blocks = (int)map_blocks;
-                e = launch_seq<TI, DK, DV, true>(a, 2 * map_blocks, s);
-            }
+    if (map_blocks <= 0) return hipSuccess;
+    // M and N in one workgroup or in two: decided for the number of transitions
+    // that sequences of the mean length would have; with a bound on the lengths,
+    // for the long sequences of the most skewed batch it allows; and when a
+    // sequence of the mean length is not split at all (the length-agnostic
+    // plan), for one sequence of all the tokens.  (The grid is sized for the
+    // bound; surplus workgroups exit at once.)
+    int64_t len = (p.T_total + p.num_seqs - 1) / p.num_seqs, nlen = p.num_seqs;
+    if (p.max_seqlen > len) {
+        len = p.max_seqlen;
+        nlen = std::max<int64_t>(1, std::min<int64_t>(p.num_seqs, p.T_total / p.max_seqlen));
+    } else if (len <= p.seg) {
+        len = p.T_total;
+        nlen = 1;
+    }
+    const double maps = (double)nlen * p.H * (len > 0 ? std::max<int64_t>(0, (len - 1) / p.seg - a.map_from) : 0);
+    bool both = false;
+    SplitCost::maps_pass(maps, p.seg / 64.0, DK == DV && sizeof(TI) == 2, &both);
+    hipError_t e;
+    if constexpr (DK == DV && sizeof(TI) == 2) {
+        if (both) {
+            e = launch_seq<TI, DK, DV, true, 2>(a, map_blocks, s);
         } else {
             a.m_blocks = (int)map_blocks;
-            e = launch_seq<TI, DK, DK, true>(a, map_blocks, s);
-            a.m_blocks = 0;
-            if (e == hipSuccess) e = launch_seq<TI, DK, DV, true>(a, map_blocks, s);
+            e = launch_seq<TI, DK, DV, true>(a, 2 * map_blocks, s);
         }
-        if (e != hipSuccess) return e;
-        if (before_fold && (e = hipStreamWaitEvent(s, before_fold, 0)) != hipSuccess) return e;
-        hipLaunchKernelGGL((seg_fold_kernel<DK, DV>), dim3((unsigned)(units * (DV / 16))), dim3(64 * (DK / 16)), 0, s,
-                           a.nl, p.H, p.initial_state, a.wsM, a.wsN, a.map_from);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else if (before_fold) {
-        e = hipStreamWaitEvent(s, before_fold, 0);
+    } else {
+        a.m_blocks = (int)map_blocks;
+        e = launch_seq<TI, DK, DK, true>(a, map_blocks, s);
+        a.m_blocks = 0;
+        if (e == hipSuccess) e = launch_seq<TI, DK, DV, true>(a, map_blocks, s);
+    }
+    return e;
+}
+
+// Time split: the fold from segment a.map_from on, after the maps (and, when
+// given, after the event before_fold).
+template <typename TI, int DK, int DV>
+hipError_t run_fold_pass(const PrefillLaunch& p, Args<TI>& a, hipStream_t s, hipEvent_t before_fold) {
+    const PrefillWorkspace ws = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg);
+    hipError_t e = hipSuccess;
+    if (before_fold && (e = hipStreamWaitEvent(s, before_fold, 0)) != hipSuccess) return e;
+    if (ws.slots > 0 && ws.splits > 0) {
+        hipLaunchKernelGGL((seg_fold_kernel<DK, DV>), dim3((unsigned)(ws.splits * p.H * (DV / 16))),
+                           dim3(64 * (DK / 16)), 0, s, a.nl, a.spl, p.H, p.initial_state, a.wsM, a.wsN, a.map_from);
+        e = hipGetLastError();
     }
     return e;
 }
@@ -2113,18 +2142,22 @@ hipError_t run(const PrefillLaunch& p, hipStream_t s) {
         hipError_t r = run_table<TI, DK, DV>(p, a, s);
         if (r != hipSuccess) return r;
         if ((r = hipEventRecord(lane->fork, s)) != hipSuccess) return r;
+        // the maps are enqueued first, so that their long chains start as soon
+        // as the pass over first segments, whose units may be many and short,
+        // begins beside them
+        a.map_from = 1;
+        if ((r = run_map_pass<TI, DK, DV>(p, a, s)) != hipSuccess) return r;
         if ((r = hipStreamWaitEvent(s2, lane->fork, 0)) != hipSuccess) return r;
         forked = true;
         a.phase = 1;
         if ((r = launch_seq<TI, DK, DV, false>(a, units, s2)) != hipSuccess) return r;
         if ((r = hipEventRecord(lane->join, s2)) != hipSuccess) return r;
-        a.map_from = 1;
-        r = run_maps_fold<TI, DK, DV>(p, a, s, lane->join);
+        r = run_fold_pass<TI, DK, DV>(p, a, s, lane->join);
         joined = r == hipSuccess;  // the fold (or its absence) waited for the join event
         if (r != hipSuccess) return r;
         a.phase = 2;
         const int64_t slots = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.seg).slots;
-        return launch_seq<TI, DK, DV, false>(a, ((int64_t)p.num_seqs + slots) * p.H, s);
+        return launch_seq<TI, DK, DV, false>(a, slots * p.H, s);
     };
     e = body();
     if (forked && !joined) {
@@ -2156,8 +2189,9 @@ hipError_t run_t(const PrefillLaunch& p, hipStream_t s) {
 template <typename TI, int DK, int DV>
 hipError_t run_maps(const PrefillLaunch& p, hipStream_t s) {
     Args<TI> a = make_args<TI>(p);
-    const hipError_t e = run_table<TI, DK, DV>(p, a, s);
-    return e != hipSuccess ? e : run_maps_fold<TI, DK, DV>(p, a, s, nullptr);
+    hipError_t e = run_table<TI, DK, DV>(p, a, s);
+    if (e == hipSuccess) e = run_map_pass<TI, DK, DV>(p, a, s);
+    return e != hipSuccess ? e : run_fold_pass<TI, DK, DV>(p, a, s, nullptr);
 }
 
 template <typename TI>

@@ -135,7 +135,11 @@ size_t gdn_prefill_workspace_bytes(int64_t T_total, int32_t num_seqs, int32_t H,
  *
  * Method: each sequence is cut into chunks (32 tokens with GDN_BF16, 64 with
  * GDN_F32), long sequences also into segments run in parallel and joined
- * through the affine map of the state.  A split call runs the first segment's
+ * through the affine map of the state.  The segment length is planned from the
+ * arguments alone: for sequences of the mean length, and, when those need no
+ * split but (sequence, head) units outnumber the 256 compute units, so that
+ * any sequence longer than T_total / (256 / H + 1) tokens is split (a
+ * balanced batch then has none, and runs as unsplit).  A split call runs the first segment's
  * output pass on a side stream, forked from and joined back into `stream` by
  * events (also when a later step of the call fails), so the call stays
  * ordered on `stream` and can be captured into a graph.  The library creates

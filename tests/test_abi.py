@@ -95,6 +95,32 @@ def test_state_alloc_overflowing_size_is_oom_without_a_device_call(lib):
 ORDER_TABLE_64 = 256  # int32 [64], rounded up to 256 bytes
 
 
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+def _prefill_ws(T, n, H, dk, dv, seg):
+    # the layout of gdn_prefill's workspace for segments of seg tokens (0: no
+    # split): M and N slots of the T // seg non-last segments, the int32 table
+    # [n + 1], the list of split sequences (at most min(n, T // (seg + 1))),
+    # then the int32 order table [n] when it is kept
+    b = 0
+    if seg > 0:
+        fs = T // seg
+        b = _al(fs * H * dk * dk * 4) + _al(fs * H * dk * dv * 4) + _al((n + 1) * 4) + \
+            _al(max(min(n, T // (seg + 1)), 1) * 4)
+    if n > 1 and (seg > 0 or n * H > 256):
+        b += _al(n * 4)
+    return b
+
+
+def _agnostic_seg(T, H):
+    # the length-agnostic split of a batch with more units than compute units:
+    # segments of T / (256 / H + 1) tokens, rounded up to a multiple of 64
+    pmax = 256 // H + 1
+    return (-(-T // pmax) + 63) // 64 * 64
+
+
 def test_unit_order_table(monkeypatch):
     # the order table (int32 [num_seqs], 256-byte rounded) is kept when the split
     # runs with more than one sequence, or when (sequence, head) units outnumber
@@ -120,9 +146,16 @@ def test_time_split_plan(monkeypatch):
     monkeypatch.delenv("GDN_PREFILL_SEGMENT", raising=False)
     # one 65,536-token sequence x 32 heads: 32 workgroups would leave most CUs idle -> split
     assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128) > 0
-    # 64 sequences of ~8K tokens x 32 heads: 2048 workgroups already -> no split,
-    # only the int32 order table [64] (more units than compute units)
-    assert gdn.gdn_prefill_workspace_bytes(540000, 64, 32, 128, 128) == ORDER_TABLE_64
+    # 64 sequences of ~8K tokens x 32 heads: 2048 workgroups already, so sequences of the
+    # mean length need no split; the length-agnostic plan splits any sequence longer than
+    # 540000 / 9 tokens (none, if the lengths are near the mean)
+    assert _agnostic_seg(540000, 32) == 60032
+    assert gdn.gdn_prefill_workspace_bytes(540000, 64, 32, 128, 128) == _prefill_ws(540000, 64, 32, 128, 128, 60032)
+    # ... but not when the segment would be shorter than 16,384 tokens
+    assert gdn.gdn_prefill_workspace_bytes(100000, 64, 32, 128, 128) == ORDER_TABLE_64
+    # nor with more than 128 heads (fewer than three segments), nor for one sequence
+    assert gdn.gdn_prefill_workspace_bytes(10 ** 7, 4, 256, 64, 64) == _al(4 * 4)
+    assert gdn.gdn_prefill_workspace_bytes(540000, 1, 512, 64, 64) == 0
     # short sequences are never split
     assert gdn.gdn_prefill_workspace_bytes(256, 1, 2, 64, 64) == 0
     assert gdn.gdn_prefill_workspace_bytes(0, 3, 2, 64, 64) == 0
@@ -133,7 +166,7 @@ def test_time_split_plan_with_a_bound_on_the_lengths(monkeypatch):
     # one 262,144-token sequence among 63 of 1,024 tokens, 32 heads: 2,048 units, so the
     # mean-length plan does not split; the bound on the lengths cuts the long sequence
     T, n, H = 262144 + 63 * 1024, 64, 32
-    assert gdn.gdn_prefill_workspace_bytes(T, n, H, 128, 128) == ORDER_TABLE_64
+    assert gdn.gdn_prefill_workspace_bytes(T, n, H, 128, 128) == _prefill_ws(T, n, H, 128, 128, _agnostic_seg(T, H))
     assert gdn.gdn_prefill_workspace_bytes_maxlen(T, n, 262144, H, 128, 128) > ORDER_TABLE_64
     # a bound of 0 is gdn_prefill's plan; balanced batches plan as without a bound
     for args in ((65536, 1, 32), (32768, 4, 32), (540000, 64, 32), (T, n, H)):
@@ -158,10 +191,13 @@ def test_time_split_workspace_layout(monkeypatch):
     # fp32, each area rounded up to 256 bytes, then the int32 table [n + 1] and,
     # with more than one sequence, the int32 order table [n]
     monkeypatch.setenv("GDN_PREFILL_SEGMENT", "8192")
-    assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 64) == 8 * 32 * 128 * 128 * 4 + 8 * 32 * 128 * 64 * 4 + 256
-    assert gdn.gdn_prefill_workspace_bytes(65535, 3, 2, 64, 64) == 7 * 2 * 64 * 64 * 4 * 2 + 256 + 256
+    assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 64) == \
+        8 * 32 * 128 * 128 * 4 + 8 * 32 * 128 * 64 * 4 + 256 + 256
+    assert gdn.gdn_prefill_workspace_bytes(65535, 3, 2, 64, 64) == 7 * 2 * 64 * 64 * 4 * 2 + 256 + 256 + 256
+    for args in ((65536, 1, 32, 128, 64), (65535, 3, 2, 64, 64), (10 ** 6, 300, 1, 64, 64)):
+        assert gdn.gdn_prefill_workspace_bytes(*args) == _prefill_ws(*args, 8192)
     monkeypatch.setenv("GDN_PREFILL_SEGMENT", "100")  # rounded up to 128
-    assert gdn.gdn_prefill_workspace_bytes(1000, 1, 1, 64, 64) == 7 * 64 * 64 * 4 * 2 + 256
+    assert gdn.gdn_prefill_workspace_bytes(1000, 1, 1, 64, 64) == 7 * 64 * 64 * 4 * 2 + 256 + 256
     monkeypatch.setenv("GDN_PREFILL_SEGMENT", "0")
     assert gdn.gdn_prefill_workspace_bytes(65536, 1, 32, 128, 128) == 0
 
@@ -233,7 +269,7 @@ def test_backward_workspace_bytes(lib):
 def _backward_ws(T, n, H, dk, dv, bf16, seg):
     # checkpoints, then with a time split of segment length seg the forward
     # pass's split workspace (M, N of the T // seg non-last segment slots, the
-    # segment table) and one d_k x d_v fp32 gradient per segment slot; without
+    # segment table, the split list) and one d_k x d_v fp32 gradient per segment slot; without
     # it, the int32 order table [n] when more than one sequence gives more
     # (sequence, head) units than the 256 compute units
     al = lambda x: (x + 255) // 256 * 256
@@ -241,7 +277,7 @@ def _backward_ws(T, n, H, dk, dv, bf16, seg):
     if seg == 0:
         return ck + (al(n * 4) if n > 1 and n * H > 256 else 0)
     fs = T // seg
-    pre = al(fs * H * dk * dk * 4) + al(fs * H * dk * dv * 4) + al((n + 1) * 4)
+    pre = al(fs * H * dk * dk * 4) + al(fs * H * dk * dv * 4) + al((n + 1) * 4) + al(max(min(n, T // (seg + 1)), 1) * 4)
     return ck + al(pre) + al((T // seg + n) * H * dk * dv * 4)
 
 

@@ -4,7 +4,9 @@ sampled (sequence, head) units in full — every output token and the final
 state of each sampled unit — and the library's result for those units is
 compared element by element.  The 2^20-token case is checked on three heads
 in full against the fp64 oracle, and on every head against the unsplit
-kernel.  The decode workload runs all 128 steps over every (sequence, head)
+kernel; a skewed batch given without a bound on its lengths, on sampled
+units in full and on the long sequence against the bounded plan.  The decode
+workload runs all 128 steps over every (sequence, head)
 and is compared with the fp64 oracle at every step."""
 
 import os
@@ -92,6 +94,31 @@ def test_varlen64():
     L = x.lengths
     longest, shortest = int(np.argmax(L)), int(np.argmin(L))
     _check_units(x, o, S, [(longest, 3), (shortest, 30), (17, 16), (63, 0)])
+
+
+@pytest.mark.timeout(600)
+def test_skewed64_without_a_bound():
+    # 63 sequences of 1,024 tokens and, last, one of 262,144, 32 heads, random initial
+    # states: 2,048 units, so sequences of the mean length would need no split, and no
+    # bound on the lengths is given; the length-agnostic plan cuts the long sequence
+    # into segments of 326,656 / 9 tokens (rounded to 64).  Two heads of the long
+    # sequence and two short units in full against the fp64 oracle; the long sequence
+    # against gdn_prefill_maxlen's plan on every head.
+    log("skewed64 without a bound: 63 x 1024 + 1 x 262144 tokens, 32 heads")
+    lens = [1024] * 63 + [262144]
+    x = inputs.make_prefill_inputs(lens, 32, 128, 128, dtype=torch.bfloat16, init_state=True, seed=41,
+                                   device="cuda")
+    T = sum(lens)
+    assert gdn.gdn_prefill_workspace_bytes(T, 64, 32, 128, 128) > 9 * 32 * 128 * 128 * 4  # split maps
+    o, S = _run(x)
+    _check_units(x, o, S, [(63, 0), (63, 31), (0, 5), (62, 17)])
+    o2, S2 = gdn.gdn_prefill_maxlen(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, 262144,
+                                    initial_state=x.initial_state)
+    torch.cuda.synchronize()
+    a = T - 262144
+    for h in range(32):
+        assert_close(f"long sequence head {h}: o vs the bounded plan", np64(o[a:, h]), np64(o2[a:, h]), TOL_BF16)
+        assert_close(f"long sequence head {h}: state vs the bounded plan", np64(S[63, h]), np64(S2[63, h]), TOL_BF16)
 
 
 @pytest.mark.timeout(600)
