@@ -54,7 +54,19 @@ int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H) {
     }
     if (num_seqs <= 0 || T_total <= 0 || H <= 0) return 0;
     const int64_t units = (int64_t)num_seqs * H;
-    if (units > 144) return 0;
+    if (units > 144) {
+        // The length-agnostic split, as for the forward pass: with more units
+        // than compute units, every sequence longer than T_total / (CUS / H + 1)
+        // tokens (a chain at least the batch's work per compute unit) is cut,
+        // whatever the lengths are; a batch without such a sequence runs its
+        // sweeps as unsplit, one workgroup per (sequence, head).  (Up to CUS
+        // units, sequences of similar lengths above that bound would be cut
+        // too, and a cut costs the backward more than it gains there.)
+        if (num_seqs < 2 || units <= kComputeUnits) return 0;
+        const int64_t pmax = kComputeUnits / H + 1;
+        const int64_t seg = ((T_total + pmax - 1) / pmax + 63) / 64 * 64;
+        return pmax >= 3 && seg >= kSpeculativeMinSegment ? seg : 0;
+    }
     const int64_t P = std::max<int64_t>(3, 512 / units), len = (T_total + num_seqs - 1) / num_seqs;
     const int64_t seg = std::max<int64_t>(512, ((len + P - 1) / P + 63) / 64 * 64);
     return (len + seg - 1) / seg >= 3 ? seg : 0;

@@ -54,9 +54,13 @@ int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H);
 //  - Without the split, when (sequence, head) units outnumber the compute
 //    units and there is more than one sequence: at ord_off the int32 order of
 //    the sequences, longest first (launch_seq_order), which both sweeps follow.
+//    With the split and more than one sequence: that order and, at pfx_off,
+//    the int32 segment prefix table [num_seqs + 1] of the sequences in that
+//    order, through which the sweeps over segments take the long sequences'
+//    segments first.
 struct BackwardWorkspace {
     int64_t slots = 0;
-    size_t pre_off = 0, d_off = 0, ord_off = 0, bytes = 0;
+    size_t pre_off = 0, d_off = 0, ord_off = 0, pfx_off = 0, bytes = 0;
     bool ord = false;
 };
 inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_seqs, int32_t H, int32_t dk,
@@ -69,6 +73,12 @@ inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_
         w.slots = T_total / seg + num_seqs;
         w.d_off = w.pre_off + al(prefill_workspace_layout(T_total, num_seqs, H, dk, dv, seg, false).bytes);
         w.bytes = w.d_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
+        if (num_seqs > 1) {
+            w.ord = true;
+            w.ord_off = w.bytes;
+            w.pfx_off = w.ord_off + al((size_t)num_seqs * sizeof(int32_t));
+            w.bytes = w.pfx_off + al(((size_t)num_seqs + 1) * sizeof(int32_t));
+        }
     } else if (num_seqs > 1 && (int64_t)num_seqs * H > kComputeUnits) {
         w.ord = true;
         w.ord_off = w.bytes;

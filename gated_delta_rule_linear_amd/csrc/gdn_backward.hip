@@ -104,8 +104,12 @@ struct BArgs {
     const float* fN;
     float* wsD;
     // without the split: workgroup b takes head b % H of sequence ord[b / H]
-    // (longest first), or of sequence b / H when ord is null
+    // (longest first), or of sequence b / H when ord is null.  With the split
+    // and pfx: workgroup b takes head b % H of segment b / H - pfx[i] of
+    // sequence ord[i], pfx[i] <= b / H < pfx[i + 1] (the long sequences'
+    // segments first); without pfx, segment slot b / H.
     const int32_t* ord;
+    const int32_t* pfx;
 };
 
 // What one workgroup of a sweep works on: head h of sequence n (tokens
@@ -134,20 +138,41 @@ __device__ __forceinline__ BUnit bwd_unit(const BArgs<TI>& a, int b) {
     }
     const int s = b / H;
     u.h = b - s * H;
-    // the last sequence whose first slot is at or before s (first slots increase with n)
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)a.cu[mid] / a.seg + mid <= s) lo = mid;
-        else hi = mid - 1;
+    if (a.pfx) {
+        // the sequences in the order ord: the last i with pfx[i] <= s
+        if (s >= a.pfx[a.num_seqs]) {
+            u.valid = false;
+            return u;
+        }
+        int lo = 0, hi = a.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.pfx[mid] <= s) lo = mid;
+            else hi = mid - 1;
+        }
+        u.n = a.ord[lo];
+        u.tb = a.cu[u.n];
+        u.te = a.cu[u.n + 1];
+        u.j = s - a.pfx[lo];
+        u.P = max(1, (int)((u.te - u.tb + a.seg - 1) / a.seg));
+        u.slot = (int)(u.tb / a.seg) + u.n + u.j;
+        u.valid = u.j < u.P;
+    } else {
+        // the last sequence whose first slot is at or before s (first slots increase with n)
+        int lo = 0, hi = a.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)a.cu[mid] / a.seg + mid <= s) lo = mid;
+            else hi = mid - 1;
+        }
+        u.n = lo;
+        u.tb = a.cu[lo];
+        u.te = a.cu[lo + 1];
+        u.j = s - (int)(u.tb / a.seg + lo);
+        u.P = max(1, (int)((u.te - u.tb + a.seg - 1) / a.seg));
+        u.slot = s;
+        u.valid = u.j >= 0 && u.j < u.P;
     }
-    u.n = lo;
-    u.tb = a.cu[lo];
-    u.te = a.cu[lo + 1];
-    u.j = s - (int)(u.tb / a.seg + lo);
-    u.P = max(1, (int)((u.te - u.tb + a.seg - 1) / a.seg));
-    u.slot = s;
-    u.valid = u.j >= 0 && u.j < u.P;
     u.sb = u.tb + (int64_t)u.j * a.seg;
     u.se = u.sb + a.seg < u.te ? u.sb + a.seg : u.te;
     return u;
@@ -904,6 +929,7 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     a.fM = a.fN = nullptr;
     a.wsD = nullptr;
     a.ord = nullptr;
+    a.pfx = nullptr;
     if (p.seg <= 0) {
         const unsigned blocks = (unsigned)((int64_t)p.num_seqs * p.H);
         const BackwardWorkspace wl = backward_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DV, p.bf16, 0);
@@ -950,6 +976,14 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     f.legacy = false;
     hipError_t e = launch_prefill_maps(f, s);
     if (e != hipSuccess) return e;
+    if (ws.ord) {
+        // the sweeps over segments take the longest sequences' segments first
+        int32_t* ord = reinterpret_cast<int32_t*>(base + ws.ord_off);
+        int32_t* pfx = reinterpret_cast<int32_t*>(base + ws.pfx_off);
+        if ((e = launch_seq_order(p.cu_seqlens, p.num_seqs, 0, ord, s, p.seg, pfx)) != hipSuccess) return e;
+        a.ord = ord;
+        a.pfx = pfx;
+    }
     const unsigned blocks = (unsigned)(ws.slots * p.H);
     hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, true>), dim3(blocks), dim3(DV * 4), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

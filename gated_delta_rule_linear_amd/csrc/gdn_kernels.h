@@ -163,8 +163,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
 // The unit order (see PrefillWorkspace): ord[0 .. num_seqs) receives the
-// sequence indices, longest first, lengths capped at cap tokens when cap > 0.
+// sequence indices, longest first, lengths capped at cap tokens when cap > 0;
+// with pfx, also pfx[0 .. num_seqs]: pfx[i] is the number of segments of seg
+// tokens (one for an empty sequence) of the sequences ord[0 .. i-1].
 hipError_t launch_seq_order(const int32_t* cu_seqlens, int32_t num_seqs, int64_t cap, int32_t* ord,
-                            hipStream_t stream);
+                            hipStream_t stream, int64_t seg = 1, int32_t* pfx = nullptr);
 
 }  // namespace gdn

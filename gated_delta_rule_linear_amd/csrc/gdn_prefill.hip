@@ -1816,7 +1816,8 @@ __device__ __forceinline__ int order_key(int len, int cap) {
     return 1 + 4 * e + sub;
 }
 __global__ __launch_bounds__(1024) void seq_order_kernel(const int32_t* __restrict__ cu, int num_seqs, int cap,
-                                                         int32_t* __restrict__ ord) {
+                                                         int32_t* __restrict__ ord, int seg,
+                                                         int32_t* __restrict__ pfx) {
     constexpr int NB = kOrderBuckets, NWV = 16;
     __shared__ int hist[NB], start[NB], done[NB];
     __shared__ int cnt[NWV][NB];
@@ -1866,6 +1867,34 @@ __global__ __launch_bounds__(1024) void seq_order_kernel(const int32_t* __restri
             }
             done[t] += sum;
         }
+        __syncthreads();
+    }
+    if (!pfx) return;
+    // pfx[i] = segments (of seg tokens; an empty sequence has one) of the
+    // sequences ord[0 .. i-1]: the workgroups of a pass over every segment
+    // take the sequences in this order (ord, written above by other threads
+    // of this workgroup, is read back after the barrier)
+    __syncthreads();
+    __shared__ int part[1024];
+    int carry = 0;
+    if (t == 0) pfx[0] = 0;
+    for (int base = 0; base < num_seqs; base += 1024) {
+        const int i = base + t;
+        int c = 0;
+        if (i < num_seqs) {
+            const int m = ord[i], len = cu[m + 1] - cu[m];
+            c = len > 0 ? (len - 1) / seg + 1 : 1;
+        }
+        part[t] = c;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int x = t >= off ? part[t - off] : 0;
+            __syncthreads();
+            part[t] += x;
+            __syncthreads();
+        }
+        if (i < num_seqs) pfx[i + 1] = carry + part[t];
+        carry += part[1023];
         __syncthreads();
     }
 }
@@ -2210,10 +2239,12 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t s) {
     return p.bf16 ? run_t<bf16>(p, s) : run_t<float>(p, s);
 }
 
-hipError_t launch_seq_order(const int32_t* cu_seqlens, int32_t num_seqs, int64_t cap, int32_t* ord, hipStream_t s) {
+hipError_t launch_seq_order(const int32_t* cu_seqlens, int32_t num_seqs, int64_t cap, int32_t* ord, hipStream_t s,
+                            int64_t seg, int32_t* pfx) {
     if (num_seqs <= 0) return hipSuccess;
     hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, s, cu_seqlens, num_seqs,
-                       (int)std::min<int64_t>(std::max<int64_t>(cap, 0), 0x7fffffff), ord);
+                       (int)std::min<int64_t>(std::max<int64_t>(cap, 0), 0x7fffffff), ord,
+                       (int)std::min<int64_t>(std::max<int64_t>(seg, 1), 0x7fffffff), pfx);
     return hipGetLastError();
 }
 

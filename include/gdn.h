@@ -279,7 +279,10 @@ int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const voi
  * * d_v * (2 for GDN_BF16, 4 for GDN_F32), rounded up to 256; with a time
  * split of segment length L (below), also gdn_prefill's split workspace for
  * segments of L tokens and (T_total / L + num_seqs) * H * d_k * d_v * 4 bytes,
- * each rounded up to 256.  Depends on the arguments and on
+ * each rounded up to 256, and with more than one sequence two int32 tables
+ * (the order of the sequences, longest first, and their segment counts) of
+ * num_seqs and num_seqs + 1 entries; without the split, that order alone when
+ * num_seqs * H exceeds 256.  Depends on the arguments and on
  * GDN_BACKWARD_SEGMENT only; 0 for invalid arguments.  The checkpoints and
  * the split are this library's design: no passage of the pages defines this
  * call. */
@@ -325,7 +328,10 @@ size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, i
  * Generation", section 3.1).
  * Time split: when few (sequence, head) pairs leave compute units idle
  * (num_seqs * H <= 144) and sequences are long, each sequence is cut into
- * segments of L tokens (a multiple of 64) swept in parallel.  The state map
+ * segments of L tokens (a multiple of 64) swept in parallel; when there are
+ * more pairs than the 256 compute units and more than one sequence, every
+ * sequence longer than L = T_total / (256 / H + 1) tokens is (when L >= 16384),
+ * so that one long sequence among short ones does not set the call's time.  The state map
  * of a segment is affine, S_end = M S_start + N, and its adjoint
  * dS_start = M^T dS_end + D.  gdn_prefill's own time split gives M, N and
  * every segment's start state; per-segment sweeps give D and a sequential

@@ -278,7 +278,9 @@ def _backward_ws(T, n, H, dk, dv, bf16, seg):
         return ck + (al(n * 4) if n > 1 and n * H > 256 else 0)
     fs = T // seg
     pre = al(fs * H * dk * dk * 4) + al(fs * H * dk * dv * 4) + al((n + 1) * 4) + al(max(min(n, T // (seg + 1)), 1) * 4)
-    return ck + al(pre) + al((T // seg + n) * H * dk * dv * 4)
+    # with more than one sequence, the order table [n] and the segment prefix table [n + 1]
+    order = al(n * 4) + al((n + 1) * 4) if n > 1 else 0
+    return ck + al(pre) + al((T // seg + n) * H * dk * dv * 4) + order
 
 
 def test_backward_workspace_bytes_split(lib, monkeypatch):
@@ -290,6 +292,11 @@ def test_backward_workspace_bytes_split(lib, monkeypatch):
     assert f(1 << 20, 1, 16, 128, 128, 1) == _backward_ws(1 << 20, 1, 16, 128, 128, True, 32768)
     # enough units to fill the chip, or sequences too short for three segments: no split
     assert f(65536, 8, 32, 128, 128, 1) == _backward_ws(65536, 8, 32, 128, 128, True, 0)
+    # more units than compute units: the length-agnostic split (sequences longer than
+    # T / (256 / H + 1) tokens are cut), when that segment is at least 16,384 tokens
+    T = 262144 + 63 * 1024
+    assert f(T, 64, 32, 128, 128, 1) == _backward_ws(T, 64, 32, 128, 128, True, _agnostic_seg(T, 32))
+    assert f(100000, 64, 32, 128, 128, 1) == _backward_ws(100000, 64, 32, 128, 128, True, 0)
     assert f(65536, 9, 32, 128, 128, 1) == _backward_ws(65536, 9, 32, 128, 128, True, 0)
     assert _backward_ws(65536, 9, 32, 128, 128, True, 0) == _backward_ws(65536, 8, 32, 128, 128, True, 0) \
         + 32 * 128 * 128 * 2 + 256  # one more sequence's checkpoint slot per head, and the order table

@@ -72,6 +72,44 @@ def test_longest_first_order_many_units(dtype, d):
     _case(lengths, 3, d, d, dtype, seed=37)
 
 
+@pytest.mark.timeout(600)
+def test_length_agnostic_split_skewed(monkeypatch):
+    # 15 sequences of 1,000 tokens and one of 140,000, 32 heads: 512 units, more than
+    # the compute units, so the plan cuts every sequence longer than T / 9 tokens (the
+    # long one, into 9 segments) and the sweeps take its segments first.  Every
+    # gradient against the unsplit pass (one workgroup per (sequence, head)); two short
+    # units also against the fp64 oracle.
+    monkeypatch.delenv("GDN_BACKWARD_SEGMENT", raising=False)
+    lengths = [1000] * 15 + [140000]
+    H, d = 32, 128
+    log("backward length-agnostic split: 15 x 1000 + 1 x 140000 tokens, 32 heads")
+    x = inputs.make_prefill_inputs(lengths, H, d, d, dtype=torch.bfloat16, init_state=True, seed=47)
+    d_o, dSf = inputs.make_cotangents(x.T_total, x.num_seqs, H, d, d, dtype=torch.bfloat16, seed=147)
+    T = x.T_total
+    unsplit_bytes = (T // 16 + 16) * H * d * d * 2
+    assert gdn.gdn_prefill_backward_workspace_bytes(T, 16, H, d, d, torch.bfloat16) > unsplit_bytes + (1 << 20)
+    to_device(x)
+    d_o, dSf = d_o.cuda(), dSf.cuda()
+    got = _run(x, d_o, dSf)
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "0")
+    ref = _run(x, d_o, dSf)
+    for name in NAMES:
+        assert_close(f"{name} split vs unsplit", np64(got[name]), np64(ref[name]), TOL[torch.bfloat16])
+    # two short units against the oracle, each on its own tokens (units are independent)
+    cu = x.cu_seqlens.cpu().numpy()
+    for n, h in ((0, 3), (14, 30)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = lambda t: t[a:b, h:h + 1].cpu()
+        sub = inputs.PrefillInputs(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta),
+                                   torch.tensor([0, b - a], dtype=torch.int32), [b - a],
+                                   x.initial_state[n:n + 1, h:h + 1].cpu())
+        r = _oracle_grads(sub, d_o[a:b, h:h + 1].cpu(), dSf[n:n + 1, h:h + 1].cpu())
+        for name in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert_close(f"seq {n} head {h} {name}", np64(got[name][a:b, h:h + 1]), r[name], TOL[torch.bfloat16])
+        assert_close(f"seq {n} head {h} d_initial_state", np64(got["d_initial_state"][n:n + 1, h:h + 1]),
+                     r["d_initial_state"], TOL[torch.bfloat16])
+
+
 def test_small_fp32():
     # one 256-token sequence, 2 heads, d = 64, fp32, zero initial state
     _case([256], 2, 64, 64, torch.float32, init=False)
