@@ -47,8 +47,8 @@ sequences of 512..16,384 tokens with random initial states (varlen64), one
 of 1,024 tokens plus one of 262,144 (skewed64, with and without the bound on
 the lengths of gdn_prefill_maxlen), each with its roofline, sampled parity and
 a host-oracle baseline on a stated sample, after --workload-warmup (10)
-untimed calls; and gdn_prefill_backward on varlen64 (varlen64_backward) with
-its roofline and sampled parity.  --no-workloads skips them.  "device" gives
+untimed calls; and gdn_prefill_backward on varlen64 and skewed64
+(varlen64_backward, skewed64_backward) with its roofline and sampled parity.  --no-workloads skips them.  "device" gives
 the GPU's compute-unit count and clock as the runtime reports them, beside
 the published peaks the fractions use.
 """
@@ -213,8 +213,15 @@ def summarize_pmc(paths):
 
     def short(n):
         m = re.search(r"(prefill_ws_kernel|prefill_seq_kernel|seg_fold_kernel|seg_table_kernel|decode_kernel|"
-                      r"bwd_\w+_kernel|tile_prefill_kernel)", n)
-        return m.group(0) if m else n[:40]
+                      r"bwd_\w+_kernel|tile_prefill_kernel|seq_order_kernel)", n)
+        if not m:
+            return n[:40]
+        k = m.group(0)
+        if k in ("prefill_ws_kernel", "prefill_seq_kernel"):  # transition maps or outputs (template MAP)
+            k += "<map>" if re.search(r"kernelILi\d+ELi\d+ELb1", n) else "<out>"
+        elif k == "bwd_grad_kernel":  # adjoint only or full (template DONLY)
+            k += "<adjoint-only>" if re.search(r"ELb1EE", n) else "<full>"
+        return k
 
     per = collections.defaultdict(lambda: collections.defaultdict(list))
     dur = collections.defaultdict(dict)
@@ -597,6 +604,8 @@ def main():
         hinted["without_hint_roofline_frac"] = plain["roofline"]["frac"]
         hinted["speedup_from_hint"] = plain["ms_per_step"] / hinted["ms_per_step"]
         workloads["skewed64"] = hinted
+        if not args.no_backward:
+            workloads["skewed64_backward"] = backward_leg(gdn, "skewed64", xs, 3, 1, stream)
         del xs
         torch.cuda.empty_cache()
 
