@@ -21,8 +21,9 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued on it and the call returns without waiting; results are ready
  *     when the stream reaches that point.  Apart from the side streams of the
- *     time split (see gdn_prefill), the library keeps no state between calls;
- *     it frees no caller memory and prints nothing.
+ *     time split (see gdn_prefill) and the fixed scratch array of
+ *     gdn_prefill_noalloc, the library keeps no state between calls; it frees
+ *     no caller memory and prints nothing.
  *   - Every call returns a gdn_status.  Argument errors are reported before any
  *     memory is touched or any work is enqueued.  GDN_ERR_HIP means a HIP call
  *     (allocation aside) or a kernel launch failed; a fault inside a kernel
