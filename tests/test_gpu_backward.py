@@ -110,6 +110,19 @@ def test_length_agnostic_split_skewed(monkeypatch):
                      r["d_initial_state"], TOL[torch.bfloat16])
 
 
+@pytest.mark.parametrize("seg", [0, 64])
+def test_many_short_sequences(monkeypatch, seg):
+    # 1,500 sequences of 0 .. 150 tokens x 2 heads, d = 64, fp32: the order tables over
+    # several blocks of sequences (without the split, and with 64-token segments, where
+    # the segment prefix table orders the sweeps); every gradient against the oracle
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", str(seg))
+    rng = np.random.default_rng(61 + seg)
+    lengths = [int(v) for v in rng.integers(0, 151, 1500)]
+    for i in range(0, 1500, 9):
+        lengths[i] = 0
+    _case(lengths, 2, 64, 64, torch.float32, seed=62)
+
+
 def test_small_fp32():
     # one 256-token sequence, 2 heads, d = 64, fp32, zero initial state
     _case([256], 2, 64, 64, torch.float32, init=False)

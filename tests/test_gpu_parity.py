@@ -131,6 +131,23 @@ def test_longest_first_order_many_units(monkeypatch, dtype, d):
     _prefill_case(lengths, H, d, d, dtype, seed=33)
 
 
+@pytest.mark.parametrize("seg", [0, 64])
+def test_many_short_sequences(monkeypatch, seg):
+    # 3,000 sequences of 0 .. 40 tokens (a tenth of them empty) x 2 heads, d = 64, fp32:
+    # the order kernel and the segment table walk several blocks of sequences.  With
+    # 64-token segments a second batch, 1,500 sequences of 0 .. 300 tokens, has most of
+    # them split.  Every unit against the oracle, both states included.
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT", str(seg))
+    rng = np.random.default_rng(51 + seg)
+    lengths = [int(v) for v in rng.integers(0, 41, 3000)]
+    for i in range(0, 3000, 10):
+        lengths[i] = 0
+    _prefill_case(lengths, 2, 64, 64, torch.float32, seed=52)
+    if seg:
+        lengths = [int(v) for v in rng.integers(0, 301, 1500)]
+        _prefill_case(lengths, 2, 64, 64, torch.float32, seed=53)
+
+
 def test_split_prefill_equals_whole():
     x = inputs.make_prefill_inputs([300], 2, 128, 128, dtype=torch.bfloat16, init_state=True, seed=7)
     to_device(x)
