@@ -41,6 +41,10 @@ gdn_prefill_tiles with dense window products and with position-pair decays
 with its own roofline, sampled parity and host-oracle baseline.
 --no-tiles / --no-backward skip them.
 
+"gate_variants" times the gate forms of NEXT f1 (bf16 logits, gate computed in the
+kernel) and f4 (one log-decay per (token, head)) on the prefill_64k and decode
+shapes, with their rooflines and sampled parity.  --no-gates skips them.
+
 "workloads" times gdn_prefill on the other prefill shapes: 64 packed
 sequences of 512..16,384 tokens with random initial states (varlen64), one
 2^20-token sequence x 16 heads (long_1m), and a skewed batch of 63 sequences
@@ -86,9 +90,12 @@ BF16_CHUNK = 32  # the bf16 prefill kernel's chunk length (tokens)
 BF16_FLOP_PER_CLK_CU = 4096
 
 
-def prefill_bytes(T_tokens: int, H: int, dk: int, dv: int, n_seqs: int, elt: int = 2, init_state: bool = False):
-    """Algorithmic HBM bytes of one prefill launch: every input read once, every output written once."""
-    per_head_token = elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv
+def prefill_bytes(T_tokens: int, H: int, dk: int, dv: int, n_seqs: int, elt: int = 2, init_state: bool = False,
+                  gate_bytes=None):
+    """Algorithmic HBM bytes of one prefill launch: every input read once, every output written once
+    (gate_bytes per (token, head): 4 d_k for fp32 per-channel log-decays by default; 2 d_k for bf16
+    logits, 4 for one log-decay per (token, head))."""
+    per_head_token = elt * (2 * dk + dv) + (4 * dk if gate_bytes is None else gate_bytes) + 4 + elt * dv
     states = n_seqs * H * dk * dv * 4 * (2 if init_state else 1)
     return T_tokens * H * per_head_token + states
 
@@ -120,9 +127,10 @@ def backward_flops(T_tokens: int, H: int, dk: int, dv: int, C: int = 16):
     return T_tokens * H * per
 
 
-def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int = 2):
-    """Algorithmic HBM bytes of one decode launch: state read and written, token vectors read, o written."""
-    per = 8 * dk * dv + elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv
+def decode_bytes(N: int, H: int, dk: int, dv: int, elt: int = 2, gate_bytes=None):
+    """Algorithmic HBM bytes of one decode launch: state read and written, token vectors read, o written
+    (gate_bytes as for prefill_bytes)."""
+    per = 8 * dk * dv + elt * (2 * dk + dv) + (4 * dk if gate_bytes is None else gate_bytes) + 4 + elt * dv
     return N * H * per
 
 
@@ -347,6 +355,72 @@ def prefill_leg(gdn, name, x, steps, warmup, stream, cpu: bool, cpu_seqs: int, c
     return leg
 
 
+def gate_variants_leg(gdn, inputs, x, o, S, ws, N, Hd, d, steps, warmup, stream):
+    """gdn_prefill_logits (GDN_GATE_ALPHA_MIN, a_min = 0.9, on bf16 logits) and
+    gdn_prefill_head_gate on the prefill_64k shape (same q, k, v, beta, same plan and
+    workspace), and gdn_decode_logits / gdn_decode_head_gate on the decode shape: time,
+    algorithmic bytes, roofline; sampled parity of the prefill variants (head 0, first
+    2048 tokens) against the fp64 oracle with its own gate parameterisation."""
+    import oracle
+
+    T, H, dk = x.q.shape
+    dv = x.v.shape[2]
+    gen = torch.Generator(device=x.q.device)
+    gen.manual_seed(7)
+    # logits z ~ N(0,1) in bf16: the kernel computes g = log(0.9 + 0.1 sigmoid(z)) per channel
+    z = torch.randn((T, H, dk), generator=gen, device=x.q.device).to(torch.bfloat16)
+    # one log-decay per (token, head) in [-5, 0]
+    gh = (-5.0 * torch.sigmoid(torch.randn((T, H), generator=gen, device=x.q.device))).float()
+    tk = 2048
+    sl = lambda t: t[:tk, :1].to("cpu", torch.float64).numpy()
+    res = {"workload": "prefill_64k and decode_512x32 with the other gate forms", "steps": steps, "warmup": warmup}
+
+    def prefill_variant(name, call, gbytes, g_ref):
+        ms = time_loop(call, steps, warmup, stream)
+        b = prefill_bytes(T, H, dk, dv, 1, gate_bytes=gbytes)
+        ro, _ = oracle.recurrent(sl(x.q), sl(x.k), sl(x.v), g_ref, sl(x.beta), np.array([0, tk], np.int32))
+        gbs = b / (ms / 1e3) / 1e9
+        res[name] = {"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "algorithmic_bytes_per_launch": b,
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": gbs / HBM_PEAK_GBS},
+                     "parity_o_rel_err_head0_first2048": oracle.rel_err(o[:tk, :1].to("cpu", torch.float64).numpy(),
+                                                                         ro)}
+
+    prefill_variant("prefill_logits",
+                    lambda: gdn.gdn_prefill_logits(x.q, x.k, x.v, z, gdn.GDN_GATE_ALPHA_MIN, 0.9, x.beta, x.cu_seqlens,
+                                                   final_state=S, o=o, workspace=ws, stream=stream),
+                    2 * dk, oracle.gates_from_logits(sl(z), oracle.GATE_ALPHA_MIN, 0.9))
+    prefill_variant("prefill_head_gate",
+                    lambda: gdn.gdn_prefill_head_gate(x.q, x.k, x.v, gh, x.beta, x.cu_seqlens, final_state=S, o=o,
+                                                      workspace=ws, stream=stream),
+                    4, np.repeat(gh[:tk, :1].to("cpu", torch.float64).numpy()[:, :, None], dk, axis=2))
+    del z, gh
+    for name, kw, gbytes in (("decode_logits", {"logits": True}, 2 * dk), ("decode_head_gate", {"head_gate": True}, 4)):
+        S0, draws = inputs.make_decode_steps(N, Hd, d, d, max(1, min(steps + warmup, 32)), dtype=torch.bfloat16,
+                                             seed=0, device=x.q.device, **kw)
+        st = S0.contiguous()
+        od = torch.empty((N, Hd, d), dtype=torch.bfloat16, device=x.q.device)
+        it = [0]
+
+        def dstep():
+            dr = draws[it[0] % len(draws)]
+            it[0] += 1
+            if name == "decode_logits":
+                gdn.gdn_decode_logits(dr.q, dr.k, dr.v, dr.z, gdn.GDN_GATE_ALPHA_MIN, 0.9, dr.beta, st, o=od,
+                                      stream=stream)
+            else:
+                gdn.gdn_decode_head_gate(dr.q, dr.k, dr.v, dr.g, dr.beta, st, o=od, stream=stream)
+
+        ms = time_loop(dstep, steps, warmup, stream)
+        b = decode_bytes(N, Hd, d, d, gate_bytes=gbytes)
+        gbs = b / (ms / 1e3) / 1e9
+        res[name] = {"ms_per_step": ms, "algorithmic_bytes_per_launch": b,
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": gbs / HBM_PEAK_GBS}}
+        del S0, draws, st, od
+    return res
+
+
 def backward_leg(gdn, name, x, steps, warmup, stream):
     """Time gdn_prefill_backward over the workload x (every gradient written, the initial
     state's included; dL/do ~ N(0,1), dL/d(final state) ~ 0.02 N(0,1)); sampled parity of
@@ -422,6 +496,7 @@ def main():
     ap.add_argument("--tiles-steps", type=int, default=10)
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV", help="summarise rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--no-workloads", action="store_true")
+    ap.add_argument("--no-gates", action="store_true")
     ap.add_argument("--workload-steps", type=int, default=10)
     ap.add_argument("--workload-warmup", type=int, default=10)
     args = ap.parse_args()
@@ -488,6 +563,12 @@ def main():
     dms = time_loop(dstep, args.steps, args.warmup, stream)
     dbytes = decode_bytes(N, Hd, d, d)
     dgbs = dbytes / (dms / 1e3) / 1e9
+
+    # ---- the other gate forms (NEXT f1: bf16 logits with the gate computed in the kernel; f4: one
+    # log-decay per (token, head)) on the same prefill and decode shapes
+    gates = None
+    if not args.no_gates:
+        gates = gate_variants_leg(gdn, inputs, x, o, S, ws, N, Hd, d, args.steps, args.warmup, stream)
 
     del o
     torch.cuda.empty_cache()
@@ -643,6 +724,8 @@ def main():
                                     / (ms / 1e3),
         "parity": {"prefill_o_rel_err_head0_first2048": parity},
     }
+    if gates is not None:
+        res["gate_variants"] = gates
     if tiles is not None:
         res["tile_paths"] = tiles
     if bwd is not None:
