@@ -169,7 +169,9 @@ const char* gdn_status_string(int32_t status) {
     switch (status) {
         case GDN_OK: return "ok";
         case GDN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, negative size, short workspace)";
-        case GDN_ERR_UNSUPPORTED: return "unsupported configuration (d_k and d_v must be 64 or 128; dtype f32 or bf16)";
+        case GDN_ERR_UNSUPPORTED:
+            return "unsupported configuration (d_k and d_v must be 64 or 128; dtype f32 or bf16, bf16 for the logit "
+                   "and per-head gate entry points)";
         case GDN_ERR_DOMAIN: return "input outside the domain (g not in [-5, 0] or malformed cu_seqlens)";
         case GDN_ERR_OOM: return "device allocation failed";
         case GDN_ERR_HIP: return "HIP runtime error";
