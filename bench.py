@@ -226,7 +226,10 @@ def summarize_pmc(paths):
             return n[:40]
         k = m.group(0)
         if k in ("prefill_ws_kernel", "prefill_seq_kernel"):  # transition maps or outputs (template MAP)
-            k += "<map>" if re.search(r"kernelILi\d+ELi\d+ELb1", n) else "<out>"
+            k += "<map" if re.search(r"kernelILi\d+ELi\d+ELb1", n) else "<out"
+            gm = re.search(r"prefill_ws_kernelILi\d+ELi\d+ELb[01]ELi\d+ELi(\d)E", n)  # gate mode
+            k += {"1": ",logits", "2": ",head gate"}.get(gm.group(1), "") if gm else ""
+            k += ">"
         elif k == "bwd_grad_kernel":  # adjoint only or full (template DONLY)
             k += "<adjoint-only>" if re.search(r"ELb1EE", n) else "<full>"
         return k
