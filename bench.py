@@ -229,6 +229,7 @@ def summarize_pmc(paths):
             k += "<map" if re.search(r"kernelILi\d+ELi\d+ELb1", n) else "<out"
             gm = re.search(r"prefill_ws_kernelILi\d+ELi\d+ELb[01]ELi\d+ELi(\d)E", n)  # gate mode
             k += {"1": ",logits", "2": ",head gate"}.get(gm.group(1), "") if gm else ""
+            k += ",q^" if re.search(r"prefill_ws_kernelILi\d+ELi\d+ELb1ELi2ELi0ELb1E", n) else ""  # backward's maps
             k += ">"
         elif k == "bwd_grad_kernel":  # adjoint only or full (template DONLY)
             k += "<adjoint-only>" if re.search(r"ELb1EE", n) else "<full>"
@@ -642,8 +643,8 @@ def main():
                "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": bgbs / HBM_PEAK_GBS, "traffic": measured_traffic("backward"),
                             "kernel": "gdn_prefill_backward call (time split planned for 128 units: "
-                                      "seg_table, prefill_ws_kernel<128,128,map>, seg_fold, "
-                                      "bwd_grad_kernel<bf16,128,128,adjoint-only>, bwd_fold_rev_kernel, "
+                                      "seg_table, prefill_ws_kernel<128,128,map,q^>, seg_fold, "
+                                      "bwd_dpass_kernel<128,128>, bwd_fold_rev_q_kernel, "
                                       "bwd_states_kernel<bf16,128,128>, bwd_grad_kernel<bf16,128,128,full>)",
                             "algorithmic_bytes_per_launch": bbytes},
                "mfma": {"flops_per_launch": bflops, "achieved": bflops / (bms / 1e3) / 1e12,

@@ -51,6 +51,11 @@ int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H);
 //    segments and the segment table); at d_off, per segment slot and head (slot
 //    cu[n] / seg + n + j for segment j of sequence n, T_total / seg + num_seqs
 //    slots) the d_k x d_v fp32 state gradient D of the reverse fold.
+//    For bf16 with d_k = d_v (D from the transition pass, see launch_backward)
+//    also, at ml_off, the last segment's transition M of every split sequence
+//    (d_k x d_k fp32 per split-list entry and head, min(num_seqs,
+//    T_total / (seg + 1)) entries), and at qh_off the bf16 q^ buffer
+//    [T_total, H, d_k].
 //  - Without the split, when (sequence, head) units outnumber the compute
 //    units and there is more than one sequence: at ord_off the int32 order of
 //    the sequences, longest first (launch_seq_order), which both sweeps follow.
@@ -59,9 +64,9 @@ int64_t plan_backward_segment(int64_t T_total, int32_t num_seqs, int32_t H);
 //    order, through which the sweeps over segments take the long sequences'
 //    segments first.
 struct BackwardWorkspace {
-    int64_t slots = 0;
-    size_t pre_off = 0, d_off = 0, ord_off = 0, pfx_off = 0, bytes = 0;
-    bool ord = false;
+    int64_t slots = 0, splits = 0;
+    size_t pre_off = 0, d_off = 0, ml_off = 0, qh_off = 0, ord_off = 0, pfx_off = 0, bytes = 0;
+    bool ord = false, qmaps = false;
 };
 inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_seqs, int32_t H, int32_t dk,
                                                    int32_t dv, bool bf16, int64_t seg) {
@@ -73,6 +78,13 @@ inline BackwardWorkspace backward_workspace_layout(int64_t T_total, int32_t num_
         w.slots = T_total / seg + num_seqs;
         w.d_off = w.pre_off + al(prefill_workspace_layout(T_total, num_seqs, H, dk, dv, seg, false).bytes);
         w.bytes = w.d_off + al((size_t)w.slots * H * dk * dv * sizeof(float));
+        if (bf16 && dk == dv) {
+            w.qmaps = true;
+            w.splits = std::min<int64_t>(num_seqs, T_total / (seg + 1));
+            w.ml_off = w.bytes;
+            w.qh_off = w.ml_off + al((size_t)w.splits * H * dk * dk * sizeof(float));
+            w.bytes = w.qh_off + al((size_t)T_total * H * dk * 2);
+        }
         if (num_seqs > 1) {
             w.ord = true;
             w.ord_off = w.bytes;

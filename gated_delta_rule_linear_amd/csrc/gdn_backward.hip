@@ -51,13 +51,25 @@
 // cut into segments of seg tokens and every sweep runs one workgroup per
 // (segment, head).  The forward map of a segment is affine in its start
 // state, S_end = M S_start + N, and the reverse map of its state gradient is
-// dS_start = M^T dS_end + D (D: the reverse sweep's result for dS_end = 0).
-//  a. the forward pass's own time split (launch_prefill_maps): M_j and N_j of
-//     every non-last segment and the fold S_start(j + 1) = M_j S_start(j) + N_j;
-//     bwd_grad_kernel<DONLY>: D_j of every segment but the first, the last one
-//     started from dL/d(final state), which makes it dS_end of the one before;
-//  b. bwd_fold_rev_kernel: dS_end(j - 1) = M_j^T dS_end(j) + D_j in reverse;
-//  c. sweeps 1 and 2 per segment, from S_start(j) and dS_end(j).
+// dS_start = M^T dS_end + D.  D, the state gradient at the segment's start for
+// dS_end = 0, is the gradient of the segment's outputs o_t = S_t^T q_t with
+// S_t = M_t S_start + N_t (M_t: the transition from the segment's start
+// through token t):
+//   D = sum over the segment's tokens of q^_t dO_t^T,  q^_t = M_t^T q_t.
+// bf16 with d_k = d_v:
+//  a. the forward pass's transition pass in its q^ form
+//     (launch_prefill_maps_q): M_j and N_j of every non-last segment, M of
+//     every split sequence's last segment, q^ of every segment j >= 1, and the
+//     fold S_start(j + 1) = M_j S_start(j) + N_j;
+//  b. bwd_dpass_kernel: D_j of every segment j >= 1 from q^ and dO;
+//  c. bwd_fold_rev_q_kernel: from dS_end of the last segment (dL/d(final
+//     state)), dS_end(j - 1) = M_j^T dS_end(j) + D_j in reverse;
+//  d. sweeps 1 and 2 per segment, from S_start(j) and dS_end(j).
+// Otherwise D_j comes from a reverse sweep of the dS recurrence alone
+// (bwd_grad_kernel<DONLY>, every segment but the first, the last one started
+// from dL/d(final state), which makes it dS_end of the one before), after the
+// forward pass's maps and fold (launch_prefill_maps), and bwd_fold_rev_kernel
+// composes the maps of the non-last segments.
 #include <type_traits>
 
 #include "gdn_backward.h"
@@ -549,6 +561,109 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_fold_rev_kernel(const int3
         [&](int i) { return wsD + ((size_t)(base + P - 2 - i) * H + h) * DK * DV; });
 }
 
+// Time split, bf16 with d_k = d_v: the offset of the reverse map of segment
+// j >= 1 of a split sequence, D_j = sum over its tokens t of q^_t dO_t^T.  One
+// workgroup per (non-last slot k, head): the segment after non-last segment k,
+// i.e. j = k - nl[n] + 1 of sequence n.  Wave w accumulates rows
+// [16w, 16w + 16) of D over all d_k columns (d_v = d_k).  Tiles of 64 tokens of
+// q^ and dO are copied into LDS transposed, tokens contiguous per channel:
+// each lane loads 8 channels of two adjacent tokens and writes them as 8
+// two-token words (the 32 lanes of a token pair range write 32 consecutive
+// words, so the stores of a wave spread over the banks); the next tile's loads
+// are in flight while the current one is contracted with 16x16x32 bf16
+// products.
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 16)) void bwd_dpass_kernel(const int32_t* __restrict__ cu,
+                                                                   const int32_t* __restrict__ nl, int num_seqs,
+                                                                   int H, int64_t seg, const bf16* __restrict__ qh,
+                                                                   const bf16* __restrict__ dO,
+                                                                   float* __restrict__ wsD) {
+    static_assert(DK == DV, "square state");
+    constexpr int NW = DK / 16, NT = 64 * NW, TT = 64, SP = TT + 8, CT = DV / 16;
+    constexpr int NCG = DK / 8;            // 8-channel groups of a row
+    static_assert((TT / 2) * NCG == NT, "one (token pair, channel group) per thread");
+    __shared__ __attribute__((aligned(16))) bf16 qT[DK * SP];
+    __shared__ __attribute__((aligned(16))) bf16 oT[DV * SP];
+    const int k = blockIdx.x / H, h = blockIdx.x - k * H;
+    if (k >= nl[num_seqs]) return;
+    int lo = 0, hi = num_seqs - 1;  // the sequence n with nl[n] <= k < nl[n + 1]
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (nl[mid + 1] > k) hi = mid;
+        else lo = mid + 1;
+    }
+    const int n = lo, j = k - nl[n] + 1;
+    const int64_t tb = cu[n] + (int64_t)j * seg, te = tb + seg < cu[n + 1] ? tb + seg : cu[n + 1];
+    const int L = (int)(te - tb);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int tp = tid % (TT / 2), cg = tid / (TT / 2);  // this thread's token pair and channel group
+    bf16x8 xq[2], xo[2];
+    auto load = [&](int t0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = t0 + 2 * tp + u;
+            const size_t off = ((size_t)(tb + t) * H + h) * DK + 8 * cg;
+            xq[u] = t < L ? *reinterpret_cast<const bf16x8*>(qh + off) : bf16x8{};
+            xo[u] = t < L ? *reinterpret_cast<const bf16x8*>(dO + off) : bf16x8{};
+        }
+    };
+    floatx4 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = zero4();
+    if (L > 0) load(0);
+    for (int t0 = 0; t0 < L; t0 += TT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            *reinterpret_cast<bf16x2*>(qT + (8 * cg + e) * SP + 2 * tp) = bf16x2{xq[0][e], xq[1][e]};
+            *reinterpret_cast<bf16x2*>(oT + (8 * cg + e) * SP + 2 * tp) = bf16x2{xo[0][e], xo[1][e]};
+        }
+        __syncthreads();
+        if (t0 + TT < L) load(t0 + TT);
+#pragma unroll
+        for (int kk = 0; kk < TT / 32; ++kk) {
+            // A[c][t] = q^[t][c], B[t][v] = dO[t][v]: lane r + 16g supplies tokens 32kk + 8g .. +7
+            const bf16x8 fa = *reinterpret_cast<const bf16x8*>(qT + (16 * w + r) * SP + 32 * kk + 8 * g);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                acc[ct] = Mma<bf16>::mma(fa, *reinterpret_cast<const bf16x8*>(oT + (16 * ct + r) * SP + 32 * kk + 8 * g),
+                                         acc[ct]);
+        }
+        __syncthreads();
+    }
+    // lane r + 16g holds D[16w + 4g + i][16ct + r]
+    float* D = wsD + (((size_t)(cu[n] / seg) + n + j) * H + h) * DK * DV;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) D[(size_t)(16 * w + 4 * g + i) * DV + 16 * ct + r] = acc[ct][i];
+}
+
+// Time split, bf16 with d_k = d_v: the reverse fold, per (split-list entry kk,
+// head) and 16 state columns, from x = dL/d(final state) (or zero): for
+// j = P-1 down to 1, x <- M_j^T x + D_j, the gradient at the end of segment
+// j - 1, written over D_j (M_{P-1} from wsML slot kk, M_j for j < P-1 from
+// slot nl[n] + j of the forward maps).
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 16)) void bwd_fold_rev_q_kernel(const int32_t* cu, const int32_t* nl,
+                                                                        const int32_t* spl, int H, int64_t seg,
+                                                                        const float* fM, const float* wsML,
+                                                                        const float* dSf, float* wsD) {
+    const int unit = blockIdx.x, kk = unit / H, h = unit - kk * H;
+    const int n = spl[kk];
+    if (n < 0) return;
+    const int P = nl[n + 1] - nl[n] + 1;
+    const int64_t base = cu[n] / seg + n;
+    const float* x0 = dSf ? dSf + ((size_t)n * H + h) * DK * DV : nullptr;
+    // step i takes segment j = P - 1 - i
+    auto d_at = [&](int i) { return wsD + ((size_t)(base + P - 1 - i) * H + h) * DK * DV; };
+    fold_columns<DK, DV, true>(
+        x0, P - 1, blockIdx.y,
+        [&](int i) {
+            return i == 0 ? wsML + ((size_t)kk * H + h) * DK * DK : fM + ((size_t)(nl[n] + P - 1 - i) * H + h) * DK * DK;
+        },
+        d_at);
+}
+
 // Reverse sweep over the sub-chunks of one (sequence, head), or with a time
 // split of one (segment, head), last to first, from the gradient of the state
 // at its end: that of the final state, or for a non-last segment the one the
@@ -974,7 +1089,37 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     f.seg = p.seg;
     f.workspace = base + ws.pre_off;
     f.legacy = false;
-    hipError_t e = launch_prefill_maps(f, s);
+    hipError_t e;
+    if constexpr (DK == DV && sizeof(TI) == 2) {
+        // D from the transition pass's q^: no adjoint-only sweep
+        bf16* qh = reinterpret_cast<bf16*>(base + ws.qh_off);
+        const float* wsML = reinterpret_cast<const float*>(base + ws.ml_off);
+        const int32_t* spl = reinterpret_cast<const int32_t*>(base + ws.pre_off + pw.spl_off);
+        if ((e = launch_prefill_maps_q(f, qh, const_cast<float*>(wsML), s)) != hipSuccess) return e;
+        if (ws.ord) {
+            int32_t* ord = reinterpret_cast<int32_t*>(base + ws.ord_off);
+            int32_t* pfx = reinterpret_cast<int32_t*>(base + ws.pfx_off);
+            if ((e = launch_seq_order(p.cu_seqlens, p.num_seqs, 0, ord, s, p.seg, pfx)) != hipSuccess) return e;
+            a.ord = ord;
+            a.pfx = pfx;
+        }
+        if (pw.slots > 0) {
+            hipLaunchKernelGGL((bwd_dpass_kernel<DK, DV>), dim3((unsigned)(pw.slots * p.H)), dim3(64 * (DK / 16)), 0,
+                               s, a.cu, a.nl, p.num_seqs, p.H, p.seg, qh, a.dO, a.wsD);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (pw.splits > 0) {
+            hipLaunchKernelGGL((bwd_fold_rev_q_kernel<DK, DV>), dim3((unsigned)(pw.splits * p.H), DV / 16),
+                               dim3(64 * (DK / 16)), 0, s, a.cu, a.nl, spl, p.H, p.seg, a.fM, wsML, a.dSf, a.wsD);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        const unsigned blocks = (unsigned)(ws.slots * p.H);
+        hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
+        return hipGetLastError();
+    }
+    e = launch_prefill_maps(f, s);
     if (e != hipSuccess) return e;
     if (ws.ord) {
         // the sweeps over segments take the longest sequences' segments first

@@ -161,6 +161,14 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 // nl[n] + j of wsN the start state of segment j + 1.  o and final_state are
 // not used.
 hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t stream);
+// The same for the backward's time split with q^ (bf16, d_k = d_v, per-channel
+// gates; M and N in one workgroup): besides the above, for every segment j >= 1
+// of a split sequence, q^_t = M_{j,t}^T q_t for its tokens t into qh (bf16
+// [T_total, H, d_k]; M_{j,t}: the transition from the segment's start through
+// token t), and the last segment's transition M into slot kk of wsML
+// (d_k x d_k fp32 per (split-list entry, head), the sequence in entry kk of the
+// split list).
+hipError_t launch_prefill_maps_q(const PrefillLaunch& p, void* qh, float* wsML, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
 // The unit order (see PrefillWorkspace): ord[0 .. num_seqs) receives the
 // sequence indices, longest first, lengths capped at cap tokens when cap > 0;

@@ -145,6 +145,13 @@ struct Args {
     // workgroup b takes head b % H of sequence ord[b / H] (longest first), or
     // of sequence b / H when ord is null
     const int32_t* ord;
+    // Transition pass for the backward (QH): q^_t = M_t^T q_t of every segment
+    // after the first goes to qh ([T, H, d_k]; M_t: the transition from the
+    // segment's start through token t), and workgroups from m_blocks on take the
+    // last segment of the split sequences in spl, whose M goes to wsML (slot kk
+    // for spl[kk])
+    TI* qh;
+    float* wsML;
 };
 
 template <typename T>
@@ -371,7 +378,7 @@ struct Unit {
     float* sf2;
     bool eye, vzero, valid;
 };
-template <typename TI, int DK, int DV, bool MAP, int NCB>
+template <typename TI, int DK, int DV, bool MAP, int NCB, bool QH = false>
 __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
     const int H = a.H;
     Unit u;
@@ -380,6 +387,21 @@ __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
     u.eye = u.vzero = false;
     u.valid = true;
     if constexpr (MAP && NCB == 2) {
+        if (QH && b >= a.m_blocks) {
+            // the last segment of split sequence spl[kk]: its M (to wsML) and q^; N is not kept
+            const int kk = (b - a.m_blocks) / H;
+            u.h = b - a.m_blocks - kk * H;
+            const int n = a.spl[kk];
+            if (n < 0) {
+                u.valid = false;
+                return u;
+            }
+            u.tb = a.cu[n] + (int64_t)(a.nl[n + 1] - a.nl[n]) * a.seg;
+            u.te = a.cu[n + 1];
+            u.eye = true;
+            u.sf = a.wsML + ((size_t)kk * H + u.h) * DK * DK;
+            return u;
+        }
         const int k = b / H;
         u.h = b - k * H;
         if (k >= a.nl[a.num_seqs]) {
@@ -1054,14 +1076,16 @@ struct CfgW {
 };
 
 // Key side: waves 0 .. NK-1.  Prepares chunk i in iteration i.
-template <int DK, int DV, bool MAP, int NCB, bool ZG>
+template <int DK, int DV, bool MAP, int NCB, bool ZG, bool QH = false>
 __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, int h, int64_t tb, int64_t te,
                                        int nch) {
     typedef CfgW<DK, DV, NCB> P;
     typedef bf16 TI;
     typedef Mma<bf16> M;
     typedef bf16x8 frag;
-    constexpr bool OUT = !MAP;
+    // the q operands and P are formed for outputs: those of the output pass,
+    // and q^ of a transition pass for the backward (QH)
+    constexpr bool OUT = !MAP || QH;
     constexpr int CW = P::CW, KM = P::KM;
     const int H = a.H;
     char* stg = smem + P::OFF_STG;
@@ -1169,7 +1193,7 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                 if constexpr (OUT) qv[tt] = *reinterpret_cast<const bf16x2*>(stg_q + (t0 + tt) * DK + ch);
             }
         }
-        if constexpr (MAP)
+        if constexpr (MAP && !QH)
             if (i >= 1 && kw < 2) inverse_to(reinterpret_cast<frag*>(smem + ((i - 1) & 1) * P::SZ_BUF + P::B_TB));
         if (act) {
             auto group_sum = [&]() {
@@ -1573,13 +1597,14 @@ __device__ __forceinline__ void ws_key_head(const Args<bf16>& a, char* smem, int
 }
 
 // State side: waves NK .. NK+NS-1.  Runs chunk i-1 in iteration i.
-template <int DK, int DV, bool MAP, int NCB, bool HG>
+template <int DK, int DV, bool MAP, int NCB, bool HG, bool QH = false>
 __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw, const Unit& u, int nch) {
     typedef CfgW<DK, DV, NCB> P;
     typedef bf16 TI;
     typedef Mma<bf16> M;
     typedef bf16x8 frag;
-    constexpr bool OUT = !MAP;
+    constexpr bool OUT = !MAP || QH;
+    static_assert(!QH || (MAP && NCB == 2 && DK == DV), "q^ from the M block of a two-block transition pass");
     constexpr int CW = P::CW, KM = P::KM, RT = P::RT;
     const int H = a.H, h = u.h;
     const int64_t tb = u.tb, te = u.te;
@@ -1683,9 +1708,12 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                 // O = Q~ S + P U from the state at the chunk start (bS) and U,
                 // with buffer stores: rows t >= L lie past the extent of the
                 // resource and the hardware drops them, so every lane stores
-                // (no branch, and the count of stores in flight is fixed)
+                // (no branch, and the count of stores in flight is fixed).
+                // QH: the same product of the M block (block 0) is q^ (d_k = d_v,
+                // so its rows have vrow elements too), stored for every segment
+                // (the first segment's is not used; skipping it costs registers).
                 const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
-                    a.o + ((size_t)c0 * H + h) * DV, 0, L * vrow * 2, BUFFER_RSRC_WORD3);
+                    (QH ? a.qh : a.o) + ((size_t)c0 * H + h) * DV, 0, L * vrow * 2, BUFFER_RSRC_WORD3);
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     floatx4 O = zero4();
@@ -1736,20 +1764,24 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
 
 // GMODE 0: per-channel g; 1: per-channel g from bf16 logits (Args::z, gate,
 // gate_param); 2: one g per (token, head) (Args::g is [T, H])
-template <int DK, int DV, bool MAP, int NCB, int GMODE>
+// QH (MAP, NCB = 2, per-channel gates): the transition pass of the
+// backward's time split, which also forms q^ of the segments after the first
+// and takes the split sequences' last segments.
+template <int DK, int DV, bool MAP, int NCB, int GMODE, bool QH = false>
 __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(Args<bf16> a) {
     typedef CfgW<DK, DV, NCB> P;
     static_assert(NCB == 1 || (MAP && DK == DV), "two column blocks only for transitions with d_k = d_v");
+    static_assert(!QH || GMODE == 0, "q^ transition pass: per-channel gates");
     __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
-    const Unit u = resolve_unit<bf16, DK, DV, MAP, NCB>(a, blockIdx.x);
+    const Unit u = resolve_unit<bf16, DK, DV, MAP, NCB, QH>(a, blockIdx.x);
     if (!u.valid) return;
     const int nch = (int)((u.te - u.tb + P::CW - 1) / P::CW);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w < P::NK) {
         if constexpr (GMODE == 2) ws_key_head<DK, DV, MAP, NCB>(a, smem, w, u.h, u.tb, u.te, nch);
-        else ws_key<DK, DV, MAP, NCB, GMODE == 1>(a, smem, w, u.h, u.tb, u.te, nch);
+        else ws_key<DK, DV, MAP, NCB, GMODE == 1, QH>(a, smem, w, u.h, u.tb, u.te, nch);
     } else {
-        ws_state<DK, DV, MAP, NCB, GMODE == 2>(a, smem, w - P::NK, u, nch);
+        ws_state<DK, DV, MAP, NCB, GMODE == 2, QH>(a, smem, w - P::NK, u, nch);
     }
 }
 
@@ -1989,6 +2021,8 @@ Args<TI> make_args(const PrefillLaunch& p) {
     a.gate = p.gate;
     a.gate_param = p.gate_param;
     a.ord = nullptr;
+    a.qh = nullptr;
+    a.wsML = nullptr;
     return a;
 }
 
@@ -2223,6 +2257,27 @@ hipError_t run_maps(const PrefillLaunch& p, hipStream_t s) {
     return e != hipSuccess ? e : run_fold_pass<TI, DK, DV>(p, a, s, nullptr);
 }
 
+// The backward's forward half with q^ (bf16, d_k = d_v, per-channel gates):
+// the table, one transition pass over the non-last segments (slots
+// 0 .. slots-1) and the split sequences' last segments (the `splits` list
+// after them), then the fold from segment 0.
+template <int DK>
+hipError_t run_maps_q(const PrefillLaunch& p, bf16* qh, float* wsML, hipStream_t s) {
+    Args<bf16> a = make_args<bf16>(p);
+    hipError_t e = run_table<bf16, DK, DK>(p, a, s);
+    if (e != hipSuccess) return e;
+    const PrefillWorkspace ws = prefill_workspace_layout(p.T_total, p.num_seqs, p.H, DK, DK, p.seg);
+    a.qh = qh;
+    a.wsML = wsML;
+    a.m_blocks = (int)(ws.slots * p.H);
+    if ((ws.slots + ws.splits) * p.H > 0)
+        hipLaunchKernelGGL((prefill_ws_kernel<DK, DK, true, 2, 0, true>),
+                           dim3((unsigned)((ws.slots + ws.splits) * p.H)), dim3(CfgW<DK, DK, 2>::NT), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    a.m_blocks = 0;
+    return run_fold_pass<bf16, DK, DK>(p, a, s, nullptr);
+}
+
 template <typename TI>
 hipError_t run_maps_t(const PrefillLaunch& p, hipStream_t s) {
     if (p.dk == 128 && p.dv == 128) return run_maps<TI, 128, 128>(p, s);
@@ -2251,6 +2306,14 @@ hipError_t launch_seq_order(const int32_t* cu_seqlens, int32_t num_seqs, int64_t
 hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t s) {
     if ((int64_t)p.num_seqs * p.H == 0 || p.seg <= 0) return hipSuccess;
     return p.bf16 ? run_maps_t<bf16>(p, s) : run_maps_t<float>(p, s);
+}
+
+hipError_t launch_prefill_maps_q(const PrefillLaunch& p, void* qh, float* wsML, hipStream_t s) {
+    if (!p.bf16 || p.dk != p.dv || p.seg <= 0 || p.gate != GATE_LOG || (p.dk != 64 && p.dk != 128))
+        return hipErrorInvalidValue;
+    if ((int64_t)p.num_seqs * p.H == 0) return hipSuccess;
+    return p.dk == 128 ? run_maps_q<128>(p, static_cast<bf16*>(qh), wsML, s)
+                       : run_maps_q<64>(p, static_cast<bf16*>(qh), wsML, s);
 }
 
 }  // namespace gdn

@@ -280,7 +280,10 @@ int32_t gdn_decode_logits(const void* q, const void* k, const void* v, const voi
  * * d_v * (2 for GDN_BF16, 4 for GDN_F32), rounded up to 256; with a time
  * split of segment length L (below), also gdn_prefill's split workspace for
  * segments of L tokens and (T_total / L + num_seqs) * H * d_k * d_v * 4 bytes,
- * each rounded up to 256, and with more than one sequence two int32 tables
+ * for GDN_BF16 with d_k = d_v also min(num_seqs, T_total / (L + 1)) * H * d_k
+ * * d_k * 4 bytes (the last segments' transitions) and T_total * H * d_k * 2
+ * bytes (a bf16 buffer of q^ below), each rounded up to 256, and with more
+ * than one sequence two int32 tables
  * (the order of the sequences, longest first, and their segment counts) of
  * num_seqs and num_seqs + 1 entries; without the split, that order alone when
  * num_seqs * H exceeds 256.  Depends on the arguments and on
@@ -334,9 +337,14 @@ size_t gdn_prefill_backward_workspace_bytes(int64_t T_total, int32_t num_seqs, i
  * sequence longer than L = T_total / (256 / H + 1) tokens is (when L >= 16384),
  * so that one long sequence among short ones does not set the call's time.  The state map
  * of a segment is affine, S_end = M S_start + N, and its adjoint
- * dS_start = M^T dS_end + D.  gdn_prefill's own time split gives M, N and
- * every segment's start state; per-segment sweeps give D and a sequential
- * fold every segment's end gradient; then both sweeps run per segment.
+ * dS_start = M^T dS_end + D, where D, the gradient of the segment's outputs
+ * o_t = (M_t S_start + N_t)^T q_t with respect to its start state, is the sum
+ * over its tokens of q^_t dO_t^T, q^_t = M_t^T q_t (M_t: the transition
+ * through token t).  gdn_prefill's own time split gives M, N and every
+ * segment's start state; for GDN_BF16 with d_k = d_v its transition pass also
+ * forms q^ and one streaming pass D, otherwise per-segment reverse sweeps give
+ * D; a sequential fold gives every segment's end gradient; then both sweeps
+ * run per segment.
  * Same results up to rounding.  GDN_BACKWARD_SEGMENT=L forces the length
  * (rounded up to a multiple of 64), 0 turns the split off; it must not
  * change between the workspace query and the call. */

@@ -278,9 +278,13 @@ def _backward_ws(T, n, H, dk, dv, bf16, seg):
         return ck + (al(n * 4) if n > 1 and n * H > 256 else 0)
     fs = T // seg
     pre = al(fs * H * dk * dk * 4) + al(fs * H * dk * dv * 4) + al((n + 1) * 4) + al(max(min(n, T // (seg + 1)), 1) * 4)
+    # bf16 with d_k = d_v (the reverse maps' offsets from the transition pass): the last
+    # segment's d_k x d_k fp32 transition per split-list entry and head, and the bf16
+    # q^ buffer [T, H, d_k]
+    qmaps = al(min(n, T // (seg + 1)) * H * dk * dk * 4) + al(T * H * dk * 2) if bf16 and dk == dv else 0
     # with more than one sequence, the order table [n] and the segment prefix table [n + 1]
     order = al(n * 4) + al((n + 1) * 4) if n > 1 else 0
-    return ck + al(pre) + al((T // seg + n) * H * dk * dv * 4) + order
+    return ck + al(pre) + al((T // seg + n) * H * dk * dv * 4) + qmaps + order
 
 
 def test_backward_workspace_bytes_split(lib, monkeypatch):
