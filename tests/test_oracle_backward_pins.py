@@ -140,3 +140,25 @@ def test_backward_empty_sequence_passes_the_state_gradient_through():
     WS = rng.standard_normal(c["S0"].shape)
     gr = _grads(c, np.zeros((T, H, dv)), WS)
     np.testing.assert_array_equal(gr["d_initial_state"][0], WS[0])
+
+
+def test_start_state_gradient_is_sum_of_transported_queries():
+    # The outputs of a sequence are affine in its start state: S_t = M_t S_0 + N_t,
+    # with M_t the state reached from S_0 = I with v = 0 (the transition through
+    # token t), so o_t = S_t^T q_t and, with dL/d(final state) = 0,
+    #   dL/dS_0 = sum_t (M_t^T q_t) dO_t^T.
+    # M_t^T q_t is the recurrence's own output from I with v = 0 (a d_k-column
+    # state); the sum is checked against the oracle's reverse recurrence.
+    rng = np.random.default_rng(23)
+    c = _rand_case(rng, [7, 0, 12], H=2, dk=4, dv=3)
+    T, H, dv = c["v"].shape
+    dk = c["k"].shape[2]
+    dO = rng.standard_normal((T, H, dv))
+    gr = oracle.backward(c["q"], c["k"], c["v"], c["g"], c["beta"], c["cu"], dO, initial_state=c["S0"])
+    eye = np.broadcast_to(np.eye(dk), (len(c["cu"]) - 1, H, dk, dk)).copy()
+    qhat, _ = oracle.recurrent(c["q"], c["k"], np.zeros((T, H, dk)), c["g"], c["beta"], c["cu"], initial_state=eye)
+    for n in range(len(c["cu"]) - 1):
+        a, b = c["cu"][n], c["cu"][n + 1]
+        for h in range(H):
+            D = qhat[a:b, h].T @ dO[a:b, h]  # sum_t q^_t dO_t^T, d_k x d_v
+            np.testing.assert_allclose(gr["d_initial_state"][n, h], D, rtol=1e-12, atol=1e-12)
