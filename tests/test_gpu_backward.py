@@ -204,9 +204,11 @@ def test_bf16_rectangular_longer(dk, dv):
 
 @pytest.mark.parametrize("seg,dk,dv,dtype", [(64, 128, 128, torch.bfloat16), (64, 64, 64, torch.float32),
                                              (128, 64, 128, torch.bfloat16), (64, 128, 64, torch.bfloat16),
-                                             (192, 128, 128, torch.float32)])
+                                             (192, 128, 128, torch.float32), (64, 64, 64, torch.bfloat16)])
 def test_split_ragged(monkeypatch, seg, dk, dv, dtype):
-    # empty sequences, sequences of one, two and many segments, ragged last segments
+    # empty sequences, sequences of one, two and many segments, ragged last segments (129 and 130
+    # tokens end in last segments of one and two tokens at seg = 64); bf16 with d_k = d_v takes the
+    # reverse maps' offsets from the transition pass's q^, the other cases from adjoint-only sweeps
     monkeypatch.setenv("GDN_BACKWARD_SEGMENT", str(seg))
     _case([1, 15, 16, 17, 63, 0, 130, 700, 128, 129], 3, dk, dv, dtype, seed=10)
 
@@ -226,6 +228,20 @@ def test_split_units_multiple_of_eight_rectangular(monkeypatch):
 def test_split_no_initial_state_no_final_gradient(monkeypatch):
     monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "64")
     _case([200, 0, 33], 2, 128, 128, torch.bfloat16, init=False, final=False, seed=12)
+
+
+def test_split_matches_unsplit_bf16(monkeypatch):
+    # bf16 with d_k = d_v: the split with q^ against the unsplit call, within the bf16 tolerance
+    x = inputs.make_prefill_inputs([900, 300], 2, 128, 128, dtype=torch.bfloat16, init_state=True, seed=15)
+    d_o, dSf = inputs.make_cotangents(x.T_total, x.num_seqs, 2, 128, 128, dtype=torch.bfloat16, seed=115)
+    to_device(x)
+    d_o, dSf = d_o.cuda(), dSf.cuda()
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "0")
+    a = _run(x, d_o, dSf)
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "128")
+    b = _run(x, d_o, dSf)
+    for name in NAMES:
+        assert_close(name, np64(b[name]), np64(a[name]), TOL[torch.bfloat16])
 
 
 def test_split_matches_unsplit(monkeypatch):
