@@ -399,6 +399,9 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
             }
         }
     }
+    // (gradient kernel, bf16: the checkpoint's copy, issued at the top of the
+    // iteration, has landed in every wave before the value-column steps read it)
+    if constexpr (P::GX && P::STAGE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     return vv;
 }
@@ -760,9 +763,6 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         if (nsub > 0) {
             dma_inputs<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, sb + CB * (nsub - 1), sub_len(nsub - 1), w,
                                                          tid0 & 63);
-            if constexpr (!DONLY)
-                dma_rows<DV * P::ES, DK, P::NW, true>(slot(nsub - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w,
-                                                      tid0 & 63);
         }
     }
     for (int64_t c = nsub - 1; c >= 0; --c) {
@@ -778,6 +778,11 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
         if constexpr (P::STAGE) __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
         lds_barrier();  // ... and every wave's; the previous sub-chunk is done with LDS
+        // bf16: this sub-chunk's checkpoint into the staging area.  It stays there
+        // through the key-channel outputs, which read its rows from LDS; its copy
+        // is waited for at the end of prep.
+        if constexpr (P::STAGE && !DONLY)
+            dma_rows<DV * P::ES, DK, P::NW, true>(ck, (size_t)DV * P::ES, DK, smem + P::ST_C, w, lane);
         if constexpr (!DONLY) flush(r, g);
         const floatx4 vv = prep<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0, L, tid, col0);
         if constexpr (P::STAGE)
@@ -845,10 +850,7 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             for (int rt = 0; rt < P::RT; ++rt) fds[rt] = dS[rt] * *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
             dU = M::mma(lds_perm(sHN + r * P::SK, mm, g), acc_perm<TI>(fds, mm, P::RT), dU);
         }
-        lds_barrier();  // M is ready; every read of the staged checkpoint is done
-        if constexpr (P::STAGE && !DONLY)
-            if (c > 0)
-                dma_rows<DV * P::ES, DK, P::NW, true>(slot(c - 1), (size_t)DV * P::ES, DK, smem + P::ST_C, w, lane);
+        lds_barrier();  // M is ready
         const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
         dU = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sP + 4 * lane)), K::cvt(dOc), dU);
         // dRm = M^T dU, dR = diag(b) dRm = dv
@@ -899,8 +901,8 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         // Contractions over d_v, one pass over the value rows: the token-pair
         // matrices (the same in every wave) and, for each of this wave's
         // key-channel tiles i0 = 16 it, the products with state rows i0 + r (the
-        // checkpoint, from global memory where its copy into LDS left it in the
-        // cache, and F dS).
+        // checkpoint: its staged copy in LDS for bf16, global memory for fp32;
+        // and F dS).
         floatx4 dPT = zero4(), dPa = zero4(), dAa = zero4(), dAT = zero4();
         floatx4 z1[P::TPW], x1[P::TPW], y1[P::TPW];
         float d1[P::TPW];  // sum_j (F dS)[i0 + r][j] S0[i0 + r][j] over this lane's j
@@ -923,7 +925,12 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
                 const int it = w + P::NW * j;
                 if (P::RT % P::NW != 0 && it >= P::RT) break;
                 const int i0 = 16 * it;
-                const frag fs0 = *reinterpret_cast<const frag*>(ck + (size_t)(i0 + r) * DV + mm * P::KSTEP + g * P::KW);
+                frag fs0;
+                if constexpr (P::STAGE)  // the staged copy (16-byte pieces permuted per row)
+                    fs0 = *reinterpret_cast<const frag*>(reinterpret_cast<const char*>(stg_c) +
+                                                         swz_off<DV * P::ES, P::ES>(i0 + r, mm * P::KSTEP + g * P::KW));
+                else
+                    fs0 = *reinterpret_cast<const frag*>(ck + (size_t)(i0 + r) * DV + mm * P::KSTEP + g * P::KW);
                 const frag ffs = lds_nat(sFS + (i0 + r) * P::SV, mm, g);
                 z1[j] = M::mma(fs0, fo, z1[j]);
                 x1[j] = M::mma(fs0, fr, x1[j]);
