@@ -81,6 +81,13 @@ namespace {
 
 using namespace t16;
 
+// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle); with stride 0, stores at or past num_records bytes are
+// dropped.
+constexpr uint32_t kBufWord3 = 0x00020000u;
+typedef unsigned int u32x2b __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4b __attribute__((ext_vector_type(4)));
+
 template <typename TI>
 struct BArgs {
     const TI* q;
@@ -734,23 +741,48 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
     for (int j = 0; j < P::TPW; ++j) o_dq[j] = o_dk[j] = o_dg[j] = zero4();
     size_t o_row0 = 0;
     int o_L = 0;  // 0: nothing pending
+    // The stores go through buffer resources that end at the sub-chunk's last
+    // (token, head) row: the hardware drops rows past it (a shorter last
+    // sub-chunk), so no store needs a branch.
     auto flush = [&](int r, int g) {
         if (o_L == 0) return;
+        const uint32_t rows = (uint32_t)o_L * (uint32_t)H;  // rows o_row0 .. o_row0 + rows - 1 of [T, H]
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(a.dv + o_row0 * DV, 0, rows * DV * P::ES, kBufWord3);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = 4 * g + i;
-            if (t < o_L) a.dv[(o_row0 + (size_t)t * H) * DV + col0 + r] = from_f32<TI>(o_dv[i]);
-            if (w == 0 && r == 0 && t < o_L) a.dbeta[o_row0 + (size_t)t * H] = o_db[i];
+            const uint32_t off = ((uint32_t)(4 * g + i) * H * DV + col0 + r) * P::ES;
+            if constexpr (P::ES == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f32<TI>(o_dv[i])), rv,
+                                                      off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)o_dv[i]), rv, off, 0, 0);
         }
+        if (w == 0 && r == 0) {
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(a.dbeta + o_row0, 0, rows * 4, kBufWord3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)o_db[i]), rb,
+                                                      (uint32_t)(4 * g + i) * H * 4, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t rq =
+            __builtin_amdgcn_make_buffer_rsrc(a.dq + o_row0 * DK, 0, rows * DK * P::ES, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(a.dk + o_row0 * DK, 0, rows * DK * P::ES, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(a.dg + o_row0 * DK, 0, rows * DK * 4, kBufWord3);
 #pragma unroll
         for (int j = 0; j < P::TPW; ++j) {
             const int it = w + P::NW * j;
-            if (it < P::RT && r < o_L) {
-                const size_t off = (o_row0 + (size_t)r * H) * DK + 16 * it + 4 * g;
-                *reinterpret_cast<typename F4::type*>(a.dq + off) = F4::t(o_dq[j]);
-                *reinterpret_cast<typename F4::type*>(a.dk + off) = F4::t(o_dk[j]);
-                *reinterpret_cast<floatx4*>(a.dg + off) = o_dg[j];
+            if (P::RT % P::NW != 0 && it >= P::RT) break;
+            const uint32_t e = (uint32_t)r * H * DK + 16 * it + 4 * g;  // element offset of (token r, channel)
+            if constexpr (P::ES == 2) {
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2b, F4::t(o_dq[j])), rq, e * 2, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2b, F4::t(o_dk[j])), rk, e * 2, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4b, o_dq[j]), rq, e * 4, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4b, o_dk[j]), rk, e * 4, 0, 0);
             }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4b, o_dg[j]), rg, e * 4, 0, 0);
         }
     };
     // sub-chunk c of the segment: checkpoint slot and length
