@@ -653,8 +653,8 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_dpass_kernel(const int32_t
 // j = P-1 down to 1, x <- M_j^T x + D_j, the gradient at the end of segment
 // j - 1, written over D_j (M_{P-1} from wsML slot kk, M_j for j < P-1 from
 // slot nl[n] + j of the forward maps).
-template <int DK, int DV>
-__global__ __launch_bounds__(64 * (DK / 16)) void bwd_fold_rev_q_kernel(const int32_t* cu, const int32_t* nl,
+template <int DK, int DV, int DEPTH = 2>
+__global__ __launch_bounds__(64 * (DK / 16), DEPTH == 1 ? 2 : 1) void bwd_fold_rev_q_kernel(const int32_t* cu, const int32_t* nl,
                                                                         const int32_t* spl, int H, int64_t seg,
                                                                         const float* fM, const float* wsML,
                                                                         const float* dSf, float* wsD) {
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_fold_rev_q_kernel(const in
     const float* x0 = dSf ? dSf + ((size_t)n * H + h) * DK * DV : nullptr;
     // step i takes segment j = P - 1 - i
     auto d_at = [&](int i) { return wsD + ((size_t)(base + P - 1 - i) * H + h) * DK * DV; };
-    fold_columns<DK, DV, true>(
+    fold_columns<DK, DV, true, DEPTH>(
         x0, P - 1, blockIdx.y,
         [&](int i) {
             return i == 0 ? wsML + ((size_t)kk * H + h) * DK * DK : fM + ((size_t)(nl[n] + P - 1 - i) * H + h) * DK * DK;
@@ -1148,8 +1148,13 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         if (pw.splits > 0) {
-            hipLaunchKernelGGL((bwd_fold_rev_q_kernel<DK, DV>), dim3((unsigned)(pw.splits * p.H), DV / 16),
-                               dim3(64 * (DK / 16)), 0, s, a.cu, a.nl, spl, p.H, p.seg, a.fM, wsML, a.dSf, a.wsD);
+            // more workgroups than CUs: the shallower prefetch, two workgroups per CU
+            if (pw.splits * p.H * (DV / 16) > kComputeUnits)
+                hipLaunchKernelGGL((bwd_fold_rev_q_kernel<DK, DV, 1>), dim3((unsigned)(pw.splits * p.H), DV / 16),
+                                   dim3(64 * (DK / 16)), 0, s, a.cu, a.nl, spl, p.H, p.seg, a.fM, wsML, a.dSf, a.wsD);
+            else
+                hipLaunchKernelGGL((bwd_fold_rev_q_kernel<DK, DV, 2>), dim3((unsigned)(pw.splits * p.H), DV / 16),
+                                   dim3(64 * (DK / 16)), 0, s, a.cu, a.nl, spl, p.H, p.seg, a.fM, wsML, a.dSf, a.wsD);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         const unsigned blocks = (unsigned)(ws.slots * p.H);

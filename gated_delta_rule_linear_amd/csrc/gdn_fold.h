@@ -13,8 +13,10 @@
 // memory; M_j^T: four loads that 16 lanes make over 64 contiguous bytes), and
 // its B-operand values are the rows 16b + 4g + s of tile b that lane group g
 // of that tile's accumulator holds.  x passes between the waves through LDS
-// in the accumulator layout (4 KiB per 64 rows); the operands of step j + 2
-// are loaded while step j runs.
+// in the accumulator layout (4 KiB per 64 rows); the operands of step
+// j + DEPTH are loaded while step j runs (DEPTH 2 for one workgroup per CU,
+// DEPTH 1 so that two fit in a CU's registers when there are more
+// workgroups than CUs).
 #pragma once
 
 #include "gdn_mfma.h"
@@ -26,8 +28,9 @@ namespace gdn {
 // (d_k x d_k, row-major) for the j-th step taken; add_at(j): B_j (d_k x d_v,
 // row-major), read and then overwritten with the step's result.  Every
 // thread of the workgroup calls it with the same arguments.
-template <int DK, int DV, bool TRANSPOSED, typename MapAt, typename AddAt>
+template <int DK, int DV, bool TRANSPOSED, int DEPTH = 2, typename MapAt, typename AddAt>
 __device__ __forceinline__ void fold_columns(const float* x0, int steps, int cb, MapAt map_at, AddAt add_at) {
+    static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth");
     constexpr int RT = DK / 16;
     __shared__ floatx4 xs[RT][64];  // xs[t][l] = x[16t + 4g + i][16cb + r], lane l = r + 16g
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
@@ -57,9 +60,9 @@ __device__ __forceinline__ void fold_columns(const float* x0, int steps, int cb,
 #pragma unroll
         for (int i = 0; i < 4; ++i) nn[i] = B[(size_t)i * DV];
     };
-    // step j with its operands in (m, nn); those of step j + 2 go to (m2, n2)
+    // step j with its operands in (m, nn); those of step j + DEPTH go to (m2, n2)
     auto step = [&](int j, const floatx4(&m)[RT], const floatx4& nn, floatx4(&m2)[RT], floatx4& n2) {
-        if (j + 2 < steps) load(j + 2, m2, n2);
+        if (j + DEPTH < steps) load(j + DEPTH, m2, n2);
         __syncthreads();  // xs holds the current x
         floatx4 xb[RT];
 #pragma unroll
@@ -79,13 +82,22 @@ __device__ __forceinline__ void fold_columns(const float* x0, int steps, int cb,
 #pragma unroll
         for (int i = 0; i < 4; ++i) B[(size_t)i * DV] = acc[i];
     };
-    floatx4 m0[RT], m1[RT], m2[RT], n0, n1, n2;
-    if (steps > 0) load(0, m0, n0);
-    if (steps > 1) load(1, m1, n1);
-    for (int j = 0; j < steps; j += 3) {
-        step(j, m0, n0, m2, n2);
-        if (j + 1 < steps) step(j + 1, m1, n1, m0, n0);
-        if (j + 2 < steps) step(j + 2, m2, n2, m1, n1);
+    if constexpr (DEPTH == 2) {
+        floatx4 m0[RT], m1[RT], m2[RT], n0, n1, n2;
+        if (steps > 0) load(0, m0, n0);
+        if (steps > 1) load(1, m1, n1);
+        for (int j = 0; j < steps; j += 3) {
+            step(j, m0, n0, m2, n2);
+            if (j + 1 < steps) step(j + 1, m1, n1, m0, n0);
+            if (j + 2 < steps) step(j + 2, m2, n2, m1, n1);
+        }
+    } else {
+        floatx4 m0[RT], m1[RT], n0, n1;
+        if (steps > 0) load(0, m0, n0);
+        for (int j = 0; j < steps; j += 2) {
+            step(j, m0, n0, m1, n1);
+            if (j + 1 < steps) step(j + 1, m1, n1, m0, n0);
+        }
     }
 }
 

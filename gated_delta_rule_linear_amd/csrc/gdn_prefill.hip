@@ -1937,8 +1937,8 @@ __global__ __launch_bounds__(1024) void seq_order_kernel(const int32_t* __restri
 // written over N_j, from S_start(0) = S0 (or zero) when first = 0, or from
 // S_start(1) already in slot N_0 (segment 0's own end state) when first = 1;
 // fp32 matrix-core steps (fold_columns), one wave per 16-row tile.
-template <int DK, int DV>
-__global__ __launch_bounds__(64 * (DK / 16)) void seg_fold_kernel(const int32_t* __restrict__ nl,
+template <int DK, int DV, int DEPTH = 2>
+__global__ __launch_bounds__(64 * (DK / 16), DEPTH == 1 ? 2 : 1) void seg_fold_kernel(const int32_t* __restrict__ nl,
                                                                   const int32_t* __restrict__ spl, int H,
                                                                   const float* __restrict__ S0,
                                                                   const float* __restrict__ wsM,
@@ -1963,7 +1963,7 @@ __global__ __launch_bounds__(64 * (DK / 16)) void seg_fold_kernel(const int32_t*
     const int k0 = nl[n], cnt = nl[n + 1] - k0;
     if (cnt <= first) return;
     const float* x0 = first ? wsN + ((size_t)k0 * H + h) * DK * DV : S0 ? S0 + (size_t)unit * DK * DV : nullptr;
-    fold_columns<DK, DV, false>(
+    fold_columns<DK, DV, false, DEPTH>(
         x0, cnt - first, cb, [&](int j) { return wsM + ((size_t)(k0 + first + j) * H + h) * DK * DK; },
         [&](int j) { return wsN + ((size_t)(k0 + first + j) * H + h) * DK * DV; });
 }
@@ -2090,8 +2090,14 @@ hipError_t run_fold_pass(const PrefillLaunch& p, Args<TI>& a, hipStream_t s, hip
     hipError_t e = hipSuccess;
     if (before_fold && (e = hipStreamWaitEvent(s, before_fold, 0)) != hipSuccess) return e;
     if (ws.slots > 0 && ws.splits > 0) {
-        hipLaunchKernelGGL((seg_fold_kernel<DK, DV>), dim3((unsigned)(ws.splits * p.H * (DV / 16))),
-                           dim3(64 * (DK / 16)), 0, s, a.nl, a.spl, p.H, p.initial_state, a.wsM, a.wsN, a.map_from);
+        // more workgroups than CUs: the shallower prefetch, two workgroups per CU
+        const int64_t wgs = ws.splits * p.H * (DV / 16);
+        if (wgs > kComputeUnits)
+            hipLaunchKernelGGL((seg_fold_kernel<DK, DV, 1>), dim3((unsigned)wgs), dim3(64 * (DK / 16)), 0, s, a.nl,
+                               a.spl, p.H, p.initial_state, a.wsM, a.wsN, a.map_from);
+        else
+            hipLaunchKernelGGL((seg_fold_kernel<DK, DV, 2>), dim3((unsigned)wgs), dim3(64 * (DK / 16)), 0, s, a.nl,
+                               a.spl, p.H, p.initial_state, a.wsM, a.wsN, a.map_from);
         e = hipGetLastError();
     }
     return e;
