@@ -230,6 +230,13 @@ def test_split_no_initial_state_no_final_gradient(monkeypatch):
     _case([200, 0, 33], 2, 128, 128, torch.bfloat16, init=False, final=False, seed=12)
 
 
+def test_split_many_units_fold(monkeypatch):
+    # 40 split sequences x 2 heads: both folds with more workgroups (640) than compute units,
+    # which prefetch one step ahead, two workgroups per CU
+    monkeypatch.setenv("GDN_BACKWARD_SEGMENT", "128")
+    _case([260 + 7 * i for i in range(40)], 2, 128, 128, torch.bfloat16, seed=16)
+
+
 def test_split_matches_unsplit_bf16(monkeypatch):
     # bf16 with d_k = d_v: the split with q^ against the unsplit call, within the bf16 tolerance
     x = inputs.make_prefill_inputs([900, 300], 2, 128, 128, dtype=torch.bfloat16, init_state=True, seed=15)

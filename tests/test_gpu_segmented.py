@@ -55,6 +55,13 @@ def test_split_units_multiple_of_eight(monkeypatch, dk, dv, dtype):
     _case(monkeypatch, [900, 333], 8, dk, dv, dtype, 128, seed=24)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_split_many_units_fold(monkeypatch, dtype):
+    # 40 split sequences x 2 heads x 8 column blocks = 640 fold workgroups, more than
+    # the 256 compute units: the fold prefetches one step ahead, two workgroups per CU
+    _case(monkeypatch, [260 + 7 * i for i in range(40)], 2, 128, 128, dtype, 128, seed=25)
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
 def test_split_head_dims(monkeypatch, dk, dv):
     _case(monkeypatch, [300, 5, 129], 2, dk, dv, torch.bfloat16, 128, seed=21)
