@@ -654,10 +654,9 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_dpass_kernel(const int32_t
 // j - 1, written over D_j (M_{P-1} from wsML slot kk, M_j for j < P-1 from
 // slot nl[n] + j of the forward maps).
 template <int DK, int DV, int DEPTH = 2>
-__global__ __launch_bounds__(64 * (DK / 16), DEPTH == 1 ? 2 : 1) void bwd_fold_rev_q_kernel(const int32_t* cu, const int32_t* nl,
-                                                                        const int32_t* spl, int H, int64_t seg,
-                                                                        const float* fM, const float* wsML,
-                                                                        const float* dSf, float* wsD) {
+__global__ __launch_bounds__(64 * (DK / 16), DEPTH == 1 ? 2 : 1) void bwd_fold_rev_q_kernel(
+    const int32_t* cu, const int32_t* nl, const int32_t* spl, int H, int64_t seg, const float* fM,
+    const float* wsML, const float* dSf, float* wsD) {
     const int unit = blockIdx.x, kk = unit / H, h = unit - kk * H;
     const int n = spl[kk];
     if (n < 0) return;

@@ -145,11 +145,12 @@ struct Args {
     // workgroup b takes head b % H of sequence ord[b / H] (longest first), or
     // of sequence b / H when ord is null
     const int32_t* ord;
-    // Transition pass for the backward (QH): q^_t = M_t^T q_t of every segment
-    // after the first goes to qh ([T, H, d_k]; M_t: the transition from the
-    // segment's start through token t), and workgroups from m_blocks on take the
-    // last segment of the split sequences in spl, whose M goes to wsML (slot kk
-    // for spl[kk])
+    // Transition pass for the backward (QH): q^_t = M_t^T q_t of the tokens of
+    // every segment it takes goes to qh ([T, H, d_k]; M_t: the transition from
+    // the segment's start through token t; the backward reads those of the
+    // segments after the first), and workgroups from m_blocks on take the last
+    // segment of the split sequences in spl, whose M goes to wsML (slot kk for
+    // spl[kk])
     TI* qh;
     float* wsML;
 };
@@ -1765,8 +1766,8 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
 // GMODE 0: per-channel g; 1: per-channel g from bf16 logits (Args::z, gate,
 // gate_param); 2: one g per (token, head) (Args::g is [T, H])
 // QH (MAP, NCB = 2, per-channel gates): the transition pass of the
-// backward's time split, which also forms q^ of the segments after the first
-// and takes the split sequences' last segments.
+// backward's time split, which also forms q^ and takes the split sequences'
+// last segments.
 template <int DK, int DV, bool MAP, int NCB, int GMODE, bool QH = false>
 __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(Args<bf16> a) {
     typedef CfgW<DK, DV, NCB> P;
@@ -1938,11 +1939,9 @@ __global__ __launch_bounds__(1024) void seq_order_kernel(const int32_t* __restri
 // S_start(1) already in slot N_0 (segment 0's own end state) when first = 1;
 // fp32 matrix-core steps (fold_columns), one wave per 16-row tile.
 template <int DK, int DV, int DEPTH = 2>
-__global__ __launch_bounds__(64 * (DK / 16), DEPTH == 1 ? 2 : 1) void seg_fold_kernel(const int32_t* __restrict__ nl,
-                                                                  const int32_t* __restrict__ spl, int H,
-                                                                  const float* __restrict__ S0,
-                                                                  const float* __restrict__ wsM,
-                                                                  float* __restrict__ wsN, int first) {
+__global__ __launch_bounds__(64 * (DK / 16), DEPTH == 1 ? 2 : 1) void seg_fold_kernel(
+    const int32_t* __restrict__ nl, const int32_t* __restrict__ spl, int H, const float* __restrict__ S0,
+    const float* __restrict__ wsM, float* __restrict__ wsN, int first) {
     // one workgroup per (split sequence, head, 16 columns): workgroup slot
     // `us` = k H + h is head h of the k-th sequence in spl
     constexpr int NCB = DV / 16;
