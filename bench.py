@@ -79,9 +79,9 @@ METRIC = "prefill tokens/s (H=32,d=128,T=64K bf16) + decode HBM GB/s; % of roofl
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published (no sparsity)
 KERNEL_SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_mfma.h", "gdn_device.h", "gdn_api.cpp", "gdn_kernels.h",
-                  "gdn_fold.h"]
+                  "gdn_fold.h", "gdn_segunit.h"]
 BACKWARD_SOURCES = ["gdn_backward.hip", "gdn_backward.h", "gdn_tile16.h", "gdn_mfma.h", "gdn_device.h",
-                    "gdn_api_backward.cpp", "gdn_prefill.hip", "gdn_kernels.h", "gdn_fold.h"]
+                    "gdn_api_backward.cpp", "gdn_prefill.hip", "gdn_kernels.h", "gdn_fold.h", "gdn_segunit.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 BF16_CHUNK = 32  # the bf16 prefill kernel's chunk length (tokens)
@@ -230,6 +230,7 @@ def summarize_pmc(paths):
             gm = re.search(r"prefill_ws_kernelILi\d+ELi\d+ELb[01]ELi\d+ELi(\d)E", n)  # gate mode
             k += {"1": ",logits", "2": ",head gate"}.get(gm.group(1), "") if gm else ""
             k += ",q^" if re.search(r"prefill_ws_kernelILi\d+ELi\d+ELb1ELi2ELi0ELb1E", n) else ""  # backward's maps
+            k += ",checkpoints" if re.search(r"prefill_ws_kernelILi\d+ELi\d+ELb1ELi1ELi0ELb0ELb1E", n) else ""
             k += ">"
         elif k == "bwd_grad_kernel":  # adjoint only or full (template DONLY)
             k += "<adjoint-only>" if re.search(r"ELb1EE", n) else "<full>"
@@ -645,7 +646,8 @@ def main():
                             "kernel": "gdn_prefill_backward call (time split planned for 128 units: "
                                       "seg_table, prefill_ws_kernel<128,128,map,q^>, seg_fold, "
                                       "bwd_dpass_kernel<128,128>, bwd_fold_rev_q_kernel, "
-                                      "bwd_states_kernel<bf16,128,128>, bwd_grad_kernel<bf16,128,128,full>)",
+                                      "prefill_ws_kernel<128,128,map,checkpoints>, "
+                                      "bwd_grad_kernel<bf16,128,128,full>)",
                             "algorithmic_bytes_per_launch": bbytes},
                "mfma": {"flops_per_launch": bflops, "achieved": bflops / (bms / 1e3) / 1e12,
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -38,9 +38,11 @@
 // accumulation for bf16 inputs, fp32 throughout for fp32 inputs).
 //
 // Two sweeps per call, one workgroup per (sequence, head) each:
-//  1. bwd_states_kernel walks the sub-chunks forward and stores every
-//     sub-chunk's start state (a checkpoint, in the input dtype) in the
-//     caller's workspace;
+//  1. a forward sweep stores every sub-chunk's start state (a checkpoint, in
+//     the input dtype) in the caller's workspace: for bf16 the prefill's
+//     warp-specialised kernel in its checkpoint form, which walks 32-token
+//     chunks and stores the state at each chunk's start and after its 16th
+//     token (launch_backward_checkpoints); for fp32 bwd_states_kernel;
 //  2. bwd_grad_kernel walks them backward, carrying dS in registers, and
 //     writes dq, dk, dv, dg, dbeta and the initial state's gradient.
 // The workgroup has d_v / 16 waves; for state-shaped quantities wave w owns
@@ -74,6 +76,7 @@
 
 #include "gdn_backward.h"
 #include "gdn_fold.h"
+#include "gdn_segunit.h"
 #include "gdn_tile16.h"
 
 namespace gdn {
@@ -106,6 +109,7 @@ struct BArgs {
     float* dbeta;
     float* dS0;        // [num_seqs, H, DK, DV] or null (not wanted)
     TI* ck;            // checkpoints: slot (cu[n] / 16 + n + c, h) is the start state of sub-chunk c of sequence n
+                       // (fp32: row-major; bf16: in column blocks of 16, see dma_ck_blocks)
     int H;
     // Time split (seg > 0, a multiple of 64): sequence n is cut into segments of
     // seg tokens.  From the forward pass's split, for segment j < last of
@@ -131,70 +135,11 @@ struct BArgs {
     const int32_t* pfx;
 };
 
-// What one workgroup of a sweep works on: head h of sequence n (tokens
-// [tb, te)), its segment j of P (tokens [sb, se)), slot the segment's slot.
-struct BUnit {
-    int n, h, j, P, slot;
-    int64_t tb, te, sb, se;
-    bool valid;
-};
+// What one workgroup of a sweep works on (gdn_segunit.h).
+typedef SegUnit BUnit;
 template <typename TI>
 __device__ __forceinline__ BUnit bwd_unit(const BArgs<TI>& a, int b) {
-    BUnit u;
-    const int H = a.H;
-    if (a.seg == 0) {
-        const int nb = b / H;
-        u.h = b - nb * H;
-        u.n = a.ord ? a.ord[nb] : nb;
-        u.tb = a.cu[u.n];
-        u.te = a.cu[u.n + 1];
-        u.j = u.slot = 0;
-        u.P = 1;
-        u.sb = u.tb;
-        u.se = u.te;
-        u.valid = true;
-        return u;
-    }
-    const int s = b / H;
-    u.h = b - s * H;
-    if (a.pfx) {
-        // the sequences in the order ord: the last i with pfx[i] <= s
-        if (s >= a.pfx[a.num_seqs]) {
-            u.valid = false;
-            return u;
-        }
-        int lo = 0, hi = a.num_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (a.pfx[mid] <= s) lo = mid;
-            else hi = mid - 1;
-        }
-        u.n = a.ord[lo];
-        u.tb = a.cu[u.n];
-        u.te = a.cu[u.n + 1];
-        u.j = s - a.pfx[lo];
-        u.P = max(1, (int)((u.te - u.tb + a.seg - 1) / a.seg));
-        u.slot = (int)(u.tb / a.seg) + u.n + u.j;
-        u.valid = u.j < u.P;
-    } else {
-        // the last sequence whose first slot is at or before s (first slots increase with n)
-        int lo = 0, hi = a.num_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)a.cu[mid] / a.seg + mid <= s) lo = mid;
-            else hi = mid - 1;
-        }
-        u.n = lo;
-        u.tb = a.cu[lo];
-        u.te = a.cu[lo + 1];
-        u.j = s - (int)(u.tb / a.seg + lo);
-        u.P = max(1, (int)((u.te - u.tb + a.seg - 1) / a.seg));
-        u.slot = s;
-        u.valid = u.j >= 0 && u.j < u.P;
-    }
-    u.sb = u.tb + (int64_t)u.j * a.seg;
-    u.se = u.sb + a.seg < u.te ? u.sb + a.seg : u.te;
-    return u;
+    return seg_unit(a, b);
 }
 
 // LDS layout.  "Natural" matrices are row-major over the contraction index
@@ -258,6 +203,29 @@ struct BCfg {
     static_assert(B_NK % 16 == 0 && B_TK % 16 == 0 && B_NV % 16 == 0 && B_FS % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
+
+// Copy of a bf16 checkpoint into the staging area as DK rows of DV elements,
+// each row's 16-byte pieces permuted as dma_rows<..., SWZ = true> permutes them
+// (piece p of row i to slot p ^ (i mod (DV / 8))).  The checkpoint pass stores
+// a slot in column blocks of 16 (element (i, c) at ((c / 16) DK + i) 16 + c % 16),
+// so piece p of row i is the (p mod 2)-th half of row i of block p / 2; the
+// rows that one copy instruction takes are consecutive, so it reads whole
+// 128-byte lines of each block.
+template <int DK, int DV, int NW>
+__device__ __forceinline__ void dma_ck_blocks(const bf16* ck, char* dst, int w, int lane) {
+    constexpr int LPR = DV * 2 / 16, RPI = 64 / LPR, NI = DK * DV * 2 / 1024;
+#pragma unroll
+    for (int i0 = 0; i0 < NI; i0 += NW) {
+        const int i = i0 + w;
+        if (NI % NW == 0 || i < NI) {
+            const int row = i * RPI + lane / LPR;
+            const int piece = (lane % LPR) ^ (row % LPR);
+            __builtin_amdgcn_global_load_lds(
+                as_global(reinterpret_cast<const char*>(ck) + ((piece >> 1) * DK + row) * 32 + (piece & 1) * 16),
+                as_lds(dst + i * 1024), 16, 0, 0);
+        }
+    }
+}
 
 // Copy of one sub-chunk's raw inputs (t0: first token, L tokens) into the staging area.
 template <typename TI, int DK, int DV, bool FULL, int NWX = DV / 16, bool LITE = false>
@@ -456,7 +424,8 @@ __device__ __forceinline__ floatx4 gram_inverse(char* smem, int lane) {
 // Forward sweep over the sub-chunks of one (sequence, head), or with a time
 // split of one (segment, head), storing every sub-chunk's start state (its
 // checkpoint), from the initial state or from the segment's start state left
-// by the forward fold.
+// by the forward fold.  Used for fp32 inputs (bf16 checkpoints come from the
+// prefill kernel's checkpoint pass).
 template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
     typedef BCfg<TI, DK, DV, false> P;
@@ -813,7 +782,7 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         // through the key-channel outputs, which read its rows from LDS; its copy
         // is waited for at the end of prep.
         if constexpr (P::STAGE && !DONLY)
-            dma_rows<DV * P::ES, DK, P::NW, true>(ck, (size_t)DV * P::ES, DK, smem + P::ST_C, w, lane);
+            dma_ck_blocks<DK, DV, P::NW>(ck, smem + P::ST_C, w, lane);
         if constexpr (!DONLY) flush(r, g);
         const floatx4 vv = prep<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0, L, tid, col0);
         if constexpr (P::STAGE)
@@ -1056,6 +1025,37 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
     }
 }
 
+// The checkpoint sweep over `blocks` units: bf16 on the prefill's kernel in
+// 32-token chunks (launch_backward_checkpoints, the same slots), fp32 on
+// bwd_states_kernel.
+template <typename TI, int DK, int DV>
+hipError_t run_states(const BArgs<TI>& a, int64_t blocks, hipStream_t s) {
+    if constexpr (sizeof(TI) == 2) {
+        CheckpointLaunch c;
+        c.k = a.k;
+        c.v = a.v;
+        c.g = a.g;
+        c.beta = a.beta;
+        c.cu_seqlens = a.cu;
+        c.initial_state = a.S0;
+        c.num_seqs = a.num_seqs;
+        c.H = a.H;
+        c.dk = DK;
+        c.dv = DV;
+        c.seg = a.seg;
+        c.nl = a.nl;
+        c.seg_start = a.fN;
+        c.ord = a.ord;
+        c.pfx = a.pfx;
+        c.ck = a.ck;
+        c.blocks = blocks;
+        return launch_backward_checkpoints(c, s);
+    } else {
+        hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3((unsigned)blocks), dim3(DV * 4), 0, s, a);
+        return hipGetLastError();
+    }
+}
+
 template <typename TI, int DK, int DV>
 hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     BArgs<TI> a;
@@ -1093,8 +1093,7 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
             if (e != hipSuccess) return e;
             a.ord = ord;
         }
-        hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
-        hipError_t e = hipGetLastError();
+        hipError_t e = run_states<TI, DK, DV>(a, blocks, s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
         return hipGetLastError();
@@ -1157,8 +1156,7 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         const unsigned blocks = (unsigned)(ws.slots * p.H);
-        hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = run_states<TI, DK, DV>(a, blocks, s)) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
         return hipGetLastError();
     }
@@ -1178,8 +1176,7 @@ hipError_t run_bwd(const BackwardLaunch& p, hipStream_t s) {
     hipLaunchKernelGGL((bwd_fold_rev_kernel<DK, DV>), dim3((unsigned)((int64_t)p.num_seqs * p.H), DV / 16),
                        dim3(64 * (DK / 16)), 0, s, a.cu, a.nl, p.H, p.seg, a.fM, a.wsD);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_states_kernel<TI, DK, DV>), dim3(blocks), dim3(DV * 4), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = run_states<TI, DK, DV>(a, blocks, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grad_kernel<TI, DK, DV, false>), dim3(blocks), dim3(DV * 4), 0, s, a);
     return hipGetLastError();
 }

@@ -169,6 +169,33 @@ hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t stream);
 // (d_k x d_k fp32 per (split-list entry, head), the sequence in entry kk of the
 // split list).
 hipError_t launch_prefill_maps_q(const PrefillLaunch& p, void* qh, float* wsML, hipStream_t stream);
+// The backward's checkpoint pass on the prefill's bf16 kernel: the state at
+// the start of every 16-token window of each unit (one (sequence, head), or
+// with the time split one (segment, head); the units and their order are those
+// of the backward's sweeps) in bf16 to slot (cu[n] / 16 + n + c, h) of ck
+// ([slot][H][d_k][d_v]; c: the window's index in sequence n).  A unit starts
+// from initial_state (or zero) or, for segment j >= 1 of sequence n, from slot
+// nl[n] + j - 1 of seg_start (launch_prefill_maps' wsN).
+struct CheckpointLaunch {
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const int32_t* cu_seqlens;
+    const float* initial_state;  // may be null
+    int32_t num_seqs;
+    int32_t H;
+    int32_t dk;
+    int32_t dv;
+    int64_t seg;                 // 0: no split
+    const int32_t* nl;           // time split only
+    const float* seg_start;      // time split only
+    const int32_t* ord;          // may be null
+    const int32_t* pfx;          // time split: may be null
+    void* ck;
+    int64_t blocks;              // grid: the backward's sweeps' grid
+};
+hipError_t launch_backward_checkpoints(const CheckpointLaunch& c, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
 // The unit order (see PrefillWorkspace): ord[0 .. num_seqs) receives the
 // sequence indices, longest first, lengths capped at cap tokens when cap > 0;

@@ -59,6 +59,7 @@
 #include "gdn_fold.h"
 #include "gdn_kernels.h"
 #include "gdn_mfma.h"
+#include "gdn_segunit.h"
 
 namespace gdn {
 namespace {
@@ -153,6 +154,14 @@ struct Args {
     // spl[kk])
     TI* qh;
     float* wsML;
+    // Checkpoint pass for the backward (CKP): the units of seg_unit (ord, and
+    // with the split pfx; seg as above), each started from S0 (its sequence's
+    // initial state, or zero) or, for segment j >= 1 of sequence n, from slot
+    // nl[n] + j - 1 of wsN; the start state of the unit's 16-token window c goes
+    // to ck slot (cu[n] / 16 + n + (sb - cu[n]) / 16 + c, h) ([slot][H][d_k * d_v],
+    // in column blocks: element (i, c) at ((c / 16) d_k + i) 16 + c % 16).
+    const int32_t* pfx;
+    TI* ck;
 };
 
 template <typename T>
@@ -230,6 +239,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // are dropped (stores) or return 0 (loads).
 constexpr uint32_t BUFFER_RSRC_WORD3 = 0x00020000u;
 typedef unsigned int u32x2 __attribute__((__vector_size__(8)));
+typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
 
 // x[e] += a * x[e][lane J of this lane's 16-lane row], e = 0..3: four
 // v_fmac_f32 whose first source is read through the DPP row_newbcast
@@ -377,17 +387,29 @@ struct Unit {
     const float* s0;
     float* sf;
     float* sf2;
+    void* ck;  // CKP: the checkpoint slot of the unit's first 16-token window
     bool eye, vzero, valid;
 };
-template <typename TI, int DK, int DV, bool MAP, int NCB, bool QH = false>
+template <typename TI, int DK, int DV, bool MAP, int NCB, bool QH = false, bool CKP = false>
 __device__ __forceinline__ Unit resolve_unit(const Args<TI>& a, int b) {
     const int H = a.H;
     Unit u;
     u.s0 = nullptr;
     u.sf = u.sf2 = nullptr;
+    u.ck = nullptr;
     u.eye = u.vzero = false;
     u.valid = true;
-    if constexpr (MAP && NCB == 2) {
+    if constexpr (CKP) {
+        const SegUnit su = seg_unit(a, b);
+        u.valid = su.valid;
+        if (!su.valid) return u;
+        u.h = su.h;
+        u.tb = su.sb;
+        u.te = su.se;
+        if (su.j == 0) u.s0 = a.S0 ? a.S0 + ((size_t)su.n * H + su.h) * DK * DV : nullptr;
+        else u.s0 = a.wsN + ((size_t)(a.nl[su.n] + su.j - 1) * H + su.h) * DK * DV;
+        u.ck = a.ck + (((size_t)(su.tb >> 4) + su.n + (size_t)((su.sb - su.tb) >> 4)) * H + su.h) * DK * DV;
+    } else if constexpr (MAP && NCB == 2) {
         if (QH && b >= a.m_blocks) {
             // the last segment of split sequence spl[kk]: its M (to wsML) and q^; N is not kept
             const int kk = (b - a.m_blocks) / H;
@@ -1076,8 +1098,18 @@ struct CfgW {
     static_assert(TPL >= 4 && (TPL & (TPL - 1)) == 0, "token groups");
 };
 
+// Slot of (row r, tokens 4g .. 4g+3) inside 16-row tile rt of the checkpoint
+// pass's K_dec_mid operand (16 x 16 A-operand fragments of 64 slots of 4 bf16).
+// The XOR spreads a key wave's store of one token quad over 64 channels across
+// all the LDS banks; a fragment read is still one slot per lane.
+__device__ __forceinline__ int kdm_slot(int rt, int r, int g) { return (16 * g + r) ^ (rt & 1) ^ ((rt & 2) << 3); }
+
 // Key side: waves 0 .. NK-1.  Prepares chunk i in iteration i.
-template <int DK, int DV, bool MAP, int NCB, bool ZG, bool QH = false>
+// CKP (with MAP): the backward's checkpoint pass; besides the transition's
+// operands, K_dec_mid = k e^{G_15 - G} of the first 16 tokens (in the unused
+// q-operand area) and e^{G_15} (in the unused P area), from which the state
+// side forms the state after token 15.
+template <int DK, int DV, bool MAP, int NCB, bool ZG, bool QH = false, bool CKP = false>
 __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, int h, int64_t tb, int64_t te,
                                        int nch) {
     typedef CfgW<DK, DV, NCB> P;
@@ -1247,6 +1279,21 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
             fast = __all(tot[0] >= BUDGET && tot[1] >= BUDGET);
             const floatx2 gam = pow2v(tot);
             if (grp == 0) *reinterpret_cast<floatx2*>(GM + ch) = gam;
+            floatx2 emid = floatx2{0.f, 0.f};  // CKP: e^{G_15}
+            if constexpr (CKP) {
+                emid = pow2v(mid);
+                if (grp == 0) *reinterpret_cast<floatx2*>(reinterpret_cast<float*>(buf + P::B_PO) + ch) = emid;
+            }
+            // CKP: K_dec_mid of tokens t .. t+3 (t < 16, a multiple of 4), channels ch, ch + 1
+            auto store_kdm4 = [&](int t, const floatx2* km) {
+                TI* KDM = reinterpret_cast<TI*>(buf + P::B_QO);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int c = ch + e, rt = c >> 4;
+                    *reinterpret_cast<bf16x4*>(KDM + (rt * 64 + kdm_slot(rt, c & 15, t >> 2)) * 4) =
+                        bf16x4{(bf16)km[0][e], (bf16)km[1][e], (bf16)km[2][e], (bf16)km[3][e]};
+                }
+            };
             // byte offset of (t0 + tt, ch) in the bf16 operand layout: that of
             // (t0, ch) with tt XORed into bits 4.. (t0 is a multiple of TPL, a
             // power of two, and a group stays in one 16-row block)
@@ -1273,7 +1320,7 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
             if (fast) {
 #pragma unroll
                 for (int tq = 0; tq < P::TPL; tq += 4) {
-                    floatx2 kd[4];
+                    floatx2 kd[4], km[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int tt = tq + j, t = t0 + tt;
@@ -1284,19 +1331,23 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                         put(KO, tt, kk * e);
                         put(KH, tt, kh);
                         kd[j] = kh * gam;  // K_dec = k e^(G_L - G)
+                        km[j] = kh * emid;  // K_dec_mid = k e^(G_15 - G), t <= 15
                     }
                     store_kd4(t0 + tq, kd);
+                    if constexpr (CKP)
+                        if (t0 < 16) store_kdm4(t0 + tq, km);
                 }
             } else {
 #pragma unroll
                 for (int tq = 0; tq < P::TPL; tq += 4) {
-                    floatx2 kd[4];
+                    floatx2 kd[4], km[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int tt = tq + j, t = t0 + tt;
                         G = fma2(ld_g(t), LOG2E, G);
                         const floatx2 kk = ld_k(t);
                         const floatx2 e0 = pow2v(G), em = pow2v(G - mid), eim = pow2v(mid - G);
+                        km[j] = kk * eim;  // K_dec_mid = k e^(G_15 - G), t <= 15
                         if constexpr (OUT) {
                             const floatx2 qq = ld_q(t);
                             put(QO, tt, qq * e0);
@@ -1308,6 +1359,8 @@ __device__ __forceinline__ void ws_key(const Args<bf16>& a, char* smem, int kw, 
                         kd[j] = kk * pow2v(tot - G);
                     }
                     store_kd4(t0 + tq, kd);
+                    if constexpr (CKP)
+                        if (t0 < 16) store_kdm4(t0 + tq, km);
                 }
             }
         }
@@ -1598,7 +1651,10 @@ __device__ __forceinline__ void ws_key_head(const Args<bf16>& a, char* smem, int
 }
 
 // State side: waves NK .. NK+NS-1.  Runs chunk i-1 in iteration i.
-template <int DK, int DV, bool MAP, int NCB, bool HG, bool QH = false>
+// CKP: stores the state at the start of each 16-token window of the chunk in
+// bf16 (checkpoints for the backward): the chunk's start state, and the state
+// after token 15, diag(e^{G_15}) S + K_dec_mid^T U_0 (U_0: rows 0 .. 15 of U).
+template <int DK, int DV, bool MAP, int NCB, bool HG, bool QH = false, bool CKP = false>
 __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw, const Unit& u, int nch) {
     typedef CfgW<DK, DV, NCB> P;
     typedef bf16 TI;
@@ -1606,6 +1662,7 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
     typedef bf16x8 frag;
     constexpr bool OUT = !MAP || QH;
     static_assert(!QH || (MAP && NCB == 2 && DK == DV), "q^ from the M block of a two-block transition pass");
+    static_assert(!CKP || (MAP && NCB == 1 && !HG && !QH), "checkpoints: one state block, per-channel gates");
     constexpr int CW = P::CW, KM = P::KM, RT = P::RT;
     const int H = a.H, h = u.h;
     const int64_t tb = u.tb, te = u.te;
@@ -1640,6 +1697,38 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
     };
     if (nch > 0) load_v(0, g0, r0);
 
+    // CKP: a checkpoint slot holds the state in column blocks: the 16 columns of
+    // state wave s are block s, d_k rows of 32 bytes (element (i, c) at
+    // ((c / 16) d_k + i) 16 + c % 16), so each wave's part is one contiguous
+    // 4 KiB.  The wave assembles it in its own LDS area, in the same layout, and
+    // copies it out with 16-byte stores (whole cache lines).
+    char* ckst = smem + P::LDS + sw * DK * 32;
+    // rows of 16-row tile rt from this lane's rows as bf16 pairs (p01: rows 4g,
+    // 4g+1 of column col0 + r; p23: rows 4g+2, 4g+3) into the wave's area.  A
+    // lane and its neighbour r ^ 1 swap one pair (DPP quad_perm [1, 0, 3, 2]),
+    // so each writes two whole 4-byte words: the even lane rows 4g, 4g+1 and
+    // the odd lane rows 4g+2, 4g+3 of columns (r & ~1, r | 1).
+    auto ck_put = [&](int rt, uint32_t p01, uint32_t p23, int r, int g) {
+        const bool odd = (r & 1) != 0;
+        const uint32_t send = odd ? p01 : p23, own = odd ? p23 : p01;
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xf, 0xf, false);
+        const uint32_t lo = odd ? recv : own, hi = odd ? own : recv;
+        char* dst = ckst + (16 * rt + 4 * g + (odd ? 2 : 0)) * 32 + (r & ~1) * 2;
+        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(dst + 32) = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+    };
+    // the wave's assembled block to its place in the slot (LDS operations of a
+    // wave complete in order, so the reads see this wave's writes)
+    auto ck_flush = [&](__amdgpu_buffer_rsrc_t rs, int lane) {
+#pragma unroll
+        for (int k = 0; k < DK * 32 / 1024; ++k) {
+            const uint32_t off = (uint32_t)(k * 1024 + lane * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(ckst + off), rs,
+                                                   (uint32_t)(sw * DK * 32) + off, 0, 0);
+        }
+    };
+    auto pack2 = [](float x, float y) { return __builtin_bit_cast(uint32_t, bf16x2{(bf16)x, (bf16)y}); };
+
     for (int i = 0; i <= nch; ++i) {
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
@@ -1664,6 +1753,13 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
 #pragma unroll
             for (int e = 0; e < 4; ++e) vr[I][e] = vnext[I][e];
         if (i < nch) load_v(i, g, r);
+        // CKP: the slot of the chunk's window w (0, 1); the second one's extent is
+        // zero when the chunk has no second window, so its stores are dropped
+        // (the count of stores per iteration is fixed)
+        auto ck_slot = [&](int w) {
+            TI* p = static_cast<TI*>(u.ck) + (size_t)(2 * (act ? j : 0) + w) * H * DK * DV;
+            return __builtin_amdgcn_make_buffer_rsrc(p, 0, w == 0 || L > 16 ? DK * DV * 2 : 0, BUFFER_RSRC_WORD3);
+        };
 
         // ---- S1: K~ S and the right-hand side beta (V - K~ S)
         frag bS[NCB][KM];
@@ -1674,6 +1770,16 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                 const bool vblock = NCB == 1 || cb == 1;
 #pragma unroll
                 for (int m = 0; m < KM; ++m) bS[cb][m] = acc_perm<TI>(S[cb], m, RT);
+                if constexpr (CKP) {
+                    // bS[m] holds rows 4g .. 4g+3 of tiles 2m and 2m + 1 in bf16
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) {
+                        const u32x4 w = __builtin_bit_cast(u32x4, bS[cb][m]);
+                        ck_put(2 * m, w[0], w[1], r, g);
+                        ck_put(2 * m + 1, w[2], w[3], r, g);
+                    }
+                    ck_flush(ck_slot(0), lane);
+                }
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
                     floatx4 ks = zero4();
@@ -1699,6 +1805,21 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
                 const floatx4 r1 = M::mma(an, acc_perm<TI>(U, 0, 1), R[cb][1]);
                 U[1] = M::mma(l1, acc_perm<TI>(&r1, 0, 1), zero4());
                 bU[cb] = acc_perm<TI>(U, 0, 2);
+                if constexpr (CKP) {
+                    // the state after token 15: U_0 in accumulator layout is the B
+                    // operand of a 16-token product as it is
+                    const TI* KDM = reinterpret_cast<const TI*>(buf + P::B_QO);
+                    const float* GMM = reinterpret_cast<const float*>(buf + P::B_PO);
+                    const bf16x4 bu0 = bf16x4{(bf16)U[0][0], (bf16)U[0][1], (bf16)U[0][2], (bf16)U[0][3]};
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        floatx4 sm = S[cb][rt] * *reinterpret_cast<const floatx4*>(GMM + 16 * rt + 4 * g);
+                        sm = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                            *reinterpret_cast<const bf16x4*>(KDM + (rt * 64 + kdm_slot(rt, r, g)) * 4), bu0, sm, 0, 0, 0);
+                        ck_put(rt, pack2(sm[0], sm[1]), pack2(sm[2], sm[3]), r, g);
+                    }
+                    ck_flush(ck_slot(1), lane);
+                }
                 if constexpr (HG) {
 #pragma unroll
                     for (int I = 0; I < 2; ++I) U[I] *= *reinterpret_cast<const floatx4*>(EG + CW + 16 * I + 4 * g);
@@ -1768,21 +1889,23 @@ __device__ __forceinline__ void ws_state(const Args<bf16>& a, char* smem, int sw
 // QH (MAP, NCB = 2, per-channel gates): the transition pass of the
 // backward's time split, which also forms q^ and takes the split sequences'
 // last segments.
-template <int DK, int DV, bool MAP, int NCB, int GMODE, bool QH = false>
+template <int DK, int DV, bool MAP, int NCB, int GMODE, bool QH = false, bool CKP = false>
 __global__ __launch_bounds__((CfgW<DK, DV, NCB>::NT), 1) void prefill_ws_kernel(Args<bf16> a) {
     typedef CfgW<DK, DV, NCB> P;
     static_assert(NCB == 1 || (MAP && DK == DV), "two column blocks only for transitions with d_k = d_v");
     static_assert(!QH || GMODE == 0, "q^ transition pass: per-channel gates");
-    __shared__ __attribute__((aligned(1024))) char smem[P::LDS];
-    const Unit u = resolve_unit<bf16, DK, DV, MAP, NCB, QH>(a, blockIdx.x);
+    static_assert(!CKP || (MAP && NCB == 1 && GMODE == 0 && !QH), "checkpoint pass");
+    // (CKP: after the layout, each state wave's area for assembling checkpoints)
+    __shared__ __attribute__((aligned(1024))) char smem[P::LDS + (CKP ? P::NS * DK * 32 : 0)];
+    const Unit u = resolve_unit<bf16, DK, DV, MAP, NCB, QH, CKP>(a, blockIdx.x);
     if (!u.valid) return;
     const int nch = (int)((u.te - u.tb + P::CW - 1) / P::CW);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w < P::NK) {
         if constexpr (GMODE == 2) ws_key_head<DK, DV, MAP, NCB>(a, smem, w, u.h, u.tb, u.te, nch);
-        else ws_key<DK, DV, MAP, NCB, GMODE == 1, QH>(a, smem, w, u.h, u.tb, u.te, nch);
+        else ws_key<DK, DV, MAP, NCB, GMODE == 1, QH, CKP>(a, smem, w, u.h, u.tb, u.te, nch);
     } else {
-        ws_state<DK, DV, MAP, NCB, GMODE == 2, QH>(a, smem, w - P::NK, u, nch);
+        ws_state<DK, DV, MAP, NCB, GMODE == 2, QH, CKP>(a, smem, w - P::NK, u, nch);
     }
 }
 
@@ -2022,6 +2145,8 @@ Args<TI> make_args(const PrefillLaunch& p) {
     a.ord = nullptr;
     a.qh = nullptr;
     a.wsML = nullptr;
+    a.pfx = nullptr;
+    a.ck = nullptr;
     return a;
 }
 
@@ -2311,6 +2436,44 @@ hipError_t launch_seq_order(const int32_t* cu_seqlens, int32_t num_seqs, int64_t
 hipError_t launch_prefill_maps(const PrefillLaunch& p, hipStream_t s) {
     if ((int64_t)p.num_seqs * p.H == 0 || p.seg <= 0) return hipSuccess;
     return p.bf16 ? run_maps_t<bf16>(p, s) : run_maps_t<float>(p, s);
+}
+
+namespace {
+
+template <int DK, int DV>
+hipError_t run_checkpoints(const CheckpointLaunch& c, hipStream_t s) {
+    typedef CfgW<DK, DV, 1> P;
+    static_assert(P::LDS + P::NS * DK * 32 <= 160 * 1024, "LDS budget");
+    Args<bf16> a = {};
+    a.k = static_cast<const bf16*>(c.k);
+    a.v = static_cast<const bf16*>(c.v);
+    a.g = c.g;
+    a.beta = c.beta;
+    a.cu = c.cu_seqlens;
+    a.S0 = c.initial_state;
+    a.H = c.H;
+    a.num_seqs = c.num_seqs;
+    a.seg = (int)c.seg;
+    a.nl = c.nl;
+    a.wsN = const_cast<float*>(c.seg_start);
+    a.gate = GATE_LOG;
+    a.ord = c.ord;
+    a.pfx = c.pfx;
+    a.ck = static_cast<bf16*>(c.ck);
+    hipLaunchKernelGGL((prefill_ws_kernel<DK, DV, true, 1, 0, false, true>), dim3((unsigned)c.blocks), dim3(P::NT), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_checkpoints(const CheckpointLaunch& c, hipStream_t s) {
+    if ((c.dk != 64 && c.dk != 128) || (c.dv != 64 && c.dv != 128) || c.seg < 0 || c.seg > INT32_MAX ||
+        c.blocks > UINT32_MAX)
+        return hipErrorInvalidValue;
+    if (c.blocks <= 0) return hipSuccess;
+    if (c.dk == 128) return c.dv == 128 ? run_checkpoints<128, 128>(c, s) : run_checkpoints<128, 64>(c, s);
+    return c.dv == 128 ? run_checkpoints<64, 128>(c, s) : run_checkpoints<64, 64>(c, s);
 }
 
 hipError_t launch_prefill_maps_q(const PrefillLaunch& p, void* qh, float* wsML, hipStream_t s) {
