@@ -204,6 +204,13 @@ struct BCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
+// Element offset of (key channel c, token t) in a transposed [DK][16] operand.
+// The 4-token group of t is XORed with bits 3-4 of c: the stores of one token
+// pair by a wave (64 channel pairs) then spread over 16 LDS banks instead of 4,
+// and a read of 4 tokens of one channel is still one aligned group (a wave's
+// read of 16 channels covers every bank twice, as without the XOR).
+__device__ __forceinline__ int tr_idx(int c, int t) { return c * CB + (t ^ (((c >> 3) & 3) << 2)); }
+
 // Copy of a bf16 checkpoint into the staging area as DK rows of DV elements,
 // each row's 16-byte pieces permuted as dma_rows<..., SWZ = true> permutes them
 // (piece p of row i to slot p ^ (i mod (DV / 8))).  The checkpoint pass stores
@@ -367,10 +374,10 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = c0 + j;
-            *reinterpret_cast<T2*>(sHT + c * CB + 2 * tp) = Two<TI>::t(floatx2{kh[0][j], kh[1][j]});
+            *reinterpret_cast<T2*>(sHT + tr_idx(c, 2 * tp)) = Two<TI>::t(floatx2{kh[0][j], kh[1][j]});
             if constexpr (FULL) {
-                *reinterpret_cast<T2*>(sKT + c * CB + 2 * tp) = Two<TI>::t(floatx2{kt[0][j], kt[1][j]});
-                *reinterpret_cast<T2*>(sQT + c * CB + 2 * tp) = Two<TI>::t(floatx2{qt[0][j], qt[1][j]});
+                *reinterpret_cast<T2*>(sKT + tr_idx(c, 2 * tp)) = Two<TI>::t(floatx2{kt[0][j], kt[1][j]});
+                *reinterpret_cast<T2*>(sQT + tr_idx(c, 2 * tp)) = Two<TI>::t(floatx2{qt[0][j], qt[1][j]});
             }
         }
     }
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
         // S <- gamma S + F (k^T U)
 #pragma unroll
         for (int rt = 0; rt < P::RT; ++rt) {
-            const floatx4 d = K::mma(K::load(sHT + (16 * rt + r) * CB + 4 * g), bu, zero4());
+            const floatx4 d = K::mma(K::load(sHT + tr_idx(16 * rt + r, 4 * g)), bu, zero4());
             const floatx4 gm = *reinterpret_cast<const floatx4*>(sGAM + 16 * rt + 4 * g);
             const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
             S[rt] = gm * S[rt] + ff * d;
@@ -887,8 +894,8 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             const typename K::frag bo = K::cvt(dOc), br2 = K::cvt(ndR);
 #pragma unroll
             for (int rt = 0; rt < P::RT; ++rt) {
-                floatx4 x = K::mma(K::load(sQT + (16 * rt + r) * CB + 4 * g), bo, zero4());
-                x = K::mma(K::load(sKT + (16 * rt + r) * CB + 4 * g), br2, x);
+                floatx4 x = K::mma(K::load(sQT + tr_idx(16 * rt + r, 4 * g)), bo, zero4());
+                x = K::mma(K::load(sKT + tr_idx(16 * rt + r, 4 * g)), br2, x);
                 const floatx4 gm = *reinterpret_cast<const floatx4*>(sGAM + 16 * rt + 4 * g);
                 const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
                 dS[rt] = gm * dS[rt] + em * x;
@@ -979,10 +986,10 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + i0 + 4 * g);
             const float bt = sBETA[r];
             floatx4 Z = em * z1[j], X = -(bt * em) * x1[j];
-            Z = K::mma(K::load(sHT + (i0 + r) * CB + 4 * g), bPT, Z);
-            X = K::mma(K::load(sHT + (i0 + r) * CB + 4 * g), bKKT, X);
-            floatx4 Y = K::mma(K::load(sKT + (i0 + r) * CB + 4 * g), bKKa, y1[j]);
-            Y = K::mma(K::load(sQT + (i0 + r) * CB + 4 * g), bPa, Y);
+            Z = K::mma(K::load(sHT + tr_idx(i0 + r, 4 * g)), bPT, Z);
+            X = K::mma(K::load(sHT + tr_idx(i0 + r, 4 * g)), bKKT, X);
+            floatx4 Y = K::mma(K::load(sKT + tr_idx(i0 + r, 4 * g)), bKKa, y1[j]);
+            Y = K::mma(K::load(sQT + tr_idx(i0 + r, 4 * g)), bPa, Y);
             const floatx4 khat = F4::f(*reinterpret_cast<const typename F4::type*>(sHN + r * P::SK + i0 + 4 * g));
             const floatx4 ktil = F4::f(*reinterpret_cast<const typename F4::type*>(sKN + r * P::SK + i0 + 4 * g));
             const floatx4 qtil = F4::f(*reinterpret_cast<const typename F4::type*>(sQN + r * P::SK + i0 + 4 * g));
