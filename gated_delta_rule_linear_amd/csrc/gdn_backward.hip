@@ -211,6 +211,24 @@ struct BCfg {
 // read of 16 channels covers every bank twice, as without the XOR).
 __device__ __forceinline__ int tr_idx(int c, int t) { return c * CB + (t ^ (((c >> 3) & 3) << 2)); }
 
+// Stores x[i] = X[row0 + 4g + i][col0 + r] (i = 0..3) of this lane into a
+// row-major bf16 LDS matrix with an even row stride ld, as whole 4-byte words:
+// a lane and its neighbour r ^ 1 swap one pair of rows (DPP quad_perm
+// [1, 0, 3, 2]), then the even lane stores rows 4g, 4g+1 and the odd lane rows
+// 4g+2, 4g+3 of columns (r & ~1, r | 1).  (Two lanes storing the two halves of
+// one word conflict in the LDS banks.)
+__device__ __forceinline__ void pair_store(bf16* base, int ld, int row0, int col0, floatx4 x, int r, int g) {
+    const uint32_t p01 = __builtin_bit_cast(uint32_t, bf16x2{(bf16)x[0], (bf16)x[1]});
+    const uint32_t p23 = __builtin_bit_cast(uint32_t, bf16x2{(bf16)x[2], (bf16)x[3]});
+    const bool odd = (r & 1) != 0;
+    const uint32_t send = odd ? p01 : p23, own = odd ? p23 : p01;
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xf, 0xf, false);
+    const uint32_t lo = odd ? recv : own, hi = odd ? own : recv;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(base + (row0 + 4 * g + (odd ? 2 : 0)) * ld + col0 + (r & ~1));
+    dst[0] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    dst[ld / 2] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
 // Copy of a bf16 checkpoint into the staging area as DK rows of DV elements,
 // each row's 16-byte pieces permuted as dma_rows<..., SWZ = true> permutes them
 // (piece p of row i to slot p ^ (i mod (DV / 8))).  The checkpoint pass stores
@@ -875,7 +893,14 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         }
         o_dv = dR;
         // exchange: F dS, U, dRm (natural layouts) for the key-channel products
-        if constexpr (!DONLY) {
+        if constexpr (!DONLY && P::ES == 2) {
+#pragma unroll
+            for (int rt = 0; rt < P::RT; ++rt)
+                pair_store(sFS, P::SV, 16 * rt, col0, *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g) * dS[rt],
+                           r, g);
+            pair_store(sU, P::SV, 0, col0, U, r, g);
+            pair_store(sDR, P::SV, 0, col0, dRm, r, g);
+        } else if constexpr (!DONLY) {
 #pragma unroll
             for (int rt = 0; rt < P::RT; ++rt) {
                 const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
