@@ -670,9 +670,9 @@ __global__ __launch_bounds__(64 * (DK / 16), DEPTH == 1 ? 2 : 1) void bwd_fold_r
 // Reverse sweep over the sub-chunks of one (sequence, head), or with a time
 // split of one (segment, head), last to first, from the gradient of the state
 // at its end: that of the final state, or for a non-last segment the one the
-// reverse fold left.  A sub-chunk's outputs are stored at the start of the next
-// iteration, after its wait for the copies in flight, so that wait does not
-// include them.
+// reverse fold left.  A sub-chunk's outputs are stored in the next iteration,
+// after its waits for the copies in flight (the inputs, then the checkpoint), so
+// those waits do not include them.
 // DONLY (time split, segments after the first): only the state-gradient
 // recursion, from a zero end gradient (the last segment: from dL/d(final
 // state)); its result is written to the segment's slot for the reverse fold.
@@ -808,8 +808,11 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         // is waited for at the end of prep.
         if constexpr (P::STAGE && !DONLY)
             dma_ck_blocks<DK, DV, P::NW>(ck, smem + P::ST_C, w, lane);
-        if constexpr (!DONLY) flush(r, g);
         const floatx4 vv = prep<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0, L, tid, col0);
+        // the previous sub-chunk's outputs, after prep's wait for the checkpoint
+        // (vector-memory counts complete in issue order, so stores issued
+        // before that wait would have been waited for with it)
+        if constexpr (!DONLY) flush(r, g);
         if constexpr (P::STAGE)
             if (c > 0) dma_inputs<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0 - CB, sub_len(c - 1), w, lane);
         floatx4 kk = zero4();
