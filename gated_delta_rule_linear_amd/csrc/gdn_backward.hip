@@ -187,8 +187,10 @@ struct BCfg {
     static constexpr int OFF_MI = OFF_N + 256 * 4;                     // M [16][16]
     static constexpr int OFF_MT = OFF_MI + 256 * 4;                    // M^T [16][16]
     static constexpr int OFF_P = OFF_MT + 256 * 4;                     // P, accumulator layout by lane (FULL)
+    static constexpr bool KE = GX && STAGE;
+    static constexpr int OFF_KE = OFF_P + (FULL ? 256 * 4 : 0);        // k e^G = k~ E natural   (KE)
     // staging (rows packed back to back, as the DMA writes them)
-    static constexpr int OFF_STG = OFF_P + (FULL ? 256 * 4 : 0);
+    static constexpr int OFF_STG = OFF_KE + (KE ? B_NK : 0);
     static constexpr int ST_G = OFF_STG;                               // g [16][DK] fp32
     static constexpr int ST_K = ST_G + CB * DK * 4;                    // k [16][DK]
     static constexpr int ST_Q = ST_K + CB * DK * ES;                   // q [16][DK]   (FULL)
@@ -295,6 +297,7 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
     TI* sKT = reinterpret_cast<TI*>(smem + P::OFF_KT);
     TI* sQT = reinterpret_cast<TI*>(smem + P::OFF_QT);
     TI* sDO = reinterpret_cast<TI*>(smem + P::OFF_DO);
+    TI* sKE = reinterpret_cast<TI*>(smem + P::OFF_KE);
     const float* stg_g = reinterpret_cast<const float*>(smem + P::ST_G);
     const TI* stg_k = reinterpret_cast<const TI*>(smem + P::ST_K);
     const TI* stg_q = reinterpret_cast<const TI*>(smem + P::ST_Q);
@@ -364,6 +367,8 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
         if ((4 * DK) % P::NT != 0 && i >= 4 * DK) break;
         const int cp = i % (DK / 2), tp = i / (DK / 2), c0 = 2 * cp;
         const floatx2 ml = *reinterpret_cast<const floatx2*>(sML + c0);
+        floatx2 em2 = floatx2{0.f, 0.f};
+        if constexpr (P::KE) em2 = *reinterpret_cast<const floatx2*>(sEM + c0);
         floatx2 kt[2], kh[2], qt[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -384,6 +389,7 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
             kh[u] = kk2 * ei;
             *reinterpret_cast<T2*>(sKN + t * P::SK + c0) = Two<TI>::t(kt[u]);
             *reinterpret_cast<T2*>(sHN + t * P::SK + c0) = Two<TI>::t(kh[u]);
+            if constexpr (P::KE) *reinterpret_cast<T2*>(sKE + t * P::SK + c0) = Two<TI>::t(kt[u] * em2);
             if constexpr (FULL) {
                 qt[u] = qq2 * e;
                 *reinterpret_cast<T2*>(sQN + t * P::SK + c0) = Two<TI>::t(qt[u]);
@@ -698,7 +704,6 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
     const float* sML = reinterpret_cast<const float*>(smem + P::OFF_ML);
     const float* sEM = reinterpret_cast<const float*>(smem + P::OFF_EM);
     const float* sFF = reinterpret_cast<const float*>(smem + P::OFF_FF);
-    const float* sGAM = reinterpret_cast<const float*>(smem + P::OFF_GAM);
     float* sDG15 = reinterpret_cast<float*>(smem + P::OFF_DG15);
     const float* sBETA = reinterpret_cast<const float*>(smem + P::OFF_BETA);
     float* sDB = reinterpret_cast<float*>(smem + P::OFF_DB);
@@ -716,8 +721,11 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
     const float* sMT = reinterpret_cast<const float*>(smem + P::OFF_MT);
     float* sP = reinterpret_cast<float*>(smem + P::OFF_P);
     const TI* stg_c = reinterpret_cast<const TI*>(smem + P::ST_C);
+    const TI* sKE = reinterpret_cast<const TI*>(smem + P::OFF_KE);
 
-    // dS = dL/d(state at the end of the current sub-chunk), own columns
+    // dS = dL/d(state at the end of the current sub-chunk), own columns.  Inside
+    // an iteration it holds F dS from the operand preparation on, and the dS
+    // update leaves dS of the sub-chunk before: gamma dS + E x = E (F dS + x).
     floatx4 dS[P::RT];
     const float* dsf;
     if (u.j == u.P - 1) dsf = a.dSf ? a.dSf + ((size_t)n * H + h) * DK * DV : nullptr;
@@ -829,34 +837,36 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             for (int i = 0; i < 4; ++i) Pa[i] = r <= 4 * g + i ? Pa[i] : 0.f;
             *reinterpret_cast<floatx4*>(sP + 4 * lane) = Pa;
         }
-        // R = V - k~ (E S0), S0 from the checkpoint
+        // R = V - k~ (E S0), S0 from the checkpoint: the B operand's element e of
+        // step mm is S0[k][col0 + r] with k in the permuted order.  bf16: as the
+        // staged copy holds it (k = 32 mm + 16 (e / 4) + 4g + e % 4), with E moved
+        // to the other operand, k~ E = k e^G; fp32: E S0 from global memory
+        // (k = 16 (mm / 4) + 4g + mm % 4).
         floatx4 acc = zero4();
         if constexpr (!DONLY) {
 #pragma unroll(P::UNR)
             for (int mm = 0; mm < P::KM; ++mm) {
-                // only the accumulator tiles this step reads are loaded (bf16: tiles 2mm, 2mm + 1; fp32: tile mm / 4)
-                floatx4 es[P::RT];
+                frag fb;
+                if constexpr (P::KE) {
+                    const char* cb = reinterpret_cast<const char*>(stg_c);
+                    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+                    u16x2 pr[P::KW / 2];
 #pragma unroll
-                for (int rt = 0; rt < P::RT; ++rt) es[rt] = zero4();
-#pragma unroll
-                for (int rt = 0; rt < P::RT; ++rt) {
-                    const bool used = P::KW == 8 ? (rt >> 1) == mm : (rt == (mm >> 2));
-                    if (used) {
-                        const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = 16 * rt + 4 * g + i;
-                            float s;
-                            if constexpr (P::STAGE)
-                                s = to_f32(*reinterpret_cast<const TI*>(reinterpret_cast<const char*>(stg_c) +
-                                                                         swz_off<DV * P::ES, P::ES>(row, col0 + r)));
-                            else
-                                s = to_f32(ck[row * DV + col0 + r]);
-                            es[rt][i] = em[i] * s;
-                        }
+                    for (int e = 0; e < P::KW; e += 2) {
+                        const int row = 32 * mm + 16 * (e >> 2) + 4 * g + (e & 3);
+                        const unsigned short lo =
+                            *reinterpret_cast<const unsigned short*>(cb + swz_off<DV * P::ES, P::ES>(row, col0 + r));
+                        const unsigned short hi =
+                            *reinterpret_cast<const unsigned short*>(cb + swz_off<DV * P::ES, P::ES>(row + 1, col0 + r));
+                        pr[e / 2] = u16x2{lo, hi};
                     }
+                    fb = __builtin_bit_cast(frag, pr);
+                    acc = M::mma(lds_perm(sKE + r * P::SK, mm, g), fb, acc);
+                } else {
+                    const int row = 16 * (mm >> 2) + 4 * g + (mm & 3);
+                    fb = sEM[row] * to_f32(ck[row * DV + col0 + r]);
+                    acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), fb, acc);
                 }
-                acc = M::mma(lds_perm(sKN + r * P::SK, mm, g), acc_perm<TI>(es, mm, P::RT), acc);
             }
         }
         floatx4 R, br;
@@ -869,15 +879,13 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         floatx4 dOc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dOc[i] = to_f32(sDO[(4 * g + i) * P::SV + col0 + r]);
+        // dS -> F dS
+#pragma unroll
+        for (int rt = 0; rt < P::RT; ++rt) dS[rt] = dS[rt] * *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
         // dU = k^ (F dS) + P^T dO (the second term once P is shared)
         floatx4 dU = zero4();
 #pragma unroll(P::UNR)
-        for (int mm = 0; mm < P::KM; ++mm) {
-            floatx4 fds[P::RT];
-#pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt) fds[rt] = dS[rt] * *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
-            dU = M::mma(lds_perm(sHN + r * P::SK, mm, g), acc_perm<TI>(fds, mm, P::RT), dU);
-        }
+        for (int mm = 0; mm < P::KM; ++mm) dU = M::mma(lds_perm(sHN + r * P::SK, mm, g), acc_perm<TI>(dS, mm, P::RT), dU);
         lds_barrier();  // M is ready
         const floatx4 U = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sMI + r * 16 + 4 * g)), K::cvt(br), zero4());
         dU = K::mma(K::cvt(*reinterpret_cast<const floatx4*>(sP + 4 * lane)), K::cvt(dOc), dU);
@@ -898,35 +906,28 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         // exchange: F dS, U, dRm (natural layouts) for the key-channel products
         if constexpr (!DONLY && P::ES == 2) {
 #pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt)
-                pair_store(sFS, P::SV, 16 * rt, col0, *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g) * dS[rt],
-                           r, g);
+            for (int rt = 0; rt < P::RT; ++rt) pair_store(sFS, P::SV, 16 * rt, col0, dS[rt], r, g);
             pair_store(sU, P::SV, 0, col0, U, r, g);
             pair_store(sDR, P::SV, 0, col0, dRm, r, g);
         } else if constexpr (!DONLY) {
 #pragma unroll
-            for (int rt = 0; rt < P::RT; ++rt) {
-                const floatx4 ff = *reinterpret_cast<const floatx4*>(sFF + 16 * rt + 4 * g);
+            for (int rt = 0; rt < P::RT; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sFS[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(ff[i] * dS[rt][i]);
-            }
+                for (int i = 0; i < 4; ++i) sFS[(16 * rt + 4 * g + i) * P::SV + col0 + r] = from_f32<TI>(dS[rt][i]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sU[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(U[i]);
                 sDR[(4 * g + i) * P::SV + col0 + r] = from_f32<TI>(dRm[i]);
             }
         }
-        // dS <- gamma dS + E (q~^T dO - k~^T dR)
+        // dS <- gamma dS + E (q~^T dO - k~^T dR) = E (F dS + q~^T dO - k~^T dR)
         {
             const typename K::frag bo = K::cvt(dOc), br2 = K::cvt(ndR);
 #pragma unroll
             for (int rt = 0; rt < P::RT; ++rt) {
-                floatx4 x = K::mma(K::load(sQT + tr_idx(16 * rt + r, 4 * g)), bo, zero4());
+                floatx4 x = K::mma(K::load(sQT + tr_idx(16 * rt + r, 4 * g)), bo, dS[rt]);
                 x = K::mma(K::load(sKT + tr_idx(16 * rt + r, 4 * g)), br2, x);
-                const floatx4 gm = *reinterpret_cast<const floatx4*>(sGAM + 16 * rt + 4 * g);
-                const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g);
-                dS[rt] = gm * dS[rt] + em * x;
+                dS[rt] = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g) * x;
             }
         }
         if constexpr (DONLY) continue;
@@ -940,12 +941,10 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         // and F dS).
         floatx4 dPT = zero4(), dPa = zero4(), dAa = zero4(), dAT = zero4();
         floatx4 z1[P::TPW], x1[P::TPW], y1[P::TPW];
-        float d1[P::TPW];  // sum_j (F dS)[i0 + r][j] S0[i0 + r][j] over this lane's j
+        // (F dS) S0^T over the tile's rows: its diagonal is rowsum((F dS) * S0)
+        floatx4 d1[P::TPW];
 #pragma unroll
-        for (int j = 0; j < P::TPW; ++j) {
-            z1[j] = x1[j] = y1[j] = zero4();
-            d1[j] = 0.f;
-        }
+        for (int j = 0; j < P::TPW; ++j) z1[j] = x1[j] = y1[j] = d1[j] = zero4();
 #pragma unroll(P::UNR4)
         for (int mm = 0; mm < P::KV; ++mm) {
             const frag fo = lds_nat(sDO + r * P::SV, mm, g);
@@ -970,12 +969,7 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
                 z1[j] = M::mma(fs0, fo, z1[j]);
                 x1[j] = M::mma(fs0, fr, x1[j]);
                 y1[j] = M::mma(ffs, fu, y1[j]);
-                if constexpr (P::KW == 1) {
-                    d1[j] += (float)fs0 * (float)ffs;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < P::KW; ++e) d1[j] += (float)fs0[e] * (float)ffs[e];
-                }
+                d1[j] = M::mma(ffs, fs0, d1[j]);
             }
         }
         floatx4 dKKa, dKKT;
@@ -1006,10 +1000,12 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             const int it = w + P::NW * j;
             if (P::RT % P::NW != 0 && it >= P::RT) break;
             const int i0 = 16 * it;
-            float dd = d1[j];
-            dd += __shfl_xor(dd, 16);
-            dd += __shfl_xor(dd, 32);
-            if (g == 0) sDG15[i0 + r] = dd * sEM[i0 + r];
+            // diagonal element (r, r) sits in lane r of lane group r / 4, entry r % 4
+            if (g == (r >> 2)) {
+                const int e = r & 3;
+                const float dd = e == 0 ? d1[j][0] : e == 1 ? d1[j][1] : e == 2 ? d1[j][2] : d1[j][3];
+                sDG15[i0 + r] = dd * sEM[i0 + r];
+            }
             // lane r + 16g: key channel i = i0 + 4g + e, token t = r
             const floatx4 em = *reinterpret_cast<const floatx4*>(sEM + i0 + 4 * g);
             const float bt = sBETA[r];
