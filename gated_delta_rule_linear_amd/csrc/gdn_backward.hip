@@ -220,8 +220,7 @@ __device__ __forceinline__ int tr_idx(int c, int t) { return c * CB + (t ^ (((c 
 // 4g+2, 4g+3 of columns (r & ~1, r | 1).  (Two lanes storing the two halves of
 // one word conflict in the LDS banks.)
 __device__ __forceinline__ void pair_store(bf16* base, int ld, int row0, int col0, floatx4 x, int r, int g) {
-    const uint32_t p01 = __builtin_bit_cast(uint32_t, bf16x2{(bf16)x[0], (bf16)x[1]});
-    const uint32_t p23 = __builtin_bit_cast(uint32_t, bf16x2{(bf16)x[2], (bf16)x[3]});
+    const uint32_t p01 = pk_bf16(x[0], x[1]), p23 = pk_bf16(x[2], x[3]);
     const bool odd = (r & 1) != 0;
     const uint32_t send = odd ? p01 : p23, own = odd ? p23 : p01;
     const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xf, 0xf, false);
@@ -844,23 +843,27 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         // (k = 16 (mm / 4) + 4g + mm % 4).
         floatx4 acc = zero4();
         if constexpr (!DONLY) {
+            // bf16: byte address of (row 4g + i, column col0 + r) in the staged
+            // copy (swz_off), i = 0..3; rows 16 past it are 16 row strides
+            // further (a row's swizzle depends on the row mod 16 only), an
+            // offset the loads take as an immediate
+            const char* cbi[4];
+            if constexpr (P::KE) {
+                constexpr int LPR = DV * P::ES / 16, PER = 16 / P::ES;
+                const int c = col0 + r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    cbi[i] = reinterpret_cast<const char*>(stg_c) + (4 * g + i) * (DV * P::ES) +
+                             ((c / PER) ^ ((4 * g + i) % LPR)) * 16 + (c % PER) * P::ES;
+            }
 #pragma unroll(P::UNR)
             for (int mm = 0; mm < P::KM; ++mm) {
                 frag fb;
                 if constexpr (P::KE) {
-                    const char* cb = reinterpret_cast<const char*>(stg_c);
-                    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-                    u16x2 pr[P::KW / 2];
+                    static_assert(DV * P::ES / 16 == 16 || DV * P::ES / 16 == 8, "row swizzle period divides 16");
 #pragma unroll
-                    for (int e = 0; e < P::KW; e += 2) {
-                        const int row = 32 * mm + 16 * (e >> 2) + 4 * g + (e & 3);
-                        const unsigned short lo =
-                            *reinterpret_cast<const unsigned short*>(cb + swz_off<DV * P::ES, P::ES>(row, col0 + r));
-                        const unsigned short hi =
-                            *reinterpret_cast<const unsigned short*>(cb + swz_off<DV * P::ES, P::ES>(row + 1, col0 + r));
-                        pr[e / 2] = u16x2{lo, hi};
-                    }
-                    fb = __builtin_bit_cast(frag, pr);
+                    for (int e = 0; e < P::KW; ++e)
+                        fb[e] = *reinterpret_cast<const TI*>(cbi[e & 3] + (32 * mm + 16 * (e >> 2)) * (DV * P::ES));
                     acc = M::mma(lds_perm(sKE + r * P::SK, mm, g), fb, acc);
                 } else {
                     const int row = 16 * (mm >> 2) + 4 * g + (mm & 3);

@@ -14,6 +14,15 @@ namespace t16 {
 constexpr int CB = 16;                           // tokens per sub-chunk
 constexpr float LOG2E_B = 1.4426950408889634f;   // G is carried in log2 units
 
+// Two fp32 values rounded to bf16 (to nearest even) in one 32-bit word, the
+// first in the low half: one v_cvt_pk_bf16_f32.  (A bf16 vector built element
+// by element that feeds a 16x16x16 matrix-core operand is compiled as single
+// conversions joined by permutes.)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
+}
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
 // Contractions over the 16 tokens of a sub-chunk.  Lane r + 16g supplies
 // A[r][4g .. 4g+3] and B[4g .. 4g+3][r]: the register layout of a 16 x 16
 // accumulator (lane r + 16g holds C[4g + i][r]) is such a B operand as it is,
@@ -23,7 +32,9 @@ struct K16;
 template <>
 struct K16<bf16> {
     typedef bf16x4 frag;
-    __device__ __forceinline__ static frag cvt(floatx4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+    __device__ __forceinline__ static frag cvt(floatx4 x) {
+        return __builtin_bit_cast(bf16x4, u32x2v{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])});
+    }
     __device__ __forceinline__ static frag load(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
     __device__ __forceinline__ static floatx4 mma(frag a, frag b, floatx4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -50,7 +61,7 @@ template <>
 struct Two<bf16> {
     typedef bf16x2 type;
     __device__ __forceinline__ static floatx2 f(bf16x2 x) { return floatx2{(float)x[0], (float)x[1]}; }
-    __device__ __forceinline__ static bf16x2 t(floatx2 x) { return bf16x2{(bf16)x[0], (bf16)x[1]}; }
+    __device__ __forceinline__ static bf16x2 t(floatx2 x) { return __builtin_bit_cast(bf16x2, pk_bf16(x[0], x[1])); }
 };
 template <>
 struct Two<float> {
@@ -64,7 +75,9 @@ template <>
 struct Four<bf16> {
     typedef bf16x4 type;
     __device__ __forceinline__ static floatx4 f(bf16x4 x) { return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
-    __device__ __forceinline__ static bf16x4 t(floatx4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+    __device__ __forceinline__ static bf16x4 t(floatx4 x) {
+        return __builtin_bit_cast(bf16x4, u32x2v{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])});
+    }
 };
 template <>
 struct Four<float> {
