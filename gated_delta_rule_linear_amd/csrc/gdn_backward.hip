@@ -161,7 +161,7 @@ struct BCfg {
     static constexpr int RT = DK / 16;                      // 16-row tiles of d_k
     static constexpr int TPW = (RT + NW - 1) / NW;          // key-channel tiles per wave
     static constexpr int UNR = KW == 8 ? 8 : 4;             // unroll of the contraction loops
-    static constexpr int UNR4 = KW == 8 ? 2 : 4;            // ... of the key-channel outputs' pass over d_v
+    static constexpr int UNR4 = KW == 8 ? 4 : 4;            // ... of the key-channel outputs' pass over d_v
     static constexpr int SK = DK + 16 / ES, SV = DV + 16 / ES;
     static constexpr int B_NK = CB * SK * ES, B_TK = DK * CB * ES, B_NV = CB * SV * ES, B_FS = DK * SV * ES;
     static constexpr int OFF_KN = 0;                                   // k~ natural [16][SK]
@@ -307,6 +307,40 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
     auto clampt = [&](int t) { return t < L ? t : L - 1; };
 
     // 1. cumulative log-decay of each key channel (rows past L count as g = 0)
+    if constexpr (P::STAGE && P::NT >= 4 * DK) {
+        // four lanes per channel, one per group of four tokens: wave w takes
+        // channels 16w + r (r = lane mod 16), its lane group q tokens 4q .. 4q+3.
+        // Each lane writes the sums over its group's prefix, then reads the four
+        // group totals (written by lanes of the same wave: LDS operations of a
+        // wave complete in order) and adds the totals before its group.
+        if (tid < 4 * DK) {
+            const int ch = 16 * (tid >> 6) + (tid & 15), qd = (tid >> 4) & 3;
+            float Gq[4], acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * qd + i;
+                acc = __builtin_fmaf(t < L ? stg_g[t * DK + ch] : 0.f, LOG2E_B, acc);
+                Gq[i] = acc;
+            }
+            sG[(4 * qd + 3) * DK + ch] = acc;
+            asm volatile("" ::: "memory");
+            float tot[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tot[q] = sG[(4 * q + 3) * DK + ch];
+            asm volatile("" ::: "memory");
+            const float off = (qd > 0 ? tot[0] : 0.f) + (qd > 1 ? tot[1] : 0.f) + (qd > 2 ? tot[2] : 0.f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sG[(4 * qd + i) * DK + ch] = Gq[i] + off;
+            if (qd == 0) {
+                const float m = tot[0] + tot[1], G = m + tot[2] + tot[3];
+                sML[ch] = m;
+                sEM[ch] = __builtin_amdgcn_exp2f(m);
+                sFF[ch] = __builtin_amdgcn_exp2f(G - m);
+                sGAM[ch] = __builtin_amdgcn_exp2f(G);
+            }
+        }
+        if (tid < CB) sBETA[tid] = tid < L ? stg_b[tid] : 0.f;
+    } else {
     if (tid < DK) {
         float x[CB];
 #pragma unroll
@@ -332,6 +366,7 @@ __device__ __forceinline__ floatx4 prep(const BArgs<TI>& a, char* smem, int h, i
         if constexpr (P::STAGE) b = stg_b[t];
         else b = a.beta[row0 + (size_t)clampt(t) * H];
         sBETA[t] = t < L ? b : 0.f;
+    }
     }
     if constexpr (FULL) {
         // dO rows into the padded layout (16-byte pieces; rows past L are zero)
