@@ -189,8 +189,13 @@ struct BCfg {
     static constexpr int OFF_P = OFF_MT + 256 * 4;                     // P, accumulator layout by lane (FULL)
     static constexpr bool KE = GX && STAGE;
     static constexpr int OFF_KE = OFF_P + (FULL ? 256 * 4 : 0);        // k e^G = k~ E natural   (KE)
+    // dq, dk of a sub-chunk [16][DK] in the input dtype, rows padded by 16 bytes (KE): the
+    // key-channel tiles of every wave, stored to HBM as whole rows
+    static constexpr int SO = DK * ES + 16;
+    static constexpr int OFF_OQ = OFF_KE + (KE ? B_NK : 0);
+    static constexpr int OFF_OK = OFF_OQ + (KE ? CB * SO : 0);
     // staging (rows packed back to back, as the DMA writes them)
-    static constexpr int OFF_STG = OFF_KE + (KE ? B_NK : 0);
+    static constexpr int OFF_STG = OFF_OK + (KE ? CB * SO : 0);
     static constexpr int ST_G = OFF_STG;                               // g [16][DK] fp32
     static constexpr int ST_K = ST_G + CB * DK * 4;                    // k [16][DK]
     static constexpr int ST_Q = ST_K + CB * DK * ES;                   // q [16][DK]   (FULL)
@@ -805,12 +810,31 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc(a.dk + o_row0 * DK, 0, rows * DK * P::ES, kBufWord3);
         const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(a.dg + o_row0 * DK, 0, rows * DK * 4, kBufWord3);
+        if constexpr (P::KE) {
+            // dq and dk from their staged rows: 16-byte pieces, 16 lanes per 256-byte
+            // row, so each store covers whole cache lines (waves of the first half
+            // take dq, the others dk, at d = 128)
+            constexpr int PR = DK * P::ES / 16, NPC = CB * PR;
+            static_assert(NPC % 64 == 0, "a wave's pieces lie in one matrix");
+#pragma unroll
+            for (int p0 = 0; p0 < 2 * NPC; p0 += P::NT) {
+                const int pw = p0 + 64 * w;  // the wave's first piece (uniform)
+                if ((2 * NPC) % P::NT == 0 || pw < 2 * NPC) {
+                    const int mk = pw / NPC, q = pw % NPC + 16 * g + r, row = q / PR, cp = q % PR;
+                    const u32x4b x =
+                        *reinterpret_cast<const u32x4b*>(smem + (mk ? P::OFF_OK : P::OFF_OQ) + row * P::SO + cp * 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(x, mk ? rk : rq, (uint32_t)row * H * DK * P::ES + cp * 16,
+                                                           0, 0);
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < P::TPW; ++j) {
             const int it = w + P::NW * j;
             if (P::RT % P::NW != 0 && it >= P::RT) break;
             const uint32_t e = (uint32_t)r * H * DK + 16 * it + 4 * g;  // element offset of (token r, channel)
-            if constexpr (P::ES == 2) {
+            if constexpr (P::KE) {
+            } else if constexpr (P::ES == 2) {
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2b, F4::t(o_dq[j])), rq, e * 2, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2b, F4::t(o_dk[j])), rk, e * 2, 0, 0);
             } else {
@@ -1058,8 +1082,15 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             const floatx4 Gl = *reinterpret_cast<const floatx4*>(sG + r * DK + i0 + 4 * g);
             const floatx4 ml = *reinterpret_cast<const floatx4*>(sML + i0 + 4 * g);
             const floatx4 ef = exp2v(Gl - ml), eb = exp2v(ml - Gl);
-            o_dq[j] = ef * Z;
-            o_dk[j] = ef * X + eb * Y;
+            if constexpr (P::KE) {
+                // lane r + 16g: token r, channels i0 + 4g .. i0 + 4g + 3
+                char* rowq = smem + P::OFF_OQ + r * P::SO + (i0 + 4 * g) * P::ES;
+                *reinterpret_cast<u32x2b*>(rowq) = __builtin_bit_cast(u32x2b, F4::t(ef * Z));
+                *reinterpret_cast<u32x2b*>(rowq + (P::OFF_OK - P::OFF_OQ)) = __builtin_bit_cast(u32x2b, F4::t(ef * X + eb * Y));
+            } else {
+                o_dq[j] = ef * Z;
+                o_dk[j] = ef * X + eb * Y;
+            }
             floatx4 dG = qtil * Z + ktil * X - khat * Y;
             floatx4 d2;
 #pragma unroll
@@ -1084,6 +1115,7 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * ge + i) * DV + col0 + re] = dS[rt][i];
         return;
     }
+    if constexpr (P::KE) lds_barrier();  // every wave's staged dq, dk rows of the last sub-chunk
     flush(r0, g0);
     if (u.j == 0 && a.dS0) {
         float* dst = a.dS0 + ((size_t)n * H + h) * DK * DV;
