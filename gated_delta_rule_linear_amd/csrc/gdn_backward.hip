@@ -878,10 +878,10 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         if constexpr (P::STAGE && !DONLY)
             dma_ck_blocks<DK, DV, P::NW>(ck, smem + P::ST_C, w, tid0 & 63);
         const floatx4 vv = prep<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0, L, tid, col0);
-        // the previous sub-chunk's outputs, after prep's wait for the checkpoint
-        // (vector-memory counts complete in issue order, so stores issued
-        // before that wait would have been waited for with it)
-        if constexpr (!DONLY) flush(r0, g0);
+        // the next sub-chunk's inputs, after prep's wait for the checkpoint
+        // (vector-memory counts complete in issue order, so anything issued
+        // before that wait would have been waited for with it); the previous
+        // sub-chunk's outputs are stored later, in the value-column steps
         if constexpr (P::STAGE)
             if (c > 0) dma_inputs<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0 - CB, sub_len(c - 1), w, tid0 & 63);
         floatx4 kk = zero4();
@@ -967,6 +967,7 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
                 if (r == 0) sDB[w * CB + t] = p;
             }
         }
+        if constexpr (!DONLY) flush(r0, g0);  // the previous sub-chunk's outputs, before o_dv is replaced
         o_dv = dR;
         // exchange: F dS, U, dRm (natural layouts) for the key-channel products
         if constexpr (!DONLY && P::ES == 2) {
