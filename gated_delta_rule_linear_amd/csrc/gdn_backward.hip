@@ -878,12 +878,12 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         if constexpr (P::STAGE && !DONLY)
             dma_ck_blocks<DK, DV, P::NW>(ck, smem + P::ST_C, w, tid0 & 63);
         const floatx4 vv = prep<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0, L, tid, col0);
-        // the next sub-chunk's inputs, after prep's wait for the checkpoint
-        // (vector-memory counts complete in issue order, so anything issued
-        // before that wait would have been waited for with it); the previous
-        // sub-chunk's outputs are stored later, in the value-column steps
-        if constexpr (P::STAGE)
-            if (c > 0) dma_inputs<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0 - CB, sub_len(c - 1), w, tid0 & 63);
+        // (the previous sub-chunk's outputs are stored in the value-column steps
+        // and the next sub-chunk's inputs copied after the dS update, both after
+        // prep's wait for the checkpoint: vector-memory counts complete in issue
+        // order, so anything issued before that wait would have been waited for
+        // with it; spread over the iteration, the stores and copies do not queue
+        // behind one another)
         floatx4 kk = zero4();
         if (w == 0) kk = gram_inverse<TI, DK, DV, true, DV / 16, DONLY>(smem, lane);
 
@@ -996,6 +996,9 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
                 dS[rt] = *reinterpret_cast<const floatx4*>(sEM + 16 * rt + 4 * g) * x;
             }
         }
+        // the next sub-chunk's inputs (every staged row was read by prep)
+        if constexpr (P::STAGE)
+            if (c > 0) dma_inputs<TI, DK, DV, true, DV / 16, DONLY>(a, smem, h, t0 - CB, sub_len(c - 1), w, tid0 & 63);
         if constexpr (DONLY) continue;
         lds_barrier();
 
