@@ -161,7 +161,7 @@ struct BCfg {
     static constexpr int RT = DK / 16;                      // 16-row tiles of d_k
     static constexpr int TPW = (RT + NW - 1) / NW;          // key-channel tiles per wave
     static constexpr int UNR = KW == 8 ? 8 : 4;             // unroll of the contraction loops
-    static constexpr int UNR4 = KW == 8 ? 4 : 4;            // ... of the key-channel outputs' pass over d_v
+    static constexpr int UNR4 = 4;                          // ... of the key-channel outputs' pass over d_v
     static constexpr int SK = DK + 16 / ES, SV = DV + 16 / ES;
     static constexpr int B_NK = CB * SK * ES, B_TK = DK * CB * ES, B_NV = CB * SV * ES, B_FS = DK * SV * ES;
     static constexpr int OFF_KN = 0;                                   // k~ natural [16][SK]
@@ -536,10 +536,7 @@ __global__ __launch_bounds__(DV * 4, 1) void bwd_states_kernel(BArgs<TI> a) {
         const int L = (int)(se - t0 < CB ? se - t0 : CB);
         // lane-derived values are recomputed every iteration (opaque to the
         // compiler), so addresses built from them are not hoisted out of the
-        // loop and held in registers for its whole length; the copies and the
-        // deferred output stores take the plain lane values instead, so their
-        // per-lane offsets are formed once (32 more VGPRs, 80 fewer VALU
-        // instructions per iteration)
+        // loop and held in registers for its whole length
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -866,7 +863,10 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
         const TI* ck = slot(c);
         // lane-derived values are recomputed every iteration (opaque to the
         // compiler), so addresses built from them are not hoisted out of the
-        // loop and held in registers for its whole length
+        // loop and held in registers for its whole length; the copies and the
+        // deferred output stores take the plain lane values instead, so their
+        // per-lane offsets are formed once (32 more VGPRs, 80 fewer VALU
+        // instructions per iteration)
         int tid = tid0;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, r = lane & 15, g = lane >> 4;
