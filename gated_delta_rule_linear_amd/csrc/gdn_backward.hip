@@ -834,6 +834,7 @@ __global__ __launch_bounds__(DV * 4, DONLY ? DV / 32 : 1) void bwd_grad_kernel(B
             if (P::RT % P::NW != 0 && it >= P::RT) break;
             const uint32_t e = (uint32_t)r * H * DK + 16 * it + 4 * g;  // element offset of (token r, channel)
             if constexpr (P::KE) {
+                // (dq and dk: stored as whole rows above)
             } else if constexpr (P::ES == 2) {
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2b, F4::t(o_dq[j])), rq, e * 2, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2b, F4::t(o_dk[j])), rk, e * 2, 0, 0);
