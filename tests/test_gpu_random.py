@@ -48,7 +48,7 @@ def _forward_cases(count=60, seed=2026):
     return cases
 
 
-def _backward_cases(count=24, seed=2027):
+def _backward_cases(count=48, seed=2027):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(count):
